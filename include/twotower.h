@@ -1,0 +1,248 @@
+/*
+ * twotower.h -- C ABI of the block-diffusion denoise-step library for AMD MI355X (gfx950).
+ *
+ * The library computes the hot path of TwoTower block-wise autoregressive diffusion decoding:
+ * one denoise step of the trainable denoiser tower, in which the S positions of the current
+ * block attend, under one softmax, to the frozen context tower's KV cache of the same layer and
+ * to the block's own bidirectional KV, followed by confidence unmasking of the block logits.
+ * Sources: "Nemotron-TwoTower: Diffusion Language Modeling with Pretrained Autoregressive
+ * Context" explainer (gist.science), sections "Architektur", "Generierungsprozess" and
+ * "Training und Konditionierung"; "NVIDIA loest den zentralen Kompromiss moderner LLMs"
+ * (gotburnout.io), section "2. Denoiser Tower"; dgnews.ru report on Nemotron-Labs-TwoTower,
+ * architecture and test-results sections.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers unless a field says "host". Arrays of pointers in
+ *   tt_denoise_step_args are host arrays holding device pointers.
+ * - The caller owns every buffer. The library never allocates or frees device memory and keeps
+ *   no pointer after returning. Buffers must stay alive until the stream work completes.
+ * - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null stream). No call
+ *   synchronizes with the host.
+ * - Workspace protocol: call with ws == NULL to have *ws_bytes set to the required size (nothing
+ *   is launched, TT_OK is returned). Then call with ws pointing to at least *ws_bytes bytes of
+ *   device memory (256-byte aligned). A smaller *ws_bytes returns TT_ENOSPACE and sets
+ *   *ws_bytes to the required size. The workspace content on entry does not matter.
+ * - Errors are return codes only; the library never prints or aborts. Every argument check runs
+ *   on the host before anything is launched, so an error leaves all outputs untouched.
+ *   TT_EHIP means a HIP launch failed; asynchronous device faults surface at the caller's next
+ *   synchronization.
+ * - Results are deterministic: fixed reduction order, no floating-point atomics.
+ * - Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef TWOTOWER_H
+#define TWOTOWER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TWOTOWER_ABI_VERSION 1
+
+typedef enum {
+  TT_OK = 0,
+  TT_EINVAL = 1,   /* invalid argument: null/misaligned pointer, negative or inconsistent size */
+  TT_ENOTSUP = 2,  /* valid but unsupported shape or dtype combination */
+  TT_ENOSPACE = 3, /* workspace too small; *ws_bytes holds the required size */
+  TT_EHIP = 4      /* a HIP runtime call or kernel launch failed */
+} tt_status;
+
+typedef enum { TT_FP32 = 0, TT_BF16 = 1 } tt_dtype;
+
+/*
+ * Block attention of the denoiser at one layer (twotower_block_attn).
+ *
+ * Definition (explainer, "Architektur" / "Generierungsprozess"; gotburnout.io, "2. Denoiser
+ * Tower"): for every sequence b, query head h, block position i, with KV head
+ * g = h / (num_q_heads / num_kv_heads), the keys are the context rows 0..ctx_lens[b]-1 of KV head
+ * g followed by the S block rows of KV head g, and
+ *     s_j = scale * <q[b,i,h,:], key_j>,  m = max_j s_j,  w_j = exp(s_j - m),
+ *     out[b,i,h,:] = sum_j w_j value_j / sum_j w_j,   lse[b,h,i] = m + ln(sum_j w_j).
+ * No mask: the context holds only tokens before the block (causal across blocks); inside the
+ * block every query sees every block key, its own position included.
+ *
+ * Layouts (elements of `dtype`, innermost last, all contiguous):
+ *   q        [batch, S, num_q_heads, head_dim]
+ *   k_pages  [num_pages, num_kv_heads, page_size, head_dim]     token-major pages
+ *   v_pages  [num_pages, num_kv_heads, head_dim, page_size]     dim-major pages
+ *   block_table [batch, max_pages_per_seq] int32: context row t of sequence b is in page
+ *            block_table[b, t / page_size] at offset t % page_size
+ *   ctx_lens [batch] int32, 0 <= ctx_lens[b] <= max_ctx_len
+ *   k_blk    [batch, num_kv_heads, S, head_dim]
+ *   v_blk    [batch, num_kv_heads, head_dim, S]                 dim-major, like v_pages
+ *   out      [batch, S, num_q_heads, head_dim] in `out_dtype`
+ *   lse      [batch, num_q_heads, S] fp32, natural log; optional (NULL = not written)
+ * A contiguous cache is the case page_size >= max_ctx_len, block_table[b] = {b}.
+ *
+ * Supported: dtype TT_BF16 (bf16 MFMA, fp32 softmax and accumulation, probabilities rounded to
+ * bf16 for the PV product) or TT_FP32 (fp32 throughout); out_dtype TT_FP32, or equal to dtype.
+ * head_dim in {64, 128}; 1 <= S <= 64; num_q_heads % num_kv_heads == 0; page_size a positive
+ * multiple of 64; max_ctx_len <= max_pages_per_seq * page_size. Pointers 16-byte aligned.
+ * Unsupported shapes return TT_ENOTSUP.
+ *
+ * Device-side checks: a sequence whose ctx_lens[b] lies outside [0, max_ctx_len], or whose
+ * needed block_table entries lie outside [0, num_pages), gets NaN in all its outputs (nothing out
+ * of bounds is read). Page slots past ctx_lens[b] are never used, so they may hold anything.
+ *
+ * num_splits: number of context partitions per (sequence, KV head) at max_ctx_len (0 = chosen
+ * by the library to fill the GPU). Partitions are merged exactly with their log-sum-exp weights;
+ * the result depends on num_splits only through floating-point rounding.
+ */
+typedef struct {
+  int32_t batch, S, num_q_heads, num_kv_heads, head_dim;
+  int32_t dtype;       /* tt_dtype of q, k_pages, v_pages, k_blk, v_blk */
+  int32_t out_dtype;   /* tt_dtype of out */
+  float scale;         /* softmax scale, e.g. 1/sqrt(head_dim) */
+  const void *q;
+  const void *k_pages;
+  const void *v_pages;
+  int32_t num_pages, page_size, max_pages_per_seq, max_ctx_len;
+  const int32_t *block_table;
+  const int32_t *ctx_lens;
+  const void *k_blk;
+  const void *v_blk;
+  void *out;
+  float *lse;
+  int32_t num_splits;
+  int32_t reserved0;
+} tt_block_attn_args;
+
+/*
+ * Confidence unmasking of one step (twotower_unmask).
+ *
+ * Definition (explainer, "Training und Konditionierung", sampling paragraph; dgnews.ru,
+ * test-results section): every still-masked position is predicted in parallel; positions whose
+ * confidence is above `threshold` are committed, the others stay masked. For each b and each i
+ * with masked[b,i] != 0: token = the lowest index of the row maximum of logits[b,i,:],
+ * confidence = 1 / sum_j exp(logits[b,i,j] - max) (the largest softmax probability), computed in
+ * fp32. Position i is committed iff confidence > threshold (strict). If min_commit != 0 and no
+ * masked position of sequence b is committed, the masked position with the largest confidence is
+ * committed (lowest i on ties). If commit_all != 0 every masked position is committed.
+ * Committing sets tokens[b,i] = token and masked[b,i] = 0. Positions with masked[b,i] == 0 are
+ * neither read nor written (their logits rows are never loaded).
+ *
+ * Layouts: logits fp32, row (b, i) starts at element (b*S + i) * ld, vocab contiguous elements;
+ *   masked uint8 [batch, S] (in/out); tokens int32 [batch, S] (in/out);
+ *   confidence fp32 [batch, S] (optional out, written for positions masked on entry);
+ *   n_committed int32 [batch] (optional out).
+ * Supported: 1 <= S <= 64, 1 <= vocab < 2^31, ld >= vocab. Logits must be finite.
+ */
+typedef struct {
+  int32_t batch, S, vocab;
+  int32_t reserved0;
+  int64_t ld;
+  const float *logits;
+  uint8_t *masked;
+  int32_t *tokens;
+  float *confidence;
+  int32_t *n_committed;
+  float threshold;
+  int32_t min_commit;
+  int32_t commit_all;
+  int32_t reserved1;
+} tt_unmask_args;
+
+/*
+ * Dense projections of the synthetic attention-only denoiser (twotower_qkv_projection,
+ * twotower_out_projection, twotower_lm_head). The pages give no layer shapes; the model is a
+ * residual stream H [rows = batch*S, hidden] (bf16) with, per attention layer,
+ *   [Q | K_blk | V_blk] = H W_qkv^T,  W_qkv bf16 [(Hq + 2*Hkv)*head_dim, hidden]
+ *   H <- H + O W_o^T,                  W_o   bf16 [hidden, Hq*head_dim]
+ * and logits = H W_lm^T,               W_lm  bf16 [vocab, hidden], fp32 logits [rows, vocab].
+ * Weights are stored [out_features, in_features]. The block's own KV is rewritten every step
+ * because the block changes (explainer, "Generierungsprozess").
+ * Products accumulate in fp32 and are rounded once to the output type.
+ */
+typedef struct {
+  int32_t batch, S, hidden, num_q_heads, num_kv_heads, head_dim;
+  const void *h;        /* bf16 [batch, S, hidden] */
+  const void *w_qkv;    /* bf16 [(Hq + 2*Hkv)*head_dim, hidden] */
+  void *q;              /* bf16 [batch, S, Hq, head_dim] */
+  void *k_blk;          /* bf16 [batch, Hkv, S, head_dim] */
+  void *v_blk;          /* bf16 [batch, Hkv, head_dim, S] */
+} tt_qkv_args;
+
+typedef struct {
+  int32_t rows, hidden, in_features;
+  int32_t reserved0;
+  const void *h_in;     /* bf16 [rows, hidden] residual input (may equal h_out) */
+  const void *o;        /* bf16 [rows, in_features] attention output */
+  const void *w_o;      /* bf16 [hidden, in_features] */
+  void *h_out;          /* bf16 [rows, hidden] = h_in + o W_o^T */
+} tt_out_proj_args;
+
+typedef struct {
+  int32_t rows, hidden, vocab;
+  int32_t reserved0;
+  int64_t ld;           /* row stride of logits in elements, >= vocab, multiple of 4 */
+  const void *h;        /* bf16 [rows, hidden] */
+  const void *w_lm;     /* bf16 [vocab, hidden] */
+  float *logits;        /* fp32 [rows, ld] */
+} tt_lm_head_args;
+
+/*
+ * One denoise step of the synthetic denoiser (twotower_denoise_step): for each layer l,
+ * twotower_qkv_projection (rewrites k_blk[l], v_blk[l]) -> twotower_block_attn over
+ * (k_pages[l], v_pages[l]) and the block KV of layer l (layer-aligned: denoiser layer l reads the
+ * context tower's layer l, gotburnout.io "2. Denoiser Tower") -> twotower_out_projection; then
+ * twotower_lm_head -> twotower_unmask. Layer 0 reads h_in; the residual stream is kept in h_work.
+ * All layers share batch, S, heads, head_dim, block_table, ctx_lens and page geometry (taken from
+ * `attn`; attn.q/k_pages/v_pages/k_blk/v_blk/out/lse are ignored). The context caches are only
+ * read. Sequences with no masked position left still run the dense math (their results are
+ * discarded by the unmasking, which reads no committed row).
+ *
+ * timing_events: optional host array of 2*num_layers hipEvent_t; if not NULL, events[2l] and
+ * events[2l+1] are recorded on `stream` immediately before and after the main attention kernel
+ * of layer l (profiling hook, NULL in normal use).
+ */
+typedef struct {
+  int32_t num_layers, hidden, vocab;
+  int32_t reserved0;
+  tt_block_attn_args attn;
+  const void *const *k_pages;   /* host array [num_layers] of device pointers */
+  const void *const *v_pages;
+  const void *const *w_qkv;
+  const void *const *w_o;
+  void *const *k_blk;           /* host array [num_layers]: block KV, rewritten every step */
+  void *const *v_blk;
+  const void *w_lm;
+  const void *h_in;             /* bf16 [batch, S, hidden], read only */
+  void *h_work;                 /* bf16 [batch, S, hidden], residual stream after the step */
+  void *q;                      /* bf16 [batch, S, Hq, head_dim] scratch */
+  void *attn_out;               /* bf16 [batch, S, Hq, head_dim] scratch */
+  float *logits;                /* fp32 [batch, S, logits_ld] */
+  int64_t logits_ld;
+  tt_unmask_args unmask;        /* masked/tokens/confidence/n_committed/threshold/flags used;
+                                   batch/S/vocab/ld/logits are taken from the step */
+  void *const *timing_events;
+} tt_denoise_step_args;
+
+tt_status twotower_block_attn(const tt_block_attn_args *args, void *ws, size_t *ws_bytes,
+                              void *stream);
+tt_status twotower_unmask(const tt_unmask_args *args, void *ws, size_t *ws_bytes, void *stream);
+tt_status twotower_qkv_projection(const tt_qkv_args *args, void *ws, size_t *ws_bytes,
+                                  void *stream);
+tt_status twotower_out_projection(const tt_out_proj_args *args, void *ws, size_t *ws_bytes,
+                                  void *stream);
+tt_status twotower_lm_head(const tt_lm_head_args *args, void *ws, size_t *ws_bytes, void *stream);
+tt_status twotower_denoise_step(const tt_denoise_step_args *args, void *ws, size_t *ws_bytes,
+                                void *stream);
+
+/* Static string for a status code ("TT_OK", ...); never NULL. */
+const char *twotower_status_string(int32_t status);
+/* TWOTOWER_ABI_VERSION of the built library. */
+int32_t twotower_abi_version(void);
+/* sizeof of the argument structs, for bindings to check their mirrors:
+ * 0 tt_block_attn_args, 1 tt_unmask_args, 2 tt_qkv_args, 3 tt_out_proj_args,
+ * 4 tt_lm_head_args, 5 tt_denoise_step_args; -1 for an unknown index. */
+int64_t twotower_struct_size(int32_t which);
+/* Byte offset of field `field` (0-based declaration order) in struct `which`; -1 if unknown. */
+int64_t twotower_struct_offset(int32_t which, int32_t field);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TWOTOWER_H */

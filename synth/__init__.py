@@ -106,7 +106,7 @@ def attn_case(seed: int, *, B: int, S: int, Hq: int, Hkv: int, D: int, ctx_lens,
     """Q/K/V ~ N(0, 1) in the paged layout.
 
     ``ctx_lens``: sequence of B context lengths. ``page_size`` None means one page per sequence
-    (contiguous context, page_size = max length rounded up to 16). With ``shuffle_pages`` the
+    (contiguous context, page_size = max length rounded up to a multiple of 64). With ``shuffle_pages`` the
     pages of all sequences sit in the pool in a random order. ``spare_frac`` adds unused pool
     pages; ``nan_poison`` fills unused pages and the tail of every last page with NaN.
     ``outlier_frac`` of the context positions, drawn independently per KV head, get their whole
@@ -116,7 +116,7 @@ def attn_case(seed: int, *, B: int, S: int, Hq: int, Hkv: int, D: int, ctx_lens,
     ctx_lens = np.asarray(ctx_lens, dtype=np.int32).reshape(B)
     Lmax = int(ctx_lens.max()) if B else 0
     if page_size is None:
-        page_size = max(16, -(-Lmax // 16) * 16)
+        page_size = max(64, -(-Lmax // 64) * 64)
     pages_per_seq = [-(-int(L) // page_size) for L in ctx_lens]
     n_used = sum(pages_per_seq)
     n_pool = max(1, n_used + int(math.ceil(spare_frac * n_used)))

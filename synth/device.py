@@ -1,0 +1,67 @@
+"""Seeded on-device inputs for the 6-layer, 32K-context block loop (bulk data too large to
+generate on the host). Distributions and layouts only; no method arithmetic.
+
+Model (one reading, stated with the library): residual stream H [B, S, hidden]; per layer
+W_qkv [(Hq + 2 Hkv) D, hidden] and W_o [hidden, Hq D] ~ N(0, 1/fan_in); lm-head W_lm
+[V, hidden] ~ N(0, 1/hidden); context KV per layer ~ N(0, 1) as a contiguous cache (one page per
+sequence: k [B, Hkv, L, D], v [B, Hkv, D, L]); a fresh H ~ N(0, 1) per denoise step.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+
+@dataclasses.dataclass
+class LoopModel:
+    B: int
+    S: int
+    L: int
+    layers: int
+    Hq: int
+    Hkv: int
+    D: int
+    hidden: int
+    vocab: int
+    T: int
+    k_pages: list
+    v_pages: list
+    w_qkv: list
+    w_o: list
+    w_lm: torch.Tensor
+    block_table: torch.Tensor
+    ctx_lens: torch.Tensor
+    h_steps: list
+
+
+def _randn(shape, gen, device, std=1.0):
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to(torch.bfloat16)
+
+
+def loop_model(seed: int = 5, *, B=8, S=16, L=32768, layers=6, Hq=32, Hkv=2, D=128, hidden=2048,
+               vocab=131072, T=16, device="cuda") -> LoopModel:
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    Lp = max(64, -(-L // 64) * 64)
+    k_pages, v_pages, w_qkv, w_o = [], [], [], []
+    for _ in range(layers):
+        k_pages.append(_randn((B, Hkv, Lp, D), g, dev))
+        v_pages.append(_randn((B, Hkv, D, Lp), g, dev))
+        w_qkv.append(_randn(((Hq + 2 * Hkv) * D, hidden), g, dev, 1.0 / math.sqrt(hidden)))
+        w_o.append(_randn((hidden, Hq * D), g, dev, 1.0 / math.sqrt(Hq * D)))
+    w_lm = _randn((vocab, hidden), g, dev, 1.0 / math.sqrt(hidden))
+    h_steps = []
+    for t in range(T):
+        gt = torch.Generator(device=dev)
+        gt.manual_seed(seed * 1000 + t)
+        h_steps.append(_randn((B, S, hidden), gt, dev))
+    block_table = torch.arange(B, dtype=torch.int32, device=dev).view(B, 1)
+    ctx_lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    return LoopModel(B, S, L, layers, Hq, Hkv, D, hidden, vocab, T, k_pages, v_pages, w_qkv, w_o,
+                     w_lm, block_table, ctx_lens, h_steps)

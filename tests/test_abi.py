@@ -1,0 +1,168 @@
+"""The C ABI without a GPU: symbols, struct layouts, host-side validation and workspace sizing.
+
+Every call here either fails validation or is a workspace-size query (ws == NULL), both of which
+return before any HIP call, so nothing runs on a device.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from two_tower_cross_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "twotower.h")
+
+FAKE = 0x10000  # a 256-byte aligned fake device address; never dereferenced by these calls
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(twotower_\w+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert "twotower_block_attn" in names and "twotower_unmask" in names
+    assert "twotower_denoise_step" in names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_struct_layouts_match_the_header(L):
+    for i, st in enumerate(_lib.STRUCTS):
+        assert C.sizeof(st) == L.twotower_struct_size(i), st.__name__
+        for j, (name, _) in enumerate(st._fields_):
+            assert getattr(st, name).offset == L.twotower_struct_offset(i, j), (st.__name__, name)
+        assert L.twotower_struct_offset(i, len(st._fields_)) == -1
+    assert L.twotower_struct_size(99) == -1
+
+
+def test_status_strings(L):
+    assert [_lib.status_string(s) for s in range(5)] == [
+        "TT_OK", "TT_EINVAL", "TT_ENOTSUP", "TT_ENOSPACE", "TT_EHIP"]
+    assert _lib.status_string(1234) == "TT_UNKNOWN"
+
+
+def attn_args(**over):
+    a = _lib.BlockAttnArgs()
+    vals = dict(batch=8, S=16, num_q_heads=32, num_kv_heads=2, head_dim=128, dtype=_lib.TT_BF16,
+                out_dtype=_lib.TT_FP32, scale=128 ** -0.5, q=FAKE, k_pages=FAKE, v_pages=FAKE,
+                num_pages=8, page_size=32768, max_pages_per_seq=1, max_ctx_len=32768,
+                block_table=FAKE, ctx_lens=FAKE, k_blk=FAKE, v_blk=FAKE, out=FAKE, lse=None,
+                num_splits=0)
+    vals.update(over)
+    for k, v in vals.items():
+        setattr(a, k, v)
+    return a
+
+
+def query(name, a):
+    n = C.c_size_t(12345)
+    st = _lib.call(name, a, None, n, None)
+    return st, n.value
+
+
+def test_attention_workspace_query_and_plan():
+    st, n = query("twotower_block_attn", attn_args())
+    assert st == _lib.TT_OK
+    # auto plan at B*Hkv = 16 units: 16 partitions of 2048 tokens, 256-row fp32 partials + lse
+    items = 8 * 2 * 16
+    expect = -(-items * 256 * 128 * 4 // 256) * 256 + -(-items * 256 * 4 // 256) * 256
+    assert n == expect
+    # one partition needs no workspace
+    st, n = query("twotower_block_attn", attn_args(num_splits=1))
+    assert st == _lib.TT_OK and n == 0
+    st, n = query("twotower_block_attn", attn_args(dtype=_lib.TT_FP32, out_dtype=_lib.TT_FP32))
+    assert st == _lib.TT_OK and n == 0
+
+
+def test_attention_workspace_too_small_reports_size():
+    a = attn_args()
+    st, need = query("twotower_block_attn", a)
+    n = C.c_size_t(need - 1)
+    st = _lib.call("twotower_block_attn", a, C.c_void_p(FAKE), n, None)
+    assert st == _lib.TT_ENOSPACE and n.value == need
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(head_dim=96), _lib.TT_ENOTSUP),
+    (dict(S=65), _lib.TT_ENOTSUP),
+    (dict(page_size=100, max_ctx_len=100), _lib.TT_ENOTSUP),
+    (dict(out_dtype=_lib.TT_BF16, dtype=_lib.TT_FP32), _lib.TT_ENOTSUP),
+    (dict(num_q_heads=31), _lib.TT_EINVAL),
+    (dict(S=0), _lib.TT_EINVAL),
+    (dict(scale=-1.0), _lib.TT_EINVAL),
+    (dict(scale=float("nan")), _lib.TT_EINVAL),
+    (dict(max_ctx_len=32769), _lib.TT_EINVAL),
+    (dict(q=FAKE + 8), _lib.TT_EINVAL),
+    (dict(v_pages=None), _lib.TT_EINVAL),
+    (dict(ctx_lens=None), _lib.TT_EINVAL),
+    (dict(num_splits=-1), _lib.TT_EINVAL),
+    (dict(dtype=7), _lib.TT_EINVAL),
+])
+def test_attention_argument_errors(over, code):
+    st, _ = query("twotower_block_attn", attn_args(**over))
+    assert st == code, _lib.status_string(st)
+
+
+def unmask_args(**over):
+    a = _lib.UnmaskArgs()
+    vals = dict(batch=8, S=16, vocab=131072, ld=131072, logits=FAKE, masked=FAKE, tokens=FAKE,
+                confidence=None, n_committed=None, threshold=0.9, min_commit=1, commit_all=0)
+    vals.update(over)
+    for k, v in vals.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_unmask_workspace_and_errors():
+    st, n = query("twotower_unmask", unmask_args())
+    assert st == _lib.TT_OK and n == 8 * 16 * 16 * 16
+    for over, code in [(dict(S=65), _lib.TT_ENOTSUP), (dict(ld=100), _lib.TT_EINVAL),
+                       (dict(threshold=float("nan")), _lib.TT_EINVAL),
+                       (dict(tokens=None), _lib.TT_EINVAL), (dict(vocab=0), _lib.TT_EINVAL),
+                       (dict(tokens=FAKE + 2), _lib.TT_EINVAL)]:
+        assert query("twotower_unmask", unmask_args(**over))[0] == code, over
+
+
+def test_projection_queries_and_errors():
+    q = _lib.QkvArgs(8, 16, 2048, 32, 2, 128, FAKE, FAKE, FAKE, FAKE, FAKE)
+    st, n = query("twotower_qkv_projection", q)
+    assert st == _lib.TT_OK and n % 256 == 0
+    q.hidden = 2044
+    assert query("twotower_qkv_projection", q)[0] == _lib.TT_ENOTSUP
+    o = _lib.OutProjArgs(128, 2048, 4096, 0, FAKE, FAKE, FAKE, FAKE)
+    assert query("twotower_out_projection", o)[0] == _lib.TT_OK
+    o.o = FAKE + 4
+    assert query("twotower_out_projection", o)[0] == _lib.TT_EINVAL
+    lm = _lib.LmHeadArgs(128, 2048, 131072, 0, 131072, FAKE, FAKE, FAKE)
+    st, n = query("twotower_lm_head", lm)
+    assert st == _lib.TT_OK and n == 0   # 2048 feature tiles fill the GPU without K partitions
+    lm.ld = 131070
+    assert query("twotower_lm_head", lm)[0] == _lib.TT_EINVAL
+
+
+def test_denoise_step_validation():
+    a = _lib.DenoiseStepArgs()
+    a.num_layers, a.hidden, a.vocab = 6, 2048, 131072
+    a.attn = attn_args()
+    assert query("twotower_denoise_step", a)[0] == _lib.TT_EINVAL   # layer arrays missing
+    arr = (C.c_void_p * 6)(*([FAKE] * 6))
+    vpp = C.POINTER(C.c_void_p)
+    for f in ("k_pages", "v_pages", "w_qkv", "w_o", "k_blk", "v_blk"):
+        setattr(a, f, C.cast(arr, vpp))
+    for f in ("w_lm", "h_in", "h_work", "q", "attn_out", "logits"):
+        setattr(a, f, FAKE)
+    a.logits_ld = 131072
+    a.unmask = unmask_args()
+    st, n = query("twotower_denoise_step", a)
+    assert st == _lib.TT_OK and n > 0
+    a.attn = attn_args(dtype=_lib.TT_FP32)
+    assert query("twotower_denoise_step", a)[0] == _lib.TT_ENOTSUP

@@ -1,0 +1,217 @@
+"""GPU parity of twotower_block_attn against the fp64 oracle (element by element).
+
+Definition checked: the block queries attend, under one softmax, to the context tower's same-layer
+KV rows and the block's own KV rows (Nemotron-TwoTower explainer, "Architektur" /
+"Generierungsprozess"). Tolerances: max-abs 1e-5 for fp32 inputs, 2e-2 for bf16 inputs (fp32
+output; bf16 output is compared with the oracle rounded to bf16 at the same 2e-2).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import two_tower_cross_amd as tt
+from oracle import attention as oattn
+from gpu_util import DEV, TOL_BF16, TOL_FP32, dev_case, gpu_attn, max_abs, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def check(case, out, lse, tol, lse_tol=None):
+    ref, ref_lse = oattn.block_attention_case(case)
+    err = max_abs(out, ref)
+    assert err <= tol, f"max-abs {err:.3g} > {tol}"
+    if lse is not None:
+        lerr = max_abs(lse, ref_lse)
+        assert lerr <= (lse_tol or tol), f"lse max-abs {lerr:.3g}"
+    return ref
+
+
+# ------------------------------------------------------------------ the workload configurations
+
+def test_tiny_fp32():
+    case = synth.config_attn("tiny_fp32")
+    out, lse = gpu_attn(case)
+    check(case, out, lse, TOL_FP32)
+
+
+def test_tiny_fp32_ragged_and_empty_context():
+    for L in (0, 1, 37, 255):
+        case = synth.config_attn("tiny_fp32", ctx_len=L)
+        out, lse = gpu_attn(case)
+        check(case, out, lse, TOL_FP32)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3, 16, 64])
+def test_ctx4k_bf16_splits(splits):
+    case = synth.config_attn("ctx4k_bf16")
+    out, lse = gpu_attn(case, num_splits=splits)
+    check(case, out, lse, TOL_BF16)
+
+
+def test_ctx4k_bf16_output_in_bf16():
+    case = synth.config_attn("ctx4k_bf16")
+    out, _ = gpu_attn(case, out_dtype=torch.bfloat16)
+    ref, _ = oattn.block_attention_case(case)
+    ref16 = torch.from_numpy(ref).to(torch.bfloat16).double().numpy()
+    assert max_abs(out, ref16) <= TOL_BF16
+
+
+def test_ragged_paged_batch():
+    case = synth.config_attn("ragged32_paged")
+    assert np.isnan(case.k_pages).any()          # unused pages and page tails are poisoned
+    for splits in (0, 8):
+        out, lse = gpu_attn(case, num_splits=splits)
+        assert not np.isnan(out).any()
+        check(case, out, lse, TOL_BF16)
+
+
+@pytest.mark.parametrize("splits", [0, 64, 128, 256])
+def test_long_context_131072(splits):
+    case = synth.config_attn("long128k")
+    out, lse = gpu_attn(case, num_splits=splits)
+    check(case, out, lse, TOL_BF16)
+
+
+def test_loop32k_layer_shape():
+    case = synth.config_attn("loop32k_layer")
+    out, lse = gpu_attn(case, out_dtype=torch.float32)
+    check(case, out, lse, TOL_BF16)
+
+
+# ------------------------------------------------------------------------ closed forms on the GPU
+
+def test_identical_keys_give_mean_of_values():
+    case = synth.attn_case(50, B=2, S=16, Hq=32, Hkv=2, D=128, ctx_lens=[700, 64], page_size=256,
+                           dtype="bf16")
+    case.k_pages[...] = 0.5
+    case.k_blk[...] = 0.5
+    out, lse = gpu_attn(case)
+    ref = check(case, out, lse, TOL_BF16)
+    # every weight is exactly 1 on the GPU too: the result is the plain mean of the values
+    for b in range(2):
+        n = int(case.ctx_lens[b]) + 16
+        s = case.scale * 0.5 * case.q[b].astype(np.float64).sum(-1)        # [S, Hq]
+        np.testing.assert_allclose(lse[b], math.log(n) + s.T, atol=1e-4)
+
+
+def test_zero_query_gives_mean_and_log_count():
+    case = synth.attn_case(51, B=1, S=16, Hq=16, Hkv=1, D=64, ctx_lens=[1000], page_size=1024,
+                           dtype="bf16")
+    case.q[...] = 0.0
+    out, lse = gpu_attn(case, num_splits=3)
+    check(case, out, lse, TOL_BF16)
+    np.testing.assert_allclose(lse, math.log(1016), atol=1e-5)
+
+
+def test_single_dominant_key_returns_its_value():
+    case = synth.attn_case(52, B=1, S=16, Hq=2, Hkv=1, D=128, ctx_lens=[512], page_size=512,
+                           dtype="bf16")
+    # key 300 is 8 * q-direction with a margin of >= 40 in score over every other key
+    qdir = np.zeros(128, np.float32); qdir[0] = 1.0
+    case.q[...] = 0.0
+    case.q[..., 0] = 8.0
+    case.k_pages[...] = synth.round_to_bf16(case.k_pages * 0.01)
+    case.k_blk[...] = synth.round_to_bf16(case.k_blk * 0.01)
+    case.k_pages[case.block_table[0, 0], 0, 300, :] = 0.0
+    case.k_pages[case.block_table[0, 0], 0, 300, 0] = 64.0
+    out, lse = gpu_attn(case)
+    v = case.v_pages[case.block_table[0, 0], 0, :, 300]
+    for h in range(2):
+        np.testing.assert_allclose(out[0, :, h, :], np.broadcast_to(v, (16, 128)), atol=1e-5)
+
+
+def test_page_order_is_bit_invariant_and_block_order_within_tolerance():
+    case = synth.attn_case(53, B=3, S=16, Hq=32, Hkv=2, D=128, ctx_lens=[1000, 3000, 64],
+                           page_size=256, dtype="bf16", spare_frac=0.5)
+    d = dev_case(case)
+    ref, ref_lse = gpu_attn(case, d)
+    g = synth.rng(54)
+    P = case.k_pages.shape[0]
+    perm = g.permutation(P)
+    inv = np.argsort(perm)
+    d2 = dict(d, k_pages=d["k_pages"][torch.from_numpy(perm).to(DEV)].contiguous(),
+              v_pages=d["v_pages"][torch.from_numpy(perm).to(DEV)].contiguous(),
+              block_table=torch.from_numpy(inv[case.block_table].astype(np.int32)).to(DEV))
+    out, lse = gpu_attn(case, d2)
+    assert np.array_equal(out, ref) and np.array_equal(lse, ref_lse)
+    bp = torch.from_numpy(g.permutation(16)).to(DEV)
+    d3 = dict(d, k_blk=d["k_blk"][:, :, bp].contiguous(), v_blk=d["v_blk"][:, :, :, bp].contiguous())
+    out, _ = gpu_attn(case, d3)
+    assert max_abs(out, ref) <= 2e-3
+
+
+def test_split_count_only_changes_rounding():
+    case = synth.attn_case(55, B=2, S=16, Hq=32, Hkv=2, D=128, ctx_lens=[5000, 2000],
+                           page_size=256, dtype="bf16")
+    outs = [gpu_attn(case, num_splits=s)[0] for s in (1, 2, 7, 20, 79)]
+    for o in outs[1:]:
+        assert max_abs(o, outs[0]) <= 2e-3
+
+
+# -------------------------------------------------------------------------------- shapes / edges
+
+@pytest.mark.parametrize("S,Hq,Hkv,D", [
+    (16, 4, 4, 128),    # MHA: 16 query rows per KV head, padded to one 32-row wavefront
+    (1, 8, 1, 128),     # a single block position
+    (5, 6, 2, 64),      # rows = 15, head_dim 64
+    (32, 32, 2, 128),   # 512 rows: two row groups per KV head
+    (64, 4, 1, 64),     # the largest block
+    (16, 16, 1, 64),
+])
+def test_shapes_bf16(S, Hq, Hkv, D):
+    case = synth.attn_case(60 + S, B=2, S=S, Hq=Hq, Hkv=Hkv, D=D, ctx_lens=[333, 1200],
+                           page_size=128, dtype="bf16")
+    for splits in (1, 0):
+        out, lse = gpu_attn(case, num_splits=splits)
+        check(case, out, lse, TOL_BF16)
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,D", [(16, 8, 2, 128), (3, 3, 1, 64)])
+def test_shapes_fp32(S, Hq, Hkv, D):
+    case = synth.attn_case(70 + S, B=2, S=S, Hq=Hq, Hkv=Hkv, D=D, ctx_lens=[300, 5],
+                           page_size=64, dtype="fp32")
+    out, lse = gpu_attn(case)
+    check(case, out, lse, TOL_FP32)
+
+
+def test_empty_context_and_tiny_tails():
+    case = synth.attn_case(80, B=4, S=16, Hq=32, Hkv=2, D=128, ctx_lens=[0, 1, 63, 65],
+                           page_size=64, dtype="bf16", nan_poison=True, spare_frac=1.0)
+    for splits in (0, 1, 2):
+        out, lse = gpu_attn(case, num_splits=splits, max_ctx_len=128)
+        check(case, out, lse, TOL_BF16)
+
+
+def test_bad_lengths_and_pages_give_nan_rows_only():
+    case = synth.attn_case(81, B=3, S=16, Hq=32, Hkv=2, D=128, ctx_lens=[500, 700, 900],
+                           page_size=256, dtype="bf16")
+    d = dev_case(case)
+    lens = d["ctx_lens"].clone()
+    lens[1] = 5000                        # above max_ctx_len
+    bt = d["block_table"].clone()
+    bt[2, 1] = 10_000                     # page index outside the pool
+    d.update(ctx_lens=lens, block_table=bt)
+    ref, _ = oattn.block_attention_case(case)
+    for splits in (1, 0):
+        out, lse = gpu_attn(case, d, num_splits=splits, max_ctx_len=1024)
+        assert np.isnan(out[1]).all() and np.isnan(out[2]).all() and np.isnan(lse[1:]).all()
+        assert max_abs(out[0], ref[0]) <= TOL_BF16
+
+
+def test_deterministic_and_outputs_stay_in_bounds():
+    case = synth.config_attn("ctx4k_bf16", ctx_len=3000)
+    d = dev_case(case)
+    guard = torch.full((2, 16 * 32 * 128 + 64), 7.0, dtype=torch.float32, device=DEV)
+    outs = []
+    for _ in range(3):
+        out = guard[0, 32:32 + 16 * 32 * 128].view(1, 16, 32, 128)
+        tt.block_attn(d["q"], d["k_pages"], d["v_pages"], d["block_table"], d["ctx_lens"],
+                      d["k_blk"], d["v_blk"], scale=case.scale, max_ctx_len=3000, out=out)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy().copy())
+        assert (guard[0, :32] == 7.0).all() and (guard[0, -32:] == 7.0).all()
+        assert (guard[1] == 7.0).all()
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])

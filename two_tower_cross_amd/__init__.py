@@ -1,0 +1,290 @@
+"""Thin PyTorch binding of ``libtwotower.so`` (MI355X denoise step of TwoTower block diffusion).
+
+Tensors supply device memory and torch's current stream supplies the HIP stream; every step of
+the computation runs in the library's hand-written HIP kernels. The functions here only check
+tensor metadata, build the C argument structs and size the workspace. If the shared library
+is missing, every call raises ``LibraryNotBuilt`` (there is no fallback).
+
+Layouts follow ``include/twotower.h``:
+q [B,S,Hq,D]; k_pages [P,Hkv,page,D]; v_pages [P,Hkv,D,page]; k_blk [B,Hkv,S,D];
+v_blk [B,Hkv,D,S]; block_table [B,max_pages] int32; ctx_lens [B] int32; logits [B,S,V] fp32.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+
+import torch
+
+from . import _lib
+from ._lib import LibraryNotBuilt, TwoTowerError, TT_BF16, TT_FP32  # noqa: F401
+
+__all__ = ["block_attn", "unmask", "qkv_projection", "out_projection", "lm_head", "DenoiseStep",
+           "LibraryNotBuilt", "TwoTowerError", "library_path"]
+
+
+def library_path() -> str:
+    _lib.lib()
+    return _lib.LIB_PATH
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TT_BF16
+    if t.dtype == torch.float32:
+        return TT_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _p(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, device, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _run(name: str, args, device) -> None:
+    n = C.c_size_t(0)
+    st = _lib.call(name, args, None, n, None)
+    if st != _lib.TT_OK:
+        raise TwoTowerError(name, st)
+    ws = torch.empty(n.value, dtype=torch.uint8, device=device) if n.value else None
+    st = _lib.call(name, args, _p(ws), n, _stream())
+    if st != _lib.TT_OK:
+        raise TwoTowerError(name, st)
+
+
+def _attn_struct(q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, out, lse, scale,
+                 max_ctx_len, num_splits):
+    B, S, Hq, D = q.shape
+    P, Hkv, page, _ = k_pages.shape
+    a = _lib.BlockAttnArgs()
+    a.batch, a.S, a.num_q_heads, a.num_kv_heads, a.head_dim = B, S, Hq, Hkv, D
+    a.dtype = _dt(q)
+    a.out_dtype = _dt(out) if out is not None else a.dtype
+    a.scale = float(scale)
+    a.q, a.k_pages, a.v_pages = _p(q), _p(k_pages), _p(v_pages)
+    a.num_pages, a.page_size = P, page
+    a.max_pages_per_seq = block_table.shape[1]
+    a.max_ctx_len = int(max_ctx_len)
+    a.block_table, a.ctx_lens = _p(block_table), _p(ctx_lens)
+    a.k_blk, a.v_blk = _p(k_blk), _p(v_blk)
+    a.out, a.lse = _p(out), _p(lse)
+    a.num_splits = int(num_splits)
+    return a
+
+
+def block_attn(q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, *, scale=None,
+               max_ctx_len=None, out_dtype=None, return_lse=False, num_splits=0, out=None):
+    """Denoiser block attention at one layer; returns ``out`` (and ``lse`` [B,Hq,S] fp32).
+
+    ``max_ctx_len`` bounds ctx_lens (used to plan the context partitions; default: the page
+    table's capacity). ``num_splits`` 0 lets the library choose the partition count.
+    """
+    dev = q.device
+    _check(q, "q", dev, ndim=4)
+    B, S, Hq, D = q.shape
+    _check(k_pages, "k_pages", dev, q.dtype, 4)
+    _check(v_pages, "v_pages", dev, q.dtype, 4)
+    _check(k_blk, "k_blk", dev, q.dtype, 4)
+    _check(v_blk, "v_blk", dev, q.dtype, 4)
+    _check(block_table, "block_table", dev, torch.int32, 2)
+    _check(ctx_lens, "ctx_lens", dev, torch.int32, 1)
+    P, Hkv, page, Dk = k_pages.shape
+    if (Dk != D or tuple(v_pages.shape) != (P, Hkv, D, page)
+            or tuple(k_blk.shape) != (B, Hkv, S, D) or tuple(v_blk.shape) != (B, Hkv, D, S)
+            or block_table.shape[0] != B or ctx_lens.shape[0] != B):
+        raise ValueError("inconsistent attention shapes")
+    if out is None:
+        od = q.dtype if out_dtype is None else out_dtype
+        out = torch.empty((B, S, Hq, D), dtype=od, device=dev)
+    else:
+        _check(out, "out", dev, None, 4)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev) if return_lse else None
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_ctx_len is None:
+        max_ctx_len = block_table.shape[1] * page
+    a = _attn_struct(q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, out, lse, scale,
+                     max_ctx_len, num_splits)
+    _run("twotower_block_attn", a, dev)
+    return (out, lse) if return_lse else out
+
+
+def unmask(logits, masked, tokens, threshold, *, min_commit=False, commit_all=False):
+    """Confidence unmasking; updates ``masked`` and ``tokens`` in place.
+
+    Returns (confidence [B,S] fp32, written where masked on entry; n_committed [B] int32).
+    """
+    dev = logits.device
+    _check(masked, "masked", dev, torch.uint8, 2)
+    _check(tokens, "tokens", dev, torch.int32, 2)
+    if logits.dtype != torch.float32 or logits.dim() != 3 or logits.stride(2) != 1:
+        raise ValueError("logits must be fp32 [B,S,V] with unit vocab stride")
+    B, S, V = logits.shape
+    if logits.stride(0) != S * logits.stride(1):
+        raise ValueError("logits rows must be evenly strided")
+    conf = torch.full((B, S), float("nan"), dtype=torch.float32, device=dev)
+    ncom = torch.zeros((B,), dtype=torch.int32, device=dev)
+    a = _lib.UnmaskArgs()
+    a.batch, a.S, a.vocab, a.ld = B, S, V, logits.stride(1)
+    a.logits, a.masked, a.tokens = _p(logits), _p(masked), _p(tokens)
+    a.confidence, a.n_committed = _p(conf), _p(ncom)
+    a.threshold = float(threshold)
+    a.min_commit, a.commit_all = int(bool(min_commit)), int(bool(commit_all))
+    _run("twotower_unmask", a, dev)
+    return conf, ncom
+
+
+def qkv_projection(h, w_qkv, num_q_heads, num_kv_heads, head_dim):
+    """[Q | K_blk | V_blk] = H W_qkv^T scattered to q [B,S,Hq,D], k_blk [B,Hkv,S,D],
+    v_blk [B,Hkv,D,S] (bf16)."""
+    dev = h.device
+    _check(h, "h", dev, torch.bfloat16, 3)
+    _check(w_qkv, "w_qkv", dev, torch.bfloat16, 2)
+    B, S, hidden = h.shape
+    if tuple(w_qkv.shape) != ((num_q_heads + 2 * num_kv_heads) * head_dim, hidden):
+        raise ValueError("w_qkv shape mismatch")
+    q = torch.empty((B, S, num_q_heads, head_dim), dtype=torch.bfloat16, device=dev)
+    kb = torch.empty((B, num_kv_heads, S, head_dim), dtype=torch.bfloat16, device=dev)
+    vb = torch.empty((B, num_kv_heads, head_dim, S), dtype=torch.bfloat16, device=dev)
+    a = _lib.QkvArgs()
+    a.batch, a.S, a.hidden = B, S, hidden
+    a.num_q_heads, a.num_kv_heads, a.head_dim = num_q_heads, num_kv_heads, head_dim
+    a.h, a.w_qkv, a.q, a.k_blk, a.v_blk = _p(h), _p(w_qkv), _p(q), _p(kb), _p(vb)
+    _run("twotower_qkv_projection", a, dev)
+    return q, kb, vb
+
+
+def out_projection(h_in, o, w_o, out=None):
+    """H_out = H_in + O W_o^T (bf16). ``o`` is [..., in_features] with the rows of ``h_in``."""
+    dev = h_in.device
+    _check(h_in, "h_in", dev, torch.bfloat16)
+    _check(o, "o", dev, torch.bfloat16)
+    _check(w_o, "w_o", dev, torch.bfloat16, 2)
+    hidden, inf = w_o.shape
+    rows = h_in.numel() // hidden
+    if h_in.shape[-1] != hidden or o.numel() != rows * inf:
+        raise ValueError("out_projection shape mismatch")
+    if out is None:
+        out = torch.empty_like(h_in)
+    a = _lib.OutProjArgs()
+    a.rows, a.hidden, a.in_features = rows, hidden, inf
+    a.h_in, a.o, a.w_o, a.h_out = _p(h_in), _p(o), _p(w_o), _p(out)
+    _run("twotower_out_projection", a, dev)
+    return out
+
+
+def lm_head(h, w_lm, out=None):
+    """logits = H W_lm^T in fp32, shape h.shape[:-1] + (vocab,)."""
+    dev = h.device
+    _check(h, "h", dev, torch.bfloat16)
+    _check(w_lm, "w_lm", dev, torch.bfloat16, 2)
+    vocab, hidden = w_lm.shape
+    rows = h.numel() // hidden
+    if out is None:
+        out = torch.empty(tuple(h.shape[:-1]) + (vocab,), dtype=torch.float32, device=dev)
+    a = _lib.LmHeadArgs()
+    a.rows, a.hidden, a.vocab, a.ld = rows, hidden, vocab, vocab
+    a.h, a.w_lm, a.logits = _p(h), _p(w_lm), _p(out)
+    _run("twotower_lm_head", a, dev)
+    return out
+
+
+class DenoiseStep:
+    """One denoise step of the synthetic attention-only denoiser, reused across steps.
+
+    Holds the per-layer context caches (read only), weights and the block-KV / scratch buffers,
+    so that calling it only enqueues kernels on the current stream.
+    """
+
+    def __init__(self, *, k_pages, v_pages, w_qkv, w_o, w_lm, block_table, ctx_lens,
+                 max_ctx_len, num_q_heads, num_kv_heads, head_dim, batch, S, scale=None,
+                 num_splits=0):
+        dev = w_lm.device
+        self.device = dev
+        self.L = len(k_pages)
+        vocab, hidden = w_lm.shape
+        self.hidden, self.vocab = hidden, vocab
+        self.B, self.S = batch, S
+        self.Hq, self.Hkv, self.D = num_q_heads, num_kv_heads, head_dim
+        bf = torch.bfloat16
+        self._keep = [list(k_pages), list(v_pages), list(w_qkv), list(w_o), w_lm, block_table,
+                      ctx_lens]
+        self.k_blk = [torch.empty((batch, num_kv_heads, S, head_dim), dtype=bf, device=dev)
+                      for _ in range(self.L)]
+        self.v_blk = [torch.empty((batch, num_kv_heads, head_dim, S), dtype=bf, device=dev)
+                      for _ in range(self.L)]
+        self.q = torch.empty((batch, S, num_q_heads, head_dim), dtype=bf, device=dev)
+        self.attn_out = torch.empty_like(self.q)
+        self.h_work = torch.empty((batch, S, hidden), dtype=bf, device=dev)
+        self.logits = torch.empty((batch, S, vocab), dtype=torch.float32, device=dev)
+        self.confidence = torch.full((batch, S), float("nan"), dtype=torch.float32, device=dev)
+        self.n_committed = torch.zeros((batch,), dtype=torch.int32, device=dev)
+
+        def arr(ts):
+            a = (C.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+            return a
+
+        self._arrs = [arr(k_pages), arr(v_pages), arr(w_qkv), arr(w_o), arr(self.k_blk),
+                      arr(self.v_blk)]
+        a = _lib.DenoiseStepArgs()
+        a.num_layers, a.hidden, a.vocab = self.L, hidden, vocab
+        P, _, page, _ = k_pages[0].shape
+        a.attn.batch, a.attn.S = batch, S
+        a.attn.num_q_heads, a.attn.num_kv_heads, a.attn.head_dim = num_q_heads, num_kv_heads, head_dim
+        a.attn.dtype = a.attn.out_dtype = TT_BF16
+        a.attn.scale = float(1.0 / math.sqrt(head_dim) if scale is None else scale)
+        a.attn.num_pages, a.attn.page_size = P, page
+        a.attn.max_pages_per_seq = block_table.shape[1]
+        a.attn.max_ctx_len = int(max_ctx_len)
+        a.attn.block_table, a.attn.ctx_lens = _p(block_table), _p(ctx_lens)
+        a.attn.num_splits = int(num_splits)
+        vpp = C.POINTER(C.c_void_p)
+        a.k_pages, a.v_pages, a.w_qkv, a.w_o, a.k_blk, a.v_blk = [C.cast(x, vpp) for x in self._arrs]
+        a.w_lm = _p(w_lm)
+        a.h_work, a.q, a.attn_out, a.logits = _p(self.h_work), _p(self.q), _p(self.attn_out), _p(self.logits)
+        a.logits_ld = vocab
+        a.unmask.confidence, a.unmask.n_committed = _p(self.confidence), _p(self.n_committed)
+        self.args = a
+        self._ws = None
+        self._ws_n = C.c_size_t(0)
+
+    def __call__(self, h_in, masked, tokens, *, threshold, min_commit=True, commit_all=False,
+                 timing_events=None):
+        """Enqueue one step; updates masked/tokens in place, fills confidence/n_committed."""
+        a = self.args
+        a.h_in = _p(h_in)
+        a.unmask.masked, a.unmask.tokens = _p(masked), _p(tokens)
+        a.unmask.threshold = float(threshold)
+        a.unmask.min_commit, a.unmask.commit_all = int(bool(min_commit)), int(bool(commit_all))
+        if timing_events is not None:
+            self._ev = (C.c_void_p * len(timing_events))(*timing_events)
+            a.timing_events = C.cast(self._ev, C.POINTER(C.c_void_p))
+        else:
+            a.timing_events = None
+        if self._ws is None:
+            n = C.c_size_t(0)
+            st = _lib.call("twotower_denoise_step", a, None, n, None)
+            if st != _lib.TT_OK:
+                raise TwoTowerError("twotower_denoise_step", st)
+            self._ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=self.device)
+            self._ws_n = C.c_size_t(self._ws.numel())
+        st = _lib.call("twotower_denoise_step", a, _p(self._ws), self._ws_n, _stream())
+        if st != _lib.TT_OK:
+            raise TwoTowerError("twotower_denoise_step", st)
+        return self.confidence, self.n_committed

@@ -1,0 +1,534 @@
+// C ABI of the denoise-step library: argument validation, workspace sizing, partition planning
+// and the composition of one denoise step. No device memory is allocated here; every kernel is
+// enqueued on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/twotower.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kTargetWorkgroups = 256;  // one work-group per compute unit on MI355X
+constexpr int kMinChunk = 256;          // context tokens per partition, lower bound
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Validated geometry of one block-attention call.
+struct AttnPlan {
+  tt::AttnParams p{};
+  size_t ws_bytes = 0;
+  bool use_bf16 = false;
+};
+
+tt_status plan_attn(const tt_block_attn_args *a, bool check_pointers, AttnPlan *out) {
+  if (!a) return TT_EINVAL;
+  if (a->batch < 0 || a->S < 1 || a->num_q_heads < 1 || a->num_kv_heads < 1) return TT_EINVAL;
+  if (a->num_q_heads % a->num_kv_heads != 0) return TT_EINVAL;
+  if (a->dtype != TT_FP32 && a->dtype != TT_BF16) return TT_EINVAL;
+  if (a->out_dtype != TT_FP32 && a->out_dtype != TT_BF16) return TT_EINVAL;
+  if (!(a->scale > 0.f) || !std::isfinite(a->scale)) return TT_EINVAL;
+  if (a->num_pages < 1 || a->page_size < 1 || a->max_pages_per_seq < 1 || a->max_ctx_len < 0)
+    return TT_EINVAL;
+  if ((int64_t)a->max_ctx_len > (int64_t)a->max_pages_per_seq * a->page_size) return TT_EINVAL;
+  if (a->num_splits < 0) return TT_EINVAL;
+  if (a->head_dim != 64 && a->head_dim != 128) return TT_ENOTSUP;
+  if (a->S > 64) return TT_ENOTSUP;
+  if (a->page_size % 64 != 0) return TT_ENOTSUP;
+  if (a->out_dtype != TT_FP32 && a->out_dtype != a->dtype) return TT_ENOTSUP;
+  if (check_pointers) {
+    const void *p16[] = {a->q, a->k_pages, a->v_pages, a->k_blk, a->v_blk, a->out};
+    for (const void *p : p16)
+      if (!p || !aligned(p, 16)) return TT_EINVAL;
+    if (!a->block_table || !aligned(a->block_table, 4)) return TT_EINVAL;
+    if (!a->ctx_lens || !aligned(a->ctx_lens, 4)) return TT_EINVAL;
+    if (a->lse && !aligned(a->lse, 4)) return TT_EINVAL;
+  }
+  tt::AttnParams &p = out->p;
+  p.q = a->q;
+  p.k_pages = a->k_pages;
+  p.v_pages = a->v_pages;
+  p.k_blk = a->k_blk;
+  p.v_blk = a->v_blk;
+  p.block_table = a->block_table;
+  p.ctx_lens = a->ctx_lens;
+  p.out = a->out;
+  p.lse = a->lse;
+  p.B = a->batch;
+  p.S = a->S;
+  p.Hq = a->num_q_heads;
+  p.Hkv = a->num_kv_heads;
+  p.G = a->num_q_heads / a->num_kv_heads;
+  p.D = a->head_dim;
+  p.num_pages = a->num_pages;
+  p.page_size = a->page_size;
+  p.max_pages = a->max_pages_per_seq;
+  p.max_ctx_len = a->max_ctx_len;
+  p.scale = a->scale;
+  p.out_bf16 = a->out_dtype == TT_BF16;
+  out->use_bf16 = a->dtype == TT_BF16;
+  const int64_t rows = (int64_t)p.G * p.S;
+  if (rows > (1 << 20)) return TT_ENOTSUP;
+  p.rows = (int)rows;
+  const int rows_pad = (int)cdiv(rows, 32) * 32;
+  p.rows_per_group = std::min(rows_pad, 256);
+  p.row_groups = (int)cdiv(rows_pad, p.rows_per_group);
+  if (!out->use_bf16 || a->max_ctx_len == 0) {
+    p.splits = 1;
+    p.chunk = std::max(64, (int)cdiv(std::max(a->max_ctx_len, 1), 64) * 64);
+  } else {
+    const int64_t units = std::max<int64_t>(1, (int64_t)p.B * p.Hkv * p.row_groups);
+    int64_t want = a->num_splits > 0 ? a->num_splits : cdiv(kTargetWorkgroups, units);
+    want = std::max<int64_t>(1, want);
+    int64_t chunk = cdiv(cdiv(a->max_ctx_len, want), 64) * 64;
+    if (a->num_splits == 0) chunk = std::max<int64_t>(chunk, kMinChunk);
+    chunk = std::max<int64_t>(chunk, 64);
+    p.chunk = (int)chunk;
+    p.splits = (int)cdiv(a->max_ctx_len, chunk);
+  }
+  if (p.splits > 65535 || (int64_t)p.B * p.Hkv * p.row_groups > 65535) return TT_ENOTSUP;
+  out->ws_bytes = 0;
+  if (p.splits > 1) {
+    const size_t items = (size_t)p.B * p.Hkv * p.row_groups * p.splits;
+    out->ws_bytes = align_up(items * p.rows_per_group * p.D * sizeof(float)) +
+                    align_up(items * p.rows_per_group * sizeof(float));
+  }
+  return TT_OK;
+}
+
+hipError_t run_attn(AttnPlan &pl, void *ws, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+  tt::AttnParams &p = pl.p;
+  if (p.B == 0) return hipSuccess;
+  if (!pl.use_bf16) return tt::launch_block_attn_f32(p, stream, e0, e1);
+  if (p.splits > 1) {
+    const size_t items = (size_t)p.B * p.Hkv * p.row_groups * p.splits;
+    char *w = static_cast<char *>(ws);
+    p.part_o = reinterpret_cast<float *>(w);
+    p.part_lse = reinterpret_cast<float *>(w + align_up(items * p.rows_per_group * p.D * sizeof(float)));
+  }
+  hipError_t e = tt::launch_block_attn_bf16(p, stream, e0, e1);
+  if (e != hipSuccess || p.splits == 1) return e;
+  return tt::launch_attn_reduce(p, stream);
+}
+
+tt_status ws_protocol(size_t need, void *ws, size_t *ws_bytes, bool *launch) {
+  *launch = false;
+  if (!ws_bytes) return TT_EINVAL;
+  if (!ws) {
+    *ws_bytes = need;
+    return TT_OK;
+  }
+  if (*ws_bytes < need) {
+    *ws_bytes = need;
+    return TT_ENOSPACE;
+  }
+  if (need > 0 && !aligned(ws, kAlign)) return TT_EINVAL;
+  *launch = true;
+  return TT_OK;
+}
+
+// ---------------------------------------------------------------------------------- unmask
+struct UnmaskPlan {
+  tt::UnmaskParams p{};
+  size_t ws_bytes = 0;
+};
+
+tt_status plan_unmask(const tt_unmask_args *a, bool check_logits, UnmaskPlan *out) {
+  if (!a) return TT_EINVAL;
+  if (a->batch < 0 || a->S < 1 || a->vocab < 1 || a->ld < a->vocab) return TT_EINVAL;
+  if (std::isnan(a->threshold)) return TT_EINVAL;
+  if (a->S > 64) return TT_ENOTSUP;
+  if (check_logits && (!a->logits || !aligned(a->logits, 4))) return TT_EINVAL;
+  if (!a->masked || !a->tokens || !aligned(a->tokens, 4)) return TT_EINVAL;
+  if (a->confidence && !aligned(a->confidence, 4)) return TT_EINVAL;
+  if (a->n_committed && !aligned(a->n_committed, 4)) return TT_EINVAL;
+  tt::UnmaskParams &p = out->p;
+  p.logits = a->logits;
+  p.ld = a->ld;
+  p.masked = a->masked;
+  p.tokens = a->tokens;
+  p.confidence = a->confidence;
+  p.n_committed = a->n_committed;
+  p.B = a->batch;
+  p.S = a->S;
+  p.vocab = a->vocab;
+  p.chunk = 8192;
+  p.chunks = (int)cdiv(a->vocab, p.chunk);
+  p.threshold = a->threshold;
+  p.min_commit = a->min_commit != 0;
+  p.commit_all = a->commit_all != 0;
+  if ((int64_t)p.B * p.S > 65535) return TT_ENOTSUP;
+  out->ws_bytes = align_up((size_t)p.B * p.S * p.chunks * 4 * sizeof(float));
+  return TT_OK;
+}
+
+hipError_t run_unmask(UnmaskPlan &pl, void *ws, hipStream_t stream) {
+  if (pl.p.B == 0) return hipSuccess;
+  pl.p.part = static_cast<float *>(ws);
+  return tt::launch_unmask(pl.p, stream);
+}
+
+// ---------------------------------------------------------------------------------- linear
+int choose_ksplit(int M, int N, int K) {
+  const int64_t tiles = cdiv(N, 64) * cdiv(M, 128);
+  int64_t ks = cdiv(kTargetWorkgroups, tiles);
+  ks = std::min<int64_t>(ks, std::max<int64_t>(1, K / 256));
+  return (int)std::max<int64_t>(1, ks);
+}
+
+size_t linear_ws(const tt::LinearParams &p) {
+  return p.ksplit > 1 ? align_up((size_t)p.ksplit * p.M * p.N * sizeof(float)) : 0;
+}
+
+hipError_t run_linear(tt::LinearParams p, void *ws, hipStream_t stream) {
+  if (p.M == 0 || p.N == 0) return hipSuccess;
+  p.part = static_cast<float *>(ws);
+  return tt::launch_linear(p, stream);
+}
+
+tt_status plan_qkv(const tt_qkv_args *a, bool check_pointers, tt::LinearParams *p) {
+  if (!a) return TT_EINVAL;
+  if (a->batch < 0 || a->S < 1 || a->hidden < 1 || a->num_q_heads < 1 || a->num_kv_heads < 1 ||
+      a->head_dim < 1)
+    return TT_EINVAL;
+  if (a->hidden % 8 != 0 || a->head_dim % 4 != 0) return TT_ENOTSUP;
+  if (check_pointers) {
+    if (!a->h || !a->w_qkv || !aligned(a->h, 16) || !aligned(a->w_qkv, 16)) return TT_EINVAL;
+    if (!a->q || !a->k_blk || !a->v_blk || !aligned(a->q, 8) || !aligned(a->k_blk, 8) ||
+        !aligned(a->v_blk, 2))
+      return TT_EINVAL;
+  }
+  *p = tt::LinearParams{};
+  p->x = a->h;
+  p->w = a->w_qkv;
+  p->M = a->batch * a->S;
+  p->N = (a->num_q_heads + 2 * a->num_kv_heads) * a->head_dim;
+  p->K = a->hidden;
+  p->epi = tt::EPI_QKV;
+  p->q = a->q;
+  p->k_blk = a->k_blk;
+  p->v_blk = a->v_blk;
+  p->S = a->S;
+  p->Hq = a->num_q_heads;
+  p->Hkv = a->num_kv_heads;
+  p->D = a->head_dim;
+  p->ksplit = choose_ksplit(p->M, p->N, p->K);
+  return TT_OK;
+}
+
+tt_status plan_out(const tt_out_proj_args *a, bool check_pointers, tt::LinearParams *p) {
+  if (!a) return TT_EINVAL;
+  if (a->rows < 0 || a->hidden < 1 || a->in_features < 1) return TT_EINVAL;
+  if (a->hidden % 4 != 0 || a->in_features % 8 != 0) return TT_ENOTSUP;
+  if (check_pointers) {
+    if (!a->h_in || !a->o || !a->w_o || !a->h_out) return TT_EINVAL;
+    if (!aligned(a->o, 16) || !aligned(a->w_o, 16) || !aligned(a->h_in, 8) || !aligned(a->h_out, 8))
+      return TT_EINVAL;
+  }
+  *p = tt::LinearParams{};
+  p->x = a->o;
+  p->w = a->w_o;
+  p->M = a->rows;
+  p->N = a->hidden;
+  p->K = a->in_features;
+  p->epi = tt::EPI_RESIDUAL;
+  p->residual = a->h_in;
+  p->y_bf16 = a->h_out;
+  p->ksplit = choose_ksplit(p->M, p->N, p->K);
+  return TT_OK;
+}
+
+tt_status plan_lm(const tt_lm_head_args *a, bool check_pointers, tt::LinearParams *p) {
+  if (!a) return TT_EINVAL;
+  if (a->rows < 0 || a->hidden < 1 || a->vocab < 1 || a->ld < a->vocab) return TT_EINVAL;
+  if (a->hidden % 8 != 0 || a->vocab % 4 != 0 || a->ld % 4 != 0) return TT_ENOTSUP;
+  if (check_pointers) {
+    if (!a->h || !a->w_lm || !a->logits) return TT_EINVAL;
+    if (!aligned(a->h, 16) || !aligned(a->w_lm, 16) || !aligned(a->logits, 16)) return TT_EINVAL;
+  }
+  *p = tt::LinearParams{};
+  p->x = a->h;
+  p->w = a->w_lm;
+  p->M = a->rows;
+  p->N = a->vocab;
+  p->K = a->hidden;
+  p->epi = tt::EPI_F32;
+  p->y = a->logits;
+  p->ldy = a->ld;
+  p->ksplit = choose_ksplit(p->M, p->N, p->K);
+  return TT_OK;
+}
+
+tt_status hip_status(hipError_t e) { return e == hipSuccess ? TT_OK : TT_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+tt_status twotower_block_attn(const tt_block_attn_args *args, void *ws, size_t *ws_bytes,
+                              void *stream) {
+  AttnPlan pl;
+  tt_status st = plan_attn(args, true, &pl);
+  if (st != TT_OK) return st;
+  bool launch;
+  st = ws_protocol(pl.ws_bytes, ws, ws_bytes, &launch);
+  if (st != TT_OK || !launch) return st;
+  return hip_status(run_attn(pl, ws, static_cast<hipStream_t>(stream), nullptr, nullptr));
+}
+
+tt_status twotower_unmask(const tt_unmask_args *args, void *ws, size_t *ws_bytes, void *stream) {
+  UnmaskPlan pl;
+  tt_status st = plan_unmask(args, true, &pl);
+  if (st != TT_OK) return st;
+  bool launch;
+  st = ws_protocol(pl.ws_bytes, ws, ws_bytes, &launch);
+  if (st != TT_OK || !launch) return st;
+  return hip_status(run_unmask(pl, ws, static_cast<hipStream_t>(stream)));
+}
+
+tt_status twotower_qkv_projection(const tt_qkv_args *args, void *ws, size_t *ws_bytes,
+                                  void *stream) {
+  tt::LinearParams p;
+  tt_status st = plan_qkv(args, true, &p);
+  if (st != TT_OK) return st;
+  bool launch;
+  st = ws_protocol(linear_ws(p), ws, ws_bytes, &launch);
+  if (st != TT_OK || !launch) return st;
+  return hip_status(run_linear(p, ws, static_cast<hipStream_t>(stream)));
+}
+
+tt_status twotower_out_projection(const tt_out_proj_args *args, void *ws, size_t *ws_bytes,
+                                  void *stream) {
+  tt::LinearParams p;
+  tt_status st = plan_out(args, true, &p);
+  if (st != TT_OK) return st;
+  bool launch;
+  st = ws_protocol(linear_ws(p), ws, ws_bytes, &launch);
+  if (st != TT_OK || !launch) return st;
+  return hip_status(run_linear(p, ws, static_cast<hipStream_t>(stream)));
+}
+
+tt_status twotower_lm_head(const tt_lm_head_args *args, void *ws, size_t *ws_bytes, void *stream) {
+  tt::LinearParams p;
+  tt_status st = plan_lm(args, true, &p);
+  if (st != TT_OK) return st;
+  bool launch;
+  st = ws_protocol(linear_ws(p), ws, ws_bytes, &launch);
+  if (st != TT_OK || !launch) return st;
+  return hip_status(run_linear(p, ws, static_cast<hipStream_t>(stream)));
+}
+
+tt_status twotower_denoise_step(const tt_denoise_step_args *a, void *ws, size_t *ws_bytes,
+                                void *stream) {
+  if (!a || a->num_layers < 1 || a->hidden < 1 || a->vocab < 1) return TT_EINVAL;
+  const tt_block_attn_args &g = a->attn;
+  if (g.dtype != TT_BF16) return TT_ENOTSUP;
+  if (!a->k_pages || !a->v_pages || !a->w_qkv || !a->w_o || !a->k_blk || !a->v_blk)
+    return TT_EINVAL;
+  if (!a->w_lm || !a->h_in || !a->h_work || !a->q || !a->attn_out || !a->logits) return TT_EINVAL;
+  if (a->logits_ld < a->vocab) return TT_EINVAL;
+
+  // Plan every stage once (layer 0's pointers; the geometry is shared by all layers).
+  tt_block_attn_args ga = g;
+  ga.q = a->q;
+  ga.k_pages = a->k_pages[0];
+  ga.v_pages = a->v_pages[0];
+  ga.k_blk = a->k_blk[0];
+  ga.v_blk = a->v_blk[0];
+  ga.out = a->attn_out;
+  ga.out_dtype = TT_BF16;
+  ga.lse = nullptr;
+  AttnPlan ap;
+  tt_status st = plan_attn(&ga, true, &ap);
+  if (st != TT_OK) return st;
+
+  tt_qkv_args qa{};
+  qa.batch = g.batch;
+  qa.S = g.S;
+  qa.hidden = a->hidden;
+  qa.num_q_heads = g.num_q_heads;
+  qa.num_kv_heads = g.num_kv_heads;
+  qa.head_dim = g.head_dim;
+  qa.h = a->h_in;
+  qa.w_qkv = a->w_qkv[0];
+  qa.q = a->q;
+  qa.k_blk = a->k_blk[0];
+  qa.v_blk = a->v_blk[0];
+  tt::LinearParams qp;
+  if ((st = plan_qkv(&qa, true, &qp)) != TT_OK) return st;
+
+  tt_out_proj_args oa{};
+  oa.rows = g.batch * g.S;
+  oa.hidden = a->hidden;
+  oa.in_features = g.num_q_heads * g.head_dim;
+  oa.h_in = a->h_in;
+  oa.o = a->attn_out;
+  oa.w_o = a->w_o[0];
+  oa.h_out = a->h_work;
+  tt::LinearParams op;
+  if ((st = plan_out(&oa, true, &op)) != TT_OK) return st;
+
+  tt_lm_head_args la{};
+  la.rows = g.batch * g.S;
+  la.hidden = a->hidden;
+  la.vocab = a->vocab;
+  la.ld = a->logits_ld;
+  la.h = a->h_work;
+  la.w_lm = a->w_lm;
+  la.logits = a->logits;
+  tt::LinearParams lp;
+  if ((st = plan_lm(&la, true, &lp)) != TT_OK) return st;
+
+  tt_unmask_args ua = a->unmask;
+  ua.batch = g.batch;
+  ua.S = g.S;
+  ua.vocab = a->vocab;
+  ua.ld = a->logits_ld;
+  ua.logits = a->logits;
+  UnmaskPlan up;
+  if ((st = plan_unmask(&ua, true, &up)) != TT_OK) return st;
+
+  for (int l = 0; l < a->num_layers; ++l) {
+    const void *p16[] = {a->k_pages[l], a->v_pages[l], a->w_qkv[l], a->w_o[l]};
+    for (const void *p : p16)
+      if (!p || !aligned(p, 16)) return TT_EINVAL;
+    if (!a->k_blk[l] || !a->v_blk[l] || !aligned(a->k_blk[l], 16) || !aligned(a->v_blk[l], 16))
+      return TT_EINVAL;
+  }
+
+  const size_t need = std::max({ap.ws_bytes, up.ws_bytes, linear_ws(qp), linear_ws(op),
+                                linear_ws(lp)});
+  bool launch;
+  st = ws_protocol(need, ws, ws_bytes, &launch);
+  if (st != TT_OK || !launch) return st;
+  if (g.batch == 0) return TT_OK;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int l = 0; l < a->num_layers; ++l) {
+    const void *h_prev = l == 0 ? a->h_in : a->h_work;
+    qp.x = h_prev;
+    qp.w = a->w_qkv[l];
+    qp.k_blk = a->k_blk[l];
+    qp.v_blk = a->v_blk[l];
+    hipError_t e = run_linear(qp, ws, s);
+    if (e != hipSuccess) return TT_EHIP;
+    AttnPlan al = ap;
+    al.p.k_pages = a->k_pages[l];
+    al.p.v_pages = a->v_pages[l];
+    al.p.k_blk = a->k_blk[l];
+    al.p.v_blk = a->v_blk[l];
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (a->timing_events) {
+      e0 = static_cast<hipEvent_t>(a->timing_events[2 * l]);
+      e1 = static_cast<hipEvent_t>(a->timing_events[2 * l + 1]);
+    }
+    if ((e = run_attn(al, ws, s, e0, e1)) != hipSuccess) return TT_EHIP;
+    op.residual = h_prev;
+    op.w = a->w_o[l];
+    if ((e = run_linear(op, ws, s)) != hipSuccess) return TT_EHIP;
+  }
+  if (run_linear(lp, ws, s) != hipSuccess) return TT_EHIP;
+  if (run_unmask(up, ws, s) != hipSuccess) return TT_EHIP;
+  return TT_OK;
+}
+
+const char *twotower_status_string(int32_t status) {
+  switch (status) {
+    case TT_OK: return "TT_OK";
+    case TT_EINVAL: return "TT_EINVAL";
+    case TT_ENOTSUP: return "TT_ENOTSUP";
+    case TT_ENOSPACE: return "TT_ENOSPACE";
+    case TT_EHIP: return "TT_EHIP";
+    default: return "TT_UNKNOWN";
+  }
+}
+
+int32_t twotower_abi_version(void) { return TWOTOWER_ABI_VERSION; }
+
+int64_t twotower_struct_size(int32_t which) {
+  switch (which) {
+    case 0: return sizeof(tt_block_attn_args);
+    case 1: return sizeof(tt_unmask_args);
+    case 2: return sizeof(tt_qkv_args);
+    case 3: return sizeof(tt_out_proj_args);
+    case 4: return sizeof(tt_lm_head_args);
+    case 5: return sizeof(tt_denoise_step_args);
+    default: return -1;
+  }
+}
+
+#define TT_OFF(T, f) (int64_t) offsetof(T, f)
+int64_t twotower_struct_offset(int32_t which, int32_t field) {
+  static const int64_t attn[] = {
+      TT_OFF(tt_block_attn_args, batch), TT_OFF(tt_block_attn_args, S),
+      TT_OFF(tt_block_attn_args, num_q_heads), TT_OFF(tt_block_attn_args, num_kv_heads),
+      TT_OFF(tt_block_attn_args, head_dim), TT_OFF(tt_block_attn_args, dtype),
+      TT_OFF(tt_block_attn_args, out_dtype), TT_OFF(tt_block_attn_args, scale),
+      TT_OFF(tt_block_attn_args, q), TT_OFF(tt_block_attn_args, k_pages),
+      TT_OFF(tt_block_attn_args, v_pages), TT_OFF(tt_block_attn_args, num_pages),
+      TT_OFF(tt_block_attn_args, page_size), TT_OFF(tt_block_attn_args, max_pages_per_seq),
+      TT_OFF(tt_block_attn_args, max_ctx_len), TT_OFF(tt_block_attn_args, block_table),
+      TT_OFF(tt_block_attn_args, ctx_lens), TT_OFF(tt_block_attn_args, k_blk),
+      TT_OFF(tt_block_attn_args, v_blk), TT_OFF(tt_block_attn_args, out),
+      TT_OFF(tt_block_attn_args, lse), TT_OFF(tt_block_attn_args, num_splits),
+      TT_OFF(tt_block_attn_args, reserved0)};
+  static const int64_t unm[] = {
+      TT_OFF(tt_unmask_args, batch), TT_OFF(tt_unmask_args, S), TT_OFF(tt_unmask_args, vocab),
+      TT_OFF(tt_unmask_args, reserved0), TT_OFF(tt_unmask_args, ld),
+      TT_OFF(tt_unmask_args, logits), TT_OFF(tt_unmask_args, masked),
+      TT_OFF(tt_unmask_args, tokens), TT_OFF(tt_unmask_args, confidence),
+      TT_OFF(tt_unmask_args, n_committed), TT_OFF(tt_unmask_args, threshold),
+      TT_OFF(tt_unmask_args, min_commit), TT_OFF(tt_unmask_args, commit_all),
+      TT_OFF(tt_unmask_args, reserved1)};
+  static const int64_t qkv[] = {
+      TT_OFF(tt_qkv_args, batch), TT_OFF(tt_qkv_args, S), TT_OFF(tt_qkv_args, hidden),
+      TT_OFF(tt_qkv_args, num_q_heads), TT_OFF(tt_qkv_args, num_kv_heads),
+      TT_OFF(tt_qkv_args, head_dim), TT_OFF(tt_qkv_args, h), TT_OFF(tt_qkv_args, w_qkv),
+      TT_OFF(tt_qkv_args, q), TT_OFF(tt_qkv_args, k_blk), TT_OFF(tt_qkv_args, v_blk)};
+  static const int64_t outp[] = {
+      TT_OFF(tt_out_proj_args, rows), TT_OFF(tt_out_proj_args, hidden),
+      TT_OFF(tt_out_proj_args, in_features), TT_OFF(tt_out_proj_args, reserved0),
+      TT_OFF(tt_out_proj_args, h_in), TT_OFF(tt_out_proj_args, o), TT_OFF(tt_out_proj_args, w_o),
+      TT_OFF(tt_out_proj_args, h_out)};
+  static const int64_t lm[] = {
+      TT_OFF(tt_lm_head_args, rows), TT_OFF(tt_lm_head_args, hidden),
+      TT_OFF(tt_lm_head_args, vocab), TT_OFF(tt_lm_head_args, reserved0),
+      TT_OFF(tt_lm_head_args, ld), TT_OFF(tt_lm_head_args, h), TT_OFF(tt_lm_head_args, w_lm),
+      TT_OFF(tt_lm_head_args, logits)};
+  static const int64_t step[] = {
+      TT_OFF(tt_denoise_step_args, num_layers), TT_OFF(tt_denoise_step_args, hidden),
+      TT_OFF(tt_denoise_step_args, vocab), TT_OFF(tt_denoise_step_args, reserved0),
+      TT_OFF(tt_denoise_step_args, attn), TT_OFF(tt_denoise_step_args, k_pages),
+      TT_OFF(tt_denoise_step_args, v_pages), TT_OFF(tt_denoise_step_args, w_qkv),
+      TT_OFF(tt_denoise_step_args, w_o), TT_OFF(tt_denoise_step_args, k_blk),
+      TT_OFF(tt_denoise_step_args, v_blk), TT_OFF(tt_denoise_step_args, w_lm),
+      TT_OFF(tt_denoise_step_args, h_in), TT_OFF(tt_denoise_step_args, h_work),
+      TT_OFF(tt_denoise_step_args, q), TT_OFF(tt_denoise_step_args, attn_out),
+      TT_OFF(tt_denoise_step_args, logits), TT_OFF(tt_denoise_step_args, logits_ld),
+      TT_OFF(tt_denoise_step_args, unmask), TT_OFF(tt_denoise_step_args, timing_events)};
+  const int64_t *tab = nullptr;
+  int n = 0;
+  switch (which) {
+    case 0: tab = attn; n = sizeof(attn) / sizeof(attn[0]); break;
+    case 1: tab = unm; n = sizeof(unm) / sizeof(unm[0]); break;
+    case 2: tab = qkv; n = sizeof(qkv) / sizeof(qkv[0]); break;
+    case 3: tab = outp; n = sizeof(outp) / sizeof(outp[0]); break;
+    case 4: tab = lm; n = sizeof(lm) / sizeof(lm[0]); break;
+    case 5: tab = step; n = sizeof(step) / sizeof(step[0]); break;
+    default: return -1;
+  }
+  if (field < 0 || field >= n) return -1;
+  return tab[field];
+}
+#undef TT_OFF
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// Host-side launchers of the gfx950 kernels (internal to the library; the public ABI is
+// include/twotower.h). Every launcher enqueues on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tt {
+
+// ---------------------------------------------------------------------------- block attention
+struct AttnParams {
+  const void *q, *k_pages, *v_pages, *k_blk, *v_blk;
+  const int32_t *block_table, *ctx_lens;
+  void *out;
+  float *lse;
+  float *part_o;    // [items, rows_per_group, D] fp32 partial outputs (splits > 1)
+  float *part_lse;  // [items, rows_per_group]
+  int B, S, Hq, Hkv, G, D;
+  int rows;            // G * S query rows per (sequence, KV head)
+  int rows_per_group;  // rows handled by one work-group (multiple of 32, <= 256)
+  int row_groups;
+  int num_pages, page_size, max_pages, max_ctx_len;
+  int chunk;   // context tokens per partition (multiple of 64)
+  int splits;  // partitions per (sequence, KV head, row group)
+  float scale;
+  int out_bf16;
+};
+
+hipError_t launch_block_attn_bf16(const AttnParams &p, hipStream_t stream, hipEvent_t ev_begin,
+                                  hipEvent_t ev_end);
+hipError_t launch_block_attn_f32(const AttnParams &p, hipStream_t stream, hipEvent_t ev_begin,
+                                 hipEvent_t ev_end);
+hipError_t launch_attn_reduce(const AttnParams &p, hipStream_t stream);
+
+// ------------------------------------------------------------------------------------ unmask
+struct UnmaskParams {
+  const float *logits;
+  int64_t ld;
+  uint8_t *masked;
+  int32_t *tokens;
+  float *confidence;
+  int32_t *n_committed;
+  float *part;  // [B*S, chunks, 3] (max, index bits, sum)
+  int B, S, vocab, chunk, chunks;
+  float threshold;
+  int min_commit, commit_all;
+};
+
+hipError_t launch_unmask(const UnmaskParams &p, hipStream_t stream);
+
+// ------------------------------------------------------------------------ skinny bf16 linear
+enum Epilogue : int {
+  EPI_F32 = 0,       // y fp32 [M, ldy]
+  EPI_QKV = 1,       // scatter to q [B,S,Hq,D], k_blk [B,Hkv,S,D], v_blk [B,Hkv,D,S] (bf16)
+  EPI_RESIDUAL = 2,  // y bf16 [M, N] = residual bf16 [M, N] + x w^T
+};
+
+struct LinearParams {
+  const void *x;  // bf16 [M, K]
+  const void *w;  // bf16 [N, K]
+  int M, N, K;
+  int ksplit;     // partitions of K (>= 1); > 1 uses `part` and a reduce pass
+  float *part;    // [ksplit, M, N] fp32 when ksplit > 1
+  int epi;
+  // EPI_F32
+  float *y;
+  int64_t ldy;
+  // EPI_QKV
+  void *q, *k_blk, *v_blk;
+  int S, Hq, Hkv, D;
+  // EPI_RESIDUAL
+  const void *residual;
+  void *y_bf16;
+};
+
+hipError_t launch_linear(const LinearParams &p, hipStream_t stream);
+
+}  // namespace tt
