@@ -19,10 +19,12 @@
  *   no pointer after returning. Buffers must stay alive until the stream work completes.
  * - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null stream). No call
  *   synchronizes with the host.
- * - Workspace protocol: call with ws == NULL to have *ws_bytes set to the required size (nothing
- *   is launched, TT_OK is returned). Then call with ws pointing to at least *ws_bytes bytes of
- *   device memory (256-byte aligned). A smaller *ws_bytes returns TT_ENOSPACE and sets
- *   *ws_bytes to the required size. The workspace content on entry does not matter.
+ * - Workspace protocol: a call with ws == NULL is always a size query: it sets *ws_bytes to the
+ *   required size, launches nothing and returns TT_OK. To run, call with a non-NULL ws pointing
+ *   to at least that many bytes of device memory (256-byte aligned), passing its size in
+ *   *ws_bytes; when the required size is 0 any non-NULL ws is accepted and never dereferenced.
+ *   A smaller *ws_bytes returns TT_ENOSPACE and sets *ws_bytes to the required size. The
+ *   workspace content on entry does not matter.
  * - Errors are return codes only; the library never prints or aborts. Every argument check runs
  *   on the host before anything is launched, so an error leaves all outputs untouched.
  *   TT_EHIP means a HIP launch failed; asynchronous device faults surface at the caller's next

@@ -62,7 +62,9 @@ def _run(name: str, args, device) -> None:
     st = _lib.call(name, args, None, n, None)
     if st != _lib.TT_OK:
         raise TwoTowerError(name, st)
-    ws = torch.empty(n.value, dtype=torch.uint8, device=device) if n.value else None
+    # ws == NULL always means "query": a call that needs no workspace still gets a buffer.
+    ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=device)
+    n = C.c_size_t(ws.numel())
     st = _lib.call(name, args, _p(ws), n, _stream())
     if st != _lib.TT_OK:
         raise TwoTowerError(name, st)
