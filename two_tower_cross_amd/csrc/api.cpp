@@ -15,6 +15,7 @@ namespace {
 
 constexpr int kTargetWorkgroups = 256;  // one work-group per compute unit on MI355X
 constexpr int kMinChunk = 256;          // context tokens per partition, lower bound
+constexpr int kMaxPartitionPages = 4096;  // page ids one attention work-group stages in LDS
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -92,6 +93,8 @@ tt_status plan_attn(const tt_block_attn_args *a, bool check_pointers, AttnPlan *
     int64_t chunk = cdiv(cdiv(a->max_ctx_len, want), 64) * 64;
     if (a->num_splits == 0) chunk = std::max<int64_t>(chunk, kMinChunk);
     chunk = std::max<int64_t>(chunk, 64);
+    // a partition's page ids are staged on chip: at most kMaxPartitionPages of them
+    chunk = std::min<int64_t>(chunk, (int64_t)(kMaxPartitionPages - 2) * a->page_size);
     p.chunk = (int)chunk;
     p.splits = (int)cdiv(a->max_ctx_len, chunk);
   }

@@ -31,10 +31,24 @@ namespace tt {
 constexpr int kTile = 64;
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
+constexpr int kStages = 4;             // LDS ring depth: up to 3 tiles in flight per work-group
+constexpr float kRescaleLog2 = 8.0f;   // the running max moves only when it grows by > 2^8
+constexpr int kMaxPartPages = 4096;    // page ids of one partition staged in LDS (16 KB)
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
 __device__ __forceinline__ int swap_bits23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
+
+// XOR keys of the 16-byte chunk swizzle. K rows (one token, D*2 bytes): the 32 lanes that read
+// one MFMA operand hold tokens swap_bits23(lane) of a 32-token sub-tile, so keying on
+// swap_bits23(token) gives every group of 8 (and of 16) consecutive lanes distinct chunk slots.
+// V rows (one dimension, 128 bytes): distinct slots for 8 consecutive rows and, within each row
+// parity, for 16 consecutive rows. Both hold for 32 and for 64 LDS banks.
+template <int D>
+__device__ __forceinline__ int kkey(int t) { return swap_bits23(t & 15) & (D / 8 - 1); }
+__device__ __forceinline__ int vkey(int d) { return ((d >> 1) & 7) ^ ((d & 1) << 2); }
 
 // Keep the first n (0..8) bf16 elements of a 16-byte chunk, zero the rest.
 __device__ __forceinline__ u32x4 keep_first(u32x4 v, int n) {
@@ -48,103 +62,149 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int n) {
 }
 
 template <int D>
-struct TileRegs {
-  static constexpr int KCH = kTile * D / 8 / kThreads;  // 16-byte K chunks per thread
-  static constexpr int VCH = D * kTile / 8 / kThreads;  // 16-byte V chunks per thread
-  u32x4 k[KCH];
-  u32x4 v[VCH];
+struct Geom {
+  static constexpr int KBYTES = kTile * D * 2;
+  static constexpr int VBYTES = D * kTile * 2;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int KCH = KBYTES / 16 / kThreads;  // 16-byte K chunks per thread per tile
+  static constexpr int VCH = VBYTES / 16 / kThreads;
+  static constexpr int LOADS = KCH + VCH;             // DMA instructions per thread per tile
 };
 
-// Global -> registers for one context tile: `valid` tokens starting at page offset off0.
+// Full 64-token context tile -> LDS stage, asynchronously (global_load_lds, 16 B per lane).
+// Instruction j of wave w fills LDS bytes [(j*8 + w)*1024, +1024) lane by lane; the source of
+// each lane is the logical chunk that the swizzle places in that slot.
 template <int D>
-__device__ __forceinline__ void fetch_ctx_tile(TileRegs<D> &r, const uint16_t *kbase,
-                                               const uint16_t *vbase, int page_size, int valid,
-                                               int tid) {
+__device__ __forceinline__ void dma_tile(char *stage, const uint16_t *kbase,
+                                         const uint16_t *vbase, int page_size, int wave,
+                                         int lane) {
+  constexpr int KC = D / 8;
 #pragma unroll
-  for (int c = 0; c < TileRegs<D>::KCH; ++c) {
-    const int idx = tid + c * kThreads;
-    const int row = idx / (D / 8), ch = idx % (D / 8);
-    u32x4 z = {0u, 0u, 0u, 0u};
-    r.k[c] = row < valid ? ld_global_16(kbase + (size_t)row * D + ch * 8) : z;
+  for (int j = 0; j < Geom<D>::KCH; ++j) {
+    const int seg = j * kWaves + wave;
+    const int f = seg * 64 + lane;
+    const int r = f / KC, p = f % KC;
+    const int c = p ^ kkey<D>(r);
+    __builtin_amdgcn_global_load_lds(kbase + (size_t)r * D + c * 8, LDS_PTR(stage + seg * 1024),
+                                     16, 0, 0);
   }
 #pragma unroll
-  for (int c = 0; c < TileRegs<D>::VCH; ++c) {
-    const int idx = tid + c * kThreads;
-    const int d = idx / 8, ch = idx % 8;
-    u32x4 z = {0u, 0u, 0u, 0u};
-    const int n = valid - ch * 8;
-    u32x4 x = n > 0 ? ld_global_16(vbase + (size_t)d * page_size + ch * 8) : z;
-    r.v[c] = n >= 8 ? x : keep_first(x, n > 0 ? n : 0);
+  for (int j = 0; j < Geom<D>::VCH; ++j) {
+    const int seg = j * kWaves + wave;
+    const int f = seg * 64 + lane;
+    const int d = f / 8, p = f % 8;
+    const int c = p ^ vkey(d);
+    __builtin_amdgcn_global_load_lds(vbase + (size_t)d * page_size + c * 8,
+                                     LDS_PTR(stage + Geom<D>::KBYTES + seg * 1024), 16, 0, 0);
   }
 }
 
+// Partial context tile (`valid` < 64 tokens) -> LDS through registers, zero-filling the tokens
+// past the end so that whatever the page holds there never reaches the MFMA.
 template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D> &r, uint16_t *ks, uint16_t *vts,
-                                           int tid) {
-#pragma unroll
-  for (int c = 0; c < TileRegs<D>::KCH; ++c) {
-    const int idx = tid + c * kThreads;
-    const int row = idx / (D / 8), ch = idx % (D / 8);
-    st_lds_16(ks + row * D + ((ch ^ (row & 7)) * 8), r.k[c]);
+__device__ void load_tail_tile(char *stage, const uint16_t *kbase, const uint16_t *vbase,
+                               int page_size, int valid, int tid) {
+  constexpr int KC = D / 8;
+  uint16_t *ks = reinterpret_cast<uint16_t *>(stage);
+  uint16_t *vs = reinterpret_cast<uint16_t *>(stage + Geom<D>::KBYTES);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int f = tid; f < kTile * KC; f += kThreads) {
+    const int r = f / KC, c = f % KC;
+    const u32x4 x = r < valid ? ld_global_16(kbase + (size_t)r * D + c * 8) : z;
+    st_lds_16(ks + r * D + ((c ^ kkey<D>(r)) << 3), x);
   }
-#pragma unroll
-  for (int c = 0; c < TileRegs<D>::VCH; ++c) {
-    const int idx = tid + c * kThreads;
-    const int d = idx / 8, ch = idx % 8;
-    st_lds_16(vts + d * kTile + ((ch ^ (d & 7)) * 8), r.v[c]);
+  for (int f = tid; f < D * 8; f += kThreads) {
+    const int d = f / 8, c = f % 8;
+    const int n = valid - c * 8;
+    u32x4 x = n > 0 ? ld_global_16(vbase + (size_t)d * page_size + c * 8) : z;
+    x = keep_first(x, n < 0 ? 0 : (n > 8 ? 8 : n));
+    st_lds_16(vs + d * kTile + ((c ^ vkey(d)) << 3), x);
   }
 }
 
-// The block's own S keys/values of (b, g) into an LDS tile (element-wise; S need not be a
+// The block's own S keys/values of (b, g) into an LDS stage (element-wise; S need not be a
 // multiple of 8). Tokens >= S are zero.
 template <int D>
-__device__ void load_block_tile(uint16_t *ks, uint16_t *vts, const uint16_t *kblk,
-                                const uint16_t *vblk, int S, int tid) {
+__device__ void load_block_tile(char *stage, const uint16_t *kblk, const uint16_t *vblk, int S,
+                                int tid) {
+  uint16_t *ks = reinterpret_cast<uint16_t *>(stage);
+  uint16_t *vs = reinterpret_cast<uint16_t *>(stage + Geom<D>::KBYTES);
   for (int idx = tid; idx < kTile * D; idx += kThreads) {
     const int tok = idx / D, d = idx % D;
     const uint16_t x = tok < S ? kblk[tok * D + d] : (uint16_t)0;
-    ks[tok * D + (((d >> 3) ^ (tok & 7)) << 3) + (d & 7)] = x;
+    ks[tok * D + (((d >> 3) ^ kkey<D>(tok)) << 3) + (d & 7)] = x;
   }
   for (int idx = tid; idx < D * kTile; idx += kThreads) {
     const int d = idx / kTile, tok = idx % kTile;
     const uint16_t x = tok < S ? vblk[d * S + tok] : (uint16_t)0;
-    vts[d * kTile + (((tok >> 3) ^ (d & 7)) << 3) + (tok & 7)] = x;
+    vs[d * kTile + (((tok >> 3) ^ vkey(d)) << 3) + (tok & 7)] = x;
   }
 }
 
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+}
+
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8); expcnt and
+// lgkmcnt are left at their maxima so only vector-memory operations are waited for. Issued through
+// the builtin so that the compiler's own wait insertion knows about them.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Wait until at most `tiles_in_flight` tiles of DMA (LOADS instructions each) are outstanding.
+template <int LOADS>
+__device__ __forceinline__ void wait_dma(int tiles_in_flight) {
+  if (tiles_in_flight >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LOADS));
+  else if (tiles_in_flight == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS));
+  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+}
+
 // One LDS tile (`valid` tokens, <= 64) into the running softmax state of this wave's 32 rows.
-template <int D>
-__device__ __forceinline__ void attend_tile(const uint16_t *ks, const uint16_t *vts, int valid,
-                                            const u32x4 *qreg, f32x16 *oacc, float &m,
-                                            float &lpart, float c, int lane) {
+// m is the (possibly stale) reference maximum in raw score units; it only moves when some row's
+// maximum exceeds it by more than 2^kRescaleLog2 in probability, so exp2 stays <= 2^8.
+template <int D, bool FULL>
+__device__ __forceinline__ void attend_tile(const char *stage, int valid, const u32x4 *qreg,
+                                            f32x16 *oacc, float &m, float &lpart, float c,
+                                            int lane) {
+  const uint16_t *ks = reinterpret_cast<const uint16_t *>(stage);
+  const uint16_t *vts = reinterpret_cast<const uint16_t *>(stage + Geom<D>::KBYTES);
   const int col = lane & 31, hh = lane >> 5;
+  const int kk_key = kkey<D>(swap_bits23(col));
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
     const int base = sub * 32;
-    if (base >= valid) break;
+    if (!FULL && base >= valid) break;
     f32x16 s = {};
     const int tok = base + swap_bits23(col);
     const uint16_t *krow = ks + tok * D;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       const int ch = kk * 2 + hh;
-      s = mfma32x32x16(ld_lds_16(krow + ((ch ^ (tok & 7)) << 3)), qreg[kk], s);
+      s = mfma32x32x16(ld_lds_16(krow + ((ch ^ kk_key) << 3)), qreg[kk], s);
     }
-    const int nv = valid - base;
-    if (nv < 32) {
+    if (!FULL) {
+      const int nv = valid - base;
+      if (nv < 32) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int t = (i >> 3) * 16 + hh * 8 + (i & 7);
-        if (t >= nv) s[i] = -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          const int t = (i >> 3) * 16 + hh * 8 + (i & 7);
+          if (t >= nv) s[i] = -INFINITY;
+        }
       }
     }
     float mx = s[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
     mx = fmaxf(mx, swap_halves(mx));
-    const float mnew = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c);
-    const float mc = mnew * c;
+    if (__ballot((mx - m) * c > kRescaleLog2)) {
+      const float mnew = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c);
+      lpart *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
+      m = mnew;
+    }
+    const float mc = m * c;
     float p[16];
     float psum = 0.f;
 #pragma unroll
@@ -152,38 +212,27 @@ __device__ __forceinline__ void attend_tile(const uint16_t *ks, const uint16_t *
       p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -mc));
       psum += p[i];
     }
+    lpart += psum;
     u32x4 p0, p1;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       p0[w] = pack_bf16x2(p[2 * w], p[2 * w + 1]);
       p1[w] = pack_bf16x2(p[8 + 2 * w], p[8 + 2 * w + 1]);
     }
-    lpart = lpart * alpha + psum;
-    m = mnew;
-    if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
-    }
+    const int vk = vkey(col);
+    const int ch0 = (sub * 4 + hh) ^ vk, ch1 = (sub * 4 + 2 + hh) ^ vk;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
-      const int d = mb * 32 + col;
-      const uint16_t *vrow = vts + d * kTile;
-      const int ch0 = sub * 4 + hh, ch1 = sub * 4 + 2 + hh;
-      oacc[mb] = mfma32x32x16(ld_lds_16(vrow + ((ch0 ^ (d & 7)) << 3)), p0, oacc[mb]);
-      oacc[mb] = mfma32x32x16(ld_lds_16(vrow + ((ch1 ^ (d & 7)) << 3)), p1, oacc[mb]);
+      const uint16_t *vrow = vts + (mb * 32 + col) * kTile;
+      oacc[mb] = mfma32x32x16(ld_lds_16(vrow + (ch0 << 3)), p0, oacc[mb]);
+      oacc[mb] = mfma32x32x16(ld_lds_16(vrow + (ch1 << 3)), p1, oacc[mb]);
     }
   }
 }
 
 template <int D>
-struct AttnSmem {
-  uint16_t k[2][kTile * D];
-  uint16_t vt[2][D * kTile];
-};
-
-template <int D>
 __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) AttnSmem<D> sm;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int split = blockIdx.x;
   const int item_bgr = blockIdx.y;
   const int rg = item_bgr % p.row_groups;
@@ -199,28 +248,71 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   const bool has_block = split == 0;
   if (!has_block && t_begin >= Lc && !bad) return;  // partition past this sequence's context
 
-  const int n_ctx_tiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
-  const int n_tiles = (has_block ? 1 : 0) + n_ctx_tiles;
+  const int n_ctx = t_end > t_begin ? t_end - t_begin : 0;
+  const int n_full = n_ctx / kTile;            // full tiles: asynchronous ring
+  const int tail = n_ctx - n_full * kTile;     // tokens of the last, partial tile
 
   const uint16_t *kp = static_cast<const uint16_t *>(p.k_pages);
   const uint16_t *vp = static_cast<const uint16_t *>(p.v_pages);
   const int32_t *btab = p.block_table + (size_t)b * p.max_pages;
+  // The partition's page ids are staged in LDS once (the ring loop then issues no vector load of
+  // its own besides the DMA). Any id outside the pool makes the sequence bad: nothing is loaded
+  // from it and its outputs become NaN.
+  int *part_pages = reinterpret_cast<int *>(smem + kStages * Geom<D>::STAGE);
+  const int pg0 = t_begin / p.page_size;
+  const int n_pages = n_ctx > 0 ? (t_end - 1) / p.page_size - pg0 + 1 : 0;
+  int page_bad = 0;
+  for (int i = tid; i < n_pages; i += kThreads) {
+    const int page = btab[pg0 + i];
+    page_bad |= page < 0 || page >= p.num_pages;
+    part_pages[i] = page;
+  }
+  if (__syncthreads_or(page_bad)) bad = true;
+  const int n_full_ok = bad ? 0 : n_full;
+  const int tail_ok = bad ? 0 : tail;
+
+  auto tile_src = [&](int t0, const uint16_t *&kb, const uint16_t *&vb) {
+    const int page = part_pages[t0 / p.page_size - pg0];
+    const int off0 = t0 % p.page_size;
+    const size_t ph = (size_t)page * p.Hkv + g;
+    kb = kp + (ph * p.page_size + off0) * D;
+    vb = vp + ph * D * p.page_size + off0;
+  };
 
   // Query rows of this wave (B operand of S^T = K Q^T): row r -> (head j, position i).
   const int col = lane & 31, hh = lane >> 5;
   const int r_local = wave * 32 + col;
   const int r = rg * p.rows_per_group + r_local;
   const bool row_ok = r < p.rows && r_local < p.rows_per_group;
-  const bool wave_active = wave * 32 < p.rows_per_group && rg * p.rows_per_group + wave * 32 < p.rows;
+  const bool wave_active =
+      wave * 32 < p.rows_per_group && rg * p.rows_per_group + wave * 32 < p.rows;
   const int jq = row_ok ? r / p.S : 0, iq = row_ok ? r % p.S : 0;
   const int h = g * p.G + jq;
   u32x4 qreg[D / 16];
   {
-    const uint16_t *qrow = static_cast<const uint16_t *>(p.q) + (((size_t)b * p.S + iq) * p.Hq + h) * D;
+    const uint16_t *qrow =
+        static_cast<const uint16_t *>(p.q) + (((size_t)b * p.S + iq) * p.Hq + h) * D;
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      qreg[kk] = row_ok ? ld_global_16(qrow + kk * 16 + hh * 8) : z;
+    for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = row_ok ? ld_global_16(qrow + kk * 16 + hh * 8) : z;
+  }
+
+  // The block's own keys (partition 0) go through the last stage, loaded before the ring starts
+  // so that waiting for them never waits for context tiles.
+  char *const block_stage = smem + (kStages - 1) * Geom<D>::STAGE;
+  if (has_block) {
+    const size_t bg = (size_t)b * p.Hkv + g;
+    load_block_tile<D>(block_stage, static_cast<const uint16_t *>(p.k_blk) + bg * p.S * D,
+                       static_cast<const uint16_t *>(p.v_blk) + bg * D * p.S, p.S, tid);
+  }
+
+  // Start the ring: context tiles 0 .. kStages-2 into stages 0 .. kStages-2.
+#pragma unroll
+  for (int n = 0; n < kStages - 1; ++n) {
+    if (n < n_full_ok) {
+      const uint16_t *kb, *vb;
+      tile_src(t_begin + n * kTile, kb, vb);
+      dma_tile<D>(smem + n * Geom<D>::STAGE, kb, vb, p.page_size, wave, lane);
     }
   }
 
@@ -230,43 +322,36 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   float m = -INFINITY, lpart = 0.f;
   const float c = p.scale * kLog2e;
 
-  // Tile n: the block tile first (partition 0), then the context tiles of this partition.
-  auto ctx_tile_of = [&](int n) { return n - (has_block ? 1 : 0); };
-  auto tile_valid = [&](int n) -> int {
-    const int ct = ctx_tile_of(n);
-    if (ct < 0) return p.S;
-    return min(kTile, t_end - (t_begin + ct * kTile));
-  };
-  auto fetch = [&](TileRegs<D> &regs, int n) {
-    const int t0 = t_begin + ctx_tile_of(n) * kTile;
-    const int page = btab[t0 / p.page_size];
-    const int off0 = t0 % p.page_size;
-    const bool page_ok = page >= 0 && page < p.num_pages;
-    if (!page_ok) bad = true;
-    const size_t ph = ((size_t)(page_ok ? page : 0) * p.Hkv + g);
-    fetch_ctx_tile<D>(regs, kp + (ph * p.page_size + off0) * D, vp + ph * D * p.page_size + off0,
-                      p.page_size, page_ok ? tile_valid(n) : 0, tid);
-  };
-
-  TileRegs<D> regs;
-  if (n_tiles > 0) {
-    if (has_block) {
-      const size_t bg = (size_t)b * p.Hkv + g;
-      load_block_tile<D>(sm.k[0], sm.vt[0], static_cast<const uint16_t *>(p.k_blk) + bg * p.S * D,
-                         static_cast<const uint16_t *>(p.v_blk) + bg * D * p.S, p.S, tid);
-    } else {
-      fetch(regs, 0);
-      store_tile<D>(regs, sm.k[0], sm.vt[0], tid);
-    }
-    if (n_tiles > 1) fetch(regs, 1);
-    __syncthreads();
+  // Q (and the first context tiles) have landed: inside the loop only the ring's own DMA is
+  // ever waited for.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  if (has_block) {
+    lds_barrier();
+    if (wave_active) attend_tile<D, false>(block_stage, p.S, qreg, oacc, m, lpart, c, lane);
   }
-  for (int n = 0; n < n_tiles; ++n) {
-    const int buf = n & 1;
-    if (wave_active) attend_tile<D>(sm.k[buf], sm.vt[buf], tile_valid(n), qreg, oacc, m, lpart, c, lane);
-    if (n + 1 < n_tiles) store_tile<D>(regs, sm.k[buf ^ 1], sm.vt[buf ^ 1], tid);
-    if (n + 2 < n_tiles) fetch(regs, n + 2);
-    __syncthreads();
+
+  for (int n = 0; n < n_full_ok; ++n) {
+    wait_dma<Geom<D>::LOADS>(min(kStages - 2, n_full_ok - 1 - n));
+    lds_barrier();  // tile n is in LDS for every wave; stage (n-1) % kStages is free again
+    const int nn = n + kStages - 1;
+    if (nn < n_full_ok) {
+      const uint16_t *kb, *vb;
+      tile_src(t_begin + nn * kTile, kb, vb);
+      dma_tile<D>(smem + (nn % kStages) * Geom<D>::STAGE, kb, vb, p.page_size, wave, lane);
+    }
+    if (wave_active)
+      attend_tile<D, true>(smem + (n % kStages) * Geom<D>::STAGE, kTile, qreg, oacc, m, lpart, c,
+                           lane);
+  }
+
+  if (tail_ok > 0) {
+    lds_barrier();  // every wave is done with the ring before a stage is overwritten
+    const uint16_t *kb, *vb;
+    tile_src(t_begin + n_full_ok * kTile, kb, vb);
+    char *st = smem + (n_full_ok % kStages) * Geom<D>::STAGE;
+    load_tail_tile<D>(st, kb, vb, p.page_size, tail_ok, tid);
+    lds_barrier();
+    if (wave_active) attend_tile<D, false>(st, tail_ok, qreg, oacc, m, lpart, c, lane);
   }
 
   if (!wave_active) return;
@@ -489,26 +574,39 @@ __global__ __launch_bounds__(256) void block_attn_f32_kernel(AttnParams p) {
 hipError_t launch_block_attn_bf16(const AttnParams &p, hipStream_t stream, hipEvent_t ev_begin,
                                   hipEvent_t ev_end) {
   dim3 grid(p.splits, p.B * p.Hkv * p.row_groups);
-  if (ev_begin) hipEventRecord(ev_begin, stream);
-  if (p.D == 128)
-    hipLaunchKernelGGL(block_attn_bf16_kernel<128>, grid, dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(block_attn_bf16_kernel<64>, grid, dim3(kThreads), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (ev_end) hipEventRecord(ev_end, stream);
+  hipError_t e = hipSuccess;
+  if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess) return e;
+  if (p.D == 128) {
+    constexpr int lds = kStages * Geom<128>::STAGE + kMaxPartPages * 4;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&block_attn_bf16_kernel<128>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(block_attn_bf16_kernel<128>, grid, dim3(kThreads), lds, stream, p);
+  } else {
+    constexpr int lds = kStages * Geom<64>::STAGE + kMaxPartPages * 4;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&block_attn_bf16_kernel<64>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(block_attn_bf16_kernel<64>, grid, dim3(kThreads), lds, stream, p);
+  }
+  e = hipGetLastError();
+  if (e == hipSuccess && ev_end) e = hipEventRecord(ev_end, stream);
   return e;
 }
 
 hipError_t launch_block_attn_f32(const AttnParams &p, hipStream_t stream, hipEvent_t ev_begin,
                                  hipEvent_t ev_end) {
   dim3 grid(p.S, p.Hq, p.B);
-  if (ev_begin) hipEventRecord(ev_begin, stream);
+  hipError_t e = hipSuccess;
+  if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess) return e;
   if (p.D == 128)
     hipLaunchKernelGGL(block_attn_f32_kernel<128>, grid, dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL(block_attn_f32_kernel<64>, grid, dim3(256), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (ev_end) hipEventRecord(ev_end, stream);
+  e = hipGetLastError();
+  if (e == hipSuccess && ev_end) e = hipEventRecord(ev_end, stream);
   return e;
 }
 
