@@ -102,7 +102,7 @@ tt_status plan_attn(const tt_block_attn_args *a, bool check_pointers, AttnPlan *
   out->ws_bytes = 0;
   if (p.splits > 1) {
     const size_t items = (size_t)p.B * p.Hkv * p.row_groups * p.splits;
-    out->ws_bytes = align_up(items * p.rows_per_group * p.D * sizeof(float)) +
+    out->ws_bytes = align_up(items * p.rows_per_group * p.D * sizeof(uint16_t)) +
                     align_up(items * p.rows_per_group * sizeof(float));
   }
   return TT_OK;
@@ -115,8 +115,8 @@ hipError_t run_attn(AttnPlan &pl, void *ws, hipStream_t stream, hipEvent_t e0, h
   if (p.splits > 1) {
     const size_t items = (size_t)p.B * p.Hkv * p.row_groups * p.splits;
     char *w = static_cast<char *>(ws);
-    p.part_o = reinterpret_cast<float *>(w);
-    p.part_lse = reinterpret_cast<float *>(w + align_up(items * p.rows_per_group * p.D * sizeof(float)));
+    p.part_o = w;
+    p.part_lse = reinterpret_cast<float *>(w + align_up(items * p.rows_per_group * p.D * sizeof(uint16_t)));
   }
   hipError_t e = tt::launch_block_attn_bf16(p, stream, e0, e1);
   if (e != hipSuccess || p.splits == 1) return e;

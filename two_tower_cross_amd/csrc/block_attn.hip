@@ -23,6 +23,8 @@
 // fp32 path: one work-group per (b, query head, block position), plain fp32 arithmetic.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -61,83 +63,161 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int n) {
   return r;
 }
 
+// LDS map of the bf16 kernel: K stages [kStages][64 tokens][D], then V stages
+// [kStages][D][64 tokens], then the partition's page ids. Every stage offset stays within the
+// 16-bit immediate of ds_read, so with the stage index known at compile time each operand read
+// is one VGPR offset plus an immediate.
 template <int D>
 struct Geom {
   static constexpr int KBYTES = kTile * D * 2;
   static constexpr int VBYTES = D * kTile * 2;
-  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int VBASE = kStages * KBYTES;
+  static constexpr int PAGES = VBASE + kStages * VBYTES;
+  static constexpr int LDS = PAGES + kMaxPartPages * 4;
   static constexpr int KCH = KBYTES / 16 / kThreads;  // 16-byte K chunks per thread per tile
   static constexpr int VCH = VBYTES / 16 / kThreads;
   static constexpr int LOADS = KCH + VCH;             // DMA instructions per thread per tile
+  static __device__ __forceinline__ constexpr int koff(int s) { return s * KBYTES; }
+  static __device__ __forceinline__ constexpr int voff(int s) { return VBASE + s * VBYTES; }
 };
 
-// Full 64-token context tile -> LDS stage, asynchronously (global_load_lds, 16 B per lane).
-// Instruction j of wave w fills LDS bytes [(j*8 + w)*1024, +1024) lane by lane; the source of
-// each lane is the logical chunk that the swizzle places in that slot.
+// Per-lane constants of one wave: LDS byte offsets of its MFMA operands within a stage and the
+// byte offsets of its DMA sources within a tile.
 template <int D>
-__device__ __forceinline__ void dma_tile(char *stage, const uint16_t *kbase,
-                                         const uint16_t *vbase, int page_size, int wave,
-                                         int lane) {
-  constexpr int KC = D / 8;
+struct LaneMap {
+  int k[D / 16];    // K operand of S^T = K Q^T, sub-tile 0 (sub-tile 1 is +32 rows)
+  int v[2][2];      // V operand of O^T += V^T P^T for (sub-tile, 16-token half), incl. VBASE
+  uint32_t kdma[Geom<D>::KCH];  // source byte offsets of this lane's K chunks in a tile
+  uint32_t vdma[Geom<D>::VCH];  // source byte offsets of its V chunks (row stride = page)
+  int kdst[Geom<D>::KCH];       // LDS byte offsets (wave-uniform) of those DMA segments
+  int vdst[Geom<D>::VCH];
+
+  __device__ __forceinline__ void init(int lane, int wave, int page_size) {
+    const int col = lane & 31, hh = lane >> 5;
+    const int tok = swap_bits23(col);
+    const int key = kkey<D>(tok);
 #pragma unroll
-  for (int j = 0; j < Geom<D>::KCH; ++j) {
-    const int seg = j * kWaves + wave;
-    const int f = seg * 64 + lane;
-    const int r = f / KC, p = f % KC;
-    const int c = p ^ kkey<D>(r);
-    __builtin_amdgcn_global_load_lds(kbase + (size_t)r * D + c * 8, LDS_PTR(stage + seg * 1024),
+    for (int kk = 0; kk < D / 16; ++kk) k[kk] = tok * D * 2 + (((kk * 2 + hh) ^ key) << 4);
+    const int vk = vkey(col);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+        v[sub][kc] = Geom<D>::VBASE + col * kTile * 2 + (((sub * 4 + kc * 2 + hh) ^ vk) << 4);
+    constexpr int KC = D / 8;
+#pragma unroll
+    for (int j = 0; j < Geom<D>::KCH; ++j) {
+      const int seg = j * kWaves + wave;
+      const int f = seg * 64 + lane;
+      const int r = f / KC, pp = f % KC;
+      kdma[j] = (uint32_t)(r * D + ((pp ^ kkey<D>(r)) << 3)) * 2u;
+      kdst[j] = seg * 1024;
+    }
+#pragma unroll
+    for (int j = 0; j < Geom<D>::VCH; ++j) {
+      const int seg = j * kWaves + wave;
+      const int f = seg * 64 + lane;
+      const int d = f / 8, pp = f % 8;
+      vdma[j] = (uint32_t)((size_t)d * page_size + ((pp ^ vkey(d)) << 3)) * 2u;
+      vdst[j] = seg * 1024;
+    }
+  }
+};
+
+// Full 64-token context tile -> LDS stage s, asynchronously (global_load_lds, 16 B per lane).
+// Each instruction fills 1024 contiguous LDS bytes lane by lane; the source of each lane is the
+// logical chunk that the swizzle places in that slot.
+template <int D>
+__device__ __forceinline__ void dma_tile(char *smem, int s, const char *kb, const char *vb,
+                                         const LaneMap<D> &lm) {
+#pragma unroll
+  for (int j = 0; j < Geom<D>::KCH; ++j)
+    __builtin_amdgcn_global_load_lds(kb + lm.kdma[j], LDS_PTR(smem + Geom<D>::koff(s) + lm.kdst[j]),
                                      16, 0, 0);
-  }
 #pragma unroll
-  for (int j = 0; j < Geom<D>::VCH; ++j) {
-    const int seg = j * kWaves + wave;
-    const int f = seg * 64 + lane;
-    const int d = f / 8, p = f % 8;
-    const int c = p ^ vkey(d);
-    __builtin_amdgcn_global_load_lds(vbase + (size_t)d * page_size + c * 8,
-                                     LDS_PTR(stage + Geom<D>::KBYTES + seg * 1024), 16, 0, 0);
-  }
+  for (int j = 0; j < Geom<D>::VCH; ++j)
+    __builtin_amdgcn_global_load_lds(vb + lm.vdma[j], LDS_PTR(smem + Geom<D>::voff(s) + lm.vdst[j]),
+                                     16, 0, 0);
 }
 
-// Partial context tile (`valid` < 64 tokens) -> LDS through registers, zero-filling the tokens
-// past the end so that whatever the page holds there never reaches the MFMA.
+// Partial context tile (`valid` < 64 tokens) -> LDS stage s through registers, zero-filling the
+// tokens past the end so that whatever the page holds there never reaches the MFMA. All of a
+// thread's loads are issued before its first store, so the tile costs one memory round trip.
 template <int D>
-__device__ void load_tail_tile(char *stage, const uint16_t *kbase, const uint16_t *vbase,
+__device__ void load_tail_tile(char *smem, int s, const uint16_t *kbase, const uint16_t *vbase,
                                int page_size, int valid, int tid) {
   constexpr int KC = D / 8;
-  uint16_t *ks = reinterpret_cast<uint16_t *>(stage);
-  uint16_t *vs = reinterpret_cast<uint16_t *>(stage + Geom<D>::KBYTES);
+  constexpr int NK = kTile * KC / kThreads, NV = D * 8 / kThreads;
+  uint16_t *ks = reinterpret_cast<uint16_t *>(smem + Geom<D>::koff(s));
+  uint16_t *vs = reinterpret_cast<uint16_t *>(smem + Geom<D>::voff(s));
   const u32x4 z = {0u, 0u, 0u, 0u};
-  for (int f = tid; f < kTile * KC; f += kThreads) {
-    const int r = f / KC, c = f % KC;
-    const u32x4 x = r < valid ? ld_global_16(kbase + (size_t)r * D + c * 8) : z;
-    st_lds_16(ks + r * D + ((c ^ kkey<D>(r)) << 3), x);
+  u32x4 xk[NK], xv[NV];
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    const int f = tid + j * kThreads, r = f / KC, c = f % KC;
+    xk[j] = r < valid ? ld_global_16(kbase + (size_t)r * D + c * 8) : z;
   }
-  for (int f = tid; f < D * 8; f += kThreads) {
-    const int d = f / 8, c = f % 8;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int f = tid + j * kThreads, d = f / 8, c = f % 8;
+    xv[j] = c * 8 < valid ? ld_global_16(vbase + (size_t)d * page_size + c * 8) : z;
+  }
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    const int f = tid + j * kThreads, r = f / KC, c = f % KC;
+    st_lds_16(ks + r * D + ((c ^ kkey<D>(r)) << 3), xk[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int f = tid + j * kThreads, d = f / 8, c = f % 8;
     const int n = valid - c * 8;
-    u32x4 x = n > 0 ? ld_global_16(vbase + (size_t)d * page_size + c * 8) : z;
-    x = keep_first(x, n < 0 ? 0 : (n > 8 ? 8 : n));
-    st_lds_16(vs + d * kTile + ((c ^ vkey(d)) << 3), x);
+    st_lds_16(vs + d * kTile + ((c ^ vkey(d)) << 3), keep_first(xv[j], n < 0 ? 0 : (n > 8 ? 8 : n)));
   }
 }
 
-// The block's own S keys/values of (b, g) into an LDS stage (element-wise; S need not be a
-// multiple of 8). Tokens >= S are zero.
+// The block's own S keys/values of (b, g) into LDS stage s; tokens >= S are zero. K rows are
+// contiguous ([S][D]); a V row holds S tokens ([D][S]), 16-byte aligned when S % 8 == 0, else
+// gathered element by element. Loads are issued before stores (one memory round trip).
 template <int D>
-__device__ void load_block_tile(char *stage, const uint16_t *kblk, const uint16_t *vblk, int S,
-                                int tid) {
-  uint16_t *ks = reinterpret_cast<uint16_t *>(stage);
-  uint16_t *vs = reinterpret_cast<uint16_t *>(stage + Geom<D>::KBYTES);
-  for (int idx = tid; idx < kTile * D; idx += kThreads) {
-    const int tok = idx / D, d = idx % D;
-    const uint16_t x = tok < S ? kblk[tok * D + d] : (uint16_t)0;
-    ks[tok * D + (((d >> 3) ^ kkey<D>(tok)) << 3) + (d & 7)] = x;
+__device__ void load_block_tile(char *smem, int s, const uint16_t *kblk, const uint16_t *vblk,
+                                int S, int tid) {
+  constexpr int KC = D / 8;
+  constexpr int NK = kTile * KC / kThreads, NV = D * 8 / kThreads;
+  uint16_t *ks = reinterpret_cast<uint16_t *>(smem + Geom<D>::koff(s));
+  uint16_t *vs = reinterpret_cast<uint16_t *>(smem + Geom<D>::voff(s));
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  u32x4 xk[NK], xv[NV];
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    const int f = tid + j * kThreads, r = f / KC, c = f % KC;
+    xk[j] = r < S ? ld_global_16(kblk + (size_t)r * D + c * 8) : z;
   }
-  for (int idx = tid; idx < D * kTile; idx += kThreads) {
-    const int d = idx / kTile, tok = idx % kTile;
-    const uint16_t x = tok < S ? vblk[d * S + tok] : (uint16_t)0;
-    vs[d * kTile + (((tok >> 3) ^ vkey(d)) << 3) + (tok & 7)] = x;
+  if ((S & 7) == 0) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int f = tid + j * kThreads, d = f / 8, c = f % 8;
+      xv[j] = c * 8 < S ? ld_global_16(vblk + (size_t)d * S + c * 8) : z;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int f = tid + j * kThreads, d = f / 8, c = f % 8;
+      uint16_t e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = c * 8 + i < S ? vblk[(size_t)d * S + c * 8 + i] : (uint16_t)0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) xv[j][w] = (uint32_t)e[2 * w] | ((uint32_t)e[2 * w + 1] << 16);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    const int f = tid + j * kThreads, r = f / KC, c = f % KC;
+    st_lds_16(ks + r * D + ((c ^ kkey<D>(r)) << 3), xk[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int f = tid + j * kThreads, d = f / 8, c = f % 8;
+    st_lds_16(vs + d * kTile + ((c ^ vkey(d)) << 3), xv[j]);
   }
 }
 
@@ -159,74 +239,109 @@ __device__ __forceinline__ void wait_dma(int tiles_in_flight) {
   else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
-// One LDS tile (`valid` tokens, <= 64) into the running softmax state of this wave's 32 rows.
-// m is the (possibly stale) reference maximum in raw score units; it only moves when some row's
-// maximum exceeds it by more than 2^kRescaleLog2 in probability, so exp2 stays <= 2^8.
+// One 64-token LDS tile (at byte offsets kst / vst of K and V) into the running softmax state of
+// this wave's 32 query rows. Two phases, each one basic block: (1) S^T of both 32-token
+// sub-tiles (two independent MFMA chains) and their row maximum; (2) the exponentials of
+// sub-tile 0, its PV product, then those of sub-tile 1 and its PV product, so the VALU work of one
+// sub-tile can issue under the MFMAs of the other. m is a reference maximum in raw score units
+// that only moves when some row's maximum exceeds it by more than 2^kRescaleLog2 in
+// probability, so every exponential stays <= 2^8.
 template <int D, bool FULL>
-__device__ __forceinline__ void attend_tile(const char *stage, int valid, const u32x4 *qreg,
+__device__ __forceinline__ void attend_tile(const char *smem, int kst, int vst, int valid,
+                                            const LaneMap<D> &lm, const u32x4 *qreg,
                                             f32x16 *oacc, float &m, float &lpart, float c,
                                             int lane) {
-  const uint16_t *ks = reinterpret_cast<const uint16_t *>(stage);
-  const uint16_t *vts = reinterpret_cast<const uint16_t *>(stage + Geom<D>::KBYTES);
-  const int col = lane & 31, hh = lane >> 5;
-  const int kk_key = kkey<D>(swap_bits23(col));
+  const int hh = lane >> 5;
+  f32x16 s0 = {}, s1 = {};
+  u32x4 a0[D / 16], a1[D / 16];
 #pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    const int base = sub * 32;
-    if (!FULL && base >= valid) break;
-    f32x16 s = {};
-    const int tok = base + swap_bits23(col);
-    const uint16_t *krow = ks + tok * D;
+  for (int kk = 0; kk < D / 16; ++kk) {
+    a0[kk] = ld_lds_16(smem + kst + lm.k[kk]);
+    a1[kk] = ld_lds_16(smem + kst + lm.k[kk] + 32 * D * 2);
+  }
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const int ch = kk * 2 + hh;
-      s = mfma32x32x16(ld_lds_16(krow + ((ch ^ kk_key) << 3)), qreg[kk], s);
-    }
-    if (!FULL) {
-      const int nv = valid - base;
-      if (nv < 32) {
+  for (int kk = 0; kk < D / 16; ++kk) {
+    s0 = mfma32x32x16(a0[kk], qreg[kk], s0);
+    s1 = mfma32x32x16(a1[kk], qreg[kk], s1);
+  }
+  // Operand reads run four K-steps ahead of the MFMAs that consume them.
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int t = (i >> 3) * 16 + hh * 8 + (i & 7);
-          if (t >= nv) s[i] = -INFINITY;
-        }
-      }
-    }
-    float mx = s[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, swap_halves(mx));
-    if (__ballot((mx - m) * c > kRescaleLog2)) {
-      const float mnew = fmaxf(m, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c);
-      lpart *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
-      m = mnew;
-    }
-    const float mc = m * c;
-    float p[16];
-    float psum = 0.f;
+  for (int i = 0; i < D / 16 - 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  if (!FULL) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -mc));
-      psum += p[i];
+      const int t = (i >> 3) * 16 + hh * 8 + (i & 7);
+      if (t >= valid) s0[i] = -INFINITY;
+      if (t + 32 >= valid) s1[i] = -INFINITY;
     }
-    lpart += psum;
-    u32x4 p0, p1;
+  }
+  float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      p0[w] = pack_bf16x2(p[2 * w], p[2 * w + 1]);
-      p1[w] = pack_bf16x2(p[8 + 2 * w], p[8 + 2 * w + 1]);
-    }
-    const int vk = vkey(col);
-    const int ch0 = (sub * 4 + hh) ^ vk, ch1 = (sub * 4 + 2 + hh) ^ vk;
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+  mx = fmaxf(mx, swap_halves(mx));
+  if (__ballot((mx - m) * c > kRescaleLog2)) {
+    const float mnew = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c);
+    lpart *= alpha;
 #pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) {
-      const uint16_t *vrow = vts + (mb * 32 + col) * kTile;
-      oacc[mb] = mfma32x32x16(ld_lds_16(vrow + (ch0 << 3)), p0, oacc[mb]);
-      oacc[mb] = mfma32x32x16(ld_lds_16(vrow + (ch1 << 3)), p1, oacc[mb]);
-    }
+    for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
+    m = mnew;
+  }
+  const float mc = m * c;
+  float psum = 0.f;
+  u32x4 pa, pb;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float e0 = __builtin_amdgcn_exp2f(fmaf(s0[2 * w], c, -mc));
+    const float e1 = __builtin_amdgcn_exp2f(fmaf(s0[2 * w + 1], c, -mc));
+    const float e2 = __builtin_amdgcn_exp2f(fmaf(s0[8 + 2 * w], c, -mc));
+    const float e3 = __builtin_amdgcn_exp2f(fmaf(s0[8 + 2 * w + 1], c, -mc));
+    psum += (e0 + e1) + (e2 + e3);
+    pa[w] = pack_bf16x2(e0, e1);
+    pb[w] = pack_bf16x2(e2, e3);
+  }
+  u32x4 v0[D / 16], v1[D / 16];
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) {
+    v0[2 * mb] = ld_lds_16(smem + vst + lm.v[0][0] + mb * 32 * kTile * 2);
+    v0[2 * mb + 1] = ld_lds_16(smem + vst + lm.v[0][1] + mb * 32 * kTile * 2);
+  }
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) {
+    v1[2 * mb] = ld_lds_16(smem + vst + lm.v[1][0] + mb * 32 * kTile * 2);
+    v1[2 * mb + 1] = ld_lds_16(smem + vst + lm.v[1][1] + mb * 32 * kTile * 2);
+  }
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) {
+    oacc[mb] = mfma32x32x16(v0[2 * mb], pa, oacc[mb]);
+    oacc[mb] = mfma32x32x16(v0[2 * mb + 1], pb, oacc[mb]);
+  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float e0 = __builtin_amdgcn_exp2f(fmaf(s1[2 * w], c, -mc));
+    const float e1 = __builtin_amdgcn_exp2f(fmaf(s1[2 * w + 1], c, -mc));
+    const float e2 = __builtin_amdgcn_exp2f(fmaf(s1[8 + 2 * w], c, -mc));
+    const float e3 = __builtin_amdgcn_exp2f(fmaf(s1[8 + 2 * w + 1], c, -mc));
+    psum += (e0 + e1) + (e2 + e3);
+    pa[w] = pack_bf16x2(e0, e1);
+    pb[w] = pack_bf16x2(e2, e3);
+  }
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) {
+    oacc[mb] = mfma32x32x16(v1[2 * mb], pa, oacc[mb]);
+    oacc[mb] = mfma32x32x16(v1[2 * mb + 1], pb, oacc[mb]);
+  }
+  lpart += psum;
+  // The exponentials of sub-tile 1 issue between the PV MFMAs of sub-tile 0.
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);
   }
 }
 
@@ -238,7 +353,8 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   const int rg = item_bgr % p.row_groups;
   const int g = (item_bgr / p.row_groups) % p.Hkv;
   const int b = item_bgr / (p.row_groups * p.Hkv);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const int L = p.ctx_lens[b];
   bool bad = L < 0 || L > p.max_ctx_len;
@@ -258,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   // The partition's page ids are staged in LDS once (the ring loop then issues no vector load of
   // its own besides the DMA). Any id outside the pool makes the sequence bad: nothing is loaded
   // from it and its outputs become NaN.
-  int *part_pages = reinterpret_cast<int *>(smem + kStages * Geom<D>::STAGE);
+  int *part_pages = reinterpret_cast<int *>(smem + Geom<D>::PAGES);
   const int pg0 = t_begin / p.page_size;
   const int n_pages = n_ctx > 0 ? (t_end - 1) / p.page_size - pg0 + 1 : 0;
   int page_bad = 0;
@@ -271,13 +387,17 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   const int n_full_ok = bad ? 0 : n_full;
   const int tail_ok = bad ? 0 : tail;
 
-  auto tile_src = [&](int t0, const uint16_t *&kb, const uint16_t *&vb) {
-    const int page = part_pages[t0 / p.page_size - pg0];
+  // Global byte address of the K and V tile that starts at context token t0 (wave-uniform).
+  auto tile_src = [&](int t0, const char *&kb, const char *&vb) {
+    const int page = __builtin_amdgcn_readfirstlane(part_pages[t0 / p.page_size - pg0]);
     const int off0 = t0 % p.page_size;
     const size_t ph = (size_t)page * p.Hkv + g;
-    kb = kp + (ph * p.page_size + off0) * D;
-    vb = vp + ph * D * p.page_size + off0;
+    kb = reinterpret_cast<const char *>(kp + (ph * p.page_size + off0) * D);
+    vb = reinterpret_cast<const char *>(vp + ph * D * p.page_size + off0);
   };
+
+  LaneMap<D> lm;
+  lm.init(lane, wave, p.page_size);
 
   // Query rows of this wave (B operand of S^T = K Q^T): row r -> (head j, position i).
   const int col = lane & 31, hh = lane >> 5;
@@ -299,10 +419,9 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
 
   // The block's own keys (partition 0) go through the last stage, loaded before the ring starts
   // so that waiting for them never waits for context tiles.
-  char *const block_stage = smem + (kStages - 1) * Geom<D>::STAGE;
   if (has_block) {
     const size_t bg = (size_t)b * p.Hkv + g;
-    load_block_tile<D>(block_stage, static_cast<const uint16_t *>(p.k_blk) + bg * p.S * D,
+    load_block_tile<D>(smem, kStages - 1, static_cast<const uint16_t *>(p.k_blk) + bg * p.S * D,
                        static_cast<const uint16_t *>(p.v_blk) + bg * D * p.S, p.S, tid);
   }
 
@@ -310,9 +429,9 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
 #pragma unroll
   for (int n = 0; n < kStages - 1; ++n) {
     if (n < n_full_ok) {
-      const uint16_t *kb, *vb;
+      const char *kb, *vb;
       tile_src(t_begin + n * kTile, kb, vb);
-      dma_tile<D>(smem + n * Geom<D>::STAGE, kb, vb, p.page_size, wave, lane);
+      dma_tile<D>(smem, n, kb, vb, lm);
     }
   }
 
@@ -327,87 +446,113 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   if (has_block) {
     lds_barrier();
-    if (wave_active) attend_tile<D, false>(block_stage, p.S, qreg, oacc, m, lpart, c, lane);
+    if (wave_active)
+      attend_tile<D, false>(smem, Geom<D>::koff(kStages - 1), Geom<D>::voff(kStages - 1) -
+                            Geom<D>::VBASE, p.S, lm, qreg, oacc, m, lpart, c, lane);
   }
 
-  for (int n = 0; n < n_full_ok; ++n) {
+  // The ring, unrolled by its depth so that every stage offset is a compile-time immediate.
+  auto ring_step = [&](auto stage_tag, int n) {
+    constexpr int S = decltype(stage_tag)::value;
     wait_dma<Geom<D>::LOADS>(min(kStages - 2, n_full_ok - 1 - n));
     lds_barrier();  // tile n is in LDS for every wave; stage (n-1) % kStages is free again
     const int nn = n + kStages - 1;
     if (nn < n_full_ok) {
-      const uint16_t *kb, *vb;
+      const char *kb, *vb;
       tile_src(t_begin + nn * kTile, kb, vb);
-      dma_tile<D>(smem + (nn % kStages) * Geom<D>::STAGE, kb, vb, p.page_size, wave, lane);
+      dma_tile<D>(smem, (S + kStages - 1) % kStages, kb, vb, lm);
     }
     if (wave_active)
-      attend_tile<D, true>(smem + (n % kStages) * Geom<D>::STAGE, kTile, qreg, oacc, m, lpart, c,
-                           lane);
+      attend_tile<D, true>(smem, Geom<D>::koff(S), Geom<D>::voff(S) - Geom<D>::VBASE, kTile, lm,
+                           qreg, oacc, m, lpart, c, lane);
+  };
+  for (int n = 0; n < n_full_ok; n += kStages) {
+    ring_step(std::integral_constant<int, 0>{}, n);
+    if (n + 1 < n_full_ok) ring_step(std::integral_constant<int, 1>{}, n + 1);
+    if (n + 2 < n_full_ok) ring_step(std::integral_constant<int, 2>{}, n + 2);
+    if (n + 3 < n_full_ok) ring_step(std::integral_constant<int, 3>{}, n + 3);
   }
 
   if (tail_ok > 0) {
     lds_barrier();  // every wave is done with the ring before a stage is overwritten
-    const uint16_t *kb, *vb;
+    const int st = n_full_ok % kStages;
+    const char *kb, *vb;
     tile_src(t_begin + n_full_ok * kTile, kb, vb);
-    char *st = smem + (n_full_ok % kStages) * Geom<D>::STAGE;
-    load_tail_tile<D>(st, kb, vb, p.page_size, tail_ok, tid);
+    load_tail_tile<D>(smem, st, reinterpret_cast<const uint16_t *>(kb),
+                      reinterpret_cast<const uint16_t *>(vb), p.page_size, tail_ok, tid);
     lds_barrier();
-    if (wave_active) attend_tile<D, false>(st, tail_ok, qreg, oacc, m, lpart, c, lane);
+    if (wave_active)
+      attend_tile<D, false>(smem, Geom<D>::koff(st), Geom<D>::voff(st) - Geom<D>::VBASE, tail_ok,
+                            lm, qreg, oacc, m, lpart, c, lane);
   }
 
+  // Epilogue. Each wave stages its normalized 32 x D output block in a private LDS slice (the
+  // ring is idle once every wave has passed this barrier) and writes it back row by row, so
+  // every store instruction covers whole contiguous rows.
+  lds_barrier();
   if (!wave_active) return;
   const float l = lpart + swap_halves(lpart);
-  const float inv = 1.0f / l;
+  const float inv = bad ? NAN : 1.0f / l;
   const float lse_val = bad ? NAN : m * p.scale + logf(l);
-  const float nanv = NAN;
-  if (p.splits == 1) {
-    if (!row_ok) return;
-    if (p.out_bf16) {
-      uint16_t *orow = static_cast<uint16_t *>(p.out) + (((size_t)b * p.S + iq) * p.Hq + h) * D;
+  const bool to_part = p.splits > 1;
+  const bool half_out = to_part || p.out_bf16;     // 2-byte elements (fp16 partial / bf16 out)
+  char *slice = smem + wave * (32 * D * 4);
+  if (half_out) {
+    uint16_t *st = reinterpret_cast<uint16_t *>(slice);
 #pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb)
+    for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d = mb * 32 + q4 * 8 + hh * 4;
-          float o0 = bad ? nanv : oacc[mb][q4 * 4 + 0] * inv, o1 = bad ? nanv : oacc[mb][q4 * 4 + 1] * inv;
-          float o2 = bad ? nanv : oacc[mb][q4 * 4 + 2] * inv, o3 = bad ? nanv : oacc[mb][q4 * 4 + 3] * inv;
-          uint2 pk;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = mb * 32 + q4 * 8 + hh * 4;
+        const float o0 = oacc[mb][q4 * 4 + 0] * inv, o1 = oacc[mb][q4 * 4 + 1] * inv;
+        const float o2 = oacc[mb][q4 * 4 + 2] * inv, o3 = oacc[mb][q4 * 4 + 3] * inv;
+        uint2 pk;
+        if (to_part) {
+          pk.x = pack_f16x2(o0, o1);
+          pk.y = pack_f16x2(o2, o3);
+        } else {
           pk.x = pack_bf16x2(o0, o1);
           pk.y = pack_bf16x2(o2, o3);
-          *reinterpret_cast<uint2 *>(orow + d) = pk;
         }
-    } else {
-      float *orow = static_cast<float *>(p.out) + (((size_t)b * p.S + iq) * p.Hq + h) * D;
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d = mb * 32 + q4 * 8 + hh * 4;
-          f32x4 o;
-          o[0] = bad ? nanv : oacc[mb][q4 * 4 + 0] * inv;
-          o[1] = bad ? nanv : oacc[mb][q4 * 4 + 1] * inv;
-          o[2] = bad ? nanv : oacc[mb][q4 * 4 + 2] * inv;
-          o[3] = bad ? nanv : oacc[mb][q4 * 4 + 3] * inv;
-          *reinterpret_cast<f32x4 *>(orow + d) = o;
-        }
-    }
-    if (p.lse && hh == 0) p.lse[((size_t)b * p.Hq + h) * p.S + iq] = lse_val;
+        *reinterpret_cast<uint2 *>(st + col * D + d) = pk;
+      }
   } else {
-    if (r_local >= p.rows_per_group) return;
-    const size_t item = (size_t)item_bgr * p.splits + split;
-    float *prow = p.part_o + (item * p.rows_per_group + r_local) * D;
+    float *st = reinterpret_cast<float *>(slice);
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = mb * 32 + q4 * 8 + hh * 4;
         f32x4 o;
-        o[0] = bad ? nanv : oacc[mb][q4 * 4 + 0] * inv;
-        o[1] = bad ? nanv : oacc[mb][q4 * 4 + 1] * inv;
-        o[2] = bad ? nanv : oacc[mb][q4 * 4 + 2] * inv;
-        o[3] = bad ? nanv : oacc[mb][q4 * 4 + 3] * inv;
-        *reinterpret_cast<f32x4 *>(prow + d) = o;
+        o[0] = oacc[mb][q4 * 4 + 0] * inv;
+        o[1] = oacc[mb][q4 * 4 + 1] * inv;
+        o[2] = oacc[mb][q4 * 4 + 2] * inv;
+        o[3] = oacc[mb][q4 * 4 + 3] * inv;
+        *reinterpret_cast<f32x4 *>(st + col * D + d) = o;
       }
-    if (hh == 0) p.part_lse[item * p.rows_per_group + r_local] = lse_val;
+  }
+  const int row_bytes = D * (half_out ? 2 : 4);
+  const int cpr = row_bytes / 16;                 // 16-byte chunks per row
+  if (to_part) {
+    const size_t item = (size_t)item_bgr * p.splits + split;
+    // rows wave*32 .. wave*32+31 of this partition are contiguous in the partial buffer
+    char *dst = reinterpret_cast<char *>(p.part_o) + (item * p.rows_per_group + wave * 32) * (size_t)row_bytes;
+    const int nrows = min(32, p.rows_per_group - wave * 32);
+    for (int f = lane; f < nrows * cpr; f += 64)
+      *reinterpret_cast<u32x4 *>(dst + (size_t)f * 16) = ld_lds_16(slice + f * 16);
+    if (hh == 0 && r_local < p.rows_per_group)
+      p.part_lse[item * p.rows_per_group + r_local] = lse_val;
+  } else {
+    char *obase = static_cast<char *>(p.out);
+    for (int f = lane; f < 32 * cpr; f += 64) {
+      const int rr = f / cpr, cc = f % cpr;
+      const int rg_row = rg * p.rows_per_group + wave * 32 + rr;
+      if (wave * 32 + rr >= p.rows_per_group || rg_row >= p.rows) continue;
+      const int j2 = rg_row / p.S, i2 = rg_row % p.S;
+      const size_t orow = ((size_t)b * p.S + i2) * p.Hq + (g * p.G + j2);
+      *reinterpret_cast<u32x4 *>(obase + orow * row_bytes + cc * 16) = ld_lds_16(slice + f * 16);
+    }
+    if (p.lse && hh == 0 && row_ok) p.lse[((size_t)b * p.Hq + h) * p.S + iq] = lse_val;
   }
 }
 
@@ -439,7 +584,13 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnParams p) {
     const float ls = p.part_lse[(item0 + s) * p.rows_per_group + r_local];
     const float w = __expf(ls - mx);
     wsum += w;
-    const f32x4 o = *reinterpret_cast<const f32x4 *>(p.part_o + ((item0 + s) * p.rows_per_group + r_local) * D + d4 * 4);
+    const uint2 ph = *reinterpret_cast<const uint2 *>(
+        reinterpret_cast<const uint16_t *>(p.part_o) + ((item0 + s) * p.rows_per_group + r_local) * D + d4 * 4);
+    f32x4 o;
+    o[0] = f16_to_f32(ph.x & 0xFFFFu);
+    o[1] = f16_to_f32(ph.x >> 16);
+    o[2] = f16_to_f32(ph.y & 0xFFFFu);
+    o[3] = f16_to_f32(ph.y >> 16);
     acc += w * o;
   }
   const float inv = 1.0f / wsum;
@@ -577,14 +728,14 @@ hipError_t launch_block_attn_bf16(const AttnParams &p, hipStream_t stream, hipEv
   hipError_t e = hipSuccess;
   if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess) return e;
   if (p.D == 128) {
-    constexpr int lds = kStages * Geom<128>::STAGE + kMaxPartPages * 4;
+    constexpr int lds = Geom<128>::LDS;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&block_attn_bf16_kernel<128>),
         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL(block_attn_bf16_kernel<128>, grid, dim3(kThreads), lds, stream, p);
   } else {
-    constexpr int lds = kStages * Geom<64>::STAGE + kMaxPartPages * 4;
+    constexpr int lds = Geom<64>::LDS;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&block_attn_bf16_kernel<64>),
         hipFuncAttributeMaxDynamicSharedMemorySize, lds);

@@ -22,9 +22,25 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
-// Two fp32 -> packed bf16x2 (lo in bits 0..15), round to nearest even.
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16x2 (lo in bits 0..15), round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
+
+// Two fp32 -> packed fp16x2 (lo in bits 0..15), round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }

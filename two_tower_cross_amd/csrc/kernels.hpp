@@ -13,7 +13,7 @@ struct AttnParams {
   const int32_t *block_table, *ctx_lens;
   void *out;
   float *lse;
-  float *part_o;    // [items, rows_per_group, D] fp32 partial outputs (splits > 1)
+  void *part_o;     // [items, rows_per_group, D] fp16 normalized partial outputs (splits > 1)
   float *part_lse;  // [items, rows_per_group]
   int B, S, Hq, Hkv, G, D;
   int rows;            // G * S query rows per (sequence, KV head)
