@@ -69,7 +69,8 @@ typedef enum { TT_FP32 = 0, TT_BF16 = 1 } tt_dtype;
  * Layouts (elements of `dtype`, innermost last, all contiguous):
  *   q        [batch, S, num_q_heads, head_dim]
  *   k_pages  [num_pages, num_kv_heads, page_size, head_dim]     token-major pages
- *   v_pages  [num_pages, num_kv_heads, head_dim, page_size]     dim-major pages
+ *   v_pages  [num_pages, num_kv_heads, page_size/64, head_dim, 64]  dim-major 64-token tiles:
+ *            row o of a page is at [page, g, o / 64, :, o % 64]
  *   block_table [batch, max_pages_per_seq] int32: context row t of sequence b is in page
  *            block_table[b, t / page_size] at offset t % page_size
  *   ctx_lens [batch] int32, 0 <= ctx_lens[b] <= max_ctx_len

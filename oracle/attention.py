@@ -20,7 +20,9 @@ K_blk(b, g)], values V_cat likewise:
     o   = sum_j w_j V_cat[j] / sum_j w_j,   lse = m + ln(sum_j w_j)
 
 Context row t of sequence b sits in page block_table[b, t // page_size] at offset
-t % page_size; K pages are [pool, Hkv, page_size, D], V pages [pool, Hkv, D, page_size]; the
+o = t % page_size. K pages are [pool, Hkv, page_size, D] (row o at [page, g, o, :]). V pages
+hold dim-major tiles of T tokens, [pool, Hkv, page_size // T, D, T] (row o at
+[page, g, o // T, :, o % T]); T = 64 when page_size is a multiple of 64, else T = page_size. The
 block's V is [B, Hkv, D, S]. Only rows t < ctx_lens[b] are read.
 """
 from __future__ import annotations
@@ -31,11 +33,14 @@ import numpy as np
 def gather_context(k_pages, v_pages, block_table, ctx_len, b, g):
     """Rows 0..ctx_len-1 of sequence b, KV head g, as float64 [L, D] keys and [L, D] values."""
     page_size = k_pages.shape[2]
+    n_tiles, D, T = v_pages.shape[2:]
+    if n_tiles * T != page_size:
+        raise ValueError("K and V pages disagree on the page size")
     t = np.arange(int(ctx_len))
     page = np.asarray(block_table)[b, t // page_size]
     off = t % page_size
     keys = np.asarray(k_pages[:, g], dtype=np.float64)[page, off, :]                 # [L, D]
-    vals = np.asarray(v_pages[:, g], dtype=np.float64).transpose(0, 2, 1)[page, off, :]
+    vals = np.asarray(v_pages[:, g], dtype=np.float64)[page, off // T, :, off % T]   # [L, D]
     return keys, vals
 
 

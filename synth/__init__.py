@@ -10,7 +10,8 @@ Layouts produced here (the library's layouts, documented in ``include/twotower.h
 
 * ``q``        ``[B, S, Hq, D]``
 * ``k_pages``  ``[num_pages, Hkv, page_size, D]``   (token-major pages)
-* ``v_pages``  ``[num_pages, Hkv, D, page_size]``   (dim-major pages)
+* ``v_pages``  ``[num_pages, Hkv, page_size // T, D, T]`` (dim-major tiles of T tokens; T = 64
+  when page_size is a multiple of 64, else T = page_size)
 * ``k_blk``    ``[B, Hkv, S, D]``
 * ``v_blk``    ``[B, Hkv, D, S]``
 * ``block_table`` ``[B, max_pages]`` int32, ``ctx_lens`` ``[B]`` int32
@@ -28,7 +29,8 @@ import math
 import numpy as np
 
 __all__ = [
-    "rng", "round_to_bf16", "bf16_bits", "bits_to_f32", "AttnCase", "attn_case",
+    "rng", "round_to_bf16", "bf16_bits", "bits_to_f32", "v_tile_width", "tile_v", "AttnCase",
+    "attn_case",
     "logits_normal", "logits_planted", "config_attn", "config_logits",
 ]
 
@@ -56,6 +58,19 @@ def bf16_bits(x_bf16_exact: np.ndarray) -> np.ndarray:
     if np.any(low[~np.isnan(x_bf16_exact)] != 0):
         raise ValueError("values are not bf16-exact")
     return (u >> 16).astype(np.uint16)
+
+
+def v_tile_width(page_size: int) -> int:
+    return 64 if page_size % 64 == 0 else page_size
+
+
+def tile_v(v_dim_major: np.ndarray) -> np.ndarray:
+    """[..., D, page] (dim-major page) -> [..., page // T, D, T] (the V page layout)."""
+    *lead, D, P = v_dim_major.shape
+    T = v_tile_width(P)
+    x = v_dim_major.reshape(*lead, D, P // T, T)
+    nd = len(lead)
+    return np.ascontiguousarray(np.moveaxis(x, nd + 1, nd))
 
 
 def bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -138,7 +153,7 @@ def attn_case(seed: int, *, B: int, S: int, Hq: int, Hkv: int, D: int, ctx_lens,
 
     fill = np.float32("nan") if nan_poison else np.float32(0.0)
     k_pages = np.full((n_pool, Hkv, page_size, D), fill, dtype=np.float32)
-    v_pages = np.full((n_pool, Hkv, D, page_size), fill, dtype=np.float32)
+    v_pages = np.full((n_pool, Hkv, D, page_size), fill, dtype=np.float32)   # dim-major, tiled below
     order = g.permutation(n_pool) if shuffle_pages else np.arange(n_pool)
     block_table = np.zeros((B, max_pages), dtype=np.int32)
     nxt = 0
@@ -152,6 +167,7 @@ def attn_case(seed: int, *, B: int, S: int, Hq: int, Hkv: int, D: int, ctx_lens,
             n = t1 - t0
             k_pages[slot, :, :n, :] = k[t0:t1].transpose(1, 0, 2)
             v_pages[slot, :, :, :n] = v[t0:t1].transpose(1, 2, 0)
+    v_pages = tile_v(v_pages)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     return AttnCase(dtype, q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, float(scale))

@@ -72,9 +72,9 @@ def query(name, a):
 def test_attention_workspace_query_and_plan():
     st, n = query("twotower_block_attn", attn_args())
     assert st == _lib.TT_OK
-    # auto plan at B*Hkv = 16 units: 16 partitions of 2048 tokens, 256-row fp32 partials + lse
+    # auto plan at B*Hkv = 16 units: 16 partitions of 2048 tokens, 256-row fp16 partials + fp32 lse
     items = 8 * 2 * 16
-    expect = -(-items * 256 * 128 * 4 // 256) * 256 + -(-items * 256 * 4 // 256) * 256
+    expect = -(-items * 256 * 128 * 2 // 256) * 256 + -(-items * 256 * 4 // 256) * 256
     assert n == expect
     # one partition needs no workspace
     st, n = query("twotower_block_attn", attn_args(num_splits=1))

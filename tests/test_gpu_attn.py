@@ -118,7 +118,7 @@ def test_single_dominant_key_returns_its_value():
     case.k_pages[case.block_table[0, 0], 0, 300, :] = 0.0
     case.k_pages[case.block_table[0, 0], 0, 300, 0] = 64.0
     out, lse = gpu_attn(case)
-    v = case.v_pages[case.block_table[0, 0], 0, :, 300]
+    v = case.v_pages[case.block_table[0, 0], 0, 300 // 64, :, 300 % 64]
     for h in range(2):
         np.testing.assert_allclose(out[0, :, h, :], np.broadcast_to(v, (16, 128)), atol=1e-5)
 

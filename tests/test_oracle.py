@@ -58,7 +58,7 @@ def test_single_key_returns_its_value():
     out, lse = run(c, k_blk=c.k_blk[:, :, :0], v_blk=c.v_blk[:, :, :, :0])
     G = c.Hq // c.Hkv
     for h in range(c.Hq):
-        v = c.v_pages[c.block_table[0, 0], h // G, :, 0]
+        v = c.v_pages[c.block_table[0, 0], h // G, 0, :, 0]
         np.testing.assert_allclose(out[0, :, h, :], np.broadcast_to(v, (2, c.D)), atol=1e-15)
     # empty context, one block key
     c = small_case(3, B=1, lens=(0,), S=1)
@@ -99,7 +99,7 @@ def test_permutation_invariance_block_context_and_pages():
     B, Hkv, D = c.B, c.Hkv, c.D
     Lmax = int(c.ctx_lens.max())
     kp = np.zeros((B, Hkv, Lmax, D), np.float32)
-    vp = np.zeros((B, Hkv, D, Lmax), np.float32)
+    vp = np.zeros((B, Hkv, D, Lmax), np.float32)       # dim-major, tiled below
     for b in range(B):
         L = int(c.ctx_lens[b])
         p = g.permutation(L)
@@ -107,7 +107,8 @@ def test_permutation_invariance_block_context_and_pages():
             kc, vc = attention.gather_context(c.k_pages, c.v_pages, c.block_table, L, b, h)
             kp[b, h, :L] = kc[p]
             vp[b, h, :, :L] = vc[p].T
-    out, _ = run(c, k_pages=kp, v_pages=vp, block_table=np.arange(B, dtype=np.int32)[:, None])
+    out, _ = run(c, k_pages=kp, v_pages=synth.tile_v(vp),
+                 block_table=np.arange(B, dtype=np.int32)[:, None])
     np.testing.assert_allclose(out, ref, atol=1e-13)
 
 
@@ -177,7 +178,7 @@ def test_affine_values():
     ref, _ = run(c)
     alpha = -1.75
     beta = synth.rng(11).standard_normal(c.D).astype(np.float32)
-    vp = alpha * c.v_pages + beta[None, None, :, None]
+    vp = alpha * c.v_pages + beta[None, None, None, :, None]
     vb = alpha * c.v_blk + beta[None, None, :, None]
     out, _ = run(c, v_pages=vp.astype(np.float32), v_blk=vb.astype(np.float32))
     np.testing.assert_allclose(out, alpha * ref + beta, atol=1e-5)
@@ -202,6 +203,20 @@ def test_matches_torch_sdpa_float64():
         np.testing.assert_allclose(out[b], ref.permute(1, 0, 2).numpy(), atol=1e-12)
 
 
+def test_v_tile_layout_addresses():
+    """Row o of a 128-token page sits at [page, g, o // 64, :, o % 64] of the V pages."""
+    c = small_case(14, B=1, Hq=2, Hkv=1, D=3, lens=(150,), page_size=128)
+    L = 150
+    _, vc = attention.gather_context(c.k_pages, c.v_pages, c.block_table, L, 0, 0)
+    for t in (0, 63, 64, 127, 128, 149):
+        page = c.block_table[0, t // 128]
+        np.testing.assert_array_equal(vc[t], c.v_pages[page, 0, (t % 128) // 64, :, t % 64])
+    dm = synth.rng(1).standard_normal((2, 3, 5, 192))
+    tv = synth.tile_v(dm)
+    assert tv.shape == (2, 3, 3, 5, 64)
+    assert tv[1, 2, 2, 4, 7] == dm[1, 2, 4, 2 * 64 + 7]
+
+
 def test_paged_layout_equals_contiguous():
     base = small_case(13, lens=(13, 8), page_size=5)
     ref, _ = run(base)
@@ -224,11 +239,11 @@ def test_golden_attention_closed_form():
     sec = [float(x) for x in rows["ctx_key_second"].split()]
     vals = [[float(x) for x in part.split()] for part in rows["ctx_values"].split("|")]
     L = len(w)
-    k_pages = np.zeros((L, 1, 1, 2)); v_pages = np.zeros((L, 1, 2, 1))
+    k_pages = np.zeros((L, 1, 1, 2)); v_pages = np.zeros((L, 1, 1, 2, 1))
     order = [1, 0]  # token 0 in pool page 1, token 1 in pool page 0
     for t in range(L):
         k_pages[order[t], 0, 0] = [math.log(w[t]), sec[t]]
-        v_pages[order[t], 0, :, 0] = vals[t]
+        v_pages[order[t], 0, 0, :, 0] = vals[t]
     bw = float(rows["blk_key_weights"]); bs = float(rows["blk_key_second"])
     k_blk = np.array([math.log(bw), bs]).reshape(1, 1, 1, 2)
     v_blk = np.array([float(x) for x in rows["blk_values"].split()]).reshape(1, 1, 2, 1)

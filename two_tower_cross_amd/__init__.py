@@ -6,7 +6,7 @@ tensor metadata, build the C argument structs and size the workspace. If the sha
 is missing, every call raises ``LibraryNotBuilt`` (there is no fallback).
 
 Layouts follow ``include/twotower.h``:
-q [B,S,Hq,D]; k_pages [P,Hkv,page,D]; v_pages [P,Hkv,D,page]; k_blk [B,Hkv,S,D];
+q [B,S,Hq,D]; k_pages [P,Hkv,page,D]; v_pages [P,Hkv,page/64,D,64]; k_blk [B,Hkv,S,D];
 v_blk [B,Hkv,D,S]; block_table [B,max_pages] int32; ctx_lens [B] int32; logits [B,S,V] fp32.
 """
 from __future__ import annotations
@@ -101,13 +101,13 @@ def block_attn(q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, *, scal
     _check(q, "q", dev, ndim=4)
     B, S, Hq, D = q.shape
     _check(k_pages, "k_pages", dev, q.dtype, 4)
-    _check(v_pages, "v_pages", dev, q.dtype, 4)
+    _check(v_pages, "v_pages", dev, q.dtype, 5)
     _check(k_blk, "k_blk", dev, q.dtype, 4)
     _check(v_blk, "v_blk", dev, q.dtype, 4)
     _check(block_table, "block_table", dev, torch.int32, 2)
     _check(ctx_lens, "ctx_lens", dev, torch.int32, 1)
     P, Hkv, page, Dk = k_pages.shape
-    if (Dk != D or tuple(v_pages.shape) != (P, Hkv, D, page)
+    if (Dk != D or page % 64 or tuple(v_pages.shape) != (P, Hkv, page // 64, D, 64)
             or tuple(k_blk.shape) != (B, Hkv, S, D) or tuple(v_blk.shape) != (B, Hkv, D, S)
             or block_table.shape[0] != B or ctx_lens.shape[0] != B):
         raise ValueError("inconsistent attention shapes")

@@ -181,11 +181,19 @@ hipError_t run_unmask(UnmaskPlan &pl, void *ws, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------------- linear
-int choose_ksplit(int M, int N, int K) {
+// Tile shape and K partitions of a skinny product (measured on MI355X at M = 128): wide 256-feature
+// tiles once N alone yields two waves of work-groups; otherwise 64-feature tiles with K split so
+// that roughly 128-256 work-groups run, each over at least 16 chunks of 64 along K.
+void choose_tiling(int M, int N, int K, tt::LinearParams *p) {
+  p->wide = cdiv(N, 256) * cdiv(M, 128) >= 2 * kTargetWorkgroups ? 1 : 0;
+  if (p->wide) {
+    p->ksplit = 1;
+    return;
+  }
   const int64_t tiles = cdiv(N, 64) * cdiv(M, 128);
   int64_t ks = cdiv(kTargetWorkgroups, tiles);
-  ks = std::min<int64_t>(ks, std::max<int64_t>(1, K / 256));
-  return (int)std::max<int64_t>(1, ks);
+  ks = std::min<int64_t>(ks, std::max<int64_t>(1, K / 1024));
+  p->ksplit = (int)std::max<int64_t>(1, ks);
 }
 
 size_t linear_ws(const tt::LinearParams &p) {
@@ -224,7 +232,7 @@ tt_status plan_qkv(const tt_qkv_args *a, bool check_pointers, tt::LinearParams *
   p->Hq = a->num_q_heads;
   p->Hkv = a->num_kv_heads;
   p->D = a->head_dim;
-  p->ksplit = choose_ksplit(p->M, p->N, p->K);
+  choose_tiling(p->M, p->N, p->K, p);
   return TT_OK;
 }
 
@@ -246,7 +254,7 @@ tt_status plan_out(const tt_out_proj_args *a, bool check_pointers, tt::LinearPar
   p->epi = tt::EPI_RESIDUAL;
   p->residual = a->h_in;
   p->y_bf16 = a->h_out;
-  p->ksplit = choose_ksplit(p->M, p->N, p->K);
+  choose_tiling(p->M, p->N, p->K, p);
   return TT_OK;
 }
 
@@ -267,7 +275,7 @@ tt_status plan_lm(const tt_lm_head_args *a, bool check_pointers, tt::LinearParam
   p->epi = tt::EPI_F32;
   p->y = a->logits;
   p->ldy = a->ld;
-  p->ksplit = choose_ksplit(p->M, p->N, p->K);
+  choose_tiling(p->M, p->N, p->K, p);
   return TT_OK;
 }
 

@@ -8,7 +8,8 @@
 //
 // bf16 path (one work-group = 8 waves = up to 256 query rows of one (b, g), one context
 // partition):
-//   * K tiles [64 tokens][D] and V tiles [D][64 tokens] (V pages are dim-major) are staged in LDS
+//   * K tiles [64 tokens][D] and V tiles [D][64 tokens] (V pages are stored as contiguous
+//     dim-major 64-token tiles, so both are single 16 KB blocks in memory) are staged in LDS
 //     with 16-byte loads; chunks are XOR-swizzled by (row & 7) so the MFMA operand reads of 32
 //     different rows hit distinct banks.
 //   * Each wave owns 32 query rows and computes S^T = K Q^T with 32x32x16 bf16 MFMA: a lane then
@@ -37,7 +38,7 @@ constexpr int kStages = 4;             // LDS ring depth: up to 3 tiles in fligh
 constexpr float kRescaleLog2 = 8.0f;   // the running max moves only when it grows by > 2^8
 constexpr int kMaxPartPages = 4096;    // page ids of one partition staged in LDS (16 KB)
 
-#define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+#define LDS_PTR(p) TT_LDS_PTR(p)
 
 __device__ __forceinline__ int swap_bits23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
@@ -50,7 +51,7 @@ __device__ __forceinline__ int swap_bits23(int r) {
 // parity, for 16 consecutive rows. Both hold for 32 and for 64 LDS banks.
 template <int D>
 __device__ __forceinline__ int kkey(int t) { return swap_bits23(t & 15) & (D / 8 - 1); }
-__device__ __forceinline__ int vkey(int d) { return ((d >> 1) & 7) ^ ((d & 1) << 2); }
+__device__ __forceinline__ int vkey(int d) { return key128(d); }
 
 // Keep the first n (0..8) bf16 elements of a 16-byte chunk, zero the rest.
 __device__ __forceinline__ u32x4 keep_first(u32x4 v, int n) {
@@ -88,11 +89,11 @@ struct LaneMap {
   int k[D / 16];    // K operand of S^T = K Q^T, sub-tile 0 (sub-tile 1 is +32 rows)
   int v[2][2];      // V operand of O^T += V^T P^T for (sub-tile, 16-token half), incl. VBASE
   uint32_t kdma[Geom<D>::KCH];  // source byte offsets of this lane's K chunks in a tile
-  uint32_t vdma[Geom<D>::VCH];  // source byte offsets of its V chunks (row stride = page)
+  uint32_t vdma[Geom<D>::VCH];  // source byte offsets of its V chunks in a [D][64] V tile
   int kdst[Geom<D>::KCH];       // LDS byte offsets (wave-uniform) of those DMA segments
   int vdst[Geom<D>::VCH];
 
-  __device__ __forceinline__ void init(int lane, int wave, int page_size) {
+  __device__ __forceinline__ void init(int lane, int wave) {
     const int col = lane & 31, hh = lane >> 5;
     const int tok = swap_bits23(col);
     const int key = kkey<D>(tok);
@@ -118,7 +119,7 @@ struct LaneMap {
       const int seg = j * kWaves + wave;
       const int f = seg * 64 + lane;
       const int d = f / 8, pp = f % 8;
-      vdma[j] = (uint32_t)((size_t)d * page_size + ((pp ^ vkey(d)) << 3)) * 2u;
+      vdma[j] = (uint32_t)(d * kTile + ((pp ^ vkey(d)) << 3)) * 2u;
       vdst[j] = seg * 1024;
     }
   }
@@ -145,7 +146,7 @@ __device__ __forceinline__ void dma_tile(char *smem, int s, const char *kb, cons
 // thread's loads are issued before its first store, so the tile costs one memory round trip.
 template <int D>
 __device__ void load_tail_tile(char *smem, int s, const uint16_t *kbase, const uint16_t *vbase,
-                               int page_size, int valid, int tid) {
+                               int valid, int tid) {
   constexpr int KC = D / 8;
   constexpr int NK = kTile * KC / kThreads, NV = D * 8 / kThreads;
   uint16_t *ks = reinterpret_cast<uint16_t *>(smem + Geom<D>::koff(s));
@@ -160,7 +161,7 @@ __device__ void load_tail_tile(char *smem, int s, const uint16_t *kbase, const u
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int f = tid + j * kThreads, d = f / 8, c = f % 8;
-    xv[j] = c * 8 < valid ? ld_global_16(vbase + (size_t)d * page_size + c * 8) : z;
+    xv[j] = c * 8 < valid ? ld_global_16(vbase + (size_t)d * kTile + c * 8) : z;
   }
 #pragma unroll
   for (int j = 0; j < NK; ++j) {
@@ -220,16 +221,6 @@ __device__ void load_block_tile(char *smem, int s, const uint16_t *kblk, const u
     st_lds_16(vs + d * kTile + ((c ^ vkey(d)) << 3), xv[j]);
   }
 }
-
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-}
-
-// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8); expcnt and
-// lgkmcnt are left at their maxima so only vector-memory operations are waited for. Issued through
-// the builtin so that the compiler's own wait insertion knows about them.
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // Wait until at most `tiles_in_flight` tiles of DMA (LOADS instructions each) are outstanding.
 template <int LOADS>
@@ -393,11 +384,11 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
     const int off0 = t0 % p.page_size;
     const size_t ph = (size_t)page * p.Hkv + g;
     kb = reinterpret_cast<const char *>(kp + (ph * p.page_size + off0) * D);
-    vb = reinterpret_cast<const char *>(vp + ph * D * p.page_size + off0);
+    vb = reinterpret_cast<const char *>(vp + (ph * (p.page_size / kTile) + off0 / kTile) * D * kTile);
   };
 
   LaneMap<D> lm;
-  lm.init(lane, wave, p.page_size);
+  lm.init(lane, wave);
 
   // Query rows of this wave (B operand of S^T = K Q^T): row r -> (head j, position i).
   const int col = lane & 31, hh = lane >> 5;
@@ -479,7 +470,7 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
     const char *kb, *vb;
     tile_src(t_begin + n_full_ok * kTile, kb, vb);
     load_tail_tile<D>(smem, st, reinterpret_cast<const uint16_t *>(kb),
-                      reinterpret_cast<const uint16_t *>(vb), p.page_size, tail_ok, tid);
+                      reinterpret_cast<const uint16_t *>(vb), tail_ok, tid);
     lds_barrier();
     if (wave_active)
       attend_tile<D, false>(smem, Geom<D>::koff(st), Geom<D>::voff(st) - Geom<D>::VBASE, tail_ok,
@@ -558,55 +549,90 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
 
 // Exact merge of the partitions of each query row: with lse* = max_p lse_p and
 // w_p = exp(lse_p - lse*), out = sum_p w_p O_p / sum_p w_p and lse = lse* + ln(sum_p w_p).
+// One work-group = 16 query rows of one (b, KV head, row group); 16 threads per row, 8 dims each.
+// The rows' LSEs are staged in LDS first, then every partition's 16-byte partial chunk is
+// requested before any is used, so a batch of 16 partitions costs two memory round trips.
+constexpr int kRedBatch = 16;
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnParams p) {
+  constexpr int TPR = D / 8;                 // threads per row
+  constexpr int RPB = 256 / TPR;             // rows per pass of the block (16 or 32)
+  __shared__ float lse_s[RPB][kRedBatch + 1];
   const int item_bgr = blockIdx.x;
   const int rg = item_bgr % p.row_groups;
   const int g = (item_bgr / p.row_groups) % p.Hkv;
   const int b = item_bgr / (p.row_groups * p.Hkv);
-  const int e = blockIdx.y * 256 + threadIdx.x;
-  const int r_local = e / (D / 4), d4 = e % (D / 4);
-  if (r_local >= p.rows_per_group) return;
-  const int r = rg * p.rows_per_group + r_local;
-  if (r >= p.rows) return;
-  const int jq = r / p.S, iq = r % p.S, h = g * p.G + jq;
-
+  const int tid = threadIdx.x;
   const int L = p.ctx_lens[b];
   const bool bad = L < 0 || L > p.max_ctx_len;
   int nact = bad || L == 0 ? 1 : (L + p.chunk - 1) / p.chunk;
   nact = min(nact, p.splits);
   const size_t item0 = (size_t)item_bgr * p.splits;
-  float mx = -INFINITY;
-  for (int s = 0; s < nact; ++s) mx = fmaxf(mx, p.part_lse[(item0 + s) * p.rows_per_group + r_local]);
-  float wsum = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < nact; ++s) {
-    const float ls = p.part_lse[(item0 + s) * p.rows_per_group + r_local];
-    const float w = __expf(ls - mx);
-    wsum += w;
-    const uint2 ph = *reinterpret_cast<const uint2 *>(
-        reinterpret_cast<const uint16_t *>(p.part_o) + ((item0 + s) * p.rows_per_group + r_local) * D + d4 * 4);
-    f32x4 o;
-    o[0] = f16_to_f32(ph.x & 0xFFFFu);
-    o[1] = f16_to_f32(ph.x >> 16);
-    o[2] = f16_to_f32(ph.y & 0xFFFFu);
-    o[3] = f16_to_f32(ph.y >> 16);
-    acc += w * o;
+  const uint16_t *part = static_cast<const uint16_t *>(p.part_o);
+  const int rr = tid / TPR, d8 = tid % TPR;
+  const int r_local = blockIdx.y * RPB + rr;
+  const bool live = r_local < p.rows_per_group && rg * p.rows_per_group + r_local < p.rows;
+
+  float mx = -INFINITY, wsum = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nact; s0 += kRedBatch) {
+    const int ns = min(kRedBatch, nact - s0);
+    __syncthreads();
+    for (int i = tid; i < RPB * kRedBatch; i += 256) {
+      const int row = i / kRedBatch, sp = i % kRedBatch;
+      const int rl = blockIdx.y * RPB + row;
+      lse_s[row][sp] = (sp < ns && rl < p.rows_per_group)
+                           ? p.part_lse[(item0 + s0 + sp) * p.rows_per_group + rl]
+                           : -INFINITY;
+    }
+    __syncthreads();
+    if (!live) continue;
+    u32x4 v[kRedBatch];
+#pragma unroll
+    for (int sp = 0; sp < kRedBatch; ++sp)
+      if (sp < ns)
+        v[sp] = ld_global_16(part + ((item0 + s0 + sp) * p.rows_per_group + r_local) * D + d8 * 8);
+    float bmx = mx;
+#pragma unroll
+    for (int sp = 0; sp < kRedBatch; ++sp)
+      if (sp < ns) bmx = fmaxf(bmx, lse_s[rr][sp]);
+    const float rescale = __expf(mx - bmx);   // 0 for the first batch (mx = -inf)
+    wsum *= rescale;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= rescale;
+    mx = bmx;
+#pragma unroll
+    for (int sp = 0; sp < kRedBatch; ++sp) {
+      if (sp < ns) {
+        const float w = __expf(lse_s[rr][sp] - mx);
+        wsum += w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += w * f16_to_f32(v[sp][e] & 0xFFFFu);
+          acc[2 * e + 1] += w * f16_to_f32(v[sp][e] >> 16);
+        }
+      }
+    }
   }
-  const float inv = 1.0f / wsum;
-  const float nanv = NAN;
-  acc *= inv;
-  if (bad) acc = f32x4{nanv, nanv, nanv, nanv};
-  const size_t o_off = (((size_t)b * p.S + iq) * p.Hq + h) * D + d4 * 4;
+  if (!live) return;
+  const float inv = bad ? NAN : 1.0f / wsum;
+  const int r = rg * p.rows_per_group + r_local;
+  const int jq = r / p.S, iq = r % p.S, h = g * p.G + jq;
+  const size_t o_off = (((size_t)b * p.S + iq) * p.Hq + h) * D + d8 * 8;
   if (p.out_bf16) {
-    uint2 pk;
-    pk.x = pack_bf16x2(acc[0], acc[1]);
-    pk.y = pack_bf16x2(acc[2], acc[3]);
-    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.out) + o_off) = pk;
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+    *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(p.out) + o_off) = o;
   } else {
-    *reinterpret_cast<f32x4 *>(static_cast<float *>(p.out) + o_off) = acc;
+    float *o = static_cast<float *>(p.out) + o_off;
+    const f32x4 lo = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    const f32x4 hi = {acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+    *reinterpret_cast<f32x4 *>(o) = lo;
+    *reinterpret_cast<f32x4 *>(o + 4) = hi;
   }
-  if (p.lse && d4 == 0) p.lse[((size_t)b * p.Hq + h) * p.S + iq] = bad ? nanv : mx + logf(wsum);
+  if (p.lse && d8 == 0) p.lse[((size_t)b * p.Hq + h) * p.S + iq] = bad ? NAN : mx + logf(wsum);
 }
 
 // fp32 path: one work-group per (position i, query head h, sequence b); keys in tiles of 256.
@@ -699,8 +725,10 @@ __global__ __launch_bounds__(256) void block_attn_f32_kernel(AttnParams p) {
         } else {
           const int tt = jj - p.S;
           const int page = btab[tt / p.page_size];
+          const int off = tt % p.page_size;
           v = (page >= 0 && page < p.num_pages)
-                  ? vp[(((size_t)page * p.Hkv + g) * D + tid) * p.page_size + tt % p.page_size]
+                  ? vp[((((size_t)page * p.Hkv + g) * (p.page_size / kTile) + off / kTile) * D + tid) *
+                           kTile + off % kTile]
                   : 0.f;
         }
         acc = fmaf(pw[t], v, acc);
@@ -762,8 +790,8 @@ hipError_t launch_block_attn_f32(const AttnParams &p, hipStream_t stream, hipEve
 }
 
 hipError_t launch_attn_reduce(const AttnParams &p, hipStream_t stream) {
-  const int threads_needed = p.rows_per_group * (p.D / 4);
-  dim3 grid(p.B * p.Hkv * p.row_groups, (threads_needed + 255) / 256);
+  const int rpb = 256 / (p.D / 8);
+  dim3 grid(p.B * p.Hkv * p.row_groups, (p.rows_per_group + rpb - 1) / rpb);
   if (p.D == 128)
     hipLaunchKernelGGL(attn_reduce_kernel<128>, grid, dim3(256), 0, stream, p);
   else

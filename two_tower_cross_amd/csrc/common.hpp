@@ -77,4 +77,23 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+#define TT_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8); expcnt and
+// lgkmcnt are left at their maxima so only vector-memory operations are waited for. Issued through
+// the builtin so that the compiler's own wait insertion knows about them.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Work-group barrier for LDS hand-offs: this wave's LDS operations are complete, then s_barrier.
+// (No memory fence: outstanding global loads, including direct-to-LDS ones, are waited for
+// explicitly with waitcnt_vm.)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+}
+
+// XOR key of the 16-byte chunk swizzle for LDS rows of 128 bytes: the 8 (32-bank) and 16
+// (64-bank, two rows per bank line) consecutive rows read by one operand load hit distinct slots.
+__device__ __forceinline__ int key128(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
 }  // namespace tt

@@ -60,6 +60,7 @@ struct LinearParams {
   const void *w;  // bf16 [N, K]
   int M, N, K;
   int ksplit;     // partitions of K (>= 1); > 1 uses `part` and a reduce pass
+  int wide;       // 1: 256-feature work-group tiles (large N), 0: 64-feature tiles
   float *part;    // [ksplit, M, N] fp32 when ksplit > 1
   int epi;
   // EPI_F32
