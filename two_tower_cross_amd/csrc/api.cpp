@@ -15,7 +15,7 @@ namespace {
 
 constexpr int kTargetWorkgroups = 256;  // one work-group per compute unit on MI355X
 constexpr int kMinChunk = 256;          // context tokens per partition, lower bound
-constexpr int kMaxPartitionPages = 4096;  // page ids one attention work-group stages in LDS
+constexpr int kMaxPartitionTiles = 4096;  // 64-token tile indices one attention work-group stages in LDS
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -45,6 +45,8 @@ tt_status plan_attn(const tt_block_attn_args *a, bool check_pointers, AttnPlan *
   if (a->head_dim != 64 && a->head_dim != 128) return TT_ENOTSUP;
   if (a->S > 64) return TT_ENOTSUP;
   if (a->page_size % 64 != 0) return TT_ENOTSUP;
+  // 64-token tiles of either pool are indexed with 32-bit integers
+  if ((int64_t)a->num_pages * a->num_kv_heads * (a->page_size / 64) > INT32_MAX) return TT_ENOTSUP;
   if (a->out_dtype != TT_FP32 && a->out_dtype != a->dtype) return TT_ENOTSUP;
   if (check_pointers) {
     const void *p16[] = {a->q, a->k_pages, a->v_pages, a->k_blk, a->v_blk, a->out};
@@ -93,8 +95,8 @@ tt_status plan_attn(const tt_block_attn_args *a, bool check_pointers, AttnPlan *
     int64_t chunk = cdiv(cdiv(a->max_ctx_len, want), 64) * 64;
     if (a->num_splits == 0) chunk = std::max<int64_t>(chunk, kMinChunk);
     chunk = std::max<int64_t>(chunk, 64);
-    // a partition's page ids are staged on chip: at most kMaxPartitionPages of them
-    chunk = std::min<int64_t>(chunk, (int64_t)(kMaxPartitionPages - 2) * a->page_size);
+    // a partition's tile indices are staged on chip: at most kMaxPartitionTiles of them
+    chunk = std::min<int64_t>(chunk, (int64_t)kMaxPartitionTiles * 64);
     p.chunk = (int)chunk;
     p.splits = (int)cdiv(a->max_ctx_len, chunk);
   }

@@ -36,7 +36,8 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kStages = 4;             // LDS ring depth: up to 3 tiles in flight per work-group
 constexpr float kRescaleLog2 = 8.0f;   // the running max moves only when it grows by > 2^8
-constexpr int kMaxPartPages = 4096;    // page ids of one partition staged in LDS (16 KB)
+constexpr float kLaneSumMax = 4096.f;  // pipelined loop: bound on a lane's 16 weights of a sub-tile
+constexpr int kMaxPartTiles = 4096;    // tile indices of one partition staged in LDS (16 KB)
 
 #define LDS_PTR(p) TT_LDS_PTR(p)
 
@@ -65,16 +66,18 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int n) {
 }
 
 // LDS map of the bf16 kernel: K stages [kStages][64 tokens][D], then V stages
-// [kStages][D][64 tokens], then the partition's page ids. Every stage offset stays within the
-// 16-bit immediate of ds_read, so with the stage index known at compile time each operand read
-// is one VGPR offset plus an immediate.
+// [kStages][D][64 tokens], then the partition's tile indices. Every K offset, and every V offset
+// relative to VBASE (which the lanes' V offsets include), stays within the 16-bit immediate of
+// ds_read, so with the stage known at compile time each operand read is one VGPR plus an
+// immediate.
 template <int D>
 struct Geom {
   static constexpr int KBYTES = kTile * D * 2;
   static constexpr int VBYTES = D * kTile * 2;
   static constexpr int VBASE = kStages * KBYTES;
-  static constexpr int PAGES = VBASE + kStages * VBYTES;
-  static constexpr int LDS = PAGES + kMaxPartPages * 4;
+  static constexpr int IDS = VBASE + kStages * VBYTES;
+  static constexpr int FLAGS = IDS + kMaxPartTiles * 4;  // one word per wave
+  static constexpr int LDS = FLAGS + kWaves * 4;
   static constexpr int KCH = KBYTES / 16 / kThreads;  // 16-byte K chunks per thread per tile
   static constexpr int VCH = VBYTES / 16 / kThreads;
   static constexpr int LOADS = KCH + VCH;             // DMA instructions per thread per tile
@@ -125,20 +128,28 @@ struct LaneMap {
   }
 };
 
-// Full 64-token context tile -> LDS stage s, asynchronously (global_load_lds, 16 B per lane).
+// Buffer resource over one 16 KB tile (raw, 32-bit data format; loads past the tile return 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, bytes, 0x00020000);
+}
+
+// Full 64-token context tile -> LDS stage s, asynchronously (buffer_load ... lds, 16 B per lane).
 // Each instruction fills 1024 contiguous LDS bytes lane by lane; the source of each lane is the
-// logical chunk that the swizzle places in that slot.
+// logical chunk that the swizzle places in that slot. The tile base goes into the (scalar) buffer
+// resource, so a lane's source is a 32-bit offset.
 template <int D>
 __device__ __forceinline__ void dma_tile(char *smem, int s, const char *kb, const char *vb,
                                          const LaneMap<D> &lm) {
+  const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kb, Geom<D>::KBYTES);
+  const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vb, Geom<D>::VBYTES);
 #pragma unroll
   for (int j = 0; j < Geom<D>::KCH; ++j)
-    __builtin_amdgcn_global_load_lds(kb + lm.kdma[j], LDS_PTR(smem + Geom<D>::koff(s) + lm.kdst[j]),
-                                     16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, LDS_PTR(smem + Geom<D>::koff(s) + lm.kdst[j]), 16,
+                                             lm.kdma[j], 0, 0, 0);
 #pragma unroll
   for (int j = 0; j < Geom<D>::VCH; ++j)
-    __builtin_amdgcn_global_load_lds(vb + lm.vdma[j], LDS_PTR(smem + Geom<D>::voff(s) + lm.vdst[j]),
-                                     16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, LDS_PTR(smem + Geom<D>::voff(s) + lm.vdst[j]), 16,
+                                             lm.vdma[j], 0, 0, 0);
 }
 
 // Partial context tile (`valid` < 64 tokens) -> LDS stage s through registers, zero-filling the
@@ -274,7 +285,7 @@ __device__ __forceinline__ void attend_tile(const char *smem, int kst, int vst, 
   float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
   for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-  mx = fmaxf(mx, swap_halves(mx));
+  mx = pair_max(mx);
   if (__ballot((mx - m) * c > kRescaleLog2)) {
     const float mnew = fmaxf(m, mx);
     const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c);
@@ -336,6 +347,147 @@ __device__ __forceinline__ void attend_tile(const char *smem, int kst, int vst, 
   }
 }
 
+// Software pipeline over the 32-token sub-tiles of the full context tiles. Window u consists of
+// a matrix half M(u), which issues the PV product of sub-tile u-1 and the QK product of sub-tile
+// u+1 and prefetches from LDS the operands of M(u+1) (V of sub-tile u, K of sub-tile u+2), and a
+// vector half V(u), the softmax of sub-tile u, which depends on neither, so the two overlap.
+// Between halves the registers carry:
+template <int D>
+struct PipeRegs {
+  f32x16 s;          // S^T of the sub-tile whose softmax is next (raw scores)
+  f32x16 sn;         // S^T of the sub-tile after it
+  u32x4 k[D / 16];   // K operand of the next QK
+  u32x4 v[D / 16];   // V operand of the next PV, [32-dim block][16-token half]
+  u32x4 pa, pb;      // P^T of the next PV (bf16), token halves 0 and 1
+  float alpha;       // factor that moves O to the current reference maximum
+  bool rescale;      // alpha != 1 (wave-uniform)
+};
+
+// M(u). KS/KH: stage and half of sub-tile u+2 (its K is loaded); VS/VH: of sub-tile u (its V is
+// loaded). O, which holds everything through sub-tile u-2 scaled by the reference maximum before
+// V(u-1), is first moved to the current one if V(u-1) changed it (a branch the whole wave takes
+// together, rarely), then the PV of sub-tile u-1 (whose P already uses the current maximum) is
+// added.
+template <int D, int KS, int KH, int VS, int VH>
+__device__ __forceinline__ void pipe_mma(const char *smem, const LaneMap<D> &lm, const u32x4 *qreg,
+                                         PipeRegs<D> &r, f32x16 *oacc) {
+  if (r.rescale) {
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= r.alpha;
+  }
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+      oacc[mb] = mfma32x32x16(r.v[2 * mb + kc], kc ? r.pb : r.pa, oacc[mb]);
+  f32x16 sn = {};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) sn = mfma32x32x16(r.k[kk], qreg[kk], sn);
+  r.sn = sn;
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+      r.v[2 * mb + kc] = ld_lds_16(smem + (Geom<D>::voff(VS) - Geom<D>::VBASE) + lm.v[VH][kc] +
+                                   mb * 32 * kTile * 2);
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    r.k[kk] = ld_lds_16(smem + Geom<D>::koff(KS) + KH * 32 * D * 2 + lm.k[kk]);
+  // Each operand read follows the MFMA that last used its registers.
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
+// Exponentials of the 16 scores a lane holds against the reference mc = m * c (base 2), packed to
+// bf16 as the B operand of the PV product, and their sum (of the rounded values, so that the
+// normalizer sums exactly the weights the product applies; one dot product with ones per pair).
+__device__ __forceinline__ float exp_pack(const f32x16 &s, float c, float mc, u32x4 &pa,
+                                          u32x4 &pb) {
+  constexpr uint32_t kOnes = 0x3F803F80u;  // bf16x2 (1, 1)
+  float ps0 = 0.f, ps1 = 0.f;
+  // (The sums are taken on the packed words before they are inserted into the operand vectors:
+  // applied to an element of the vector, the dot product was compiled to read element 0 only.)
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t a = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s[2 * w], c, -mc)),
+                                   __builtin_amdgcn_exp2f(fmaf(s[2 * w + 1], c, -mc)));
+    const uint32_t b = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s[8 + 2 * w], c, -mc)),
+                                   __builtin_amdgcn_exp2f(fmaf(s[8 + 2 * w + 1], c, -mc)));
+    ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                          __builtin_bit_cast(bf16x2, kOnes), ps0, false);
+    ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, b),
+                                          __builtin_bit_cast(bf16x2, kOnes), ps1, false);
+    pa[w] = a;
+    pb[w] = b;
+  }
+  return ps0 + ps1;
+}
+
+// V(u): softmax of sub-tile u against the reference maximum m. The exponentials are first taken
+// against the current m; only when some lane's 16 of them sum to more than 2^kLaneSumLog2 (or to
+// inf / NaN, as for the first sub-tile, when m = -inf) does the wave take the rare branch that
+// moves m to the row maximum (never down) and recomputes them, so every weight stays <= 2^12. P of
+// sub-tile u then uses the new m; O is moved to it at the start of M(u+1).
+template <int D>
+__device__ __forceinline__ void pipe_softmax(PipeRegs<D> &r, float &m, float &lpart, float c) {
+  float ps = exp_pack(r.s, c, m * c, r.pa, r.pb);
+  r.rescale = __ballot(!(ps <= kLaneSumMax)) != 0;
+  if (r.rescale) {
+    float t[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      t[j] = fmaxf(fmaxf(r.s[4 * j], r.s[4 * j + 1]), fmaxf(r.s[4 * j + 2], r.s[4 * j + 3]));
+    const float mx = pair_max(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])));
+    const float mnew = fmaxf(m, mx);
+    r.alpha = __builtin_amdgcn_exp2f((m - mnew) * c);  // 0 while m = -inf
+    m = mnew;
+    lpart *= r.alpha;
+    ps = exp_pack(r.s, c, mnew * c, r.pa, r.pb);
+  }
+  lpart += ps;
+  r.s = r.sn;
+}
+
+// Pipeline start: sub-tile 0 (stage 0, half 0) is in LDS. Computes S^T of sub-tile 0, loads the K
+// of sub-tile 1 and clears the PV operands so that window 0 adds nothing for sub-tile -1.
+template <int D>
+__device__ __forceinline__ void pipe_start(const char *smem, const LaneMap<D> &lm,
+                                           const u32x4 *qreg, PipeRegs<D> &r) {
+  u32x4 k0[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) k0[kk] = ld_lds_16(smem + Geom<D>::koff(0) + lm.k[kk]);
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    r.k[kk] = ld_lds_16(smem + Geom<D>::koff(0) + 32 * D * 2 + lm.k[kk]);
+  r.s = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) r.s = mfma32x32x16(k0[kk], qreg[kk], r.s);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) r.v[j] = z;
+  r.pa = z;
+  r.pb = z;
+  r.alpha = 1.f;
+  r.rescale = false;
+}
+
+// Pipeline end: the pending rescale, then the PV product of the last sub-tile.
+template <int D>
+__device__ __forceinline__ void pipe_finish(const PipeRegs<D> &r, f32x16 *oacc) {
+  if (r.rescale) {
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= r.alpha;
+  }
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+      oacc[mb] = mfma32x32x16(r.v[2 * mb + kc], kc ? r.pb : r.pa, oacc[mb]);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -359,36 +511,46 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   const int n_full = n_ctx / kTile;            // full tiles: asynchronous ring
   const int tail = n_ctx - n_full * kTile;     // tokens of the last, partial tile
 
-  const uint16_t *kp = static_cast<const uint16_t *>(p.k_pages);
-  const uint16_t *vp = static_cast<const uint16_t *>(p.v_pages);
   const int32_t *btab = p.block_table + (size_t)b * p.max_pages;
-  // The partition's page ids are staged in LDS once (the ring loop then issues no vector load of
-  // its own besides the DMA). Any id outside the pool makes the sequence bad: nothing is loaded
-  // from it and its outputs become NaN.
-  int *part_pages = reinterpret_cast<int *>(smem + Geom<D>::PAGES);
-  const int pg0 = t_begin / p.page_size;
-  const int n_pages = n_ctx > 0 ? (t_end - 1) / p.page_size - pg0 + 1 : 0;
+  // K and V pools are both sequences of 16 KB tiles (K [64 tokens][D], V [D][64 tokens]); context
+  // tile n of this partition (tokens t_begin + 64n ...) is tile (page * Hkv + g) * (page_size / 64)
+  // + (offset in page) / 64 of either pool. The partition's tile indices are staged in LDS once, so
+  // the ring issues no vector load of its own besides the DMA. A page id outside the pool makes the
+  // sequence bad: nothing is loaded through it and its outputs become NaN.
+  int *tile_ids = reinterpret_cast<int *>(smem + Geom<D>::IDS);
+  const int n_tiles = (n_ctx + kTile - 1) / kTile;
+  const int tpp = p.page_size / kTile;
   int page_bad = 0;
-  for (int i = tid; i < n_pages; i += kThreads) {
-    const int page = btab[pg0 + i];
+  for (int i = tid; i < n_tiles; i += kThreads) {
+    const int t = t_begin + i * kTile;
+    const int page = btab[t / p.page_size];
     page_bad |= page < 0 || page >= p.num_pages;
-    part_pages[i] = page;
+    tile_ids[i] = (page * p.Hkv + g) * tpp + (t % p.page_size) / kTile;
   }
-  if (__syncthreads_or(page_bad)) bad = true;
+  {
+    int *flags = reinterpret_cast<int *>(smem + Geom<D>::FLAGS);
+    const bool wave_bad = __ballot(page_bad) != 0;
+    if (lane == 0) flags[wave] = wave_bad;
+    __syncthreads();
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) any |= flags[w];
+    if (any) bad = true;
+  }
   const int n_full_ok = bad ? 0 : n_full;
   const int tail_ok = bad ? 0 : tail;
-
-  // Global byte address of the K and V tile that starts at context token t0 (wave-uniform).
-  auto tile_src = [&](int t0, const char *&kb, const char *&vb) {
-    const int page = __builtin_amdgcn_readfirstlane(part_pages[t0 / p.page_size - pg0]);
-    const int off0 = t0 % p.page_size;
-    const size_t ph = (size_t)page * p.Hkv + g;
-    kb = reinterpret_cast<const char *>(kp + (ph * p.page_size + off0) * D);
-    vb = reinterpret_cast<const char *>(vp + (ph * (p.page_size / kTile) + off0 / kTile) * D * kTile);
-  };
+  const char *kpool = static_cast<const char *>(p.k_pages);
+  const char *vpool = static_cast<const char *>(p.v_pages);
+  constexpr size_t kTileBytes = (size_t)kTile * D * 2;
 
   LaneMap<D> lm;
   lm.init(lane, wave);
+  // DMA of context tile n into stage n % kStages (tile indices are read after a barrier, when this
+  // wave has no LDS read in flight).
+  auto dma_ctx_tile = [&](int n, int stage) {
+    const size_t off = (size_t)__builtin_amdgcn_readfirstlane(tile_ids[n]) * kTileBytes;
+    dma_tile<D>(smem, stage, kpool + off, vpool + off, lm);
+  };
 
   // Query rows of this wave (B operand of S^T = K Q^T): row r -> (head j, position i).
   const int col = lane & 31, hh = lane >> 5;
@@ -408,8 +570,8 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
     for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = row_ok ? ld_global_16(qrow + kk * 16 + hh * 8) : z;
   }
 
-  // The block's own keys (partition 0) go through the last stage, loaded before the ring starts
-  // so that waiting for them never waits for context tiles.
+  // The block's own keys (partition 0) go through the last stage; their loads complete before any
+  // context DMA is issued, so the ring's vmcnt waits count DMA only.
   if (has_block) {
     const size_t bg = (size_t)b * p.Hkv + g;
     load_block_tile<D>(smem, kStages - 1, static_cast<const uint16_t *>(p.k_blk) + bg * p.S * D,
@@ -418,13 +580,8 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
 
   // Start the ring: context tiles 0 .. kStages-2 into stages 0 .. kStages-2.
 #pragma unroll
-  for (int n = 0; n < kStages - 1; ++n) {
-    if (n < n_full_ok) {
-      const char *kb, *vb;
-      tile_src(t_begin + n * kTile, kb, vb);
-      dma_tile<D>(smem, n, kb, vb, lm);
-    }
-  }
+  for (int n = 0; n < kStages - 1; ++n)
+    if (n < n_full_ok) dma_ctx_tile(n, n);
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -432,9 +589,6 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   float m = -INFINITY, lpart = 0.f;
   const float c = p.scale * kLog2e;
 
-  // Q (and the first context tiles) have landed: inside the loop only the ring's own DMA is
-  // ever waited for.
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   if (has_block) {
     lds_barrier();
     if (wave_active)
@@ -442,35 +596,45 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
                             Geom<D>::VBASE, p.S, lm, qreg, oacc, m, lpart, c, lane);
   }
 
-  // The ring, unrolled by its depth so that every stage offset is a compile-time immediate.
-  auto ring_step = [&](auto stage_tag, int n) {
-    constexpr int S = decltype(stage_tag)::value;
-    wait_dma<Geom<D>::LOADS>(min(kStages - 2, n_full_ok - 1 - n));
-    lds_barrier();  // tile n is in LDS for every wave; stage (n-1) % kStages is free again
-    const int nn = n + kStages - 1;
-    if (nn < n_full_ok) {
-      const char *kb, *vb;
-      tile_src(t_begin + nn * kTile, kb, vb);
-      dma_tile<D>(smem, (S + kStages - 1) % kStages, kb, vb, lm);
+  if (n_full_ok > 0) {
+    // Tile 0 is in LDS for every wave.
+    wait_dma<Geom<D>::LOADS>(min(kStages - 2, n_full_ok - 1));
+    lds_barrier();
+    PipeRegs<D> pr;
+    if (wave_active) pipe_start<D>(smem, lm, qreg, pr);
+    // Tile T is consumed by M(2T) and M(2T+1) (its V) after M(2T-2) and M(2T-1) read its K.
+    // Before M(2T): wait for tile T+1, then refill the stage of tile T-1, which every wave is done
+    // with. The ring is unrolled by its depth so that all LDS offsets are immediates.
+    auto ring_step = [&](auto stage_tag, int T) {
+      constexpr int ST = decltype(stage_tag)::value;
+      constexpr int NX = (ST + 1) % kStages;
+      if (T + 1 < n_full_ok) {
+        wait_dma<Geom<D>::LOADS>(min(1, n_full_ok - 2 - T));
+        lds_barrier();
+        if (T + kStages - 1 < n_full_ok) dma_ctx_tile(T + kStages - 1, (ST + kStages - 1) % kStages);
+      }
+      if (wave_active) {
+        pipe_mma<D, NX, 0, ST, 0>(smem, lm, qreg, pr, oacc);
+        pipe_softmax<D>(pr, m, lpart, c);
+        pipe_mma<D, NX, 1, ST, 1>(smem, lm, qreg, pr, oacc);
+        pipe_softmax<D>(pr, m, lpart, c);
+      }
+    };
+    for (int T = 0; T < n_full_ok; T += kStages) {
+      ring_step(std::integral_constant<int, 0>{}, T);
+      if (T + 1 < n_full_ok) ring_step(std::integral_constant<int, 1>{}, T + 1);
+      if (T + 2 < n_full_ok) ring_step(std::integral_constant<int, 2>{}, T + 2);
+      if (T + 3 < n_full_ok) ring_step(std::integral_constant<int, 3>{}, T + 3);
     }
-    if (wave_active)
-      attend_tile<D, true>(smem, Geom<D>::koff(S), Geom<D>::voff(S) - Geom<D>::VBASE, kTile, lm,
-                           qreg, oacc, m, lpart, c, lane);
-  };
-  for (int n = 0; n < n_full_ok; n += kStages) {
-    ring_step(std::integral_constant<int, 0>{}, n);
-    if (n + 1 < n_full_ok) ring_step(std::integral_constant<int, 1>{}, n + 1);
-    if (n + 2 < n_full_ok) ring_step(std::integral_constant<int, 2>{}, n + 2);
-    if (n + 3 < n_full_ok) ring_step(std::integral_constant<int, 3>{}, n + 3);
+    if (wave_active) pipe_finish<D>(pr, oacc);
   }
 
   if (tail_ok > 0) {
     lds_barrier();  // every wave is done with the ring before a stage is overwritten
     const int st = n_full_ok % kStages;
-    const char *kb, *vb;
-    tile_src(t_begin + n_full_ok * kTile, kb, vb);
-    load_tail_tile<D>(smem, st, reinterpret_cast<const uint16_t *>(kb),
-                      reinterpret_cast<const uint16_t *>(vb), tail_ok, tid);
+    const size_t off = (size_t)__builtin_amdgcn_readfirstlane(tile_ids[n_full_ok]) * kTileBytes;
+    load_tail_tile<D>(smem, st, reinterpret_cast<const uint16_t *>(kpool + off),
+                      reinterpret_cast<const uint16_t *>(vpool + off), tail_ok, tid);
     lds_barrier();
     if (wave_active)
       attend_tile<D, false>(smem, Geom<D>::koff(st), Geom<D>::voff(st) - Geom<D>::VBASE, tail_ok,
@@ -482,7 +646,7 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   // every store instruction covers whole contiguous rows.
   lds_barrier();
   if (!wave_active) return;
-  const float l = lpart + swap_halves(lpart);
+  const float l = pair_sum(lpart);
   const float inv = bad ? NAN : 1.0f / l;
   const float lse_val = bad ? NAN : m * p.scale + logf(l);
   const bool to_part = p.splits > 1;

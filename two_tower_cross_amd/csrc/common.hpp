@@ -67,6 +67,18 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// max / sum of x over the lane pair (lane, lane ^ 32), in every lane, without LDS: one
+// v_permlane32_swap gives each lane both halves' values.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
   return x;
