@@ -85,47 +85,32 @@ struct Geom {
   static __device__ __forceinline__ constexpr int voff(int s) { return VBASE + s * VBYTES; }
 };
 
-// Per-lane constants of one wave: LDS byte offsets of its MFMA operands within a stage and the
-// byte offsets of its DMA sources within a tile.
+// Per-lane constants of one wave. MFMA operand reads: the K operand for K-step kk of sub-tile 0 of
+// a stage is at kb ^ (kk * 32), the V operand for (sub-tile sub, 16-token half kc) at
+// vb ^ (sub * 64 + kc * 32) (these XORs only touch the chunk bits below the row bits, so they
+// commute with adding stage, sub-tile and 32-row block offsets). DMA: this lane's j-th 16-byte
+// chunk of a 16 KB tile comes from byte kdma (vdma) + j * kThreads * 16 of the source and goes to
+// LDS byte (j * kWaves + wave) * 1024 of the stage (the swizzle keys repeat with that step).
 template <int D>
 struct LaneMap {
-  int k[D / 16];    // K operand of S^T = K Q^T, sub-tile 0 (sub-tile 1 is +32 rows)
-  int v[2][2];      // V operand of O^T += V^T P^T for (sub-tile, 16-token half), incl. VBASE
-  uint32_t kdma[Geom<D>::KCH];  // source byte offsets of this lane's K chunks in a tile
-  uint32_t vdma[Geom<D>::VCH];  // source byte offsets of its V chunks in a [D][64] V tile
-  int kdst[Geom<D>::KCH];       // LDS byte offsets (wave-uniform) of those DMA segments
-  int vdst[Geom<D>::VCH];
+  int kb, vb;
+  uint32_t kdma, vdma;
+  int wave;
 
-  __device__ __forceinline__ void init(int lane, int wave) {
+  __device__ __forceinline__ void init(int lane, int wave_) {
+    wave = wave_;
     const int col = lane & 31, hh = lane >> 5;
     const int tok = swap_bits23(col);
-    const int key = kkey<D>(tok);
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) k[kk] = tok * D * 2 + (((kk * 2 + hh) ^ key) << 4);
-    const int vk = vkey(col);
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-        v[sub][kc] = Geom<D>::VBASE + col * kTile * 2 + (((sub * 4 + kc * 2 + hh) ^ vk) << 4);
-    constexpr int KC = D / 8;
-#pragma unroll
-    for (int j = 0; j < Geom<D>::KCH; ++j) {
-      const int seg = j * kWaves + wave;
-      const int f = seg * 64 + lane;
-      const int r = f / KC, pp = f % KC;
-      kdma[j] = (uint32_t)(r * D + ((pp ^ kkey<D>(r)) << 3)) * 2u;
-      kdst[j] = seg * 1024;
-    }
-#pragma unroll
-    for (int j = 0; j < Geom<D>::VCH; ++j) {
-      const int seg = j * kWaves + wave;
-      const int f = seg * 64 + lane;
-      const int d = f / 8, pp = f % 8;
-      vdma[j] = (uint32_t)(d * kTile + ((pp ^ vkey(d)) << 3)) * 2u;
-      vdst[j] = seg * 1024;
-    }
+    kb = tok * D * 2 + ((hh ^ kkey<D>(tok)) << 4);
+    vb = Geom<D>::VBASE + col * kTile * 2 + ((hh ^ vkey(col)) << 4);
+    const int f = wave * 64 + lane;
+    const int r = f / (D / 8), pk = f % (D / 8);
+    kdma = (uint32_t)(r * D + ((pk ^ kkey<D>(r)) << 3)) * 2u;
+    const int d = f / 8, pv = f % 8;
+    vdma = (uint32_t)(d * kTile + ((pv ^ vkey(d)) << 3)) * 2u;
   }
+  __device__ __forceinline__ int k(int kk) const { return kb ^ (kk * 32); }
+  __device__ __forceinline__ int v(int sub, int kc) const { return vb ^ (sub * 64 + kc * 32); }
 };
 
 // Buffer resource over one 16 KB tile (raw, 32-bit data format; loads past the tile return 0).
@@ -144,12 +129,14 @@ __device__ __forceinline__ void dma_tile(char *smem, int s, const char *kb, cons
   const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vb, Geom<D>::VBYTES);
 #pragma unroll
   for (int j = 0; j < Geom<D>::KCH; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, LDS_PTR(smem + Geom<D>::koff(s) + lm.kdst[j]), 16,
-                                             lm.kdma[j], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        kr, LDS_PTR(smem + Geom<D>::koff(s) + (j * kWaves + lm.wave) * 1024), 16, lm.kdma,
+        j * kThreads * 16, 0, 0);
 #pragma unroll
   for (int j = 0; j < Geom<D>::VCH; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, LDS_PTR(smem + Geom<D>::voff(s) + lm.vdst[j]), 16,
-                                             lm.vdma[j], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        vr, LDS_PTR(smem + Geom<D>::voff(s) + (j * kWaves + lm.wave) * 1024), 16, lm.vdma,
+        j * kThreads * 16, 0, 0);
 }
 
 // Partial context tile (`valid` < 64 tokens) -> LDS stage s through registers, zero-filling the
@@ -258,8 +245,8 @@ __device__ __forceinline__ void attend_tile(const char *smem, int kst, int vst, 
   u32x4 a0[D / 16], a1[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    a0[kk] = ld_lds_16(smem + kst + lm.k[kk]);
-    a1[kk] = ld_lds_16(smem + kst + lm.k[kk] + 32 * D * 2);
+    a0[kk] = ld_lds_16(smem + kst + lm.k(kk));
+    a1[kk] = ld_lds_16(smem + kst + 32 * D * 2 + lm.k(kk));
   }
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
@@ -310,13 +297,13 @@ __device__ __forceinline__ void attend_tile(const char *smem, int kst, int vst, 
   u32x4 v0[D / 16], v1[D / 16];
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) {
-    v0[2 * mb] = ld_lds_16(smem + vst + lm.v[0][0] + mb * 32 * kTile * 2);
-    v0[2 * mb + 1] = ld_lds_16(smem + vst + lm.v[0][1] + mb * 32 * kTile * 2);
+    v0[2 * mb] = ld_lds_16(smem + vst + mb * 32 * kTile * 2 + lm.v(0, 0));
+    v0[2 * mb + 1] = ld_lds_16(smem + vst + mb * 32 * kTile * 2 + lm.v(0, 1));
   }
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) {
-    v1[2 * mb] = ld_lds_16(smem + vst + lm.v[1][0] + mb * 32 * kTile * 2);
-    v1[2 * mb + 1] = ld_lds_16(smem + vst + lm.v[1][1] + mb * 32 * kTile * 2);
+    v1[2 * mb] = ld_lds_16(smem + vst + mb * 32 * kTile * 2 + lm.v(1, 0));
+    v1[2 * mb + 1] = ld_lds_16(smem + vst + mb * 32 * kTile * 2 + lm.v(1, 1));
   }
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) {
@@ -350,8 +337,9 @@ __device__ __forceinline__ void attend_tile(const char *smem, int kst, int vst, 
 // Software pipeline over the 32-token sub-tiles of the full context tiles. Window u consists of
 // a matrix half M(u), which issues the PV product of sub-tile u-1 and the QK product of sub-tile
 // u+1 and prefetches from LDS the operands of M(u+1) (V of sub-tile u, K of sub-tile u+2), and a
-// vector half V(u), the softmax of sub-tile u, which depends on neither, so the two overlap.
-// Between halves the registers carry:
+// vector half V(u), the softmax of sub-tile u, which depends on neither, so the two overlap (a
+// window is one basic block apart from a rarely taken branch). Between halves the registers
+// carry:
 template <int D>
 struct PipeRegs {
   f32x16 s;          // S^T of the sub-tile whose softmax is next (raw scores)
@@ -359,22 +347,13 @@ struct PipeRegs {
   u32x4 k[D / 16];   // K operand of the next QK
   u32x4 v[D / 16];   // V operand of the next PV, [32-dim block][16-token half]
   u32x4 pa, pb;      // P^T of the next PV (bf16), token halves 0 and 1
-  float alpha;       // factor that moves O to the current reference maximum
-  bool rescale;      // alpha != 1 (wave-uniform)
 };
 
 // M(u). KS/KH: stage and half of sub-tile u+2 (its K is loaded); VS/VH: of sub-tile u (its V is
-// loaded). O, which holds everything through sub-tile u-2 scaled by the reference maximum before
-// V(u-1), is first moved to the current one if V(u-1) changed it (a branch the whole wave takes
-// together, rarely), then the PV of sub-tile u-1 (whose P already uses the current maximum) is
-// added.
+// loaded). Adds the PV of sub-tile u-1 to O.
 template <int D, int KS, int KH, int VS, int VH>
 __device__ __forceinline__ void pipe_mma(const char *smem, const LaneMap<D> &lm, const u32x4 *qreg,
                                          PipeRegs<D> &r, f32x16 *oacc) {
-  if (r.rescale) {
-#pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= r.alpha;
-  }
 #pragma unroll
   for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -388,11 +367,11 @@ __device__ __forceinline__ void pipe_mma(const char *smem, const LaneMap<D> &lm,
   for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
-      r.v[2 * mb + kc] = ld_lds_16(smem + (Geom<D>::voff(VS) - Geom<D>::VBASE) + lm.v[VH][kc] +
-                                   mb * 32 * kTile * 2);
+      r.v[2 * mb + kc] = ld_lds_16(smem + (Geom<D>::voff(VS) - Geom<D>::VBASE) +
+                                   mb * 32 * kTile * 2 + lm.v(VH, kc));
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
-    r.k[kk] = ld_lds_16(smem + Geom<D>::koff(KS) + KH * 32 * D * 2 + lm.k[kk]);
+    r.k[kk] = ld_lds_16(smem + Geom<D>::koff(KS) + KH * 32 * D * 2 + lm.k(kk));
   // Each operand read follows the MFMA that last used its registers.
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -427,24 +406,26 @@ __device__ __forceinline__ float exp_pack(const f32x16 &s, float c, float mc, u3
 }
 
 // V(u): softmax of sub-tile u against the reference maximum m. The exponentials are first taken
-// against the current m; only when some lane's 16 of them sum to more than 2^kLaneSumLog2 (or to
-// inf / NaN, as for the first sub-tile, when m = -inf) does the wave take the rare branch that
-// moves m to the row maximum (never down) and recomputes them, so every weight stays <= 2^12. P of
-// sub-tile u then uses the new m; O is moved to it at the start of M(u+1).
+// against the current m; only when some lane's 16 of them sum to more than kLaneSumMax (or to inf /
+// NaN, as for the first sub-tile, when m = -inf) does the wave take the rare branch that moves m to
+// the row maximum (never down), rescales l and O (which, after M(u), holds everything through
+// sub-tile u-1) and recomputes them, so every weight stays <= kLaneSumMax.
 template <int D>
-__device__ __forceinline__ void pipe_softmax(PipeRegs<D> &r, float &m, float &lpart, float c) {
+__device__ __forceinline__ void pipe_softmax(PipeRegs<D> &r, f32x16 *oacc, float &m, float &lpart,
+                                             float c) {
   float ps = exp_pack(r.s, c, m * c, r.pa, r.pb);
-  r.rescale = __ballot(!(ps <= kLaneSumMax)) != 0;
-  if (r.rescale) {
+  if (__ballot(!(ps <= kLaneSumMax))) {
     float t[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       t[j] = fmaxf(fmaxf(r.s[4 * j], r.s[4 * j + 1]), fmaxf(r.s[4 * j + 2], r.s[4 * j + 3]));
     const float mx = pair_max(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])));
     const float mnew = fmaxf(m, mx);
-    r.alpha = __builtin_amdgcn_exp2f((m - mnew) * c);  // 0 while m = -inf
+    const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c);  // 0 while m = -inf
     m = mnew;
-    lpart *= r.alpha;
+    lpart *= alpha;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
     ps = exp_pack(r.s, c, mnew * c, r.pa, r.pb);
   }
   lpart += ps;
@@ -458,10 +439,10 @@ __device__ __forceinline__ void pipe_start(const char *smem, const LaneMap<D> &l
                                            const u32x4 *qreg, PipeRegs<D> &r) {
   u32x4 k0[D / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) k0[kk] = ld_lds_16(smem + Geom<D>::koff(0) + lm.k[kk]);
+  for (int kk = 0; kk < D / 16; ++kk) k0[kk] = ld_lds_16(smem + Geom<D>::koff(0) + lm.k(kk));
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
-    r.k[kk] = ld_lds_16(smem + Geom<D>::koff(0) + 32 * D * 2 + lm.k[kk]);
+    r.k[kk] = ld_lds_16(smem + Geom<D>::koff(0) + 32 * D * 2 + lm.k(kk));
   r.s = f32x16{};
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) r.s = mfma32x32x16(k0[kk], qreg[kk], r.s);
@@ -470,17 +451,11 @@ __device__ __forceinline__ void pipe_start(const char *smem, const LaneMap<D> &l
   for (int j = 0; j < D / 16; ++j) r.v[j] = z;
   r.pa = z;
   r.pb = z;
-  r.alpha = 1.f;
-  r.rescale = false;
 }
 
-// Pipeline end: the pending rescale, then the PV product of the last sub-tile.
+// Pipeline end: the PV product of the last sub-tile.
 template <int D>
 __device__ __forceinline__ void pipe_finish(const PipeRegs<D> &r, f32x16 *oacc) {
-  if (r.rescale) {
-#pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= r.alpha;
-  }
 #pragma unroll
   for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -615,9 +590,9 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
       }
       if (wave_active) {
         pipe_mma<D, NX, 0, ST, 0>(smem, lm, qreg, pr, oacc);
-        pipe_softmax<D>(pr, m, lpart, c);
+        pipe_softmax<D>(pr, oacc, m, lpart, c);
         pipe_mma<D, NX, 1, ST, 1>(smem, lm, qreg, pr, oacc);
-        pipe_softmax<D>(pr, m, lpart, c);
+        pipe_softmax<D>(pr, oacc, m, lpart, c);
       }
     };
     for (int T = 0; T < n_full_ok; T += kStages) {
@@ -643,7 +618,8 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
 
   // Epilogue. Each wave stages its normalized 32 x D output block in a private LDS slice (the
   // ring is idle once every wave has passed this barrier) and writes it back row by row, so
-  // every store instruction covers whole contiguous rows.
+  // every store instruction covers whole contiguous rows. In the slice the 16-byte chunks of row
+  // r are XOR-swizzled by r, so that the 32 rows one LDS store touches fall in distinct banks.
   lds_barrier();
   if (!wave_active) return;
   const float l = pair_sum(lpart);
@@ -651,9 +627,11 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   const float lse_val = bad ? NAN : m * p.scale + logf(l);
   const bool to_part = p.splits > 1;
   const bool half_out = to_part || p.out_bf16;     // 2-byte elements (fp16 partial / bf16 out)
+  const int row_bytes = D * (half_out ? 2 : 4);
+  const int cpr = row_bytes / 16;                 // 16-byte chunks per row (a power of two)
   char *slice = smem + wave * (32 * D * 4);
+  char *rowp = slice + col * row_bytes;
   if (half_out) {
-    uint16_t *st = reinterpret_cast<uint16_t *>(slice);
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
@@ -669,10 +647,10 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
           pk.x = pack_bf16x2(o0, o1);
           pk.y = pack_bf16x2(o2, o3);
         }
-        *reinterpret_cast<uint2 *>(st + col * D + d) = pk;
+        const int byte = d * 2;
+        *reinterpret_cast<uint2 *>(rowp + (((byte >> 4) ^ (col & (cpr - 1))) << 4) + (byte & 15)) = pk;
       }
   } else {
-    float *st = reinterpret_cast<float *>(slice);
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
@@ -683,18 +661,20 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
         o[1] = oacc[mb][q4 * 4 + 1] * inv;
         o[2] = oacc[mb][q4 * 4 + 2] * inv;
         o[3] = oacc[mb][q4 * 4 + 3] * inv;
-        *reinterpret_cast<f32x4 *>(st + col * D + d) = o;
+        *reinterpret_cast<f32x4 *>(rowp + ((((d * 4) >> 4) ^ (col & (cpr - 1))) << 4)) = o;
       }
   }
-  const int row_bytes = D * (half_out ? 2 : 4);
-  const int cpr = row_bytes / 16;                 // 16-byte chunks per row
+  // chunk cc of slice row rr (the un-swizzled source of a contiguous row store)
+  auto slice_chunk = [&](int rr, int cc) {
+    return ld_lds_16(slice + rr * row_bytes + ((cc ^ (rr & (cpr - 1))) << 4));
+  };
   if (to_part) {
     const size_t item = (size_t)item_bgr * p.splits + split;
     // rows wave*32 .. wave*32+31 of this partition are contiguous in the partial buffer
     char *dst = reinterpret_cast<char *>(p.part_o) + (item * p.rows_per_group + wave * 32) * (size_t)row_bytes;
     const int nrows = min(32, p.rows_per_group - wave * 32);
     for (int f = lane; f < nrows * cpr; f += 64)
-      *reinterpret_cast<u32x4 *>(dst + (size_t)f * 16) = ld_lds_16(slice + f * 16);
+      *reinterpret_cast<u32x4 *>(dst + (size_t)f * 16) = slice_chunk(f / cpr, f % cpr);
     if (hh == 0 && r_local < p.rows_per_group)
       p.part_lse[item * p.rows_per_group + r_local] = lse_val;
   } else {
@@ -705,7 +685,7 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
       if (wave * 32 + rr >= p.rows_per_group || rg_row >= p.rows) continue;
       const int j2 = rg_row / p.S, i2 = rg_row % p.S;
       const size_t orow = ((size_t)b * p.S + i2) * p.Hq + (g * p.G + j2);
-      *reinterpret_cast<u32x4 *>(obase + orow * row_bytes + cc * 16) = ld_lds_16(slice + f * 16);
+      *reinterpret_cast<u32x4 *>(obase + orow * row_bytes + cc * 16) = slice_chunk(rr, cc);
     }
     if (p.lse && hh == 0 && row_ok) p.lse[((size_t)b * p.Hq + h) * p.S + iq] = lse_val;
   }
