@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define TWOTOWER_ABI_VERSION 1
+#define TWOTOWER_ABI_VERSION 2
 
 typedef enum {
   TT_OK = 0,
@@ -155,14 +155,21 @@ typedef struct {
  *   [Q | K_blk | V_blk] = H W_qkv^T,  W_qkv bf16 [(Hq + 2*Hkv)*head_dim, hidden]
  *   H <- H + O W_o^T,                  W_o   bf16 [hidden, Hq*head_dim]
  * and logits = H W_lm^T,               W_lm  bf16 [vocab, hidden], fp32 logits [rows, vocab].
- * Weights are stored [out_features, in_features]. The block's own KV is rewritten every step
- * because the block changes (explainer, "Generierungsprozess").
+ * Weights W [out_features, in_features] (row-major bf16) are passed in the packed form written by
+ * twotower_pack_weight (once, when the weights are loaded). The block's own KV is rewritten every
+ * step because the block changes (explainer, "Generierungsprozess").
  * Products accumulate in fp32 and are rounded once to the output type.
+ *
+ * Packed weight layout (the A-operand order of the 32x32x16 bf16 matrix instruction): with
+ * Ks = ceil(in_features / 16), the bf16 element at
+ *   ((nb * Ks + s) * 64 + lane) * 8 + e     (nb < ceil(out_features / 32), s < Ks, lane < 64, e < 8)
+ * is W[nb * 32 + lane % 32][s * 16 + (lane / 32) * 8 + e], and 0 where that is outside W.
+ * Size: twotower_packed_weight_bytes(out_features, in_features) bytes.
  */
 typedef struct {
   int32_t batch, S, hidden, num_q_heads, num_kv_heads, head_dim;
   const void *h;        /* bf16 [batch, S, hidden] */
-  const void *w_qkv;    /* bf16 [(Hq + 2*Hkv)*head_dim, hidden] */
+  const void *w_qkv;    /* packed bf16 [(Hq + 2*Hkv)*head_dim, hidden] */
   void *q;              /* bf16 [batch, S, Hq, head_dim] */
   void *k_blk;          /* bf16 [batch, Hkv, S, head_dim] */
   void *v_blk;          /* bf16 [batch, Hkv, head_dim, S] */
@@ -173,7 +180,7 @@ typedef struct {
   int32_t reserved0;
   const void *h_in;     /* bf16 [rows, hidden] residual input (may equal h_out) */
   const void *o;        /* bf16 [rows, in_features] attention output */
-  const void *w_o;      /* bf16 [hidden, in_features] */
+  const void *w_o;      /* packed bf16 [hidden, in_features] */
   void *h_out;          /* bf16 [rows, hidden] = h_in + o W_o^T */
 } tt_out_proj_args;
 
@@ -182,7 +189,7 @@ typedef struct {
   int32_t reserved0;
   int64_t ld;           /* row stride of logits in elements, >= vocab, multiple of 4 */
   const void *h;        /* bf16 [rows, hidden] */
-  const void *w_lm;     /* bf16 [vocab, hidden] */
+  const void *w_lm;     /* packed bf16 [vocab, hidden] */
   float *logits;        /* fp32 [rows, ld] */
 } tt_lm_head_args;
 
@@ -207,11 +214,11 @@ typedef struct {
   tt_block_attn_args attn;
   const void *const *k_pages;   /* host array [num_layers] of device pointers */
   const void *const *v_pages;
-  const void *const *w_qkv;
+  const void *const *w_qkv;     /* packed weights (see the projections) */
   const void *const *w_o;
   void *const *k_blk;           /* host array [num_layers]: block KV, rewritten every step */
   void *const *v_blk;
-  const void *w_lm;
+  const void *w_lm;             /* packed */
   const void *h_in;             /* bf16 [batch, S, hidden], read only */
   void *h_work;                 /* bf16 [batch, S, hidden], residual stream after the step */
   void *q;                      /* bf16 [batch, S, Hq, head_dim] scratch */
@@ -233,6 +240,15 @@ tt_status twotower_out_projection(const tt_out_proj_args *args, void *ws, size_t
 tt_status twotower_lm_head(const tt_lm_head_args *args, void *ws, size_t *ws_bytes, void *stream);
 tt_status twotower_denoise_step(const tt_denoise_step_args *args, void *ws, size_t *ws_bytes,
                                 void *stream);
+
+/* Bytes of the packed form of a weight [out_features, in_features] (layout above):
+ * ceil(out_features / 32) * ceil(in_features / 16) * 1024; 0 for a non-positive size. */
+size_t twotower_packed_weight_bytes(int32_t out_features, int32_t in_features);
+/* Writes the packed form of the row-major bf16 weight w into `packed` (device memory of
+ * twotower_packed_weight_bytes bytes, owned by the caller), enqueued on `stream`. Both pointers
+ * 16-byte aligned and in_features % 8 == 0 (else TT_EINVAL / TT_ENOTSUP); no workspace. */
+tt_status twotower_pack_weight(const void *w, int32_t out_features, int32_t in_features,
+                               void *packed, void *stream);
 
 /* Static string for a status code ("TT_OK", ...); never NULL. */
 const char *twotower_status_string(int32_t status);

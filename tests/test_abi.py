@@ -132,19 +132,35 @@ def test_unmask_workspace_and_errors():
         assert query("twotower_unmask", unmask_args(**over))[0] == code, over
 
 
+def test_packed_weight_size_and_validation(L):
+    # ceil(out / 32) slabs of ceil(in / 16) 1 KB blocks
+    assert L.twotower_packed_weight_bytes(4608, 2048) == 144 * 128 * 1024
+    assert L.twotower_packed_weight_bytes(1004, 136) == 32 * 9 * 1024
+    assert L.twotower_packed_weight_bytes(0, 16) == 0
+    assert L.twotower_packed_weight_bytes(16, -1) == 0
+    # argument errors are reported before anything is enqueued
+    assert L.twotower_pack_weight(FAKE, 64, 12, FAKE, None) == _lib.TT_ENOTSUP   # 12 % 8 != 0
+    assert L.twotower_pack_weight(None, 64, 64, FAKE, None) == _lib.TT_EINVAL
+    assert L.twotower_pack_weight(FAKE, 64, 64, None, None) == _lib.TT_EINVAL
+    assert L.twotower_pack_weight(FAKE + 8, 64, 64, FAKE, None) == _lib.TT_EINVAL
+    assert L.twotower_pack_weight(FAKE, 0, 64, FAKE, None) == _lib.TT_EINVAL
+
+
 def test_projection_queries_and_errors():
     q = _lib.QkvArgs(8, 16, 2048, 32, 2, 128, FAKE, FAKE, FAKE, FAKE, FAKE)
     st, n = query("twotower_qkv_projection", q)
-    assert st == _lib.TT_OK and n % 256 == 0
+    # 72 tiles of 64 features -> K in 3 partitions (one work-group per compute unit): fp32 partials
+    assert st == _lib.TT_OK and n == 3 * 128 * 4608 * 4
     q.hidden = 2044
     assert query("twotower_qkv_projection", q)[0] == _lib.TT_ENOTSUP
     o = _lib.OutProjArgs(128, 2048, 4096, 0, FAKE, FAKE, FAKE, FAKE)
-    assert query("twotower_out_projection", o)[0] == _lib.TT_OK
+    st, n = query("twotower_out_projection", o)
+    assert st == _lib.TT_OK and n == 8 * 128 * 2048 * 4   # 32 tiles x 8 K partitions
     o.o = FAKE + 4
     assert query("twotower_out_projection", o)[0] == _lib.TT_EINVAL
     lm = _lib.LmHeadArgs(128, 2048, 131072, 0, 131072, FAKE, FAKE, FAKE)
     st, n = query("twotower_lm_head", lm)
-    assert st == _lib.TT_OK and n == 0   # 2048 feature tiles fill the GPU without K partitions
+    assert st == _lib.TT_OK and n == 0   # 512 tiles of 256 features fill the GPU without K partitions
     lm.ld = 131070
     assert query("twotower_lm_head", lm)[0] == _lib.TT_EINVAL
 

@@ -36,6 +36,27 @@ def small_model(seed=3, L=1000, layers=2, B=2, Hq=8, Hkv=2, D=128, hidden=512, V
                       vocab=V, T=16, device=DEV)
 
 
+def pack_reference(w):
+    """The packed layout written out from its definition in include/twotower.h (numpy)."""
+    N, K = w.shape
+    nbk, ks = -(-N // 32), -(-K // 16)
+    wp = np.zeros((nbk * 32, ks * 16), dtype=w.dtype)
+    wp[:N, :K] = w
+    # [nb, r, s, hh, e] -> [nb, s, hh, r, e]: lane = hh * 32 + r
+    return wp.reshape(nbk, 32, ks, 2, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
+
+
+@pytest.mark.parametrize("N,K", [(64, 64), (1004, 136), (4608, 2048), (37, 8)])
+def test_pack_weight_matches_the_documented_layout(N, K):
+    g = torch.Generator(device=DEV).manual_seed(15)
+    w = torch.randn((N, K), generator=g, device=DEV).to(torch.bfloat16)
+    pw = tt.pack_weight(w)
+    torch.cuda.synchronize()
+    got = pw.data.cpu().numpy().view(np.uint16)
+    ref = pack_reference(w.cpu().view(torch.int16).numpy().view(np.uint16))
+    assert got.shape == ref.shape and np.array_equal(got, ref)
+
+
 @pytest.mark.parametrize("shape", [(2, 16, 512, 8, 2, 128), (8, 16, 2048, 32, 2, 128),
                                    (3, 5, 264, 4, 1, 64)])
 def test_qkv_projection(shape):

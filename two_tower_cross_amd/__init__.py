@@ -20,6 +20,7 @@ from . import _lib
 from ._lib import LibraryNotBuilt, TwoTowerError, TT_BF16, TT_FP32  # noqa: F401
 
 __all__ = ["block_attn", "unmask", "qkv_projection", "out_projection", "lm_head", "DenoiseStep",
+           "PackedWeight", "pack_weight",
            "LibraryNotBuilt", "TwoTowerError", "library_path"]
 
 
@@ -152,12 +153,51 @@ def unmask(logits, masked, tokens, threshold, *, min_commit=False, commit_all=Fa
     return conf, ncom
 
 
+class PackedWeight:
+    """A bf16 weight [out_features, in_features] in the library's packed operand layout
+    (``include/twotower.h``), written by ``twotower_pack_weight``."""
+
+    def __init__(self, data, out_features, in_features):
+        self.data, self.out_features, self.in_features = data, out_features, in_features
+
+    @property
+    def shape(self):
+        return (self.out_features, self.in_features)
+
+    @property
+    def device(self):
+        return self.data.device
+
+
+def pack_weight(w):
+    """Pack a row-major bf16 weight [out_features, in_features] (on the GPU) for the projections."""
+    if isinstance(w, PackedWeight):
+        return w
+    _check(w, "w", w.device, torch.bfloat16, 2)
+    n, k = w.shape
+    nbytes = _lib.lib().twotower_packed_weight_bytes(n, k)
+    data = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=w.device)
+    st = _lib.lib().twotower_pack_weight(_p(w), n, k, _p(data), _stream())
+    if st != _lib.TT_OK:
+        raise TwoTowerError("twotower_pack_weight", st)
+    return PackedWeight(data, n, k)
+
+
+def _packed(w, name, device):
+    if not isinstance(w, PackedWeight):
+        _check(w, name, device, torch.bfloat16, 2)
+        w = pack_weight(w)
+    elif w.device != device:
+        raise ValueError(f"{name} is on {w.device}, expected {device}")
+    return w
+
+
 def qkv_projection(h, w_qkv, num_q_heads, num_kv_heads, head_dim):
     """[Q | K_blk | V_blk] = H W_qkv^T scattered to q [B,S,Hq,D], k_blk [B,Hkv,S,D],
-    v_blk [B,Hkv,D,S] (bf16)."""
+    v_blk [B,Hkv,D,S] (bf16). ``w_qkv`` is a PackedWeight or a bf16 tensor (packed here)."""
     dev = h.device
     _check(h, "h", dev, torch.bfloat16, 3)
-    _check(w_qkv, "w_qkv", dev, torch.bfloat16, 2)
+    w_qkv = _packed(w_qkv, "w_qkv", dev)
     B, S, hidden = h.shape
     if tuple(w_qkv.shape) != ((num_q_heads + 2 * num_kv_heads) * head_dim, hidden):
         raise ValueError("w_qkv shape mismatch")
@@ -167,7 +207,7 @@ def qkv_projection(h, w_qkv, num_q_heads, num_kv_heads, head_dim):
     a = _lib.QkvArgs()
     a.batch, a.S, a.hidden = B, S, hidden
     a.num_q_heads, a.num_kv_heads, a.head_dim = num_q_heads, num_kv_heads, head_dim
-    a.h, a.w_qkv, a.q, a.k_blk, a.v_blk = _p(h), _p(w_qkv), _p(q), _p(kb), _p(vb)
+    a.h, a.w_qkv, a.q, a.k_blk, a.v_blk = _p(h), _p(w_qkv.data), _p(q), _p(kb), _p(vb)
     _run("twotower_qkv_projection", a, dev)
     return q, kb, vb
 
@@ -177,7 +217,7 @@ def out_projection(h_in, o, w_o, out=None):
     dev = h_in.device
     _check(h_in, "h_in", dev, torch.bfloat16)
     _check(o, "o", dev, torch.bfloat16)
-    _check(w_o, "w_o", dev, torch.bfloat16, 2)
+    w_o = _packed(w_o, "w_o", dev)
     hidden, inf = w_o.shape
     rows = h_in.numel() // hidden
     if h_in.shape[-1] != hidden or o.numel() != rows * inf:
@@ -186,7 +226,7 @@ def out_projection(h_in, o, w_o, out=None):
         out = torch.empty_like(h_in)
     a = _lib.OutProjArgs()
     a.rows, a.hidden, a.in_features = rows, hidden, inf
-    a.h_in, a.o, a.w_o, a.h_out = _p(h_in), _p(o), _p(w_o), _p(out)
+    a.h_in, a.o, a.w_o, a.h_out = _p(h_in), _p(o), _p(w_o.data), _p(out)
     _run("twotower_out_projection", a, dev)
     return out
 
@@ -195,14 +235,14 @@ def lm_head(h, w_lm, out=None):
     """logits = H W_lm^T in fp32, shape h.shape[:-1] + (vocab,)."""
     dev = h.device
     _check(h, "h", dev, torch.bfloat16)
-    _check(w_lm, "w_lm", dev, torch.bfloat16, 2)
+    w_lm = _packed(w_lm, "w_lm", dev)
     vocab, hidden = w_lm.shape
     rows = h.numel() // hidden
     if out is None:
         out = torch.empty(tuple(h.shape[:-1]) + (vocab,), dtype=torch.float32, device=dev)
     a = _lib.LmHeadArgs()
     a.rows, a.hidden, a.vocab, a.ld = rows, hidden, vocab, vocab
-    a.h, a.w_lm, a.logits = _p(h), _p(w_lm), _p(out)
+    a.h, a.w_lm, a.logits = _p(h), _p(w_lm.data), _p(out)
     _run("twotower_lm_head", a, dev)
     return out
 
@@ -210,8 +250,9 @@ def lm_head(h, w_lm, out=None):
 class DenoiseStep:
     """One denoise step of the synthetic attention-only denoiser, reused across steps.
 
-    Holds the per-layer context caches (read only), weights and the block-KV / scratch buffers,
-    so that calling it only enqueues kernels on the current stream.
+    Holds the per-layer context caches (read only), the packed weights (bf16 tensors given here
+    are packed once, at construction) and the block-KV / scratch buffers, so that calling it only
+    enqueues kernels on the current stream.
     """
 
     def __init__(self, *, k_pages, v_pages, w_qkv, w_o, w_lm, block_table, ctx_lens,
@@ -220,6 +261,9 @@ class DenoiseStep:
         dev = w_lm.device
         self.device = dev
         self.L = len(k_pages)
+        w_qkv = [_packed(w, "w_qkv", dev) for w in w_qkv]
+        w_o = [_packed(w, "w_o", dev) for w in w_o]
+        w_lm = _packed(w_lm, "w_lm", dev)
         vocab, hidden = w_lm.shape
         self.hidden, self.vocab = hidden, vocab
         self.B, self.S = batch, S
@@ -242,8 +286,8 @@ class DenoiseStep:
             a = (C.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
             return a
 
-        self._arrs = [arr(k_pages), arr(v_pages), arr(w_qkv), arr(w_o), arr(self.k_blk),
-                      arr(self.v_blk)]
+        self._arrs = [arr(k_pages), arr(v_pages), arr([w.data for w in w_qkv]),
+                      arr([w.data for w in w_o]), arr(self.k_blk), arr(self.v_blk)]
         a = _lib.DenoiseStepArgs()
         a.num_layers, a.hidden, a.vocab = self.L, hidden, vocab
         P, _, page, _ = k_pages[0].shape
@@ -258,7 +302,7 @@ class DenoiseStep:
         a.attn.num_splits = int(num_splits)
         vpp = C.POINTER(C.c_void_p)
         a.k_pages, a.v_pages, a.w_qkv, a.w_o, a.k_blk, a.v_blk = [C.cast(x, vpp) for x in self._arrs]
-        a.w_lm = _p(w_lm)
+        a.w_lm = _p(w_lm.data)
         a.h_work, a.q, a.attn_out, a.logits = _p(self.h_work), _p(self.q), _p(self.attn_out), _p(self.logits)
         a.logits_ld = vocab
         a.unmask.confidence, a.unmask.n_committed = _p(self.confidence), _p(self.n_committed)

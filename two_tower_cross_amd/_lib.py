@@ -14,7 +14,7 @@ LIB_PATH = os.environ.get("TWOTOWER_LIB", os.path.join(HERE, "libtwotower.so"))
 
 TT_OK, TT_EINVAL, TT_ENOTSUP, TT_ENOSPACE, TT_EHIP = range(5)
 TT_FP32, TT_BF16 = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 i32, i64, f32, vp = C.c_int32, C.c_int64, C.c_float, C.c_void_p
 
@@ -109,6 +109,10 @@ def lib():
         L.twotower_struct_size.argtypes = [i32]
         L.twotower_struct_offset.restype = i64
         L.twotower_struct_offset.argtypes = [i32, i32]
+        L.twotower_packed_weight_bytes.restype = C.c_size_t
+        L.twotower_packed_weight_bytes.argtypes = [i32, i32]
+        L.twotower_pack_weight.restype = i32
+        L.twotower_pack_weight.argtypes = [vp, i32, i32, vp, vp]
         if L.twotower_abi_version() != ABI_VERSION:
             raise RuntimeError("libtwotower ABI version mismatch")
         _lib = L

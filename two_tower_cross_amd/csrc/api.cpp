@@ -183,18 +183,24 @@ hipError_t run_unmask(UnmaskPlan &pl, void *ws, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------------- linear
-// Tile shape and K partitions of a skinny product (measured on MI355X at M = 128): wide 256-feature
-// tiles once N alone yields two waves of work-groups; otherwise 64-feature tiles with K split so
-// that roughly 128-256 work-groups run, each over at least 16 chunks of 64 along K.
+// Tile shape and K partitions of a skinny product: 256-feature tiles once N alone yields a full
+// wave of work-groups (one per compute unit); otherwise 64-feature tiles with K split so that up
+// to one work-group per compute unit runs, each over at least 4 chunks of 64 along K.
+// X is addressed through a buffer resource with 32-bit byte offsets, and a packed weight slab too.
+bool linear_fits(int64_t M, int64_t K) {
+  return M * K * 2 <= INT32_MAX && cdiv(K, 16) * 1024 <= INT32_MAX;
+}
+
 void choose_tiling(int M, int N, int K, tt::LinearParams *p) {
-  p->wide = cdiv(N, 256) * cdiv(M, 128) >= 2 * kTargetWorkgroups ? 1 : 0;
+  const int64_t mt = cdiv(M, 128);
+  p->wide = cdiv(N, 256) * mt >= kTargetWorkgroups ? 1 : 0;
   if (p->wide) {
     p->ksplit = 1;
     return;
   }
-  const int64_t tiles = cdiv(N, 64) * cdiv(M, 128);
-  int64_t ks = cdiv(kTargetWorkgroups, tiles);
-  ks = std::min<int64_t>(ks, std::max<int64_t>(1, K / 1024));
+  const int64_t tiles = cdiv(N, 64) * mt;
+  int64_t ks = kTargetWorkgroups / tiles;
+  ks = std::min<int64_t>(ks, std::max<int64_t>(1, cdiv(K, 64) / 4));
   p->ksplit = (int)std::max<int64_t>(1, ks);
 }
 
@@ -220,6 +226,7 @@ tt_status plan_qkv(const tt_qkv_args *a, bool check_pointers, tt::LinearParams *
         !aligned(a->v_blk, 2))
       return TT_EINVAL;
   }
+  if (!linear_fits((int64_t)a->batch * a->S, a->hidden)) return TT_ENOTSUP;
   *p = tt::LinearParams{};
   p->x = a->h;
   p->w = a->w_qkv;
@@ -247,6 +254,7 @@ tt_status plan_out(const tt_out_proj_args *a, bool check_pointers, tt::LinearPar
     if (!aligned(a->o, 16) || !aligned(a->w_o, 16) || !aligned(a->h_in, 8) || !aligned(a->h_out, 8))
       return TT_EINVAL;
   }
+  if (!linear_fits(a->rows, a->in_features)) return TT_ENOTSUP;
   *p = tt::LinearParams{};
   p->x = a->o;
   p->w = a->w_o;
@@ -268,6 +276,7 @@ tt_status plan_lm(const tt_lm_head_args *a, bool check_pointers, tt::LinearParam
     if (!a->h || !a->w_lm || !a->logits) return TT_EINVAL;
     if (!aligned(a->h, 16) || !aligned(a->w_lm, 16) || !aligned(a->logits, 16)) return TT_EINVAL;
   }
+  if (!linear_fits(a->rows, a->hidden)) return TT_ENOTSUP;
   *p = tt::LinearParams{};
   p->x = a->h;
   p->w = a->w_lm;
@@ -286,6 +295,22 @@ tt_status hip_status(hipError_t e) { return e == hipSuccess ? TT_OK : TT_EHIP; }
 }  // namespace
 
 extern "C" {
+
+size_t twotower_packed_weight_bytes(int32_t out_features, int32_t in_features) {
+  if (out_features < 1 || in_features < 1) return 0;
+  return (size_t)cdiv(out_features, 32) * (size_t)cdiv(in_features, 16) * 1024;
+}
+
+tt_status twotower_pack_weight(const void *w, int32_t out_features, int32_t in_features,
+                               void *packed, void *stream) {
+  if (out_features < 1 || in_features < 1) return TT_EINVAL;
+  if (in_features % 8 != 0) return TT_ENOTSUP;
+  // one packed 32-feature slab is addressed with 32-bit byte offsets
+  if ((int64_t)cdiv(in_features, 16) * 1024 > INT32_MAX) return TT_ENOTSUP;
+  if (!w || !packed || !aligned(w, 16) || !aligned(packed, 16)) return TT_EINVAL;
+  return hip_status(
+      tt::launch_pack_weight(w, out_features, in_features, packed, static_cast<hipStream_t>(stream)));
+}
 
 tt_status twotower_block_attn(const tt_block_attn_args *args, void *ws, size_t *ws_bytes,
                               void *stream) {

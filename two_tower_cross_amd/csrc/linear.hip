@@ -1,14 +1,20 @@
 // Skinny bf16 products Y = X W^T (X [M, K] with M = batch * S <= a few hundred rows, W [N, K])
 // for the synthetic denoiser's projections and lm-head, on gfx950.
 //
-// The weights dominate the bytes (M = 128 against N, K in the thousands), so the kernel streams W
-// once: a work-group owns 64 or 256 output features and up to 128 rows and walks K in chunks of
-// 64.
-// W and X chunks go straight from global memory into a 3-stage LDS ring (direct-to-LDS loads,
-// 16-byte chunks XOR-swizzled per 128-byte row, two chunks in flight, explicit vmcnt waits), and
-// Y^T = W X^T is computed with 32x32x16 bf16 MFMA in fp32. When N alone gives too few
-// work-groups to fill the GPU, K is also partitioned (fp32 partials + one reduce pass, fixed
-// summation order, no atomics).
+// The weights dominate the bytes (M = 128 against N, K in the thousands) and are read once per
+// product, so they are stored pre-packed in the A-operand order of v_mfma_f32_32x32x16_bf16: a
+// 32-feature x 16-column block is 1 KB, lane-contiguous, and the blocks of one 32-feature slab
+// follow each other along K. A work-group owns NB such slabs (64 or 256 features) and all rows of
+// an M tile, and walks its K range in chunks of 64 columns:
+//   * W chunks (NB x 4 KB of contiguous runs) stream into a deep LDS ring with non-temporal
+//     direct-to-LDS loads (several chunks in flight: a compute unit keeps ~56-64 KB of weights in
+//     flight, enough to cover the memory latency at full bandwidth);
+//   * X chunks (128 rows x 64 columns, re-read by every work-group, so served by L2) go through a
+//     second ring, 16-byte chunks XOR-swizzled per 128-byte row, deep enough to cover the L2
+//     latency under load;
+//   * Y^T = W X^T with 32x32x16 bf16 MFMA in fp32; the W operand reads are lane-contiguous.
+// When N alone gives too few work-groups to fill the GPU, K is also partitioned (fp32 partials +
+// one reduce pass, fixed summation order, no atomics).
 // Epilogues: fp32 store (logits), Q/K/V scatter into the attention layouts (bf16), and residual
 // add (bf16).
 #include "common.hpp"
@@ -17,28 +23,74 @@
 namespace tt {
 
 constexpr int kLM = 128;         // rows per work-group
-constexpr int kLK = 64;          // K per chunk (128-byte LDS rows)
-constexpr int kLStages = 3;      // LDS ring depth (two chunks in flight)
+constexpr int kLK = 64;          // K columns per chunk
+// Weights are streamed once per product: non-temporal loads (about 20% more read bandwidth than
+// the default cache policy for a streaming read on gfx950). X stays cached: every work-group
+// reads it.
+constexpr int kNonTemporal = 2;
 
-// Two tile shapes. NARROW: 64 output features, 4 waves = 2 feature blocks x 2 row halves, 72 KB
-// of LDS (two work-groups per compute unit) -- for the small projections, with K partitioned
-// across work-groups. WIDE: 256 output features, 8 waves of 32 features x all 128 rows, 144 KB of
-// LDS -- for the lm-head, so that each X chunk read through L2 serves 4x more weights.
+// Two tile shapes. NB = 2: 64 output features, 4 waves = 2 slabs x 2 row halves, an 8-deep W ring
+// (64 KB) and a 6-deep X ring (96 KB) -- for the projections, with K partitioned across
+// work-groups. NB = 8: 256 output features, 8 waves of one slab x all 128 rows, 3-deep rings
+// (96 + 48 KB) -- for the lm-head, where each X chunk read through L2 then serves 4x more weights.
 template <int NB>
 struct LTile {
   static constexpr int N = NB * 32;                       // features per work-group
   static constexpr int WAVES = NB == 2 ? 4 : NB;
   static constexpr int THREADS = WAVES * 64;
   static constexpr int MB = NB == 2 ? 2 : 4;              // 32-row blocks per wave
-  static constexpr int WBYTES = N * kLK * 2;
-  static constexpr int XBYTES = kLM * kLK * 2;
-  static constexpr int STAGE = WBYTES + XBYTES;
-  static constexpr int WLOADS = WBYTES / 1024 / WAVES;    // DMA instructions per wave per chunk
+  static constexpr int WST = NB == 2 ? 8 : 3;             // W ring depth
+  static constexpr int XST = NB == 2 ? 6 : 3;             // X ring depth (<= WST)
+  static constexpr int WBYTES = NB * 4096;                // one W chunk
+  static constexpr int XBYTES = kLM * kLK * 2;            // one X chunk
+  static constexpr int XBASE = WST * WBYTES;
+  static constexpr int WLOADS = NB * 4 / WAVES;           // DMA instructions per wave per chunk
   static constexpr int XLOADS = XBYTES / 1024 / WAVES;
-  static constexpr int LOADS = WLOADS + XLOADS;
-  static constexpr int LDS = kLStages * STAGE;
+  static constexpr int LDS = XBASE + XST * XBYTES;
+  // DMA instructions issued after X(i) once X(i) is due (see linear_kernel)
+  static constexpr int AFTER = (XST - 2) * (WLOADS + XLOADS);
 };
 
+// ----------------------------------------------------------------------------- weight packing
+// P[((nb * Ks + s) * 64 + lane) * 8 + e] = W[nb * 32 + lane % 32][s * 16 + (lane / 32) * 8 + e],
+// zero outside W; Ks = ceil(K / 16), nb < ceil(N / 32). One thread per 16-byte unit.
+__global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t *w, int N, int K,
+                                                          uint16_t *out, int64_t units) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= units) return;
+  const int Ks = (K + 15) / 16;
+  const int lane = (int)(u % 64);
+  const int64_t blk = u / 64;
+  const int s = (int)(blk % Ks);
+  const int nb = (int)(blk / Ks);
+  const int n = nb * 32 + lane % 32;
+  const int k0 = s * 16 + (lane / 32) * 8;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (n < N) {
+    const uint16_t *row = w + (size_t)n * K;
+    if (k0 + 8 <= K) {
+      v = ld_global_16(row + k0);  // K % 8 == 0: 16-byte aligned
+    } else {
+      uint16_t e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = k0 + i < K ? row[k0 + i] : (uint16_t)0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = (uint32_t)e[2 * i] | ((uint32_t)e[2 * i + 1] << 16);
+    }
+  }
+  *reinterpret_cast<u32x4 *>(out + (size_t)u * 8) = v;
+}
+
+hipError_t launch_pack_weight(const void *w, int N, int K, void *out, hipStream_t stream) {
+  const int64_t units = (int64_t)((N + 31) / 32) * ((K + 15) / 16) * 64;
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_weight_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0,
+                     stream, static_cast<const uint16_t *>(w), N, K, static_cast<uint16_t *>(out),
+                     units);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------- epilogues
 __device__ __forceinline__ void epilogue4(const LinearParams &p, int m, int n, f32x4 v) {
   if (p.epi == EPI_F32) {
     *reinterpret_cast<f32x4 *>(p.y + (size_t)m * p.ldy + n) = v;
@@ -75,48 +127,54 @@ __device__ __forceinline__ void epilogue4(const LinearParams &p, int m, int n, f
   }
 }
 
-// Chunk of 64 K-columns of W rows n0.. and X rows m0.. -> LDS stage (direct-to-LDS, 16 B per
-// lane). Rows past N or M read a valid row instead (their results are never stored); the K range
-// [k, k + 64) must lie inside the row.
+// ------------------------------------------------------------------------------------ loads
+// Buffer resource over one packed 32-feature slab (Ks KB); loads past it return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void *w, int nb, int Ks) {
+  const char *base = static_cast<const char *>(w) + (size_t)nb * Ks * 1024;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, Ks * 1024,
+                                           0x00020000);
+}
+
+// W chunk c (K columns 64c .. 64c + 63) of this work-group's NB slabs -> W stage (block-major:
+// slab j at j * 4 KB, 16-column step i at i * 1 KB; a straight copy of the packed bytes).
 template <int NB>
-__device__ __forceinline__ void linear_dma(char *stage, const LinearParams &p, int n0, int m0,
-                                           int k, int wave, int lane) {
+__device__ __forceinline__ void w_dma(char *stage, const __amdgpu_buffer_rsrc_t *rs, int c,
+                                      int wave, int lane) {
   using T = LTile<NB>;
-  const uint16_t *w = static_cast<const uint16_t *>(p.w);
-  const uint16_t *x = static_cast<const uint16_t *>(p.x);
 #pragma unroll
   for (int j = 0; j < T::WLOADS; ++j) {
-    const int seg = j * T::WAVES + wave, f = seg * 64 + lane;
-    const int r = f / 8, c = (f % 8) ^ key128(f / 8);
-    const int n = min(n0 + r, p.N - 1);
-    __builtin_amdgcn_global_load_lds(w + (size_t)n * p.K + k + c * 8, TT_LDS_PTR(stage + seg * 1024), 16, 0, 0);
+    const int t = j * T::WAVES + wave;  // instruction index: slab t / 4, step t % 4
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[t / 4], TT_LDS_PTR(stage + t * 1024), 16,
+                                             lane * 16, c * 4096 + (t % 4) * 1024, 0,
+                                             kNonTemporal);
   }
+}
+
+// X chunk (rows m0 .. m0 + 127, columns k .. k + 63) -> X stage (direct-to-LDS through a buffer
+// resource over X, so that no load leaves the tensor). Rows past M read row M - 1 instead (their
+// results are never stored).
+template <int NB>
+__device__ __forceinline__ void x_dma(char *stage, __amdgpu_buffer_rsrc_t xr, const LinearParams &p,
+                                      int m0, int k, int wave, int lane) {
+  using T = LTile<NB>;
 #pragma unroll
   for (int j = 0; j < T::XLOADS; ++j) {
     const int seg = j * T::WAVES + wave, f = seg * 64 + lane;
     const int r = f / 8, c = (f % 8) ^ key128(f / 8);
     const int m = min(m0 + r, p.M - 1);
-    __builtin_amdgcn_global_load_lds(x + (size_t)m * p.K + k + c * 8,
-                                     TT_LDS_PTR(stage + T::WBYTES + seg * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, TT_LDS_PTR(stage + seg * 1024), 16,
+                                             (m * p.K + k + c * 8) * 2, 0, 0, 0);
   }
 }
 
-// Partial last chunk (k1 - k < 64 columns) through registers, zero past k1.
+// Partial last X chunk (k1 - k < 64 columns) through registers, zero past k1.
 template <int NB>
-__device__ void linear_tail(char *stage, const LinearParams &p, int n0, int m0, int k, int k1,
-                            int tid) {
+__device__ void x_tail(char *stage, const LinearParams &p, int m0, int k, int k1, int tid) {
   using T = LTile<NB>;
-  const uint16_t *w = static_cast<const uint16_t *>(p.w);
   const uint16_t *x = static_cast<const uint16_t *>(p.x);
   const u32x4 z = {0u, 0u, 0u, 0u};
-  constexpr int NW = T::N * 8 / T::THREADS, NX = kLM * 8 / T::THREADS;
-  u32x4 vw[NW], vx[NX];
-#pragma unroll
-  for (int j = 0; j < NW; ++j) {
-    const int f = tid + j * T::THREADS, r = f / 8, c = f % 8;
-    const int n = min(n0 + r, p.N - 1);
-    vw[j] = k + c * 8 < k1 ? ld_global_16(w + (size_t)n * p.K + k + c * 8) : z;
-  }
+  constexpr int NX = kLM * 8 / T::THREADS;
+  u32x4 vx[NX];
 #pragma unroll
   for (int j = 0; j < NX; ++j) {
     const int f = tid + j * T::THREADS, r = f / 8, c = f % 8;
@@ -124,33 +182,27 @@ __device__ void linear_tail(char *stage, const LinearParams &p, int n0, int m0, 
     vx[j] = k + c * 8 < k1 ? ld_global_16(x + (size_t)m * p.K + k + c * 8) : z;
   }
 #pragma unroll
-  for (int j = 0; j < NW; ++j) {
-    const int f = tid + j * T::THREADS, r = f / 8, c = f % 8;
-    st_lds_16(stage + r * 128 + ((c ^ key128(r)) << 4), vw[j]);
-  }
-#pragma unroll
   for (int j = 0; j < NX; ++j) {
     const int f = tid + j * T::THREADS, r = f / 8, c = f % 8;
-    st_lds_16(stage + T::WBYTES + r * 128 + ((c ^ key128(r)) << 4), vx[j]);
+    st_lds_16(stage + r * 128 + ((c ^ key128(r)) << 4), vx[j]);
   }
 }
 
-// Y^T[n][m] += W[n][k] X[m][k] over one LDS chunk: this wave's 32 features x (MB * 32) rows.
+// Y^T[n][m] += W[n][k] X[m][k] over one chunk: this wave's slab (32 features) x (MB * 32) rows.
 template <int NB>
-__device__ __forceinline__ void linear_chunk(const char *stage, f32x16 *acc, int nb, int mrow0,
-                                             int lane) {
+__device__ __forceinline__ void linear_chunk(const char *ws, const char *xs, f32x16 *acc, int slab,
+                                             int mrow0, int lane) {
   using T = LTile<NB>;
   const int col = lane & 31, hh = lane >> 5;
-  const int wr = nb * 32 + col;
   u32x4 a[4], bx[T::MB][4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
+    a[ks] = ld_lds_16(ws + slab * 4096 + ks * 1024 + lane * 16);
     const int ch = ks * 2 + hh;
-    a[ks] = ld_lds_16(stage + wr * 128 + ((ch ^ key128(wr)) << 4));
 #pragma unroll
     for (int mb = 0; mb < T::MB; ++mb) {
       const int xr = mrow0 + mb * 32 + col;
-      bx[mb][ks] = ld_lds_16(stage + T::WBYTES + xr * 128 + ((ch ^ key128(xr)) << 4));
+      bx[mb][ks] = ld_lds_16(xs + xr * 128 + ((ch ^ key128(xr)) << 4));
     }
   }
 #pragma unroll
@@ -159,66 +211,106 @@ __device__ __forceinline__ void linear_chunk(const char *stage, f32x16 *acc, int
     for (int mb = 0; mb < T::MB; ++mb) acc[mb] = mfma32x32x16(a[ks], bx[mb][ks], acc[mb]);
 }
 
+// Grid: (ceil(N / (32 NB)), ceil(M / 128), ksplit); the work-group's K range is chunks
+// [z * cpz, min(nch, (z + 1) * cpz)) of the ceil(K / 64) chunks.
 template <int NB>
-__global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams p, int kc) {
+__global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams p, int cpz) {
   using T = LTile<NB>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  const int n0 = blockIdx.x * T::N;
+  const int nb0 = blockIdx.x * NB;
   const int m0 = blockIdx.y * kLM;
   const int kz = blockIdx.z;
-  const int k0 = kz * kc;
-  const int k1 = min(p.K, k0 + kc);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hh = lane >> 5;
-  const int nb = NB == 2 ? (wave & 1) : wave;
+  const int slab = NB == 2 ? (wave & 1) : wave;
   const int mrow0 = NB == 2 ? (wave >> 1) * 64 : 0;
+
+  const int nch = (p.K + kLK - 1) / kLK;
+  const int Ks = (p.K + 15) / 16;
+  const int c0 = kz * cpz;
+  const int n = max(0, min(nch, c0 + cpz) - c0);   // chunks of this work-group
+  const bool tail = p.K % kLK != 0 && c0 + n == nch;  // its last chunk is partial
+  const int n_dma_x = tail ? n - 1 : n;            // chunks whose X comes by DMA
+
+  __amdgpu_buffer_rsrc_t rs[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) rs[j] = slab_rsrc(p.w, nb0 + j, Ks);
 
   f32x16 acc[T::MB];
 #pragma unroll
   for (int mb = 0; mb < T::MB; ++mb) acc[mb] = f32x16{};
-  const int nk = k1 > k0 ? k1 - k0 : 0;
-  const int n_full = nk / kLK;
-  const bool tail = nk % kLK != 0;
 
+  char *wring = smem;
+  char *xring = smem + T::XBASE;
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void *>(p.x), (short)0, p.M * p.K * 2, 0x00020000);
+  // Every step issues the same DMA: W(c) (c = step + WST - 1) and X(c') (c' = step + XST - 1).
+  // Chunks past the end are still loaded ("phantom" loads of the last W chunk and of a harmless X
+  // range) into the stage they would occupy, which nobody reads again; so the number of DMA
+  // instructions issued after X(i) when chunk i is due is always T::AFTER and one vmcnt immediate
+  // serves every step. W(i) is issued before X(i) (WST >= XST), so the wait covers both.
+  auto w_issue = [&](int c) {
+    w_dma<NB>(wring + (c % T::WST) * T::WBYTES, rs, c0 + min(c, n - 1), wave, lane);
+  };
+  auto x_issue = [&](int c) {
+    x_dma<NB>(xring + (c % T::XST) * T::XBYTES, xr, p, m0, c < n_dma_x ? (c0 + c) * kLK : 0, wave,
+              lane);
+  };
+  if (n > 0) {
+    // Prologue: W(0 .. WST-XST), then the pairs W(WST-XST+1+j), X(j) for j < XST-1.
 #pragma unroll
-  for (int i = 0; i < kLStages - 1; ++i)
-    if (i < n_full) linear_dma<NB>(smem + i * T::STAGE, p, n0, m0, k0 + i * kLK, wave, lane);
-  for (int c = 0; c < n_full; ++c) {
-    if (c + 1 < n_full) __builtin_amdgcn_s_waitcnt(waitcnt_vm(T::LOADS));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    lds_barrier();  // chunk c is in LDS for every wave; the stage of chunk c - 1 is free
-    const int cn = c + kLStages - 1;
-    if (cn < n_full)
-      linear_dma<NB>(smem + (cn % kLStages) * T::STAGE, p, n0, m0, k0 + cn * kLK, wave, lane);
-    linear_chunk<NB>(smem + (c % kLStages) * T::STAGE, acc, nb, mrow0, lane);
+    for (int c = 0; c <= T::WST - T::XST; ++c) w_issue(c);
+#pragma unroll
+    for (int j = 0; j < T::XST - 1; ++j) {
+      w_issue(T::WST - T::XST + 1 + j);
+      x_issue(j);
+    }
   }
-  if (tail) {
-    lds_barrier();
-    char *st = smem + (n_full % kLStages) * T::STAGE;
-    linear_tail<NB>(st, p, n0, m0, k0 + n_full * kLK, k1, tid);
-    lds_barrier();
-    linear_chunk<NB>(st, acc, nb, mrow0, lane);
+  for (int i = 0; i < n; ++i) {
+    if (i < n_dma_x) __builtin_amdgcn_s_waitcnt(waitcnt_vm(T::AFTER));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    lds_barrier();  // chunk i is in LDS for every wave; the stages of chunk i - 1 are free
+    w_issue(i + T::WST - 1);
+    x_issue(i + T::XST - 1);
+    char *xs = xring + (i % T::XST) * T::XBYTES;
+    if (i >= n_dma_x) {  // the partial last chunk: X through registers, zero past K
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no DMA into this stage is still in flight
+      x_tail<NB>(xs, p, m0, (c0 + i) * kLK, p.K, tid);
+      lds_barrier();
+    }
+    linear_chunk<NB>(wring + (i % T::WST) * T::WBYTES, xs, acc, slab, mrow0, lane);
   }
 
+  // Epilogue: the fp32 tile [128 rows][32 NB features] goes through LDS (16-byte chunks of row r
+  // XOR-swizzled by r, so that the 32 rows one store touches fall in distinct banks), then every
+  // thread handles 4 consecutive features of one row, consecutive threads along the row: the global
+  // stores cover whole rows instead of 32-byte pieces of 32 rows.
+  constexpr int NCH = T::N / 4;  // 16-byte chunks per tile row
+  lds_barrier();                 // every wave is done with the rings
+  float *tile = reinterpret_cast<float *>(smem);
 #pragma unroll
   for (int mb = 0; mb < T::MB; ++mb) {
-    const int m = m0 + mrow0 + mb * 32 + col;
-    if (m >= p.M) continue;
+    const int r = mrow0 + mb * 32 + col;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const int n = n0 + nb * 32 + q4 * 8 + hh * 4;
-      if (n >= p.N) continue;
-      f32x4 v;
-      v[0] = acc[mb][q4 * 4 + 0];
-      v[1] = acc[mb][q4 * 4 + 1];
-      v[2] = acc[mb][q4 * 4 + 2];
-      v[3] = acc[mb][q4 * 4 + 3];
-      if (p.ksplit > 1)
-        *reinterpret_cast<f32x4 *>(p.part + ((size_t)kz * p.M + m) * p.N + n) = v;
-      else
-        epilogue4(p, m, n, v);
+      const int ch = (slab * 32 + q4 * 8 + hh * 4) / 4;
+      const f32x4 v = {acc[mb][q4 * 4 + 0], acc[mb][q4 * 4 + 1], acc[mb][q4 * 4 + 2],
+                       acc[mb][q4 * 4 + 3]};
+      *reinterpret_cast<f32x4 *>(tile + r * T::N + ((ch ^ (r & (NCH - 1))) << 2)) = v;
     }
+  }
+  lds_barrier();
+  const int n0 = nb0 * 32;
+  for (int u = tid; u < kLM * NCH; u += T::THREADS) {
+    const int r = u / NCH, c = u % NCH;
+    const int m = m0 + r, nn = n0 + c * 4;
+    if (m >= p.M || nn >= p.N) continue;
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(tile + r * T::N + ((c ^ (r & (NCH - 1))) << 2));
+    if (p.ksplit > 1)
+      *reinterpret_cast<f32x4 *>(p.part + ((size_t)kz * p.M + m) * p.N + nn) = v;
+    else
+      epilogue4(p, m, nn, v);
   }
 }
 
@@ -235,20 +327,21 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(LinearParams p) {
 }
 
 template <int NB>
-static hipError_t launch_tile(const LinearParams &p, hipStream_t stream, int kc) {
+static hipError_t launch_tile(const LinearParams &p, hipStream_t stream, int cpz) {
   using T = LTile<NB>;
   dim3 grid((p.N + T::N - 1) / T::N, (p.M + kLM - 1) / kLM, p.ksplit);
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(&linear_kernel<NB>),
       hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(linear_kernel<NB>, grid, dim3(T::THREADS), T::LDS, stream, p, kc);
+  hipLaunchKernelGGL(linear_kernel<NB>, grid, dim3(T::THREADS), T::LDS, stream, p, cpz);
   return hipGetLastError();
 }
 
 hipError_t launch_linear(const LinearParams &p, hipStream_t stream) {
-  const int kc = ((p.K + p.ksplit - 1) / p.ksplit + kLK - 1) / kLK * kLK;
-  hipError_t e = p.wide ? launch_tile<8>(p, stream, kc) : launch_tile<2>(p, stream, kc);
+  const int nch = (p.K + kLK - 1) / kLK;
+  const int cpz = (nch + p.ksplit - 1) / p.ksplit;
+  hipError_t e = p.wide ? launch_tile<8>(p, stream, cpz) : launch_tile<2>(p, stream, cpz);
   if (e != hipSuccess || p.ksplit == 1) return e;
   const size_t total = (size_t)p.M * (p.N / 4);
   hipLaunchKernelGGL(linear_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
