@@ -28,6 +28,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 THRESHOLD = 0.9
+ATTN_SOURCE = os.path.join(ROOT, "two_tower_cross_amd", "csrc", "block_attn.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "block_attn_bf16_128_loop32k_traffic.md")
 
 
 def attn_bytes_per_launch(B, L, S, Hq, Hkv, D, e=2):
@@ -70,6 +72,16 @@ def cpu_baseline(m, threads_note, steps=2):
                       f"{dt:.2f} s for {n_tok} committed tokens"}
 
 
+def measured_traffic():
+    """HBM bytes per launch of the attention kernel from the committed counter summary, or None
+    when there is none or the kernel source changed since the counters were taken."""
+    try:
+        from two_tower_cross_amd import traffic
+        return traffic.bytes_per_launch(TRAFFIC_SUMMARY, ATTN_SOURCE)
+    except Exception:
+        return None
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -89,6 +101,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true",
                     help="do not record per-launch attention events")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed region, copy MIB MiB device to device once (the plain "
+                         "copy of known size that scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is "
@@ -156,9 +171,19 @@ def main():
         nbytes = attn_bytes_per_launch(m.B, m.L, m.S, m.Hq, m.Hkv, m.D)
         achieved = nbytes / (attn_us * 1e-6) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "traffic": measured_traffic(),
                     "kernel": "block_attn_bf16_kernel<128>", "launch_us": round(attn_us, 2),
                     "bytes_per_launch": nbytes}
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
