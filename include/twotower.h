@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define TWOTOWER_ABI_VERSION 2
+#define TWOTOWER_ABI_VERSION 3
 
 typedef enum {
   TT_OK = 0,
@@ -194,11 +194,33 @@ typedef struct {
 } tt_lm_head_args;
 
 /*
+ * lm-head fused with the unmasking (twotower_lm_head_unmask). The operation is the one of the
+ * two calls it replaces (explainer, "Training und Konditionierung", sampling paragraph: all masked
+ * positions are predicted at once and the confident ones committed): the same results as
+ * twotower_lm_head followed by twotower_unmask on its logits, without the logits round trip
+ * through memory. Every 256-logit tile of a row is reduced to (max, first argmax, sum of
+ * exp(logit - max)) inside the product and the unmasking merges those partials, so the
+ * confidences agree with the two-call path up to fp32 rounding of the sum (its order differs) and
+ * the committed tokens are the same wherever no confidence ties with the threshold or with
+ * another position within that rounding.
+ *   lm:     rows must equal unmask.batch * unmask.S. lm.logits may be NULL: the logits are then
+ *           not stored and lm.ld is ignored; otherwise they are stored as by twotower_lm_head.
+ *   unmask: masked, tokens, confidence, n_committed, threshold, min_commit, commit_all as for
+ *           twotower_unmask; its vocab, ld and logits fields are ignored (taken from lm).
+ * Rows with masked == 0 still go through the product (their tiles share the weight stream) but
+ * produce no partials and are not touched by the unmasking.
+ */
+typedef struct {
+  tt_lm_head_args lm;
+  tt_unmask_args unmask;
+} tt_lm_head_unmask_args;
+
+/*
  * One denoise step of the synthetic denoiser (twotower_denoise_step): for each layer l,
  * twotower_qkv_projection (rewrites k_blk[l], v_blk[l]) -> twotower_block_attn over
  * (k_pages[l], v_pages[l]) and the block KV of layer l (layer-aligned: denoiser layer l reads the
  * context tower's layer l, gotburnout.io "2. Denoiser Tower") -> twotower_out_projection; then
- * twotower_lm_head -> twotower_unmask. Layer 0 reads h_in; the residual stream is kept in h_work.
+ * twotower_lm_head_unmask. Layer 0 reads h_in; the residual stream is kept in h_work.
  * All layers share batch, S, heads, head_dim, block_table, ctx_lens and page geometry (taken from
  * `attn`; attn.q/k_pages/v_pages/k_blk/v_blk/out/lse are ignored). The context caches are only
  * read. Sequences with no masked position left still run the dense math (their results are
@@ -223,7 +245,7 @@ typedef struct {
   void *h_work;                 /* bf16 [batch, S, hidden], residual stream after the step */
   void *q;                      /* bf16 [batch, S, Hq, head_dim] scratch */
   void *attn_out;               /* bf16 [batch, S, Hq, head_dim] scratch */
-  float *logits;                /* fp32 [batch, S, logits_ld] */
+  float *logits;                /* fp32 [batch, S, logits_ld], optional (NULL: not stored) */
   int64_t logits_ld;
   tt_unmask_args unmask;        /* masked/tokens/confidence/n_committed/threshold/flags used;
                                    batch/S/vocab/ld/logits are taken from the step */
@@ -238,6 +260,8 @@ tt_status twotower_qkv_projection(const tt_qkv_args *args, void *ws, size_t *ws_
 tt_status twotower_out_projection(const tt_out_proj_args *args, void *ws, size_t *ws_bytes,
                                   void *stream);
 tt_status twotower_lm_head(const tt_lm_head_args *args, void *ws, size_t *ws_bytes, void *stream);
+tt_status twotower_lm_head_unmask(const tt_lm_head_unmask_args *args, void *ws, size_t *ws_bytes,
+                                  void *stream);
 tt_status twotower_denoise_step(const tt_denoise_step_args *args, void *ws, size_t *ws_bytes,
                                 void *stream);
 
@@ -256,7 +280,8 @@ const char *twotower_status_string(int32_t status);
 int32_t twotower_abi_version(void);
 /* sizeof of the argument structs, for bindings to check their mirrors:
  * 0 tt_block_attn_args, 1 tt_unmask_args, 2 tt_qkv_args, 3 tt_out_proj_args,
- * 4 tt_lm_head_args, 5 tt_denoise_step_args; -1 for an unknown index. */
+ * 4 tt_lm_head_args, 5 tt_denoise_step_args, 6 tt_lm_head_unmask_args; -1 for an unknown
+ * index. */
 int64_t twotower_struct_size(int32_t which);
 /* Byte offset of field `field` (0-based declaration order) in struct `which`; -1 if unknown. */
 int64_t twotower_struct_offset(int32_t which, int32_t field);

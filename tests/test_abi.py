@@ -165,6 +165,32 @@ def test_projection_queries_and_errors():
     assert query("twotower_lm_head", lm)[0] == _lib.TT_EINVAL
 
 
+def lm_unmask_args(**over):
+    a = _lib.LmHeadUnmaskArgs()
+    a.lm = _lib.LmHeadArgs(128, 2048, 131072, 0, 131072, FAKE, FAKE, FAKE)
+    a.unmask = unmask_args(logits=None, vocab=0, ld=0)   # ignored by the fused call
+    for k, v in over.items():
+        obj, f = k.split("__")
+        setattr(getattr(a, obj), f, v)
+    return a
+
+
+def test_lm_head_unmask_workspace_and_errors():
+    st, n = query("twotower_lm_head_unmask", lm_unmask_args())
+    # one (max, index, sum) slot of 16 bytes per row and 256-logit tile
+    assert st == _lib.TT_OK and n == 128 * 512 * 16
+    assert query("twotower_lm_head_unmask", lm_unmask_args(lm__logits=None, lm__ld=0))[0] == _lib.TT_OK
+    for over, code in [(dict(lm__rows=127), _lib.TT_EINVAL),          # rows != batch * S
+                       (dict(unmask__S=65, lm__rows=8 * 65), _lib.TT_ENOTSUP),
+                       (dict(lm__ld=131070), _lib.TT_EINVAL),
+                       (dict(lm__vocab=131074, lm__ld=131076), _lib.TT_ENOTSUP),
+                       (dict(lm__h=FAKE + 8), _lib.TT_EINVAL),
+                       (dict(lm__logits=FAKE + 4), _lib.TT_EINVAL),
+                       (dict(unmask__masked=None), _lib.TT_EINVAL),
+                       (dict(unmask__threshold=float("nan")), _lib.TT_EINVAL)]:
+        assert query("twotower_lm_head_unmask", lm_unmask_args(**over))[0] == code, over
+
+
 def test_denoise_step_validation():
     a = _lib.DenoiseStepArgs()
     a.num_layers, a.hidden, a.vocab = 6, 2048, 131072
@@ -180,5 +206,7 @@ def test_denoise_step_validation():
     a.unmask = unmask_args()
     st, n = query("twotower_denoise_step", a)
     assert st == _lib.TT_OK and n > 0
+    a.logits = None   # logits are optional: the unmasking is fused into the lm-head
+    assert query("twotower_denoise_step", a)[0] == _lib.TT_OK
     a.attn = attn_args(dtype=_lib.TT_FP32)
     assert query("twotower_denoise_step", a)[0] == _lib.TT_ENOTSUP

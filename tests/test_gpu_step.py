@@ -114,9 +114,9 @@ def compose_step(m, t, masked, tokens, threshold, min_commit, commit_all):
                           max_ctx_len=m.L, out_dtype=torch.bfloat16)
         outs[l] = (q, kb, vb, o, h)
         h = tt.out_projection(h, o, m.w_o[l])
-    logits = tt.lm_head(h, m.w_lm)
-    conf, n = tt.unmask(logits, masked, tokens, threshold, min_commit=min_commit,
-                        commit_all=commit_all)
+    conf, n, logits = tt.lm_head_unmask(h, m.w_lm, masked, tokens, threshold,
+                                        min_commit=min_commit, commit_all=commit_all,
+                                        keep_logits=True)
     return h, logits, conf, n, outs
 
 
@@ -129,7 +129,7 @@ def make_step(m, **kw):
 
 def test_step_equals_composition_of_stages_bit_for_bit():
     m = small_model()
-    step = make_step(m)
+    step = make_step(m, keep_logits=True)
     masked = torch.ones((m.B, m.S), dtype=torch.uint8, device=DEV)
     tokens = torch.full((m.B, m.S), -1, dtype=torch.int32, device=DEV)
     masked2, tokens2 = masked.clone(), tokens.clone()
@@ -209,7 +209,7 @@ def test_block_loop_invariants_small():
 def test_full_size_loop_32k_one_block():
     """6 layers, batch 8, context 32768, S = T = 16, vocab 131072: the benchmark's workload."""
     m = loop_model(5, device=DEV)
-    step = make_step(m)
+    step = make_step(m, keep_logits=True)
     before = checksum(m.k_pages[:1] + m.v_pages[-1:])
     masked, tokens, per_step, hist = run_block(m, step)
     # near-uniform logits of a random model: exactly one commit per step per sequence

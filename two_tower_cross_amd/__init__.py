@@ -19,7 +19,8 @@ import torch
 from . import _lib
 from ._lib import LibraryNotBuilt, TwoTowerError, TT_BF16, TT_FP32  # noqa: F401
 
-__all__ = ["block_attn", "unmask", "qkv_projection", "out_projection", "lm_head", "DenoiseStep",
+__all__ = ["block_attn", "unmask", "qkv_projection", "out_projection", "lm_head",
+           "lm_head_unmask", "DenoiseStep",
            "PackedWeight", "pack_weight",
            "LibraryNotBuilt", "TwoTowerError", "library_path"]
 
@@ -247,6 +248,39 @@ def lm_head(h, w_lm, out=None):
     return out
 
 
+def lm_head_unmask(h, w_lm, masked, tokens, threshold, *, min_commit=False, commit_all=False,
+                   keep_logits=False):
+    """lm-head fused with the unmasking (the logits need not reach memory).
+
+    ``h`` is bf16 [B,S,hidden]; updates ``masked`` and ``tokens`` in place. Returns
+    (confidence [B,S] fp32, n_committed [B] int32, logits [B,S,V] fp32 or None): the logits are
+    stored only when ``keep_logits``.
+    """
+    dev = h.device
+    _check(h, "h", dev, torch.bfloat16, 3)
+    _check(masked, "masked", dev, torch.uint8, 2)
+    _check(tokens, "tokens", dev, torch.int32, 2)
+    w_lm = _packed(w_lm, "w_lm", dev)
+    vocab, hidden = w_lm.shape
+    B, S, hh = h.shape
+    if hh != hidden or tuple(masked.shape) != (B, S) or tuple(tokens.shape) != (B, S):
+        raise ValueError("lm_head_unmask shape mismatch")
+    logits = (torch.empty((B, S, vocab), dtype=torch.float32, device=dev) if keep_logits
+              else None)
+    conf = torch.full((B, S), float("nan"), dtype=torch.float32, device=dev)
+    ncom = torch.zeros((B,), dtype=torch.int32, device=dev)
+    a = _lib.LmHeadUnmaskArgs()
+    a.lm.rows, a.lm.hidden, a.lm.vocab, a.lm.ld = B * S, hidden, vocab, vocab
+    a.lm.h, a.lm.w_lm, a.lm.logits = _p(h), _p(w_lm.data), _p(logits) if keep_logits else None
+    a.unmask.batch, a.unmask.S = B, S
+    a.unmask.masked, a.unmask.tokens = _p(masked), _p(tokens)
+    a.unmask.confidence, a.unmask.n_committed = _p(conf), _p(ncom)
+    a.unmask.threshold = float(threshold)
+    a.unmask.min_commit, a.unmask.commit_all = int(bool(min_commit)), int(bool(commit_all))
+    _run("twotower_lm_head_unmask", a, dev)
+    return conf, ncom, logits
+
+
 class DenoiseStep:
     """One denoise step of the synthetic attention-only denoiser, reused across steps.
 
@@ -257,7 +291,7 @@ class DenoiseStep:
 
     def __init__(self, *, k_pages, v_pages, w_qkv, w_o, w_lm, block_table, ctx_lens,
                  max_ctx_len, num_q_heads, num_kv_heads, head_dim, batch, S, scale=None,
-                 num_splits=0):
+                 num_splits=0, keep_logits=False):
         dev = w_lm.device
         self.device = dev
         self.L = len(k_pages)
@@ -278,7 +312,9 @@ class DenoiseStep:
         self.q = torch.empty((batch, S, num_q_heads, head_dim), dtype=bf, device=dev)
         self.attn_out = torch.empty_like(self.q)
         self.h_work = torch.empty((batch, S, hidden), dtype=bf, device=dev)
-        self.logits = torch.empty((batch, S, vocab), dtype=torch.float32, device=dev)
+        # the unmasking is fused into the lm-head: the logits are stored only on request
+        self.logits = (torch.empty((batch, S, vocab), dtype=torch.float32, device=dev)
+                       if keep_logits else None)
         self.confidence = torch.full((batch, S), float("nan"), dtype=torch.float32, device=dev)
         self.n_committed = torch.zeros((batch,), dtype=torch.int32, device=dev)
 
@@ -303,7 +339,8 @@ class DenoiseStep:
         vpp = C.POINTER(C.c_void_p)
         a.k_pages, a.v_pages, a.w_qkv, a.w_o, a.k_blk, a.v_blk = [C.cast(x, vpp) for x in self._arrs]
         a.w_lm = _p(w_lm.data)
-        a.h_work, a.q, a.attn_out, a.logits = _p(self.h_work), _p(self.q), _p(self.attn_out), _p(self.logits)
+        a.h_work, a.q, a.attn_out = _p(self.h_work), _p(self.q), _p(self.attn_out)
+        a.logits = _p(self.logits) if keep_logits else None
         a.logits_ld = vocab
         a.unmask.confidence, a.unmask.n_committed = _p(self.confidence), _p(self.n_committed)
         self.args = a

@@ -14,7 +14,7 @@ LIB_PATH = os.environ.get("TWOTOWER_LIB", os.path.join(HERE, "libtwotower.so"))
 
 TT_OK, TT_EINVAL, TT_ENOTSUP, TT_ENOSPACE, TT_EHIP = range(5)
 TT_FP32, TT_BF16 = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 i32, i64, f32, vp = C.c_int32, C.c_int64, C.c_float, C.c_void_p
 
@@ -52,6 +52,10 @@ class LmHeadArgs(C.Structure):
                 ("h", vp), ("w_lm", vp), ("logits", vp)]
 
 
+class LmHeadUnmaskArgs(C.Structure):
+    _fields_ = [("lm", LmHeadArgs), ("unmask", UnmaskArgs)]
+
+
 class DenoiseStepArgs(C.Structure):
     _fields_ = [("num_layers", i32), ("hidden", i32), ("vocab", i32), ("reserved0", i32),
                 ("attn", BlockAttnArgs),
@@ -63,7 +67,8 @@ class DenoiseStepArgs(C.Structure):
                 ("timing_events", C.POINTER(vp))]
 
 
-STRUCTS = [BlockAttnArgs, UnmaskArgs, QkvArgs, OutProjArgs, LmHeadArgs, DenoiseStepArgs]
+STRUCTS = [BlockAttnArgs, UnmaskArgs, QkvArgs, OutProjArgs, LmHeadArgs, DenoiseStepArgs,
+           LmHeadUnmaskArgs]
 
 ENTRY_POINTS = {
     "twotower_block_attn": (BlockAttnArgs,),
@@ -72,6 +77,7 @@ ENTRY_POINTS = {
     "twotower_out_projection": (OutProjArgs,),
     "twotower_lm_head": (LmHeadArgs,),
     "twotower_denoise_step": (DenoiseStepArgs,),
+    "twotower_lm_head_unmask": (LmHeadUnmaskArgs,),
 }
 
 

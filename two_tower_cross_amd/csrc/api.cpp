@@ -290,6 +290,61 @@ tt_status plan_lm(const tt_lm_head_args *a, bool check_pointers, tt::LinearParam
   return TT_OK;
 }
 
+// lm-head fused with the unmasking: 256-feature tiles over all of K (no split), tile triples in
+// the workspace, then the per-sequence decisions.
+struct LmUnmaskPlan {
+  tt::LinearParams lp{};
+  UnmaskPlan up;
+  size_t ws_bytes = 0;
+};
+
+tt_status plan_lm_unmask(const tt_lm_head_unmask_args *a, bool check_pointers, LmUnmaskPlan *out) {
+  if (!a) return TT_EINVAL;
+  const tt_lm_head_args &l = a->lm;
+  if (l.rows < 0 || l.hidden < 1 || l.vocab < 1) return TT_EINVAL;
+  if (l.hidden % 8 != 0 || l.vocab % 4 != 0) return TT_ENOTSUP;
+  if (l.logits && (l.ld < l.vocab || l.ld % 4 != 0)) return l.ld < l.vocab ? TT_EINVAL : TT_ENOTSUP;
+  if (check_pointers) {
+    if (!l.h || !l.w_lm || !aligned(l.h, 16) || !aligned(l.w_lm, 16)) return TT_EINVAL;
+    if (l.logits && !aligned(l.logits, 16)) return TT_EINVAL;
+  }
+  if (!linear_fits(l.rows, l.hidden)) return TT_ENOTSUP;
+  tt_unmask_args ua = a->unmask;
+  ua.vocab = l.vocab;
+  ua.ld = l.vocab;
+  ua.logits = nullptr;
+  tt_status st = plan_unmask(&ua, false, &out->up);
+  if (st != TT_OK) return st;
+  if ((int64_t)ua.batch * ua.S != l.rows) return TT_EINVAL;
+  tt::LinearParams &p = out->lp;
+  p = tt::LinearParams{};
+  p.x = l.h;
+  p.w = l.w_lm;
+  p.M = l.rows;
+  p.N = l.vocab;
+  p.K = l.hidden;
+  p.epi = tt::EPI_UNMASK;
+  p.y = l.logits;
+  p.ldy = l.logits ? l.ld : 0;
+  p.wide = 1;
+  p.ksplit = 1;
+  p.masked = ua.masked;
+  const int tiles = (int)cdiv(l.vocab, 256);
+  out->up.p.chunks = tiles;
+  out->up.p.chunk = 256;
+  out->ws_bytes = align_up((size_t)l.rows * tiles * 4 * sizeof(float));
+  return TT_OK;
+}
+
+hipError_t run_lm_unmask(LmUnmaskPlan &pl, void *ws, hipStream_t stream) {
+  if (pl.lp.M == 0) return hipSuccess;
+  pl.lp.triples = static_cast<float *>(ws);
+  pl.up.p.part = static_cast<float *>(ws);
+  hipError_t e = tt::launch_linear(pl.lp, stream);
+  if (e != hipSuccess) return e;
+  return tt::launch_unmask_tiles_finalize(pl.up.p, stream);
+}
+
 tt_status hip_status(hipError_t e) { return e == hipSuccess ? TT_OK : TT_EHIP; }
 
 }  // namespace
@@ -365,6 +420,17 @@ tt_status twotower_lm_head(const tt_lm_head_args *args, void *ws, size_t *ws_byt
   return hip_status(run_linear(p, ws, static_cast<hipStream_t>(stream)));
 }
 
+tt_status twotower_lm_head_unmask(const tt_lm_head_unmask_args *args, void *ws, size_t *ws_bytes,
+                                  void *stream) {
+  LmUnmaskPlan pl;
+  tt_status st = plan_lm_unmask(args, true, &pl);
+  if (st != TT_OK) return st;
+  bool launch;
+  st = ws_protocol(pl.ws_bytes, ws, ws_bytes, &launch);
+  if (st != TT_OK || !launch) return st;
+  return hip_status(run_lm_unmask(pl, ws, static_cast<hipStream_t>(stream)));
+}
+
 tt_status twotower_denoise_step(const tt_denoise_step_args *a, void *ws, size_t *ws_bytes,
                                 void *stream) {
   if (!a || a->num_layers < 1 || a->hidden < 1 || a->vocab < 1) return TT_EINVAL;
@@ -372,8 +438,7 @@ tt_status twotower_denoise_step(const tt_denoise_step_args *a, void *ws, size_t 
   if (g.dtype != TT_BF16) return TT_ENOTSUP;
   if (!a->k_pages || !a->v_pages || !a->w_qkv || !a->w_o || !a->k_blk || !a->v_blk)
     return TT_EINVAL;
-  if (!a->w_lm || !a->h_in || !a->h_work || !a->q || !a->attn_out || !a->logits) return TT_EINVAL;
-  if (a->logits_ld < a->vocab) return TT_EINVAL;
+  if (!a->w_lm || !a->h_in || !a->h_work || !a->q || !a->attn_out) return TT_EINVAL;
 
   // Plan every stage once (layer 0's pointers; the geometry is shared by all layers).
   tt_block_attn_args ga = g;
@@ -415,25 +480,19 @@ tt_status twotower_denoise_step(const tt_denoise_step_args *a, void *ws, size_t 
   tt::LinearParams op;
   if ((st = plan_out(&oa, true, &op)) != TT_OK) return st;
 
-  tt_lm_head_args la{};
-  la.rows = g.batch * g.S;
-  la.hidden = a->hidden;
-  la.vocab = a->vocab;
-  la.ld = a->logits_ld;
-  la.h = a->h_work;
-  la.w_lm = a->w_lm;
-  la.logits = a->logits;
-  tt::LinearParams lp;
-  if ((st = plan_lm(&la, true, &lp)) != TT_OK) return st;
-
-  tt_unmask_args ua = a->unmask;
-  ua.batch = g.batch;
-  ua.S = g.S;
-  ua.vocab = a->vocab;
-  ua.ld = a->logits_ld;
-  ua.logits = a->logits;
-  UnmaskPlan up;
-  if ((st = plan_unmask(&ua, true, &up)) != TT_OK) return st;
+  tt_lm_head_unmask_args lu{};
+  lu.lm.rows = g.batch * g.S;
+  lu.lm.hidden = a->hidden;
+  lu.lm.vocab = a->vocab;
+  lu.lm.ld = a->logits_ld;
+  lu.lm.h = a->h_work;
+  lu.lm.w_lm = a->w_lm;
+  lu.lm.logits = a->logits;
+  lu.unmask = a->unmask;
+  lu.unmask.batch = g.batch;
+  lu.unmask.S = g.S;
+  LmUnmaskPlan lup;
+  if ((st = plan_lm_unmask(&lu, true, &lup)) != TT_OK) return st;
 
   for (int l = 0; l < a->num_layers; ++l) {
     const void *p16[] = {a->k_pages[l], a->v_pages[l], a->w_qkv[l], a->w_o[l]};
@@ -443,8 +502,7 @@ tt_status twotower_denoise_step(const tt_denoise_step_args *a, void *ws, size_t 
       return TT_EINVAL;
   }
 
-  const size_t need = std::max({ap.ws_bytes, up.ws_bytes, linear_ws(qp), linear_ws(op),
-                                linear_ws(lp)});
+  const size_t need = std::max({ap.ws_bytes, lup.ws_bytes, linear_ws(qp), linear_ws(op)});
   bool launch;
   st = ws_protocol(need, ws, ws_bytes, &launch);
   if (st != TT_OK || !launch) return st;
@@ -474,8 +532,7 @@ tt_status twotower_denoise_step(const tt_denoise_step_args *a, void *ws, size_t 
     op.w = a->w_o[l];
     if ((e = run_linear(op, ws, s)) != hipSuccess) return TT_EHIP;
   }
-  if (run_linear(lp, ws, s) != hipSuccess) return TT_EHIP;
-  if (run_unmask(up, ws, s) != hipSuccess) return TT_EHIP;
+  if (run_lm_unmask(lup, ws, s) != hipSuccess) return TT_EHIP;
   return TT_OK;
 }
 
@@ -500,6 +557,7 @@ int64_t twotower_struct_size(int32_t which) {
     case 3: return sizeof(tt_out_proj_args);
     case 4: return sizeof(tt_lm_head_args);
     case 5: return sizeof(tt_denoise_step_args);
+    case 6: return sizeof(tt_lm_head_unmask_args);
     default: return -1;
   }
 }
@@ -553,6 +611,8 @@ int64_t twotower_struct_offset(int32_t which, int32_t field) {
       TT_OFF(tt_denoise_step_args, q), TT_OFF(tt_denoise_step_args, attn_out),
       TT_OFF(tt_denoise_step_args, logits), TT_OFF(tt_denoise_step_args, logits_ld),
       TT_OFF(tt_denoise_step_args, unmask), TT_OFF(tt_denoise_step_args, timing_events)};
+  static const int64_t lmu[] = {TT_OFF(tt_lm_head_unmask_args, lm),
+                                TT_OFF(tt_lm_head_unmask_args, unmask)};
   const int64_t *tab = nullptr;
   int n = 0;
   switch (which) {
@@ -562,6 +622,7 @@ int64_t twotower_struct_offset(int32_t which, int32_t field) {
     case 3: tab = outp; n = sizeof(outp) / sizeof(outp[0]); break;
     case 4: tab = lm; n = sizeof(lm) / sizeof(lm[0]); break;
     case 5: tab = step; n = sizeof(step) / sizeof(step[0]); break;
+    case 6: tab = lmu; n = sizeof(lmu) / sizeof(lmu[0]); break;
     default: return -1;
   }
   if (field < 0 || field >= n) return -1;

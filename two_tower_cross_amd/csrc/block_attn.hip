@@ -699,53 +699,51 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
 // Exact merge of the partitions of each query row: with lse* = max_p lse_p and
 // w_p = exp(lse_p - lse*), out = sum_p w_p O_p / sum_p w_p and lse = lse* + ln(sum_p w_p).
 // One work-group = 16 query rows of one (b, KV head, row group); 16 threads per row, 8 dims each.
-// The rows' LSEs are staged in LDS first, then every partition's 16-byte partial chunk is
-// requested before any is used, so a batch of 16 partitions costs two memory round trips.
+// Each thread requests its row's LSE and its 16-byte partial chunk of every partition of a batch
+// (up to 16) together with the sequence length, before any of them is used: one memory round trip
+// per batch. Partitions past the sequence's last one are loaded (the workspace holds them) but
+// not used.
 constexpr int kRedBatch = 16;
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnParams p) {
   constexpr int TPR = D / 8;                 // threads per row
   constexpr int RPB = 256 / TPR;             // rows per pass of the block (16 or 32)
-  __shared__ float lse_s[RPB][kRedBatch + 1];
   const int item_bgr = blockIdx.x;
   const int rg = item_bgr % p.row_groups;
   const int g = (item_bgr / p.row_groups) % p.Hkv;
   const int b = item_bgr / (p.row_groups * p.Hkv);
   const int tid = threadIdx.x;
-  const int L = p.ctx_lens[b];
-  const bool bad = L < 0 || L > p.max_ctx_len;
-  int nact = bad || L == 0 ? 1 : (L + p.chunk - 1) / p.chunk;
-  nact = min(nact, p.splits);
   const size_t item0 = (size_t)item_bgr * p.splits;
   const uint16_t *part = static_cast<const uint16_t *>(p.part_o);
   const int rr = tid / TPR, d8 = tid % TPR;
   const int r_local = blockIdx.y * RPB + rr;
   const bool live = r_local < p.rows_per_group && rg * p.rows_per_group + r_local < p.rows;
+  if (!live) return;
 
   float mx = -INFINITY, wsum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < nact; s0 += kRedBatch) {
-    const int ns = min(kRedBatch, nact - s0);
-    __syncthreads();
-    for (int i = tid; i < RPB * kRedBatch; i += 256) {
-      const int row = i / kRedBatch, sp = i % kRedBatch;
-      const int rl = blockIdx.y * RPB + row;
-      lse_s[row][sp] = (sp < ns && rl < p.rows_per_group)
-                           ? p.part_lse[(item0 + s0 + sp) * p.rows_per_group + rl]
-                           : -INFINITY;
-    }
-    __syncthreads();
-    if (!live) continue;
+  bool bad = false;
+  for (int s0 = 0; s0 < p.splits; s0 += kRedBatch) {
+    const int nb = min(kRedBatch, p.splits - s0);
+    float ls[kRedBatch];
     u32x4 v[kRedBatch];
 #pragma unroll
-    for (int sp = 0; sp < kRedBatch; ++sp)
-      if (sp < ns)
-        v[sp] = ld_global_16(part + ((item0 + s0 + sp) * p.rows_per_group + r_local) * D + d8 * 8);
+    for (int sp = 0; sp < kRedBatch; ++sp) {  // unconditional loads (clamped), no branches
+      const size_t it = (item0 + s0 + min(sp, nb - 1)) * p.rows_per_group + r_local;
+      ls[sp] = p.part_lse[it];
+      v[sp] = ld_global_16(part + it * D + d8 * 8);
+    }
+    asm volatile("" ::: "memory");  // keeps the length load behind the batch's loads
+    const int L = p.ctx_lens[b];    // so that one round trip serves all of them
+    bad = L < 0 || L > p.max_ctx_len;
+    const int nact = min(bad || L == 0 ? 1 : (L + p.chunk - 1) / p.chunk, p.splits);
+    if (s0 >= nact) break;
+    const int ns = min(nb, nact - s0);
     float bmx = mx;
 #pragma unroll
     for (int sp = 0; sp < kRedBatch; ++sp)
-      if (sp < ns) bmx = fmaxf(bmx, lse_s[rr][sp]);
+      if (sp < ns) bmx = fmaxf(bmx, ls[sp]);
     const float rescale = __expf(mx - bmx);   // 0 for the first batch (mx = -inf)
     wsum *= rescale;
 #pragma unroll
@@ -754,7 +752,7 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnParams p) {
 #pragma unroll
     for (int sp = 0; sp < kRedBatch; ++sp) {
       if (sp < ns) {
-        const float w = __expf(lse_s[rr][sp] - mx);
+        const float w = __expf(ls[sp] - mx);
         wsum += w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -764,7 +762,6 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnParams p) {
       }
     }
   }
-  if (!live) return;
   const float inv = bad ? NAN : 1.0f / wsum;
   const int r = rg * p.rows_per_group + r_local;
   const int jq = r / p.S, iq = r % p.S, h = g * p.G + jq;

@@ -47,12 +47,16 @@ struct UnmaskParams {
 };
 
 hipError_t launch_unmask(const UnmaskParams &p, hipStream_t stream);
+// Decisions from per-row tile triples already in p.part ([B*S, chunks, 4]), e.g. written by the
+// EPI_UNMASK linear epilogue.
+hipError_t launch_unmask_tiles_finalize(const UnmaskParams &p, hipStream_t stream);
 
 // ------------------------------------------------------------------------ skinny bf16 linear
 enum Epilogue : int {
   EPI_F32 = 0,       // y fp32 [M, ldy]
   EPI_QKV = 1,       // scatter to q [B,S,Hq,D], k_blk [B,Hkv,S,D], v_blk [B,Hkv,D,S] (bf16)
   EPI_RESIDUAL = 2,  // y bf16 [M, N] = residual bf16 [M, N] + x w^T
+  EPI_UNMASK = 3,    // per (row, 256-feature tile) triples for the unmasking; y fp32 optional
 };
 
 struct LinearParams {
@@ -72,6 +76,11 @@ struct LinearParams {
   // EPI_RESIDUAL
   const void *residual;
   void *y_bf16;
+  // EPI_UNMASK (256-feature tiles, K not split): rows with masked[m] != 0 get, for every tile t,
+  // (max, first argmax, sum of exp(y - max)) of y[m, 256 t .. 256 t + 255] at
+  // triples[(m * ceil(N / 256) + t) * 4 + 0..2]; y (fp32 [M, ldy]) is also stored when not null.
+  const uint8_t *masked;
+  float *triples;
 };
 
 hipError_t launch_linear(const LinearParams &p, hipStream_t stream);

@@ -17,8 +17,11 @@
 // one reduce pass, fixed summation order, no atomics).
 // Epilogues: fp32 store (logits), Q/K/V scatter into the attention layouts (bf16), and residual
 // add (bf16).
+#include <math.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
+#include "triple.hpp"
 
 namespace tt {
 
@@ -91,12 +94,18 @@ hipError_t launch_pack_weight(const void *w, int N, int K, void *out, hipStream_
 }
 
 // ---------------------------------------------------------------------------------- epilogues
-__device__ __forceinline__ void epilogue4(const LinearParams &p, int m, int n, f32x4 v) {
+__device__ __forceinline__ uint2 load_residual4(const LinearParams &p, int m, int n) {
+  return *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.residual) +
+                                          (size_t)m * p.N + n);
+}
+
+// rr: the residual's 4 bf16 at (m, n) when already loaded (EPI_RESIDUAL), else ignored.
+__device__ __forceinline__ void epilogue4(const LinearParams &p, int m, int n, f32x4 v,
+                                          const uint2 *rr_pre = nullptr) {
   if (p.epi == EPI_F32) {
     *reinterpret_cast<f32x4 *>(p.y + (size_t)m * p.ldy + n) = v;
   } else if (p.epi == EPI_RESIDUAL) {
-    const uint16_t *res = static_cast<const uint16_t *>(p.residual) + (size_t)m * p.N + n;
-    const uint2 rr = *reinterpret_cast<const uint2 *>(res);
+    const uint2 rr = rr_pre ? *rr_pre : load_residual4(p, m, n);
     const float r0 = __uint_as_float(rr.x << 16), r1 = __uint_as_float(rr.x & 0xFFFF0000u);
     const float r2 = __uint_as_float(rr.y << 16), r3 = __uint_as_float(rr.y & 0xFFFF0000u);
     uint2 o;
@@ -211,6 +220,66 @@ __device__ __forceinline__ void linear_chunk(const char *ws, const char *xs, f32
     for (int mb = 0; mb < T::MB; ++mb) acc[mb] = mfma32x32x16(a[ks], bx[mb][ks], acc[mb]);
 }
 
+// Fused lm-head epilogue feeding the unmasking: the fp32 tile [128 rows][256 features] is in LDS
+// (16-byte chunk c of row r at chunk slot c ^ (r & 63)). Optionally stores it as logits; then
+// four threads per row each take 64 consecutive features in increasing order (first maximum by a
+// strict '>', then the sum of exp(y - max)), merge their triples with two lane exchanges, and the
+// first writes the row's triple for this tile. Rows committed already (masked == 0) write nothing.
+template <int NB>
+__device__ void unmask_epilogue(const LinearParams &p, const float *tile, int m0, int n0, int tid) {
+  using T = LTile<NB>;
+  static_assert(T::THREADS == 4 * kLM, "four threads per row");
+  constexpr int NCH = T::N / 4;
+  if (p.y) {
+    for (int u = tid; u < kLM * NCH; u += T::THREADS) {
+      const int r = u / NCH, c = u % NCH;
+      const int m = m0 + r, nn = n0 + c * 4;
+      if (m >= p.M || nn >= p.N) continue;
+      *reinterpret_cast<f32x4 *>(p.y + (size_t)m * p.ldy + nn) =
+          *reinterpret_cast<const f32x4 *>(tile + r * T::N + ((c ^ (r & (NCH - 1))) << 2));
+    }
+  }
+  const int r = tid >> 2, q = tid & 3;
+  const int m = m0 + r;
+  const bool live = m < p.M && p.masked[m] != 0;
+  Triple t = empty_triple();
+  if (live) {
+    f32x4 v[NCH / 4];
+#pragma unroll
+    for (int j = 0; j < NCH / 4; ++j) {
+      const int c = q * (NCH / 4) + j;
+      v[j] = *reinterpret_cast<const f32x4 *>(tile + r * T::N + ((c ^ (r & (NCH - 1))) << 2));
+    }
+#pragma unroll
+    for (int j = 0; j < NCH / 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int n = n0 + (q * (NCH / 4) + j) * 4 + e;
+        if (n < p.N && v[j][e] > t.m) {
+          t.m = v[j][e];
+          t.idx = n;
+        }
+      }
+    float z = 0.f;
+    if (t.m > -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < NCH / 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n0 + (q * (NCH / 4) + j) * 4 + e < p.N) z += __expf(v[j][e] - t.m);
+    }
+    t.z = z;
+  }
+  t = merge(t, shfl_xor_triple(t, 1));
+  t = merge(t, shfl_xor_triple(t, 2));
+  if (q == 0 && live) {
+    float *o = p.triples + ((size_t)m * ((p.N + T::N - 1) / T::N) + blockIdx.x) * 4;
+    o[0] = t.m;
+    o[1] = __int_as_float(t.idx);
+    o[2] = t.z;
+  }
+}
+
 // Grid: (ceil(N / (32 NB)), ceil(M / 128), ksplit); the work-group's K range is chunks
 // [z * cpz, min(nch, (z + 1) * cpz)) of the ceil(K / 64) chunks.
 template <int NB>
@@ -287,6 +356,9 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
   // thread handles 4 consecutive features of one row, consecutive threads along the row: the global
   // stores cover whole rows instead of 32-byte pieces of 32 rows.
   constexpr int NCH = T::N / 4;  // 16-byte chunks per tile row
+  // The last steps issued phantom loads into the rings; they must land before the rings are
+  // reused for the output tile.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   lds_barrier();                 // every wave is done with the rings
   float *tile = reinterpret_cast<float *>(smem);
 #pragma unroll
@@ -302,6 +374,12 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
   }
   lds_barrier();
   const int n0 = nb0 * 32;
+  if constexpr (NB == 8) {
+    if (p.epi == EPI_UNMASK) {
+      unmask_epilogue<NB>(p, tile, m0, n0, tid);
+      return;
+    }
+  }
   for (int u = tid; u < kLM * NCH; u += T::THREADS) {
     const int r = u / NCH, c = u % NCH;
     const int m = m0 + r, nn = n0 + c * 4;
@@ -314,16 +392,29 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
   }
 }
 
+// Sum of the K partials in partition order, 8 partials requested at a time (clamped loads, no
+// branches, so that they are all in flight together).
 __global__ __launch_bounds__(256) void linear_reduce_kernel(LinearParams p) {
   const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
   const size_t total = (size_t)p.M * (p.N / 4);
   if (e >= total) return;
   const int m = (int)(e / (p.N / 4));
   const int n = (int)(e % (p.N / 4)) * 4;
-  f32x4 s = *reinterpret_cast<const f32x4 *>(p.part + (size_t)m * p.N + n);
-  for (int z = 1; z < p.ksplit; ++z)
-    s += *reinterpret_cast<const f32x4 *>(p.part + ((size_t)z * p.M + m) * p.N + n);
-  epilogue4(p, m, n, s);
+  const float *src = p.part + (size_t)m * p.N + n;
+  const size_t zstride = (size_t)p.M * p.N;
+  uint2 rr = {0u, 0u};
+  if (p.epi == EPI_RESIDUAL) rr = load_residual4(p, m, n);  // in flight with the partials
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int z0 = 0; z0 < p.ksplit; z0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = *reinterpret_cast<const f32x4 *>(src + (size_t)min(z0 + j, p.ksplit - 1) * zstride);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (z0 + j < p.ksplit) s = z0 + j == 0 ? v[j] : s + v[j];
+  }
+  epilogue4(p, m, n, s, &rr);
 }
 
 template <int NB>

@@ -9,45 +9,19 @@
 // unmask_finalize_kernel: one wavefront per sequence, lane i = block position i. Merges the
 //   chunk triples of its row, confidence = 1 / sum, threshold / fallback / commit-all decisions
 //   with wavefront ballots, then updates tokens, masked, confidence and n_committed.
+// unmask_tiles_finalize_kernel: the same decisions from the per-256-logit triples that the fused
+//   lm-head epilogue writes (hundreds per row), merged by one wavefront per row.
 #include <math.h>
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "triple.hpp"
 
 namespace tt {
 
 constexpr int kUThreads = 256;
 constexpr int kUPerThread = 32;
 constexpr int kUChunk = kUThreads * kUPerThread;  // 8192 logits per work-group
-
-struct Triple {
-  float m;  // running maximum
-  int idx;  // lowest index attaining m
-  float z;  // sum of exp(x - m)
-};
-
-__device__ __forceinline__ Triple merge(Triple a, Triple b) {
-  if (b.z == 0.f) return a;
-  if (a.z == 0.f) return b;
-  Triple r;
-  if (b.m > a.m || (b.m == a.m && b.idx < a.idx)) {
-    r.m = b.m;
-    r.idx = b.idx;
-  } else {
-    r.m = a.m;
-    r.idx = a.idx;
-  }
-  r.z = a.z * __expf(a.m - r.m) + b.z * __expf(b.m - r.m);
-  return r;
-}
-
-__device__ __forceinline__ Triple shfl_xor_triple(Triple t, int o) {
-  Triple r;
-  r.m = __shfl_xor(t.m, o, 64);
-  r.idx = __shfl_xor(t.idx, o, 64);
-  r.z = __shfl_xor(t.z, o, 64);
-  return r;
-}
 
 template <bool VEC>
 __global__ __launch_bounds__(kUThreads) void unmask_partial_kernel(UnmaskParams p) {
@@ -83,9 +57,7 @@ __global__ __launch_bounds__(kUThreads) void unmask_partial_kernel(UnmaskParams 
     }
   }
   // Elements are visited in increasing index order, so a strict '>' keeps the first maximum.
-  Triple t;
-  t.m = -INFINITY;
-  t.idx = 0x7fffffff;
+  Triple t = empty_triple();
 #pragma unroll
   for (int k = 0; k < kUPerThread / 4; ++k)
 #pragma unroll
@@ -114,26 +86,13 @@ __global__ __launch_bounds__(kUThreads) void unmask_partial_kernel(UnmaskParams 
   }
 }
 
-__global__ __launch_bounds__(64) void unmask_finalize_kernel(UnmaskParams p) {
-  const int b = blockIdx.x;
-  const int i = threadIdx.x;
+// Decisions of sequence b from the row triples, one lane per block position i (wave-wide, every
+// lane of the wave calls it): confidence = 1 / z, commit iff confidence > threshold (or commit-all),
+// the one-commit fallback by ballot, then the state update.
+__device__ __forceinline__ void commit_decisions(const UnmaskParams &p, int b, int i, Triple t) {
   const bool in = i < p.S;
   const size_t row = (size_t)b * p.S + i;
   const bool was_masked = in && p.masked[row] != 0;
-  Triple t;
-  t.m = -INFINITY;
-  t.idx = 0x7fffffff;
-  t.z = 0.f;
-  if (was_masked) {
-    for (int c = 0; c < p.chunks; ++c) {
-      const float *o = p.part + (row * p.chunks + c) * 4;
-      Triple u;
-      u.m = o[0];
-      u.idx = __float_as_int(o[1]);
-      u.z = o[2];
-      t = merge(t, u);
-    }
-  }
   const float conf = was_masked ? 1.0f / t.z : -1.0f;
   bool commit = was_masked && (p.commit_all || conf > p.threshold);
   const unsigned long long any_commit = __ballot(commit);
@@ -163,6 +122,60 @@ __global__ __launch_bounds__(64) void unmask_finalize_kernel(UnmaskParams p) {
   if (i == 0 && p.n_committed) p.n_committed[b] = __popcll(committed);
 }
 
+__device__ __forceinline__ Triple load_triple(const float *o) {
+  Triple u;
+  u.m = o[0];
+  u.idx = __float_as_int(o[1]);
+  u.z = o[2];
+  return u;
+}
+
+// A few chunk triples per row (8192-logit chunks): lane i merges the triples of position i.
+__global__ __launch_bounds__(64) void unmask_finalize_kernel(UnmaskParams p) {
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  const size_t row = (size_t)b * p.S + i;
+  Triple t = empty_triple();
+  if (i < p.S && p.masked[row] != 0)
+    for (int c = 0; c < p.chunks; ++c) t = merge(t, load_triple(p.part + (row * p.chunks + c) * 4));
+  commit_decisions(p, b, i, t);
+}
+
+// Many tile triples per row (one per 256-logit lm-head tile): wave w merges rows w, w + 16, ...
+// with its 64 lanes (strided, then a butterfly), and wave 0 takes the decisions.
+__global__ __launch_bounds__(1024) void unmask_tiles_finalize_kernel(UnmaskParams p) {
+  __shared__ Triple rows[64];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = wave; i < p.S; i += 16) {
+    const size_t row = (size_t)b * p.S + i;
+    Triple t = empty_triple();
+    if (p.masked[row] != 0) {
+      const f32x4 *src = reinterpret_cast<const f32x4 *>(p.part) + row * p.chunks;
+      for (int c0 = 0; c0 < p.chunks; c0 += 8 * 64) {  // 8 triples per lane in flight at once
+        f32x4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = c0 + j * 64 + lane;
+          v[j] = c < p.chunks ? src[c] : f32x4{-INFINITY, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          Triple u;
+          u.m = v[j][0];
+          u.idx = __float_as_int(v[j][1]);
+          u.z = v[j][2];
+          t = merge(t, u);
+        }
+      }
+      for (int o = 1; o < 64; o <<= 1) t = merge(t, shfl_xor_triple(t, o));
+    }
+    if (lane == 0) rows[i] = t;
+  }
+  __syncthreads();
+  if (wave == 0) commit_decisions(p, b, lane, lane < p.S ? rows[lane] : empty_triple());
+}
+
 hipError_t launch_unmask(const UnmaskParams &p, hipStream_t stream) {
   const bool vec = (p.ld % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.logits) & 15) == 0);
   dim3 grid(p.chunks, p.B * p.S);
@@ -173,6 +186,11 @@ hipError_t launch_unmask(const UnmaskParams &p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(unmask_finalize_kernel, dim3(p.B), dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_unmask_tiles_finalize(const UnmaskParams &p, hipStream_t stream) {
+  hipLaunchKernelGGL(unmask_tiles_finalize_kernel, dim3(p.B), dim3(1024), 0, stream, p);
   return hipGetLastError();
 }
 
