@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define TWOTOWER_ABI_VERSION 3
+#define TWOTOWER_ABI_VERSION 4
 
 typedef enum {
   TT_OK = 0,
@@ -252,8 +252,55 @@ typedef struct {
   void *const *timing_events;
 } tt_denoise_step_args;
 
+/*
+ * Context KV append after a block is committed (twotower_kv_append). Once every position of the
+ * block is committed, the frozen context tower encodes it and its keys and values join the cache
+ * that the next block attends to (explainer, "Generierungsprozess"); this call does the cache side
+ * of that: it writes, for every layer, the block's S rows at context positions ctx_lens[b] ..
+ * ctx_lens[b] + S - 1 of sequence b and advances ctx_lens[b] by S. (The rows themselves come from
+ * the context tower, which this library does not include: any [batch, Hkv, S, head_dim] keys and
+ * [batch, Hkv, head_dim, S] values are accepted, e.g. the block KV of the last denoise step.)
+ *
+ * Pages: the rows go to the pages already in the sequence's block table while they have room;
+ * each further page is popped from the top of a device-resident free-page stack
+ * (free_pages[*free_count - 1], then free_pages[*free_count - 2], ...) and written into the next
+ * block-table entry. Sequences are served in order b = 0, 1, ..., so the assignment is
+ * deterministic. A sequence whose rows do not fit (ctx_lens[b] outside 0 .. max_pages_per_seq *
+ * page_size - S, too few free pages left, or a page id it would write outside 0 .. num_pages-1)
+ * is skipped: its table, length and cache rows stay untouched and *status gets
+ * TT_APPEND_NO_ROOM_IN_TABLE, TT_APPEND_OUT_OF_PAGES or TT_APPEND_BAD_PAGE OR-ed in (*status
+ * is never cleared by the library). Everything happens on the device; the host is not
+ * synchronized.
+ *
+ * Layouts: k_pages / v_pages per layer as in tt_block_attn_args (page_size a multiple of 64);
+ *   k_new[l] [batch, num_kv_heads, S, head_dim], v_new[l] [batch, num_kv_heads, head_dim, S]
+ *   (elements of `dtype`); block_table int32 [batch, max_pages_per_seq] (in/out);
+ *   ctx_lens int32 [batch] (in/out); free_pages int32 [any], free_count int32 [1] (in/out),
+ *   status int32 [1] (in/out). Supported: 1 <= num_layers <= 16.
+ */
+#define TT_APPEND_OUT_OF_PAGES 1
+#define TT_APPEND_NO_ROOM_IN_TABLE 2
+#define TT_APPEND_BAD_PAGE 4
+typedef struct {
+  int32_t num_layers, batch, num_kv_heads, head_dim, S;
+  tt_dtype dtype;
+  int32_t num_pages, page_size, max_pages_per_seq;
+  int32_t reserved0;
+  void *const *k_pages;          /* host array [num_layers] of device pointers */
+  void *const *v_pages;
+  const void *const *k_new;      /* host array [num_layers] */
+  const void *const *v_new;
+  int32_t *block_table;
+  int32_t *ctx_lens;
+  const int32_t *free_pages;
+  int32_t *free_count;
+  int32_t *status;
+} tt_kv_append_args;
+
 tt_status twotower_block_attn(const tt_block_attn_args *args, void *ws, size_t *ws_bytes,
                               void *stream);
+tt_status twotower_kv_append(const tt_kv_append_args *args, void *ws, size_t *ws_bytes,
+                             void *stream);
 tt_status twotower_unmask(const tt_unmask_args *args, void *ws, size_t *ws_bytes, void *stream);
 tt_status twotower_qkv_projection(const tt_qkv_args *args, void *ws, size_t *ws_bytes,
                                   void *stream);
@@ -280,8 +327,8 @@ const char *twotower_status_string(int32_t status);
 int32_t twotower_abi_version(void);
 /* sizeof of the argument structs, for bindings to check their mirrors:
  * 0 tt_block_attn_args, 1 tt_unmask_args, 2 tt_qkv_args, 3 tt_out_proj_args,
- * 4 tt_lm_head_args, 5 tt_denoise_step_args, 6 tt_lm_head_unmask_args; -1 for an unknown
- * index. */
+ * 4 tt_lm_head_args, 5 tt_denoise_step_args, 6 tt_lm_head_unmask_args,
+ * 7 tt_kv_append_args; -1 for an unknown index. */
 int64_t twotower_struct_size(int32_t which);
 /* Byte offset of field `field` (0-based declaration order) in struct `which`; -1 if unknown. */
 int64_t twotower_struct_offset(int32_t which, int32_t field);

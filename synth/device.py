@@ -34,6 +34,8 @@ class LoopModel:
     block_table: torch.Tensor
     ctx_lens: torch.Tensor
     h_steps: list
+    free_pages: torch.Tensor = None   # paged variant: stack of unused pool pages
+    free_count: torch.Tensor = None
 
 
 def _randn(shape, gen, device, std=1.0):
@@ -44,15 +46,25 @@ def _randn(shape, gen, device, std=1.0):
 
 
 def loop_model(seed: int = 5, *, B=8, S=16, L=32768, layers=6, Hq=32, Hkv=2, D=128, hidden=2048,
-               vocab=131072, T=16, device="cuda") -> LoopModel:
+               vocab=131072, T=16, device="cuda", page_size=None, spare_pages=0,
+               max_pages=None) -> LoopModel:
+    """page_size None: one contiguous page per sequence. Otherwise a pool of page_size-token pages,
+    sequence b holding pages b*n .. b*n + n - 1 (n = ceil(L / page_size)) in its table of
+    max_pages entries (-1 beyond), plus spare_pages free pages on a stack for the cache to grow."""
     dev = torch.device(device)
     g = torch.Generator(device=dev)
     g.manual_seed(seed)
-    Lp = max(64, -(-L // 64) * 64)
+    if page_size is None:
+        P = max(64, -(-L // 64) * 64)
+        pool, n = B, 1
+    else:
+        P = page_size
+        n = -(-L // P)
+        pool = B * n + spare_pages
     k_pages, v_pages, w_qkv, w_o = [], [], [], []
     for _ in range(layers):
-        k_pages.append(_randn((B, Hkv, Lp, D), g, dev))
-        v_pages.append(_randn((B, Hkv, Lp // 64, D, 64), g, dev))
+        k_pages.append(_randn((pool, Hkv, P, D), g, dev))
+        v_pages.append(_randn((pool, Hkv, P // 64, D, 64), g, dev))
         w_qkv.append(_randn(((Hq + 2 * Hkv) * D, hidden), g, dev, 1.0 / math.sqrt(hidden)))
         w_o.append(_randn((hidden, Hq * D), g, dev, 1.0 / math.sqrt(Hq * D)))
     w_lm = _randn((vocab, hidden), g, dev, 1.0 / math.sqrt(hidden))
@@ -61,7 +73,15 @@ def loop_model(seed: int = 5, *, B=8, S=16, L=32768, layers=6, Hq=32, Hkv=2, D=1
         gt = torch.Generator(device=dev)
         gt.manual_seed(seed * 1000 + t)
         h_steps.append(_randn((B, S, hidden), gt, dev))
-    block_table = torch.arange(B, dtype=torch.int32, device=dev).view(B, 1)
     ctx_lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    if page_size is None:
+        block_table = torch.arange(B, dtype=torch.int32, device=dev).view(B, 1)
+        return LoopModel(B, S, L, layers, Hq, Hkv, D, hidden, vocab, T, k_pages, v_pages, w_qkv,
+                         w_o, w_lm, block_table, ctx_lens, h_steps)
+    mp = max_pages if max_pages is not None else n + 1
+    block_table = torch.full((B, mp), -1, dtype=torch.int32, device=dev)
+    block_table[:, :n] = torch.arange(B * n, dtype=torch.int32, device=dev).view(B, n)
+    free_pages = torch.arange(B * n, pool, dtype=torch.int32, device=dev)
+    free_count = torch.tensor([pool - B * n], dtype=torch.int32, device=dev)
     return LoopModel(B, S, L, layers, Hq, Hkv, D, hidden, vocab, T, k_pages, v_pages, w_qkv, w_o,
-                     w_lm, block_table, ctx_lens, h_steps)
+                     w_lm, block_table, ctx_lens, h_steps, free_pages, free_count)

@@ -210,3 +210,31 @@ def test_denoise_step_validation():
     assert query("twotower_denoise_step", a)[0] == _lib.TT_OK
     a.attn = attn_args(dtype=_lib.TT_FP32)
     assert query("twotower_denoise_step", a)[0] == _lib.TT_ENOTSUP
+
+
+def append_args(**over):
+    a = _lib.KvAppendArgs()
+    arr = (C.c_void_p * 6)(*([FAKE] * 6))
+    vpp = C.POINTER(C.c_void_p)
+    a.num_layers, a.batch, a.num_kv_heads, a.head_dim, a.S = 6, 8, 2, 128, 16
+    a.dtype, a.num_pages, a.page_size, a.max_pages_per_seq = _lib.TT_BF16, 1100, 256, 130
+    for f in ("k_pages", "v_pages", "k_new", "v_new"):
+        setattr(a, f, C.cast(arr, vpp))
+    for f in ("block_table", "ctx_lens", "free_pages", "free_count", "status"):
+        setattr(a, f, FAKE)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_kv_append_workspace_and_errors():
+    st, n = query("twotower_kv_append", append_args())
+    assert st == _lib.TT_OK and n == 256          # one int32 per sequence, 256-byte aligned
+    for over, code in [(dict(num_layers=0), _lib.TT_EINVAL), (dict(num_layers=17), _lib.TT_ENOTSUP),
+                       (dict(page_size=100), _lib.TT_ENOTSUP), (dict(S=0), _lib.TT_EINVAL),
+                       (dict(dtype=5), _lib.TT_EINVAL), (dict(free_count=None), _lib.TT_EINVAL),
+                       (dict(status=None), _lib.TT_EINVAL), (dict(k_new=None), _lib.TT_EINVAL)]:
+        assert query("twotower_kv_append", append_args(**over))[0] == code, over
+    arr = (C.c_void_p * 6)(*([FAKE] * 5 + [FAKE + 1]))   # misaligned last layer
+    a = append_args(v_pages=C.cast(arr, C.POINTER(C.c_void_p)))
+    assert query("twotower_kv_append", a)[0] == _lib.TT_EINVAL

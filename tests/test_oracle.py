@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import attention, bruteforce, step, unmask
+from oracle import attention, bruteforce, cache, step, unmask
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -516,3 +516,65 @@ def test_paged_generator_places_tokens_where_the_table_says():
     assert spare and all(np.isnan(c.k_pages[p]).all() for p in spare)
     # tail of the last page of sequence 0 (length 5, page 2) is poisoned
     assert np.isnan(c.k_pages[c.block_table[0, 2], 0, 1]).all()
+
+
+# ------------------------------------------------------------------------------ cache append
+
+def _paged_cache(seed, pool, Hkv, page, D, layers=2):
+    r = synth.rng(seed)
+    k = [r.standard_normal((pool, Hkv, page, D)) for _ in range(layers)]
+    v = [r.standard_normal((pool, Hkv, page // 64, D, 64)) for _ in range(layers)]
+    return k, v
+
+
+def test_append_extends_every_gathered_context_by_the_block_rows():
+    """Independent of the page bookkeeping: reading the cache back through the new table gives the
+    old context followed by the block rows (K row-major, V transposed from [D, S])."""
+    B, Hkv, D, S, page = 3, 2, 8, 16, 64
+    k, v = _paged_cache(50, 12, Hkv, page, D)
+    lens = np.array([60, 128, 0], np.int32)
+    table = np.full((B, 4), -1, np.int32)
+    table[0, 0], table[1, :2] = 3, [5, 7]
+    free = np.array([0, 1, 2, 4, 6, 8, 9, 10, 11], np.int32)
+    r = synth.rng(51)
+    kn = [r.standard_normal((B, Hkv, S, D)) for _ in range(2)]
+    vn = [r.standard_normal((B, Hkv, D, S)) for _ in range(2)]
+    k2, v2, t2, l2, top, st = cache.append_block(k, v, table, lens, free, len(free), kn, vn)
+    assert st == 0 and list(l2) == [76, 144, 16]
+    for layer in range(2):
+        for b in range(B):
+            for g in range(Hkv):
+                old_k, old_v = attention.gather_context(k[layer], v[layer], table, lens[b], b, g)
+                new_k, new_v = attention.gather_context(k2[layer], v2[layer], t2, l2[b], b, g)
+                np.testing.assert_array_equal(new_k, np.concatenate([old_k, kn[layer][b, g]]))
+                np.testing.assert_array_equal(new_v, np.concatenate([old_v, vn[layer][b, g].T]))
+
+
+def test_append_page_assignment_worked_example():
+    """page 64, S 16, free stack [10, 11, 12, 13] (top = 13): sequence 0 (60 rows) crosses into a
+    new page -> 13; sequence 1 (128 rows, pages full) needs one -> 12; sequence 2 (empty) -> 11."""
+    k, v = _paged_cache(52, 16, 1, 64, 4, layers=1)
+    table = np.full((3, 3), -1, np.int32)
+    table[0, 0], table[1, :2] = 0, [1, 2]
+    z = [np.zeros((3, 1, 16, 4))], [np.zeros((3, 1, 4, 16))]
+    _, _, t2, l2, top, st = cache.append_block(k, v, table, [60, 128, 0], [10, 11, 12, 13], 4, *z)
+    assert st == 0 and top == 1 and list(l2) == [76, 144, 16]
+    assert t2[0].tolist() == [0, 13, -1] and t2[1].tolist() == [1, 2, 12] and t2[2].tolist() == [11, -1, -1]
+
+
+def test_append_skips_what_does_not_fit_and_leaves_it_untouched():
+    k, v = _paged_cache(53, 8, 1, 64, 4, layers=1)
+    r = synth.rng(54)
+    kn, vn = [r.standard_normal((4, 1, 16, 4))], [r.standard_normal((4, 1, 4, 16))]
+    table = np.array([[0, -1], [1, -1], [2, -1], [3, 4]], np.int32)
+    lens = np.array([64, 10, 64, 120], np.int32)
+    # seq 0 pops page 7; seq 1 needs none; seq 2 finds the stack empty; seq 3's table is full
+    k2, v2, t2, l2, top, st = cache.append_block(k, v, table, lens, [7], 1, kn, vn)
+    assert top == 0 and list(l2) == [80, 26, 64, 120]
+    assert st == cache.OUT_OF_PAGES | cache.NO_ROOM_IN_TABLE
+    assert t2[2].tolist() == [2, -1] and t2[3].tolist() == [3, 4]
+    np.testing.assert_array_equal(k2[0][[2, 3, 4]], k[0][[2, 3, 4]])
+    np.testing.assert_array_equal(v2[0][[2, 3, 4]], v[0][[2, 3, 4]])
+    # a page id outside the pool is refused before anything is written
+    _, _, t3, l3, top3, st3 = cache.append_block(k, v, table, lens, [99], 1, kn, vn)
+    assert st3 & cache.BAD_PAGE and l3[0] == 64 and t3[0].tolist() == [0, -1] and top3 == 1

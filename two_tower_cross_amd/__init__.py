@@ -20,7 +20,7 @@ from . import _lib
 from ._lib import LibraryNotBuilt, TwoTowerError, TT_BF16, TT_FP32  # noqa: F401
 
 __all__ = ["block_attn", "unmask", "qkv_projection", "out_projection", "lm_head",
-           "lm_head_unmask", "DenoiseStep",
+           "lm_head_unmask", "kv_append", "DenoiseStep",
            "PackedWeight", "pack_weight",
            "LibraryNotBuilt", "TwoTowerError", "library_path"]
 
@@ -279,6 +279,58 @@ def lm_head_unmask(h, w_lm, masked, tokens, threshold, *, min_commit=False, comm
     a.unmask.min_commit, a.unmask.commit_all = int(bool(min_commit)), int(bool(commit_all))
     _run("twotower_lm_head_unmask", a, dev)
     return conf, ncom, logits
+
+
+def kv_append(k_pages, v_pages, k_new, v_new, block_table, ctx_lens, free_pages, free_count,
+              status):
+    """Append the committed block's rows of every layer to the paged context caches.
+
+    k_pages / v_pages / k_new / v_new: lists with one tensor per layer (k_new [B,Hkv,S,D],
+    v_new [B,Hkv,D,S]); block_table, ctx_lens, free_count ([1]) and status ([1]) int32 are
+    updated in place on the device (no host synchronization).
+    """
+    dev = block_table.device
+    L = len(k_pages)
+    if not (len(v_pages) == len(k_new) == len(v_new) == L) or L == 0:
+        raise ValueError("one k_pages / v_pages / k_new / v_new tensor per layer")
+    P, Hkv, page, D = k_pages[0].shape
+    B, _, S, _ = k_new[0].shape
+    dt = k_pages[0].dtype
+    for t in k_pages:
+        _check(t, "k_pages", dev, dt, 4)
+        if tuple(t.shape) != (P, Hkv, page, D):
+            raise ValueError("k_pages shape mismatch")
+    for t in v_pages:
+        _check(t, "v_pages", dev, dt, 5)
+        if tuple(t.shape) != (P, Hkv, page // 64, D, 64):
+            raise ValueError("v_pages shape mismatch")
+    for t in k_new:
+        _check(t, "k_new", dev, dt, 4)
+        if tuple(t.shape) != (B, Hkv, S, D):
+            raise ValueError("k_new shape mismatch")
+    for t in v_new:
+        _check(t, "v_new", dev, dt, 4)
+        if tuple(t.shape) != (B, Hkv, D, S):
+            raise ValueError("v_new shape mismatch")
+    for t, n in ((block_table, "block_table"), (ctx_lens, "ctx_lens"), (free_pages, "free_pages"),
+                 (free_count, "free_count"), (status, "status")):
+        _check(t, n, dev, torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(ctx_lens.shape) != (B,):
+        raise ValueError("block_table / ctx_lens shape mismatch")
+
+    def arr(ts):
+        return (C.c_void_p * L)(*[t.data_ptr() for t in ts])
+
+    keep = [arr(k_pages), arr(v_pages), arr(k_new), arr(v_new)]
+    vpp = C.POINTER(C.c_void_p)
+    a = _lib.KvAppendArgs()
+    a.num_layers, a.batch, a.num_kv_heads, a.head_dim, a.S = L, B, Hkv, D, S
+    a.dtype = _dt(k_pages[0])
+    a.num_pages, a.page_size, a.max_pages_per_seq = P, page, block_table.shape[1]
+    a.k_pages, a.v_pages, a.k_new, a.v_new = [C.cast(x, vpp) for x in keep]
+    a.block_table, a.ctx_lens = _p(block_table), _p(ctx_lens)
+    a.free_pages, a.free_count, a.status = _p(free_pages), _p(free_count), _p(status)
+    _run("twotower_kv_append", a, dev)
 
 
 class DenoiseStep:

@@ -14,7 +14,8 @@ LIB_PATH = os.environ.get("TWOTOWER_LIB", os.path.join(HERE, "libtwotower.so"))
 
 TT_OK, TT_EINVAL, TT_ENOTSUP, TT_ENOSPACE, TT_EHIP = range(5)
 TT_FP32, TT_BF16 = 0, 1
-ABI_VERSION = 3
+TT_APPEND_OUT_OF_PAGES, TT_APPEND_NO_ROOM_IN_TABLE, TT_APPEND_BAD_PAGE = 1, 2, 4
+ABI_VERSION = 4
 
 i32, i64, f32, vp = C.c_int32, C.c_int64, C.c_float, C.c_void_p
 
@@ -56,6 +57,16 @@ class LmHeadUnmaskArgs(C.Structure):
     _fields_ = [("lm", LmHeadArgs), ("unmask", UnmaskArgs)]
 
 
+class KvAppendArgs(C.Structure):
+    _fields_ = [("num_layers", i32), ("batch", i32), ("num_kv_heads", i32), ("head_dim", i32),
+                ("S", i32), ("dtype", i32), ("num_pages", i32), ("page_size", i32),
+                ("max_pages_per_seq", i32), ("reserved0", i32),
+                ("k_pages", C.POINTER(vp)), ("v_pages", C.POINTER(vp)),
+                ("k_new", C.POINTER(vp)), ("v_new", C.POINTER(vp)),
+                ("block_table", vp), ("ctx_lens", vp), ("free_pages", vp), ("free_count", vp),
+                ("status", vp)]
+
+
 class DenoiseStepArgs(C.Structure):
     _fields_ = [("num_layers", i32), ("hidden", i32), ("vocab", i32), ("reserved0", i32),
                 ("attn", BlockAttnArgs),
@@ -68,7 +79,7 @@ class DenoiseStepArgs(C.Structure):
 
 
 STRUCTS = [BlockAttnArgs, UnmaskArgs, QkvArgs, OutProjArgs, LmHeadArgs, DenoiseStepArgs,
-           LmHeadUnmaskArgs]
+           LmHeadUnmaskArgs, KvAppendArgs]
 
 ENTRY_POINTS = {
     "twotower_block_attn": (BlockAttnArgs,),
@@ -78,6 +89,7 @@ ENTRY_POINTS = {
     "twotower_lm_head": (LmHeadArgs,),
     "twotower_denoise_step": (DenoiseStepArgs,),
     "twotower_lm_head_unmask": (LmHeadUnmaskArgs,),
+    "twotower_kv_append": (KvAppendArgs,),
 }
 
 

@@ -21,7 +21,7 @@ DEVICE_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
                 "-Wno-unused-command-line-argument"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
 
-DEVICE_SOURCES = ["block_attn.hip", "unmask.hip", "linear.hip"]
+DEVICE_SOURCES = ["block_attn.hip", "unmask.hip", "linear.hip", "kv_append.hip"]
 # Per-source extra flags. The attention kernels run with the IEEE mode bit off: their max
 # reductions then need no NaN-quieting instruction per operand (no input of theirs is a
 # signaling NaN; NaN outputs for invalid sequences are written explicitly).

@@ -347,6 +347,54 @@ hipError_t run_lm_unmask(LmUnmaskPlan &pl, void *ws, hipStream_t stream) {
 
 tt_status hip_status(hipError_t e) { return e == hipSuccess ? TT_OK : TT_EHIP; }
 
+// ---------------------------------------------------------------------------- KV append
+static_assert(TT_APPEND_OUT_OF_PAGES == tt::kAppendOutOfPages &&
+                  TT_APPEND_NO_ROOM_IN_TABLE == tt::kAppendNoRoomInTable &&
+                  TT_APPEND_BAD_PAGE == tt::kAppendBadPage,
+              "append status flags");
+
+tt_status plan_append(const tt_kv_append_args *a, tt::AppendParams *p, size_t *ws_bytes) {
+  if (!a) return TT_EINVAL;
+  if (a->num_layers < 1 || a->batch < 0 || a->num_kv_heads < 1 || a->head_dim < 1 || a->S < 1)
+    return TT_EINVAL;
+  if (a->num_pages < 1 || a->page_size < 1 || a->max_pages_per_seq < 1) return TT_EINVAL;
+  if (a->dtype != TT_FP32 && a->dtype != TT_BF16) return TT_EINVAL;
+  if (a->num_layers > tt::kMaxAppendLayers || a->page_size % 64 != 0) return TT_ENOTSUP;
+  if ((int64_t)a->max_pages_per_seq * a->page_size > INT32_MAX ||
+      (int64_t)a->batch * a->max_pages_per_seq > INT32_MAX || a->batch > 65535)
+    return TT_ENOTSUP;
+  if (!a->k_pages || !a->v_pages || !a->k_new || !a->v_new) return TT_EINVAL;
+  if (!a->block_table || !a->ctx_lens || !a->free_pages || !a->free_count || !a->status)
+    return TT_EINVAL;
+  const uintptr_t es = a->dtype == TT_BF16 ? 2 : 4;
+  *p = tt::AppendParams{};
+  for (int l = 0; l < a->num_layers; ++l) {
+    const void *ptrs[] = {a->k_pages[l], a->v_pages[l], a->k_new[l], a->v_new[l]};
+    for (const void *q : ptrs)
+      if (!q || !aligned(q, es)) return TT_EINVAL;
+    p->k_pages[l] = a->k_pages[l];
+    p->v_pages[l] = a->v_pages[l];
+    p->k_new[l] = a->k_new[l];
+    p->v_new[l] = a->v_new[l];
+  }
+  p->block_table = a->block_table;
+  p->ctx_lens = a->ctx_lens;
+  p->free_pages = a->free_pages;
+  p->free_count = a->free_count;
+  p->status = a->status;
+  p->layers = a->num_layers;
+  p->B = a->batch;
+  p->Hkv = a->num_kv_heads;
+  p->D = a->head_dim;
+  p->S = a->S;
+  p->page_size = a->page_size;
+  p->max_pages = a->max_pages_per_seq;
+  p->num_pages = a->num_pages;
+  p->elem_bytes = (int)es;
+  *ws_bytes = align_up((size_t)std::max(a->batch, 1) * sizeof(int32_t));
+  return TT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -418,6 +466,20 @@ tt_status twotower_lm_head(const tt_lm_head_args *args, void *ws, size_t *ws_byt
   st = ws_protocol(linear_ws(p), ws, ws_bytes, &launch);
   if (st != TT_OK || !launch) return st;
   return hip_status(run_linear(p, ws, static_cast<hipStream_t>(stream)));
+}
+
+tt_status twotower_kv_append(const tt_kv_append_args *args, void *ws, size_t *ws_bytes,
+                             void *stream) {
+  tt::AppendParams p;
+  size_t need = 0;
+  tt_status st = plan_append(args, &p, &need);
+  if (st != TT_OK) return st;
+  bool launch;
+  st = ws_protocol(need, ws, ws_bytes, &launch);
+  if (st != TT_OK || !launch) return st;
+  if (p.B == 0) return TT_OK;
+  p.old_len = static_cast<int32_t *>(ws);
+  return hip_status(tt::launch_kv_append(p, static_cast<hipStream_t>(stream)));
 }
 
 tt_status twotower_lm_head_unmask(const tt_lm_head_unmask_args *args, void *ws, size_t *ws_bytes,
@@ -558,6 +620,7 @@ int64_t twotower_struct_size(int32_t which) {
     case 4: return sizeof(tt_lm_head_args);
     case 5: return sizeof(tt_denoise_step_args);
     case 6: return sizeof(tt_lm_head_unmask_args);
+    case 7: return sizeof(tt_kv_append_args);
     default: return -1;
   }
 }
@@ -613,6 +676,17 @@ int64_t twotower_struct_offset(int32_t which, int32_t field) {
       TT_OFF(tt_denoise_step_args, unmask), TT_OFF(tt_denoise_step_args, timing_events)};
   static const int64_t lmu[] = {TT_OFF(tt_lm_head_unmask_args, lm),
                                 TT_OFF(tt_lm_head_unmask_args, unmask)};
+  static const int64_t app[] = {
+      TT_OFF(tt_kv_append_args, num_layers), TT_OFF(tt_kv_append_args, batch),
+      TT_OFF(tt_kv_append_args, num_kv_heads), TT_OFF(tt_kv_append_args, head_dim),
+      TT_OFF(tt_kv_append_args, S), TT_OFF(tt_kv_append_args, dtype),
+      TT_OFF(tt_kv_append_args, num_pages), TT_OFF(tt_kv_append_args, page_size),
+      TT_OFF(tt_kv_append_args, max_pages_per_seq), TT_OFF(tt_kv_append_args, reserved0),
+      TT_OFF(tt_kv_append_args, k_pages), TT_OFF(tt_kv_append_args, v_pages),
+      TT_OFF(tt_kv_append_args, k_new), TT_OFF(tt_kv_append_args, v_new),
+      TT_OFF(tt_kv_append_args, block_table), TT_OFF(tt_kv_append_args, ctx_lens),
+      TT_OFF(tt_kv_append_args, free_pages), TT_OFF(tt_kv_append_args, free_count),
+      TT_OFF(tt_kv_append_args, status)};
   const int64_t *tab = nullptr;
   int n = 0;
   switch (which) {
@@ -623,6 +697,7 @@ int64_t twotower_struct_offset(int32_t which, int32_t field) {
     case 4: tab = lm; n = sizeof(lm) / sizeof(lm[0]); break;
     case 5: tab = step; n = sizeof(step) / sizeof(step[0]); break;
     case 6: tab = lmu; n = sizeof(lmu) / sizeof(lmu[0]); break;
+    case 7: tab = app; n = sizeof(app) / sizeof(app[0]); break;
     default: return -1;
   }
   if (field < 0 || field >= n) return -1;

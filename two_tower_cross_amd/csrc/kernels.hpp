@@ -51,6 +51,29 @@ hipError_t launch_unmask(const UnmaskParams &p, hipStream_t stream);
 // EPI_UNMASK linear epilogue.
 hipError_t launch_unmask_tiles_finalize(const UnmaskParams &p, hipStream_t stream);
 
+// ----------------------------------------------------------------------- context KV append
+constexpr int kMaxAppendLayers = 16;
+// status flags (the same values as TT_APPEND_* in include/twotower.h)
+constexpr int kAppendOutOfPages = 1;
+constexpr int kAppendNoRoomInTable = 2;
+constexpr int kAppendBadPage = 4;
+
+struct AppendParams {
+  void *k_pages[kMaxAppendLayers];      // [num_pages, Hkv, page_size, D]
+  void *v_pages[kMaxAppendLayers];      // [num_pages, Hkv, page_size / 64, D, 64]
+  const void *k_new[kMaxAppendLayers];  // [B, Hkv, S, D]
+  const void *v_new[kMaxAppendLayers];  // [B, Hkv, D, S]
+  int32_t *block_table;                 // [B, max_pages]
+  int32_t *ctx_lens;                    // [B]
+  const int32_t *free_pages;            // free-page stack; entries 0 .. *free_count - 1 valid
+  int32_t *free_count;
+  int32_t *status;                      // OR-ed flags
+  int32_t *old_len;                     // workspace [B]: length before the append, -1 = skipped
+  int layers, B, Hkv, D, S, page_size, max_pages, num_pages, elem_bytes;
+};
+
+hipError_t launch_kv_append(const AppendParams &p, hipStream_t stream);
+
 // ------------------------------------------------------------------------ skinny bf16 linear
 enum Epilogue : int {
   EPI_F32 = 0,       // y fp32 [M, ldy]
