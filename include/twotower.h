@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define TWOTOWER_ABI_VERSION 4
+#define TWOTOWER_ABI_VERSION 5
 
 typedef enum {
   TT_OK = 0,
@@ -147,6 +147,47 @@ typedef struct {
   int32_t commit_all;
   int32_t reserved1;
 } tt_unmask_args;
+
+/*
+ * Masked-diffusion training objective (twotower_mask_corrupt, twotower_masked_nll). The denoiser
+ * is trained on clean blocks corrupted by replacing tokens with [MASK] on a linear schedule and
+ * minimizes the negative log-likelihood of the original tokens at the masked positions
+ * (explainer, "Training und Konditionierung", masked-diffusion paragraph). Training itself is not
+ * part of this library; these are its two per-block kernels.
+ *
+ * twotower_mask_corrupt: sequence b takes the diffusion time t = u_time[b] (uniform draws in
+ *   [0, 1), supplied by the caller) and masks position i iff u_mask[b, i] < t (probability t:
+ *   the linear schedule); noisy[b, i] = masked ? mask_id : clean[b, i]; masked[b, i] = 0 / 1;
+ *   t_out[b] = t (optional, NULL to skip). Needs no workspace (the size query returns 0).
+ * twotower_masked_nll: for each row (b, i) with masked[b, i] != 0,
+ *     nll[b, i] = ln(sum_j exp(logits[b, i, j])) - logits[b, i, targets[b, i]]
+ *   computed in fp32 (NaN if the target is outside 0 .. vocab-1); nll = 0 at the other rows.
+ *   loss[0] = mean of nll over the masked rows of the whole batch (0 if there are none) and
+ *   n_masked[0] = their number, both optional. Logits layout as for twotower_unmask (fp32, row
+ *   (b*S + i) at element (b*S + i) * ld); batch * S <= 65535.
+ */
+typedef struct {
+  int32_t batch, S, mask_id;
+  int32_t reserved0;
+  const int32_t *clean;      /* [batch, S] */
+  const float *u_time;       /* [batch] */
+  const float *u_mask;       /* [batch, S] */
+  int32_t *noisy;            /* [batch, S] out */
+  uint8_t *masked;           /* [batch, S] out */
+  float *t_out;              /* [batch] out, optional */
+} tt_mask_corrupt_args;
+
+typedef struct {
+  int32_t batch, S, vocab;
+  int32_t reserved0;
+  int64_t ld;
+  const float *logits;
+  const int32_t *targets;    /* [batch, S] clean tokens */
+  const uint8_t *masked;     /* [batch, S] */
+  float *nll;                /* [batch, S] out */
+  float *loss;               /* [1] out, optional */
+  int32_t *n_masked;         /* [1] out, optional */
+} tt_masked_nll_args;
 
 /*
  * Dense projections of the synthetic attention-only denoiser (twotower_qkv_projection,
@@ -301,6 +342,10 @@ tt_status twotower_block_attn(const tt_block_attn_args *args, void *ws, size_t *
                               void *stream);
 tt_status twotower_kv_append(const tt_kv_append_args *args, void *ws, size_t *ws_bytes,
                              void *stream);
+tt_status twotower_mask_corrupt(const tt_mask_corrupt_args *args, void *ws, size_t *ws_bytes,
+                                void *stream);
+tt_status twotower_masked_nll(const tt_masked_nll_args *args, void *ws, size_t *ws_bytes,
+                              void *stream);
 tt_status twotower_unmask(const tt_unmask_args *args, void *ws, size_t *ws_bytes, void *stream);
 tt_status twotower_qkv_projection(const tt_qkv_args *args, void *ws, size_t *ws_bytes,
                                   void *stream);
@@ -328,7 +373,8 @@ int32_t twotower_abi_version(void);
 /* sizeof of the argument structs, for bindings to check their mirrors:
  * 0 tt_block_attn_args, 1 tt_unmask_args, 2 tt_qkv_args, 3 tt_out_proj_args,
  * 4 tt_lm_head_args, 5 tt_denoise_step_args, 6 tt_lm_head_unmask_args,
- * 7 tt_kv_append_args; -1 for an unknown index. */
+ * 7 tt_kv_append_args, 8 tt_mask_corrupt_args, 9 tt_masked_nll_args; -1 for an unknown
+ * index. */
 int64_t twotower_struct_size(int32_t which);
 /* Byte offset of field `field` (0-based declaration order) in struct `which`; -1 if unknown. */
 int64_t twotower_struct_offset(int32_t which, int32_t field);

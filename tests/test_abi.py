@@ -238,3 +238,22 @@ def test_kv_append_workspace_and_errors():
     arr = (C.c_void_p * 6)(*([FAKE] * 5 + [FAKE + 1]))   # misaligned last layer
     a = append_args(v_pages=C.cast(arr, C.POINTER(C.c_void_p)))
     assert query("twotower_kv_append", a)[0] == _lib.TT_EINVAL
+
+
+def test_loss_entry_points_validate_and_size():
+    c = _lib.MaskCorruptArgs(8, 16, 131071, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    st, n = query("twotower_mask_corrupt", c)
+    assert st == _lib.TT_OK and n == 0
+    c.u_mask = None
+    assert query("twotower_mask_corrupt", c)[0] == _lib.TT_EINVAL
+    a = _lib.MaskedNllArgs(8, 16, 131072, 0, 131072, FAKE, FAKE, FAKE, FAKE, None, None)
+    st, n = query("twotower_masked_nll", a)
+    assert st == _lib.TT_OK and n == 8 * 16 * 16 * 16     # the unmasking's chunk triples
+    a.S = 200
+    assert query("twotower_masked_nll", a)[0] == _lib.TT_OK   # no 64-position limit here
+    for over, code in [(dict(targets=None), _lib.TT_EINVAL), (dict(nll=FAKE + 2), _lib.TT_EINVAL),
+                       (dict(ld=100), _lib.TT_EINVAL), (dict(S=0), _lib.TT_EINVAL)]:
+        b = _lib.MaskedNllArgs(8, 16, 131072, 0, 131072, FAKE, FAKE, FAKE, FAKE, None, None)
+        for k, v in over.items():
+            setattr(b, k, v)
+        assert query("twotower_masked_nll", b)[0] == code, over

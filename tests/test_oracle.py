@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import attention, bruteforce, cache, step, unmask
+from oracle import attention, bruteforce, cache, loss, step, unmask
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -578,3 +578,67 @@ def test_append_skips_what_does_not_fit_and_leaves_it_untouched():
     # a page id outside the pool is refused before anything is written
     _, _, t3, l3, top3, st3 = cache.append_block(k, v, table, lens, [99], 1, kn, vn)
     assert st3 & cache.BAD_PAGE and l3[0] == 64 and t3[0].tolist() == [0, -1] and top3 == 1
+
+
+# ------------------------------------------------------------------- masked-diffusion objective
+
+def test_nll_of_uniform_logits_is_log_vocab():
+    B, S, V = 2, 5, 1000
+    x = np.full((B, S, V), 3.25)
+    masked = np.array([[1, 0, 1, 1, 0], [0, 0, 0, 0, 1]], np.uint8)
+    targets = synth.rng(55).integers(0, V, (B, S))
+    nll, mean, n = loss.masked_nll(x, targets, masked)
+    assert n == 4 and abs(mean - math.log(V)) < 1e-12
+    np.testing.assert_allclose(nll[masked == 1], math.log(V), rtol=0, atol=1e-12)
+    assert np.all(nll[masked == 0] == 0)
+
+
+def test_nll_closed_form_single_peak():
+    # target logit c, all others 0: nll = ln(e^c + V - 1) - c
+    V, c = 257, 4.5
+    x = np.zeros((1, 2, V))
+    x[0, 0, 17] = c
+    x[0, 1, 3] = c
+    nll, mean, n = loss.masked_nll(x, np.array([[17, 9]]), np.ones((1, 2), np.uint8))
+    assert abs(nll[0, 0] - (math.log(math.exp(c) + V - 1) - c)) < 1e-12
+    assert abs(nll[0, 1] - math.log(math.exp(c) + V - 1)) < 1e-12     # target is a 0 logit
+    assert n == 2 and abs(mean - nll.mean()) < 1e-15
+
+
+def test_nll_matches_torch_cross_entropy_and_is_shift_invariant():
+    torch = pytest.importorskip("torch")
+    r = synth.rng(56)
+    B, S, V = 3, 7, 513
+    x = r.standard_normal((B, S, V)) * 3
+    targets = r.integers(0, V, (B, S))
+    masked = (r.random((B, S)) < 0.6).astype(np.uint8)
+    nll, mean, n = loss.masked_nll(x, targets, masked)
+    sel = masked.reshape(-1) == 1
+    ce = torch.nn.functional.cross_entropy(torch.tensor(x.reshape(-1, V)[sel]),
+                                           torch.tensor(targets.reshape(-1)[sel]), reduction="none")
+    np.testing.assert_allclose(nll.reshape(-1)[sel], ce.numpy(), rtol=1e-12, atol=1e-12)
+    assert abs(mean - ce.mean().item()) < 1e-12
+    shifted, _, _ = loss.masked_nll(x + r.standard_normal((B, S, 1)) * 100, targets, masked)
+    np.testing.assert_allclose(shifted, nll, rtol=0, atol=1e-9)
+
+
+def test_linear_schedule_corruption():
+    r = synth.rng(57)
+    B, S = 4000, 16
+    clean = r.integers(0, 1000, (B, S)).astype(np.int32)
+    u_t = r.random(B).astype(np.float32)
+    u_m = r.random((B, S)).astype(np.float32)
+    noisy, masked, t = loss.corrupt(clean, u_t, u_m, mask_id=999999)
+    assert np.array_equal(noisy[masked == 1], np.full(int(masked.sum()), 999999))
+    assert np.array_equal(noisy[masked == 0], clean[masked == 0])
+    # masking probability equals t: the masked fraction of each time bin tracks its mean time
+    bins = np.minimum((u_t * 10).astype(int), 9)
+    for k in range(10):
+        sel = bins == k
+        frac, tm = masked[sel].mean(), u_t[sel].mean()
+        assert abs(frac - tm) < 4 * math.sqrt(tm * (1 - tm) / (sel.sum() * S)) + 1e-3
+    # t = 0 masks nothing; the comparison is strict (u == t stays clean)
+    _, m0, _ = loss.corrupt(clean[:2], np.zeros(2, np.float32), u_m[:2], 0)
+    assert not m0.any()
+    _, m1, _ = loss.corrupt(clean[:1], u_m[0, :1].copy(), u_m[:1], 0)
+    assert m1[0, 0] == 0

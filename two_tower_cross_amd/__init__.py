@@ -20,7 +20,7 @@ from . import _lib
 from ._lib import LibraryNotBuilt, TwoTowerError, TT_BF16, TT_FP32  # noqa: F401
 
 __all__ = ["block_attn", "unmask", "qkv_projection", "out_projection", "lm_head",
-           "lm_head_unmask", "kv_append", "DenoiseStep",
+           "lm_head_unmask", "kv_append", "mask_corrupt", "masked_nll", "DenoiseStep",
            "PackedWeight", "pack_weight",
            "LibraryNotBuilt", "TwoTowerError", "library_path"]
 
@@ -331,6 +331,51 @@ def kv_append(k_pages, v_pages, k_new, v_new, block_table, ctx_lens, free_pages,
     a.block_table, a.ctx_lens = _p(block_table), _p(ctx_lens)
     a.free_pages, a.free_count, a.status = _p(free_pages), _p(free_count), _p(status)
     _run("twotower_kv_append", a, dev)
+
+
+def mask_corrupt(clean, u_time, u_mask, mask_id):
+    """Linear-schedule [MASK] corruption of clean blocks [B,S] int32 with the caller's uniform
+    draws u_time [B], u_mask [B,S] (fp32 in [0, 1)). Returns (noisy int32, masked uint8, t fp32)."""
+    dev = clean.device
+    _check(clean, "clean", dev, torch.int32, 2)
+    _check(u_time, "u_time", dev, torch.float32, 1)
+    _check(u_mask, "u_mask", dev, torch.float32, 2)
+    B, S = clean.shape
+    if tuple(u_time.shape) != (B,) or tuple(u_mask.shape) != (B, S):
+        raise ValueError("mask_corrupt shape mismatch")
+    noisy = torch.empty_like(clean)
+    masked = torch.empty((B, S), dtype=torch.uint8, device=dev)
+    t = torch.empty((B,), dtype=torch.float32, device=dev)
+    a = _lib.MaskCorruptArgs()
+    a.batch, a.S, a.mask_id = B, S, int(mask_id)
+    a.clean, a.u_time, a.u_mask = _p(clean), _p(u_time), _p(u_mask)
+    a.noisy, a.masked, a.t_out = _p(noisy), _p(masked), _p(t)
+    _run("twotower_mask_corrupt", a, dev)
+    return noisy, masked, t
+
+
+def masked_nll(logits, targets, masked):
+    """NLL of targets at the masked rows of fp32 logits [B,S,V]. Returns (nll [B,S] fp32, 0 at
+    rows not masked; mean over masked rows [1] fp32; number of masked rows [1] int32)."""
+    dev = logits.device
+    _check(targets, "targets", dev, torch.int32, 2)
+    _check(masked, "masked", dev, torch.uint8, 2)
+    if logits.dtype != torch.float32 or logits.dim() != 3 or logits.stride(2) != 1:
+        raise ValueError("logits must be fp32 [B,S,V] with unit vocab stride")
+    B, S, V = logits.shape
+    if logits.stride(0) != S * logits.stride(1):
+        raise ValueError("logits rows must be evenly strided")
+    if tuple(targets.shape) != (B, S) or tuple(masked.shape) != (B, S):
+        raise ValueError("masked_nll shape mismatch")
+    nll = torch.empty((B, S), dtype=torch.float32, device=dev)
+    loss = torch.empty((1,), dtype=torch.float32, device=dev)
+    count = torch.empty((1,), dtype=torch.int32, device=dev)
+    a = _lib.MaskedNllArgs()
+    a.batch, a.S, a.vocab, a.ld = B, S, V, logits.stride(1)
+    a.logits, a.targets, a.masked = _p(logits), _p(targets), _p(masked)
+    a.nll, a.loss, a.n_masked = _p(nll), _p(loss), _p(count)
+    _run("twotower_masked_nll", a, dev)
+    return nll, loss, count
 
 
 class DenoiseStep:

@@ -15,7 +15,7 @@ LIB_PATH = os.environ.get("TWOTOWER_LIB", os.path.join(HERE, "libtwotower.so"))
 TT_OK, TT_EINVAL, TT_ENOTSUP, TT_ENOSPACE, TT_EHIP = range(5)
 TT_FP32, TT_BF16 = 0, 1
 TT_APPEND_OUT_OF_PAGES, TT_APPEND_NO_ROOM_IN_TABLE, TT_APPEND_BAD_PAGE = 1, 2, 4
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 i32, i64, f32, vp = C.c_int32, C.c_int64, C.c_float, C.c_void_p
 
@@ -67,6 +67,18 @@ class KvAppendArgs(C.Structure):
                 ("status", vp)]
 
 
+class MaskCorruptArgs(C.Structure):
+    _fields_ = [("batch", i32), ("S", i32), ("mask_id", i32), ("reserved0", i32),
+                ("clean", vp), ("u_time", vp), ("u_mask", vp), ("noisy", vp), ("masked", vp),
+                ("t_out", vp)]
+
+
+class MaskedNllArgs(C.Structure):
+    _fields_ = [("batch", i32), ("S", i32), ("vocab", i32), ("reserved0", i32), ("ld", i64),
+                ("logits", vp), ("targets", vp), ("masked", vp), ("nll", vp), ("loss", vp),
+                ("n_masked", vp)]
+
+
 class DenoiseStepArgs(C.Structure):
     _fields_ = [("num_layers", i32), ("hidden", i32), ("vocab", i32), ("reserved0", i32),
                 ("attn", BlockAttnArgs),
@@ -79,7 +91,7 @@ class DenoiseStepArgs(C.Structure):
 
 
 STRUCTS = [BlockAttnArgs, UnmaskArgs, QkvArgs, OutProjArgs, LmHeadArgs, DenoiseStepArgs,
-           LmHeadUnmaskArgs, KvAppendArgs]
+           LmHeadUnmaskArgs, KvAppendArgs, MaskCorruptArgs, MaskedNllArgs]
 
 ENTRY_POINTS = {
     "twotower_block_attn": (BlockAttnArgs,),
@@ -90,6 +102,8 @@ ENTRY_POINTS = {
     "twotower_denoise_step": (DenoiseStepArgs,),
     "twotower_lm_head_unmask": (LmHeadUnmaskArgs,),
     "twotower_kv_append": (KvAppendArgs,),
+    "twotower_mask_corrupt": (MaskCorruptArgs,),
+    "twotower_masked_nll": (MaskedNllArgs,),
 }
 
 

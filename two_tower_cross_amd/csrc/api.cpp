@@ -147,11 +147,12 @@ struct UnmaskPlan {
   size_t ws_bytes = 0;
 };
 
-tt_status plan_unmask(const tt_unmask_args *a, bool check_logits, UnmaskPlan *out) {
+// max_S: the decisions run one wavefront per sequence (S <= 64); the loss has no such limit.
+tt_status plan_unmask(const tt_unmask_args *a, bool check_logits, UnmaskPlan *out, int max_S = 64) {
   if (!a) return TT_EINVAL;
   if (a->batch < 0 || a->S < 1 || a->vocab < 1 || a->ld < a->vocab) return TT_EINVAL;
   if (std::isnan(a->threshold)) return TT_EINVAL;
-  if (a->S > 64) return TT_ENOTSUP;
+  if (a->S > max_S) return TT_ENOTSUP;
   if (check_logits && (!a->logits || !aligned(a->logits, 4))) return TT_EINVAL;
   if (!a->masked || !a->tokens || !aligned(a->tokens, 4)) return TT_EINVAL;
   if (a->confidence && !aligned(a->confidence, 4)) return TT_EINVAL;
@@ -468,6 +469,65 @@ tt_status twotower_lm_head(const tt_lm_head_args *args, void *ws, size_t *ws_byt
   return hip_status(run_linear(p, ws, static_cast<hipStream_t>(stream)));
 }
 
+tt_status twotower_mask_corrupt(const tt_mask_corrupt_args *a, void *ws, size_t *ws_bytes,
+                                void *stream) {
+  if (!a) return TT_EINVAL;
+  if (a->batch < 0 || a->S < 1) return TT_EINVAL;
+  if ((int64_t)a->batch * a->S > INT32_MAX / 2) return TT_ENOTSUP;
+  if (!a->clean || !a->u_time || !a->u_mask || !a->noisy || !a->masked) return TT_EINVAL;
+  const void *p4[] = {a->clean, a->u_time, a->u_mask, a->noisy};
+  for (const void *q : p4)
+    if (!aligned(q, 4)) return TT_EINVAL;
+  if (a->t_out && !aligned(a->t_out, 4)) return TT_EINVAL;
+  bool launch;
+  tt_status st = ws_protocol(0, ws, ws_bytes, &launch);
+  if (st != TT_OK || !launch || a->batch == 0) return st;
+  tt::CorruptParams p{};
+  p.clean = a->clean;
+  p.u_time = a->u_time;
+  p.u_mask = a->u_mask;
+  p.noisy = a->noisy;
+  p.masked = a->masked;
+  p.t = a->t_out;
+  p.B = a->batch;
+  p.S = a->S;
+  p.mask_id = a->mask_id;
+  return hip_status(tt::launch_mask_corrupt(p, static_cast<hipStream_t>(stream)));
+}
+
+tt_status twotower_masked_nll(const tt_masked_nll_args *a, void *ws, size_t *ws_bytes,
+                              void *stream) {
+  if (!a) return TT_EINVAL;
+  if (!a->targets || !a->nll || !aligned(a->targets, 4) || !aligned(a->nll, 4)) return TT_EINVAL;
+  if ((a->loss && !aligned(a->loss, 4)) || (a->n_masked && !aligned(a->n_masked, 4)))
+    return TT_EINVAL;
+  // the row reduction is the unmasking's: reuse its plan (masked rows, chunk triples)
+  tt_unmask_args ua{};
+  ua.batch = a->batch;
+  ua.S = a->S;
+  ua.vocab = a->vocab;
+  ua.ld = a->ld;
+  ua.logits = a->logits;
+  ua.masked = const_cast<uint8_t *>(a->masked);
+  ua.tokens = const_cast<int32_t *>(a->targets);  // only checked, never written here
+  ua.threshold = 0.f;
+  if (a->S < 1) return TT_EINVAL;
+  UnmaskPlan up;
+  tt_status st = plan_unmask(&ua, true, &up, /*max_S=*/65535);
+  if (st != TT_OK) return st;
+  bool launch;
+  st = ws_protocol(up.ws_bytes, ws, ws_bytes, &launch);
+  if (st != TT_OK || !launch) return st;
+  if (a->batch == 0) return TT_OK;
+  up.p.part = static_cast<float *>(ws);
+  tt::NllParams q{};
+  q.targets = a->targets;
+  q.nll = a->nll;
+  q.loss = a->loss;
+  q.count = a->n_masked;
+  return hip_status(tt::launch_masked_nll(up.p, q, static_cast<hipStream_t>(stream)));
+}
+
 tt_status twotower_kv_append(const tt_kv_append_args *args, void *ws, size_t *ws_bytes,
                              void *stream) {
   tt::AppendParams p;
@@ -621,6 +681,8 @@ int64_t twotower_struct_size(int32_t which) {
     case 5: return sizeof(tt_denoise_step_args);
     case 6: return sizeof(tt_lm_head_unmask_args);
     case 7: return sizeof(tt_kv_append_args);
+    case 8: return sizeof(tt_mask_corrupt_args);
+    case 9: return sizeof(tt_masked_nll_args);
     default: return -1;
   }
 }
@@ -687,6 +749,19 @@ int64_t twotower_struct_offset(int32_t which, int32_t field) {
       TT_OFF(tt_kv_append_args, block_table), TT_OFF(tt_kv_append_args, ctx_lens),
       TT_OFF(tt_kv_append_args, free_pages), TT_OFF(tt_kv_append_args, free_count),
       TT_OFF(tt_kv_append_args, status)};
+  static const int64_t cor[] = {
+      TT_OFF(tt_mask_corrupt_args, batch), TT_OFF(tt_mask_corrupt_args, S),
+      TT_OFF(tt_mask_corrupt_args, mask_id), TT_OFF(tt_mask_corrupt_args, reserved0),
+      TT_OFF(tt_mask_corrupt_args, clean), TT_OFF(tt_mask_corrupt_args, u_time),
+      TT_OFF(tt_mask_corrupt_args, u_mask), TT_OFF(tt_mask_corrupt_args, noisy),
+      TT_OFF(tt_mask_corrupt_args, masked), TT_OFF(tt_mask_corrupt_args, t_out)};
+  static const int64_t nll[] = {
+      TT_OFF(tt_masked_nll_args, batch), TT_OFF(tt_masked_nll_args, S),
+      TT_OFF(tt_masked_nll_args, vocab), TT_OFF(tt_masked_nll_args, reserved0),
+      TT_OFF(tt_masked_nll_args, ld), TT_OFF(tt_masked_nll_args, logits),
+      TT_OFF(tt_masked_nll_args, targets), TT_OFF(tt_masked_nll_args, masked),
+      TT_OFF(tt_masked_nll_args, nll), TT_OFF(tt_masked_nll_args, loss),
+      TT_OFF(tt_masked_nll_args, n_masked)};
   const int64_t *tab = nullptr;
   int n = 0;
   switch (which) {
@@ -698,6 +773,8 @@ int64_t twotower_struct_offset(int32_t which, int32_t field) {
     case 5: tab = step; n = sizeof(step) / sizeof(step[0]); break;
     case 6: tab = lmu; n = sizeof(lmu) / sizeof(lmu[0]); break;
     case 7: tab = app; n = sizeof(app) / sizeof(app[0]); break;
+    case 8: tab = cor; n = sizeof(cor) / sizeof(cor[0]); break;
+    case 9: tab = nll; n = sizeof(nll) / sizeof(nll[0]); break;
     default: return -1;
   }
   if (field < 0 || field >= n) return -1;

@@ -47,6 +47,26 @@ struct UnmaskParams {
 };
 
 hipError_t launch_unmask(const UnmaskParams &p, hipStream_t stream);
+// Masked-diffusion loss: NLL of the targets at the masked rows of p.logits (row triples in
+// p.part as for the unmasking), its mean over the masked rows, and the linear-schedule corruption.
+struct NllParams {
+  const int32_t *targets;  // [B*S]
+  float *nll;              // [B*S] out, 0 at rows not masked
+  float *loss;             // [1] out (may be null): mean over masked rows, 0 if none
+  int32_t *count;          // [1] out (may be null): masked rows
+};
+hipError_t launch_masked_nll(const UnmaskParams &p, const NllParams &q, hipStream_t stream);
+
+struct CorruptParams {
+  const int32_t *clean;
+  const float *u_time, *u_mask;
+  int32_t *noisy;
+  uint8_t *masked;
+  float *t;  // may be null
+  int B, S, mask_id;
+};
+hipError_t launch_mask_corrupt(const CorruptParams &p, hipStream_t stream);
+
 // Decisions from per-row tile triples already in p.part ([B*S, chunks, 4]), e.g. written by the
 // EPI_UNMASK linear epilogue.
 hipError_t launch_unmask_tiles_finalize(const UnmaskParams &p, hipStream_t stream);

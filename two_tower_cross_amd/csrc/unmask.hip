@@ -176,16 +176,95 @@ __global__ __launch_bounds__(1024) void unmask_tiles_finalize_kernel(UnmaskParam
   if (wave == 0) commit_decisions(p, b, lane, lane < p.S ? rows[lane] : empty_triple());
 }
 
-hipError_t launch_unmask(const UnmaskParams &p, hipStream_t stream) {
+// ------------------------------------------------------------------ masked-diffusion loss
+// (explainer, "Training und Konditionierung", masked-diffusion paragraph: clean blocks are
+// corrupted by replacing tokens with [MASK] on a linear schedule and the denoiser minimizes the
+// negative log-likelihood of the original tokens at the masked positions.)
+
+// Linear schedule: sequence b draws its time t = u_time[b] in [0, 1) and each position is masked
+// independently with probability t, i.e. iff u_mask[b, i] < t (the uniform draws are inputs).
+__global__ __launch_bounds__(256) void mask_corrupt_kernel(CorruptParams p) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= p.B * p.S) return;
+  const int b = e / p.S;
+  const float t = p.u_time[b];
+  const bool m = p.u_mask[e] < t;
+  p.noisy[e] = m ? p.mask_id : p.clean[e];
+  p.masked[e] = m ? 1 : 0;
+  if (p.t && e % p.S == 0) p.t[b] = t;
+}
+
+// NLL of the target token at every masked row, nll = ln(sum_j exp(x_j)) - x_target, from the
+// rows' chunk triples (one thread per row, chunks merged in order), then the mean over the masked
+// rows of the whole batch with a fixed-order reduction (wave butterflies, then the waves in order).
+// A target outside the vocabulary gives NaN.
+__global__ __launch_bounds__(1024) void nll_finalize_kernel(UnmaskParams p, NllParams q) {
+  __shared__ float wsum[16];
+  __shared__ int wcnt[16];
+  const int rows = p.B * p.S;
+  const int tid = threadIdx.x;
+  float s = 0.f;
+  int cnt = 0;
+  for (int row = tid; row < rows; row += 1024) {
+    float nll = 0.f;
+    if (p.masked[row] != 0) {
+      Triple t = empty_triple();
+      for (int c = 0; c < p.chunks; ++c)
+        t = merge(t, load_triple(p.part + ((size_t)row * p.chunks + c) * 4));
+      const int tg = q.targets[row];
+      const float x = (unsigned)tg < (unsigned)p.vocab ? p.logits[(size_t)row * p.ld + tg] : NAN;
+      nll = (t.m - x) + logf(t.z);
+      s += nll;
+      cnt += 1;
+    }
+    q.nll[row] = nll;
+  }
+  s = wave_sum(s);
+  for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+  if ((tid & 63) == 0) {
+    wsum[tid >> 6] = s;
+    wcnt[tid >> 6] = cnt;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float tot = 0.f;
+    int n = 0;
+    for (int w = 0; w < 16; ++w) {
+      tot += wsum[w];
+      n += wcnt[w];
+    }
+    if (q.loss) *q.loss = n > 0 ? tot / (float)n : 0.f;
+    if (q.count) *q.count = n;
+  }
+}
+
+static hipError_t launch_row_triples(const UnmaskParams &p, hipStream_t stream) {
   const bool vec = (p.ld % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.logits) & 15) == 0);
   dim3 grid(p.chunks, p.B * p.S);
   if (vec)
     hipLaunchKernelGGL(unmask_partial_kernel<true>, grid, dim3(kUThreads), 0, stream, p);
   else
     hipLaunchKernelGGL(unmask_partial_kernel<false>, grid, dim3(kUThreads), 0, stream, p);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_unmask(const UnmaskParams &p, hipStream_t stream) {
+  hipError_t e = launch_row_triples(p, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(unmask_finalize_kernel, dim3(p.B), dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_masked_nll(const UnmaskParams &p, const NllParams &q, hipStream_t stream) {
+  hipError_t e = launch_row_triples(p, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(nll_finalize_kernel, dim3(1), dim3(1024), 0, stream, p, q);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_corrupt(const CorruptParams &p, hipStream_t stream) {
+  const int n = p.B * p.S;
+  hipLaunchKernelGGL(mask_corrupt_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
