@@ -82,7 +82,7 @@ typedef enum { TT_FP32 = 0, TT_BF16 = 1 } tt_dtype;
  *
  * Supported: dtype TT_BF16 (bf16 MFMA, fp32 softmax and accumulation, probabilities rounded to
  * bf16 for the PV product) or TT_FP32 (fp32 throughout); out_dtype TT_FP32, or equal to dtype.
- * head_dim in {64, 128}; 1 <= S <= 64; num_q_heads % num_kv_heads == 0; page_size a positive
+ * head_dim in {64, 128}; 1 <= S <= 256; num_q_heads % num_kv_heads == 0; page_size a positive
  * multiple of 64; max_ctx_len <= max_pages_per_seq * page_size. Pointers 16-byte aligned.
  * Unsupported shapes return TT_ENOTSUP.
  *
@@ -131,7 +131,7 @@ typedef struct {
  *   masked uint8 [batch, S] (in/out); tokens int32 [batch, S] (in/out);
  *   confidence fp32 [batch, S] (optional out, written for positions masked on entry);
  *   n_committed int32 [batch] (optional out).
- * Supported: 1 <= S <= 64, 1 <= vocab < 2^31, ld >= vocab. Logits must be finite.
+ * Supported: 1 <= S <= 256, 1 <= vocab < 2^31, ld >= vocab. Logits must be finite.
  */
 typedef struct {
   int32_t batch, S, vocab;

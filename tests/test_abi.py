@@ -93,7 +93,7 @@ def test_attention_workspace_too_small_reports_size():
 
 @pytest.mark.parametrize("over,code", [
     (dict(head_dim=96), _lib.TT_ENOTSUP),
-    (dict(S=65), _lib.TT_ENOTSUP),
+    (dict(S=257), _lib.TT_ENOTSUP),
     (dict(page_size=100, max_ctx_len=100), _lib.TT_ENOTSUP),
     (dict(out_dtype=_lib.TT_BF16, dtype=_lib.TT_FP32), _lib.TT_ENOTSUP),
     (dict(num_q_heads=31), _lib.TT_EINVAL),
@@ -125,7 +125,7 @@ def unmask_args(**over):
 def test_unmask_workspace_and_errors():
     st, n = query("twotower_unmask", unmask_args())
     assert st == _lib.TT_OK and n == 8 * 16 * 16 * 16
-    for over, code in [(dict(S=65), _lib.TT_ENOTSUP), (dict(ld=100), _lib.TT_EINVAL),
+    for over, code in [(dict(S=257), _lib.TT_ENOTSUP), (dict(ld=100), _lib.TT_EINVAL),
                        (dict(threshold=float("nan")), _lib.TT_EINVAL),
                        (dict(tokens=None), _lib.TT_EINVAL), (dict(vocab=0), _lib.TT_EINVAL),
                        (dict(tokens=FAKE + 2), _lib.TT_EINVAL)]:
@@ -181,7 +181,7 @@ def test_lm_head_unmask_workspace_and_errors():
     assert st == _lib.TT_OK and n == 128 * 512 * 16
     assert query("twotower_lm_head_unmask", lm_unmask_args(lm__logits=None, lm__ld=0))[0] == _lib.TT_OK
     for over, code in [(dict(lm__rows=127), _lib.TT_EINVAL),          # rows != batch * S
-                       (dict(unmask__S=65, lm__rows=8 * 65), _lib.TT_ENOTSUP),
+                       (dict(unmask__S=257, lm__rows=8 * 257), _lib.TT_ENOTSUP),
                        (dict(lm__ld=131070), _lib.TT_EINVAL),
                        (dict(lm__vocab=131074, lm__ld=131076), _lib.TT_ENOTSUP),
                        (dict(lm__h=FAKE + 8), _lib.TT_EINVAL),

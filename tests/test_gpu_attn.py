@@ -158,8 +158,11 @@ def test_split_count_only_changes_rounding():
     (1, 8, 1, 128),     # a single block position
     (5, 6, 2, 64),      # rows = 15, head_dim 64
     (32, 32, 2, 128),   # 512 rows: two row groups per KV head
-    (64, 4, 1, 64),     # the largest block
+    (64, 4, 1, 64),
     (16, 16, 1, 64),
+    (128, 32, 2, 128),  # block size 128: two block-key tiles, 2048 rows = 8 row groups
+    (100, 8, 2, 128),   # block keys 64 + 36, S not a multiple of 8 (scalar block-V loads)
+    (256, 4, 1, 64),    # the largest block: four block-key tiles
 ])
 def test_shapes_bf16(S, Hq, Hkv, D):
     case = synth.attn_case(60 + S, B=2, S=S, Hq=Hq, Hkv=Hkv, D=D, ctx_lens=[333, 1200],
@@ -169,7 +172,7 @@ def test_shapes_bf16(S, Hq, Hkv, D):
         check(case, out, lse, TOL_BF16)
 
 
-@pytest.mark.parametrize("S,Hq,Hkv,D", [(16, 8, 2, 128), (3, 3, 1, 64)])
+@pytest.mark.parametrize("S,Hq,Hkv,D", [(16, 8, 2, 128), (3, 3, 1, 64), (128, 4, 2, 64)])
 def test_shapes_fp32(S, Hq, Hkv, D):
     case = synth.attn_case(70 + S, B=2, S=S, Hq=Hq, Hkv=Hkv, D=D, ctx_lens=[300, 5],
                            page_size=64, dtype="fp32")

@@ -60,6 +60,7 @@ CASES = [
     (8, 16, 2048, 131072, 1.0, 0.9, 0.0, True, False),   # the 32K loop's lm-head: fallback only
     (4, 16, 264, 4096, 5.0, 0.5, 0.5, False, False),
     (2, 64, 128, 2048, 2.0, 0.3, 0.2, True, True),       # commit-all, 64 positions
+    (2, 128, 256, 2048, 3.0, 0.2, 0.3, True, False),     # block size 128 (two row tiles)
 ]
 
 

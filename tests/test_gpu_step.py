@@ -234,3 +234,24 @@ def test_full_size_loop_32k_one_block():
     ref = ostep.lm_head(f64(step.h_work), f64(m.w_lm[torch.from_numpy(cols).to(DEV)]))
     got = f64(step.logits)[..., cols]
     assert max_abs(got, ref) <= 1e-4 + 1e-5 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("S", [32, 128])
+def test_block_sizes_of_the_pages(S):
+    """The block sizes the pages train and sample with besides 16 (32 in training, 128 at
+    sampling): a block decodes to completion and the last layer's attention matches the oracle."""
+    m = loop_model(9 + S, B=2, S=S, L=700, layers=2, Hq=8, Hkv=2, D=128, hidden=256, vocab=2048,
+                   T=4, device=DEV)
+    step = make_step(m)
+    masked, tokens, per_step, _ = run_block(m, step)
+    assert not masked.any() and (per_step >= 1).all() and (per_step.sum(0) == S).all()
+    l = m.layers - 1
+    for b, g in ((0, 0), (1, 1)):
+        heads = slice(g * (m.Hq // m.Hkv), (g + 1) * (m.Hq // m.Hkv))
+        ref, _ = oattn.block_attention(
+            f64(step.q[b:b + 1, :, heads]), f64(m.k_pages[l][b:b + 1, g:g + 1]),
+            f64(m.v_pages[l][b:b + 1, g:g + 1]), np.zeros((1, 1), np.int32),
+            np.array([m.L], np.int32), f64(step.k_blk[l][b:b + 1, g:g + 1]),
+            f64(step.v_blk[l][b:b + 1, g:g + 1]), 1.0 / math.sqrt(m.D))
+        ref16 = torch.from_numpy(ref).to(torch.bfloat16).double().numpy()
+        assert max_abs(f64(step.attn_out[b:b + 1, :, heads]), ref16) <= TOL_BF16

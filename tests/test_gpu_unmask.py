@@ -122,3 +122,19 @@ def test_vocab_sizes_and_row_strides(V, pad):
     np.testing.assert_array_equal(t.cpu().numpy(), ot)
     np.testing.assert_array_equal(m.cpu().numpy(), om)
     np.testing.assert_allclose(conf.cpu().numpy()[masked == 1], oc[masked == 1], rtol=1e-5)
+
+
+@pytest.mark.parametrize("S", [65, 128, 256])
+def test_blocks_larger_than_a_wavefront(S):
+    """Block sizes 32 / 128 of the pages and up to 256: the decisions span several wavefronts."""
+    B, V = 3, 4096
+    make = lambda s: synth.logits_planted(s, B, S, V, 2.0, 0.05, 0.95)
+    g = synth.rng(90 + S)
+    masked = (g.random((B, S)) < 0.8).astype(np.uint8)
+    x = guarded_logits(make, 0.9, 91 + S, min_commit=True, masked=masked)
+    tokens = g.integers(0, V, size=(B, S)).astype(np.int32)
+    compare(x, masked, tokens, 0.9, min_commit=True)
+    # the fallback, with the best position in a later wavefront
+    y = synth.logits_normal(95 + S, 1, S, V, 1.0)
+    y[0, S - 3, 11] = 12.0
+    compare(y, np.ones((1, S), np.uint8), np.full((1, S), -1, np.int32), 0.999, min_commit=True)

@@ -43,7 +43,7 @@ tt_status plan_attn(const tt_block_attn_args *a, bool check_pointers, AttnPlan *
   if ((int64_t)a->max_ctx_len > (int64_t)a->max_pages_per_seq * a->page_size) return TT_EINVAL;
   if (a->num_splits < 0) return TT_EINVAL;
   if (a->head_dim != 64 && a->head_dim != 128) return TT_ENOTSUP;
-  if (a->S > 64) return TT_ENOTSUP;
+  if (a->S > 256) return TT_ENOTSUP;
   if (a->page_size % 64 != 0) return TT_ENOTSUP;
   // 64-token tiles of either pool are indexed with 32-bit integers
   if ((int64_t)a->num_pages * a->num_kv_heads * (a->page_size / 64) > INT32_MAX) return TT_ENOTSUP;
@@ -147,8 +147,9 @@ struct UnmaskPlan {
   size_t ws_bytes = 0;
 };
 
-// max_S: the decisions run one wavefront per sequence (S <= 64); the loss has no such limit.
-tt_status plan_unmask(const tt_unmask_args *a, bool check_logits, UnmaskPlan *out, int max_S = 64) {
+// max_S: the decisions run one work-group of 256 threads per sequence (S <= 256); the loss has no
+// such limit.
+tt_status plan_unmask(const tt_unmask_args *a, bool check_logits, UnmaskPlan *out, int max_S = 256) {
   if (!a) return TT_EINVAL;
   if (a->batch < 0 || a->S < 1 || a->vocab < 1 || a->ld < a->vocab) return TT_EINVAL;
   if (std::isnan(a->threshold)) return TT_EINVAL;

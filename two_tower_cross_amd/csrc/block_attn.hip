@@ -184,7 +184,7 @@ __device__ void load_tail_tile(char *smem, int s, const uint16_t *kbase, const u
 // gathered element by element. Loads are issued before stores (one memory round trip).
 template <int D>
 __device__ void load_block_tile(char *smem, int s, const uint16_t *kblk, const uint16_t *vblk,
-                                int S, int tid) {
+                                int S, int vstride, int tid) {
   constexpr int KC = D / 8;
   constexpr int NK = kTile * KC / kThreads, NV = D * 8 / kThreads;
   uint16_t *ks = reinterpret_cast<uint16_t *>(smem + Geom<D>::koff(s));
@@ -196,11 +196,11 @@ __device__ void load_block_tile(char *smem, int s, const uint16_t *kblk, const u
     const int f = tid + j * kThreads, r = f / KC, c = f % KC;
     xk[j] = r < S ? ld_global_16(kblk + (size_t)r * D + c * 8) : z;
   }
-  if ((S & 7) == 0) {
+  if ((S & 7) == 0 && (vstride & 7) == 0) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int f = tid + j * kThreads, d = f / 8, c = f % 8;
-      xv[j] = c * 8 < S ? ld_global_16(vblk + (size_t)d * S + c * 8) : z;
+      xv[j] = c * 8 < S ? ld_global_16(vblk + (size_t)d * vstride + c * 8) : z;
     }
   } else {
 #pragma unroll
@@ -208,7 +208,8 @@ __device__ void load_block_tile(char *smem, int s, const uint16_t *kblk, const u
       const int f = tid + j * kThreads, d = f / 8, c = f % 8;
       uint16_t e[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) e[i] = c * 8 + i < S ? vblk[(size_t)d * S + c * 8 + i] : (uint16_t)0;
+      for (int i = 0; i < 8; ++i)
+        e[i] = c * 8 + i < S ? vblk[(size_t)d * vstride + c * 8 + i] : (uint16_t)0;
 #pragma unroll
       for (int w = 0; w < 4; ++w) xv[j][w] = (uint32_t)e[2 * w] | ((uint32_t)e[2 * w + 1] << 16);
     }
@@ -550,13 +551,13 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
     for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = row_ok ? ld_global_16(qrow + kk * 16 + hh * 8) : z;
   }
 
-  // The block's own keys (partition 0) go through the last stage; their loads complete before any
-  // context DMA is issued, so the ring's vmcnt waits count DMA only.
-  if (has_block) {
-    const size_t bg = (size_t)b * p.Hkv + g;
-    load_block_tile<D>(smem, kStages - 1, static_cast<const uint16_t *>(p.k_blk) + bg * p.S * D,
-                       static_cast<const uint16_t *>(p.v_blk) + bg * D * p.S, p.S, tid);
-  }
+  // The block's own keys (partition 0) go through the last stage, 64 at a time; the first tile's
+  // loads complete before any context DMA is issued (later block tiles wait for the ring's first
+  // DMA too, which only makes the ring's vmcnt waits stricter).
+  const size_t bg = (size_t)b * p.Hkv + g;
+  const uint16_t *kblk = static_cast<const uint16_t *>(p.k_blk) + bg * p.S * D;
+  const uint16_t *vblk = static_cast<const uint16_t *>(p.v_blk) + bg * D * p.S;
+  if (has_block) load_block_tile<D>(smem, kStages - 1, kblk, vblk, min(p.S, kTile), p.S, tid);
 
   // Start the ring: context tiles 0 .. kStages-2 into stages 0 .. kStages-2.
 #pragma unroll
@@ -570,10 +571,17 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   const float c = p.scale * kLog2e;
 
   if (has_block) {
-    lds_barrier();
-    if (wave_active)
-      attend_tile<D, false>(smem, Geom<D>::koff(kStages - 1), Geom<D>::voff(kStages - 1) -
-                            Geom<D>::VBASE, p.S, lm, qreg, oacc, m, lpart, c, lane);
+    for (int j0 = 0; j0 < p.S; j0 += kTile) {
+      const int nj = min(kTile, p.S - j0);
+      if (j0 > 0) {
+        lds_barrier();  // every wave is done with the previous block tile
+        load_block_tile<D>(smem, kStages - 1, kblk + (size_t)j0 * D, vblk + j0, nj, p.S, tid);
+      }
+      lds_barrier();
+      if (wave_active)
+        attend_tile<D, false>(smem, Geom<D>::koff(kStages - 1), Geom<D>::voff(kStages - 1) -
+                              Geom<D>::VBASE, nj, lm, qreg, oacc, m, lpart, c, lane);
+    }
   }
 
   if (n_full_ok > 0) {

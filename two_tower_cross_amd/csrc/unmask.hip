@@ -86,31 +86,53 @@ __global__ __launch_bounds__(kUThreads) void unmask_partial_kernel(UnmaskParams 
   }
 }
 
-// Decisions of sequence b from the row triples, one lane per block position i (wave-wide, every
-// lane of the wave calls it): confidence = 1 / z, commit iff confidence > threshold (or commit-all),
-// the one-commit fallback by ballot, then the state update.
+// Decisions of sequence b from the row triples, thread i of the work-group = block position i
+// (every thread of the work-group calls it; positions are i < S <= kDecThreads): confidence = 1 / z,
+// commit iff confidence > threshold (or commit-all), the one-commit fallback (largest
+// confidence, lowest position on ties) through per-wave reductions in LDS, then the state update.
+constexpr int kDecThreads = 256;  // largest block size S
+
 __device__ __forceinline__ void commit_decisions(const UnmaskParams &p, int b, int i, Triple t) {
+  __shared__ int any_commit_w[kDecThreads / 64], any_masked_w[kDecThreads / 64];
+  __shared__ float best_c[kDecThreads / 64];
+  __shared__ int best_i[kDecThreads / 64], n_w[kDecThreads / 64];
+  const int lane = i & 63, w = i >> 6;
   const bool in = i < p.S;
   const size_t row = (size_t)b * p.S + i;
   const bool was_masked = in && p.masked[row] != 0;
   const float conf = was_masked ? 1.0f / t.z : -1.0f;
   bool commit = was_masked && (p.commit_all || conf > p.threshold);
-  const unsigned long long any_commit = __ballot(commit);
-  const unsigned long long any_masked = __ballot(was_masked);
-  if (!any_commit && p.min_commit && any_masked) {
-    // largest confidence, lowest position on ties
-    float bc = conf;
-    int bi = was_masked ? i : 0x7fffffff;
-    for (int o = 1; o < 64; o <<= 1) {
-      const float oc = __shfl_xor(bc, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (oc > bc || (oc == bc && oi < bi)) {
-        bc = oc;
-        bi = oi;
-      }
+  // the wave's best candidate for the fallback: largest confidence, lowest position on ties
+  float bc = conf;
+  int bi = was_masked ? i : 0x7fffffff;
+  for (int o = 1; o < 64; o <<= 1) {
+    const float oc = __shfl_xor(bc, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (oc > bc || (oc == bc && oi < bi)) {
+      bc = oc;
+      bi = oi;
     }
-    commit = was_masked && i == bi;
   }
+  const bool wc = __ballot(commit) != 0, wm = __ballot(was_masked) != 0;  // whole wave
+  if (lane == 0 && w < kDecThreads / 64) {
+    any_commit_w[w] = wc;
+    any_masked_w[w] = wm;
+    best_c[w] = bc;
+    best_i[w] = bi;
+  }
+  __syncthreads();
+  bool any_commit = false, any_masked = false;
+  float gc = -1.0f;
+  int gi = 0x7fffffff;
+  for (int k = 0; k < kDecThreads / 64; ++k) {  // in wave order: ties keep the lower position
+    any_commit = any_commit || any_commit_w[k];
+    any_masked = any_masked || any_masked_w[k];
+    if (best_c[k] > gc || (best_c[k] == gc && best_i[k] < gi)) {
+      gc = best_c[k];
+      gi = best_i[k];
+    }
+  }
+  if (!any_commit && p.min_commit && any_masked) commit = was_masked && i == gi;
   if (was_masked) {
     if (p.confidence) p.confidence[row] = conf;
     if (commit) {
@@ -119,7 +141,13 @@ __device__ __forceinline__ void commit_decisions(const UnmaskParams &p, int b, i
     }
   }
   const unsigned long long committed = __ballot(commit);
-  if (i == 0 && p.n_committed) p.n_committed[b] = __popcll(committed);
+  if (lane == 0 && w < kDecThreads / 64) n_w[w] = __popcll(committed);
+  __syncthreads();
+  if (i == 0 && p.n_committed) {
+    int n = 0;
+    for (int k = 0; k < kDecThreads / 64; ++k) n += n_w[k];
+    p.n_committed[b] = n;
+  }
 }
 
 __device__ __forceinline__ Triple load_triple(const float *o) {
@@ -130,8 +158,8 @@ __device__ __forceinline__ Triple load_triple(const float *o) {
   return u;
 }
 
-// A few chunk triples per row (8192-logit chunks): lane i merges the triples of position i.
-__global__ __launch_bounds__(64) void unmask_finalize_kernel(UnmaskParams p) {
+// A few chunk triples per row (8192-logit chunks): thread i merges the triples of position i.
+__global__ __launch_bounds__(kDecThreads) void unmask_finalize_kernel(UnmaskParams p) {
   const int b = blockIdx.x;
   const int i = threadIdx.x;
   const size_t row = (size_t)b * p.S + i;
@@ -142,9 +170,9 @@ __global__ __launch_bounds__(64) void unmask_finalize_kernel(UnmaskParams p) {
 }
 
 // Many tile triples per row (one per 256-logit lm-head tile): wave w merges rows w, w + 16, ...
-// with its 64 lanes (strided, then a butterfly), and wave 0 takes the decisions.
+// with its 64 lanes (strided, then a butterfly), then threads 0 .. 255 take the decisions.
 __global__ __launch_bounds__(1024) void unmask_tiles_finalize_kernel(UnmaskParams p) {
-  __shared__ Triple rows[64];
+  __shared__ Triple rows[kDecThreads];
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int i = wave; i < p.S; i += 16) {
@@ -173,7 +201,8 @@ __global__ __launch_bounds__(1024) void unmask_tiles_finalize_kernel(UnmaskParam
     if (lane == 0) rows[i] = t;
   }
   __syncthreads();
-  if (wave == 0) commit_decisions(p, b, lane, lane < p.S ? rows[lane] : empty_triple());
+  const int i = threadIdx.x;
+  commit_decisions(p, b, i, i < p.S ? rows[i] : empty_triple());
 }
 
 // ------------------------------------------------------------------ masked-diffusion loss
@@ -251,7 +280,7 @@ static hipError_t launch_row_triples(const UnmaskParams &p, hipStream_t stream) 
 hipError_t launch_unmask(const UnmaskParams &p, hipStream_t stream) {
   hipError_t e = launch_row_triples(p, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(unmask_finalize_kernel, dim3(p.B), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL(unmask_finalize_kernel, dim3(p.B), dim3(kDecThreads), 0, stream, p);
   return hipGetLastError();
 }
 
