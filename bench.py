@@ -27,6 +27,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0   # dense bf16
 THRESHOLD = 0.9
 ATTN_SOURCE = os.path.join(ROOT, "two_tower_cross_amd", "csrc", "block_attn.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "block_attn_bf16_128_loop32k_traffic.md")
@@ -39,6 +40,11 @@ def attn_bytes_per_launch(B, L, S, Hq, Hkv, D, e=2):
     blk = 2 * B * Hkv * S * D * e
     q = B * S * Hq * D * e
     return ctx + blk + q
+
+
+def attn_flops_per_launch(B, L, S, Hq, D):
+    """QK^T and PV over every (context + block) key of every query row: 4 flops per row, key, dim."""
+    return 4 * B * Hq * S * (L + S) * D
 
 
 def cpu_baseline(m, threads_note, steps=2):
@@ -101,6 +107,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true",
                     help="do not record per-launch attention events")
+    ap.add_argument("--block-size", type=int, default=16, metavar="S",
+                    help="block size S (16 is the benchmark's workload; the pages also use 32 and "
+                         "128)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed region, copy MIB MiB device to device once (the plain "
                          "copy of known size that scales the HBM byte counters)")
@@ -115,7 +124,7 @@ def main():
     from synth.device import loop_model
 
     dev = torch.device("cuda", 0)
-    m = loop_model(5, device=dev)
+    m = loop_model(5, S=args.block_size, device=dev)
     step = tt.DenoiseStep(k_pages=m.k_pages, v_pages=m.v_pages, w_qkv=m.w_qkv, w_o=m.w_o,
                           w_lm=m.w_lm, block_table=m.block_table, ctx_lens=m.ctx_lens,
                           max_ctx_len=m.L, num_q_heads=m.Hq, num_kv_heads=m.Hkv, head_dim=m.D,
@@ -169,12 +178,20 @@ def main():
         durs = [events[2 * i].elapsed_time(events[2 * i + 1]) for i in range(len(events) // 2)]
         attn_us = 1e3 * sum(durs) / len(durs)
         nbytes = attn_bytes_per_launch(m.B, m.L, m.S, m.Hq, m.Hkv, m.D)
-        achieved = nbytes / (attn_us * 1e-6) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                    "traffic": measured_traffic(),
-                    "kernel": "block_attn_bf16_kernel<128>", "launch_us": round(attn_us, 2),
-                    "bytes_per_launch": nbytes}
+        flops = attn_flops_per_launch(m.B, m.L, m.S, m.Hq, m.D)
+        if flops / nbytes <= MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
+            achieved = nbytes / (attn_us * 1e-6) / 1e9
+            roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                        "traffic": measured_traffic() if m.S == 16 else None,
+                        "kernel": "block_attn_bf16_kernel<128>", "launch_us": round(attn_us, 2),
+                        "bytes_per_launch": nbytes}
+        else:   # past the ridge (larger blocks): the matrix cores bound the kernel
+            achieved = flops / (attn_us * 1e-6) / 1e12
+            roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
+                        "traffic": None, "kernel": "block_attn_bf16_kernel<128>",
+                        "launch_us": round(attn_us, 2), "flops_per_launch": flops}
 
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
@@ -202,12 +219,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded on-device N(0,1) KV caches, hidden states and scaled weights)",
-        "config": {"workload": "block loop: batch 8, 6 attention layers, context 32768, S=16, "
+        "config": {"workload": f"block loop: batch 8, 6 attention layers, context 32768, S={m.S}, "
                                "T=16, hidden 2048, Hq 32 / Hkv 2, head_dim 128, vocab 131072, "
                                "threshold 0.9", "global_batch": m.B, "seq_len": m.L,
                    "parallelism": "single GPU"},
-        "attn_GBps": None if roofline is None else roofline["achieved"],
-        "attn_frac_of_hbm_peak": None if roofline is None else roofline["frac"],
+        "attn_GBps": (None if roofline is None else
+                      round(attn_bytes_per_launch(m.B, m.L, m.S, m.Hq, m.Hkv, m.D) / attn_us / 1e3, 1)),
+        "attn_frac_of_hbm_peak": (None if roofline is None else
+                                  round(attn_bytes_per_launch(m.B, m.L, m.S, m.Hq, m.Hkv, m.D)
+                                        / attn_us / 1e3 / HBM_PEAK_GBPS, 4)),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

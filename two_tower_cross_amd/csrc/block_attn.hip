@@ -472,8 +472,14 @@ __device__ __forceinline__ void pipe_finish(const PipeRegs<D> &r, f32x16 *oacc) 
 template <int D>
 __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  const int split = blockIdx.x;
-  const int item_bgr = blockIdx.y;
+  // Work-groups are dealt to the 8 XCDs round robin (work-group id mod 8). The row groups of one
+  // (sequence, KV head, partition) read the same KV, so they get ids 8 apart: one XCD, adjacent
+  // in its dispatch order, one L2 serving them all.
+  const int id = blockIdx.x, R = p.row_groups;
+  const int q = (id >> 3) / R * 8 + (id & 7);  // (sequence, KV head, partition) unit
+  if (q >= p.B * p.Hkv * p.splits) return;
+  const int split = q % p.splits;
+  const int item_bgr = q / p.splits * R + (id >> 3) % R;
   const int rg = item_bgr % p.row_groups;
   const int g = (item_bgr / p.row_groups) % p.Hkv;
   const int b = item_bgr / (p.row_groups * p.Hkv);
@@ -906,7 +912,8 @@ __global__ __launch_bounds__(256) void block_attn_f32_kernel(AttnParams p) {
 
 hipError_t launch_block_attn_bf16(const AttnParams &p, hipStream_t stream, hipEvent_t ev_begin,
                                   hipEvent_t ev_end) {
-  dim3 grid(p.splits, p.B * p.Hkv * p.row_groups);
+  const int units = p.B * p.Hkv * p.splits;
+  dim3 grid((unsigned)((units + 7) / 8 * 8 * p.row_groups));
   hipError_t e = hipSuccess;
   if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess) return e;
   if (p.D == 128) {
