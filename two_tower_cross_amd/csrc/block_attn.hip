@@ -179,18 +179,24 @@ __device__ void load_tail_tile(char *smem, int s, const uint16_t *kbase, const u
   }
 }
 
-// The block's own S keys/values of (b, g) into LDS stage s; tokens >= S are zero. K rows are
-// contiguous ([S][D]); a V row holds S tokens ([D][S]), 16-byte aligned when S % 8 == 0, else
-// gathered element by element. Loads are issued before stores (one memory round trip).
+// The block's own keys/values of (b, g), 64 at a time, through registers into LDS stage s; tokens
+// past the count are zero. K rows are contiguous ([S][D]); a V row holds S tokens ([D][S]),
+// 16-byte aligned when S % 8 == 0, else gathered element by element. The fetch is split from the
+// store so that the first tile's loads can be in flight with the kernel's other first loads.
 template <int D>
-__device__ void load_block_tile(char *smem, int s, const uint16_t *kblk, const uint16_t *vblk,
-                                int S, int vstride, int tid) {
-  constexpr int KC = D / 8;
-  constexpr int NK = kTile * KC / kThreads, NV = D * 8 / kThreads;
-  uint16_t *ks = reinterpret_cast<uint16_t *>(smem + Geom<D>::koff(s));
-  uint16_t *vs = reinterpret_cast<uint16_t *>(smem + Geom<D>::voff(s));
-  const u32x4 z = {0u, 0u, 0u, 0u};
+struct BlockRegs {
+  static constexpr int NK = kTile * (D / 8) / kThreads, NV = D * 8 / kThreads;
   u32x4 xk[NK], xv[NV];
+};
+
+// Block keys/values rows 0 .. S-1 (S <= 64) into registers, zero past S.
+template <int D>
+__device__ __forceinline__ void fetch_block_tile(BlockRegs<D> &br, const uint16_t *kblk,
+                                                 const uint16_t *vblk, int S, int vstride, int tid) {
+  constexpr int KC = D / 8;
+  constexpr int NK = BlockRegs<D>::NK, NV = BlockRegs<D>::NV;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  u32x4 *xk = br.xk, *xv = br.xv;
 #pragma unroll
   for (int j = 0; j < NK; ++j) {
     const int f = tid + j * kThreads, r = f / KC, c = f % KC;
@@ -214,6 +220,16 @@ __device__ void load_block_tile(char *smem, int s, const uint16_t *kblk, const u
       for (int w = 0; w < 4; ++w) xv[j][w] = (uint32_t)e[2 * w] | ((uint32_t)e[2 * w + 1] << 16);
     }
   }
+}
+
+// ... then into LDS stage s (swizzled like the ring's tiles).
+template <int D>
+__device__ __forceinline__ void store_block_tile(char *smem, int s, const BlockRegs<D> &br, int tid) {
+  constexpr int KC = D / 8;
+  constexpr int NK = BlockRegs<D>::NK, NV = BlockRegs<D>::NV;
+  uint16_t *ks = reinterpret_cast<uint16_t *>(smem + Geom<D>::koff(s));
+  uint16_t *vs = reinterpret_cast<uint16_t *>(smem + Geom<D>::voff(s));
+  const u32x4 *xk = br.xk, *xv = br.xv;
 #pragma unroll
   for (int j = 0; j < NK; ++j) {
     const int f = tid + j * kThreads, r = f / KC, c = f % KC;
@@ -486,19 +502,49 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
+  const bool has_block = split == 0;
+  const int t_begin = split * p.chunk;
+
+  // Everything that does not depend on the sequence length is requested at once with it (one
+  // memory round trip): the length, this wave's query rows, the first block tile (partition 0)
+  // and the page of every tile the partition can hold (clamped to the table; entries past the
+  // sequence's end are loaded but not used).
   const int L = p.ctx_lens[b];
+  const int col = lane & 31, hh = lane >> 5;
+  const int r_local = wave * 32 + col;
+  const int r = rg * p.rows_per_group + r_local;
+  const bool row_ok = r < p.rows && r_local < p.rows_per_group;
+  const bool wave_active =
+      wave * 32 < p.rows_per_group && rg * p.rows_per_group + wave * 32 < p.rows;
+  const int jq = row_ok ? r / p.S : 0, iq = row_ok ? r % p.S : 0;
+  const int h = g * p.G + jq;
+  u32x4 qreg[D / 16];
+  {
+    const uint16_t *qrow =
+        static_cast<const uint16_t *>(p.q) + (((size_t)b * p.S + iq) * p.Hq + h) * D;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = row_ok ? ld_global_16(qrow + kk * 16 + hh * 8) : z;
+  }
+  const size_t bg = (size_t)b * p.Hkv + g;
+  const uint16_t *kblk = static_cast<const uint16_t *>(p.k_blk) + bg * p.S * D;
+  const uint16_t *vblk = static_cast<const uint16_t *>(p.v_blk) + bg * D * p.S;
+  BlockRegs<D> br;
+  if (has_block) fetch_block_tile<D>(br, kblk, vblk, min(p.S, kTile), p.S, tid);
+  const int32_t *btab = p.block_table + (size_t)b * p.max_pages;
+  const int n_spec = p.chunk / kTile;               // tiles of a full partition
+  int spec_page = 0;
+  if (tid < n_spec) spec_page = btab[min((t_begin + tid * kTile) / p.page_size, p.max_pages - 1)];
+
   bool bad = L < 0 || L > p.max_ctx_len;
   const int Lc = bad ? 0 : L;
-  const int t_begin = split * p.chunk;
   const int t_end = min(Lc, t_begin + p.chunk);
-  const bool has_block = split == 0;
   if (!has_block && t_begin >= Lc && !bad) return;  // partition past this sequence's context
 
   const int n_ctx = t_end > t_begin ? t_end - t_begin : 0;
   const int n_full = n_ctx / kTile;            // full tiles: asynchronous ring
   const int tail = n_ctx - n_full * kTile;     // tokens of the last, partial tile
 
-  const int32_t *btab = p.block_table + (size_t)b * p.max_pages;
   // K and V pools are both sequences of 16 KB tiles (K [64 tokens][D], V [D][64 tokens]); context
   // tile n of this partition (tokens t_begin + 64n ...) is tile (page * Hkv + g) * (page_size / 64)
   // + (offset in page) / 64 of either pool. The partition's tile indices are staged in LDS once, so
@@ -510,7 +556,7 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   int page_bad = 0;
   for (int i = tid; i < n_tiles; i += kThreads) {
     const int t = t_begin + i * kTile;
-    const int page = btab[t / p.page_size];
+    const int page = i < kThreads ? spec_page : btab[t / p.page_size];
     page_bad |= page < 0 || page >= p.num_pages;
     tile_ids[i] = (page * p.Hkv + g) * tpp + (t % p.page_size) / kTile;
   }
@@ -539,36 +585,13 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
     dma_tile<D>(smem, stage, kpool + off, vpool + off, lm);
   };
 
-  // Query rows of this wave (B operand of S^T = K Q^T): row r -> (head j, position i).
-  const int col = lane & 31, hh = lane >> 5;
-  const int r_local = wave * 32 + col;
-  const int r = rg * p.rows_per_group + r_local;
-  const bool row_ok = r < p.rows && r_local < p.rows_per_group;
-  const bool wave_active =
-      wave * 32 < p.rows_per_group && rg * p.rows_per_group + wave * 32 < p.rows;
-  const int jq = row_ok ? r / p.S : 0, iq = row_ok ? r % p.S : 0;
-  const int h = g * p.G + jq;
-  u32x4 qreg[D / 16];
-  {
-    const uint16_t *qrow =
-        static_cast<const uint16_t *>(p.q) + (((size_t)b * p.S + iq) * p.Hq + h) * D;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = row_ok ? ld_global_16(qrow + kk * 16 + hh * 8) : z;
-  }
-
-  // The block's own keys (partition 0) go through the last stage, 64 at a time; the first tile's
-  // loads complete before any context DMA is issued (later block tiles wait for the ring's first
-  // DMA too, which only makes the ring's vmcnt waits stricter).
-  const size_t bg = (size_t)b * p.Hkv + g;
-  const uint16_t *kblk = static_cast<const uint16_t *>(p.k_blk) + bg * p.S * D;
-  const uint16_t *vblk = static_cast<const uint16_t *>(p.v_blk) + bg * D * p.S;
-  if (has_block) load_block_tile<D>(smem, kStages - 1, kblk, vblk, min(p.S, kTile), p.S, tid);
-
-  // Start the ring: context tiles 0 .. kStages-2 into stages 0 .. kStages-2.
+  // Start the ring: context tiles 0 .. kStages-2 into stages 0 .. kStages-2, then the first block
+  // tile (already in registers) into the last stage; the block tile is attended while the ring's
+  // first tiles are in flight.
 #pragma unroll
   for (int n = 0; n < kStages - 1; ++n)
     if (n < n_full_ok) dma_ctx_tile(n, n);
+  if (has_block) store_block_tile<D>(smem, kStages - 1, br, tid);
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -580,8 +603,9 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
     for (int j0 = 0; j0 < p.S; j0 += kTile) {
       const int nj = min(kTile, p.S - j0);
       if (j0 > 0) {
+        fetch_block_tile<D>(br, kblk + (size_t)j0 * D, vblk + j0, nj, p.S, tid);
         lds_barrier();  // every wave is done with the previous block tile
-        load_block_tile<D>(smem, kStages - 1, kblk + (size_t)j0 * D, vblk + j0, nj, p.S, tid);
+        store_block_tile<D>(smem, kStages - 1, br, tid);
       }
       lds_barrier();
       if (wave_active)
