@@ -32,16 +32,18 @@ constexpr int kLK = 64;          // K columns per chunk
 // reads it.
 constexpr int kNonTemporal = 2;
 
-// Two tile shapes. NB = 2: 64 output features, 4 waves = 2 slabs x 2 row halves, an 8-deep W ring
-// (64 KB) and a 6-deep X ring (96 KB) -- for the projections, with K partitioned across
-// work-groups. NB = 8: 256 output features, 8 waves of one slab x all 128 rows, 3-deep rings
-// (96 + 48 KB) -- for the lm-head, where each X chunk read through L2 then serves 4x more weights.
+// Two tile shapes, 8 waves each (a wave issues a 1 KB load only every ~100 cycles and stalls
+// meanwhile, so the ring's loads are spread over as many waves as possible). NB = 2: 64 output
+// features, the waves are 2 slabs x 4 blocks of 32 rows, an 8-deep W ring (64 KB) and a 6-deep X
+// ring (96 KB) -- for the projections, with K partitioned across work-groups. NB = 8: 256 output
+// features, 8 waves of one slab x all 128 rows, 3-deep rings (96 + 48 KB) -- for the lm-head,
+// where each X chunk read through L2 then serves 4x more weights.
 template <int NB>
 struct LTile {
   static constexpr int N = NB * 32;                       // features per work-group
-  static constexpr int WAVES = NB == 2 ? 4 : NB;
+  static constexpr int WAVES = 8;
   static constexpr int THREADS = WAVES * 64;
-  static constexpr int MB = NB == 2 ? 2 : 4;              // 32-row blocks per wave
+  static constexpr int MB = NB == 2 ? 1 : 4;              // 32-row blocks per wave
   static constexpr int WST = NB == 2 ? 8 : 3;             // W ring depth
   static constexpr int XST = NB == 2 ? 6 : 3;             // X ring depth (<= WST)
   static constexpr int WBYTES = NB * 4096;                // one W chunk
@@ -293,7 +295,7 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hh = lane >> 5;
   const int slab = NB == 2 ? (wave & 1) : wave;
-  const int mrow0 = NB == 2 ? (wave >> 1) * 64 : 0;
+  const int mrow0 = NB == 2 ? (wave >> 1) * 32 : 0;
 
   const int nch = (p.K + kLK - 1) / kLK;
   const int Ks = (p.K + 15) / 16;
