@@ -329,12 +329,13 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
               lane);
   };
   if (n > 0) {
-    // Prologue: W(0 .. WST-XST), then the pairs W(WST-XST+1+j), X(j) for j < XST-1.
+    // Prologue: W(0 .. WST-XST-1), then the pairs W(WST-XST+j), X(j) for j < XST-1, so that
+    // W(0 .. WST-2) and X(0 .. XST-2) are in flight and step 0 goes on with W(WST-1), X(XST-1).
 #pragma unroll
-    for (int c = 0; c <= T::WST - T::XST; ++c) w_issue(c);
+    for (int c = 0; c < T::WST - T::XST; ++c) w_issue(c);
 #pragma unroll
     for (int j = 0; j < T::XST - 1; ++j) {
-      w_issue(T::WST - T::XST + 1 + j);
+      w_issue(T::WST - T::XST + j);
       x_issue(j);
     }
   }
