@@ -147,15 +147,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void *w, int n
 }
 
 // W chunk c (K columns 64c .. 64c + 63) of this work-group's NB slabs -> W stage (block-major:
-// slab j at j * 4 KB, 16-column step i at i * 1 KB; a straight copy of the packed bytes).
+// slab j at j * 4 KB, 16-column step i at i * 1 KB; a straight copy of the packed bytes). With
+// real false every load goes through `none` instead (a resource with no records: nothing moves).
 template <int NB>
-__device__ __forceinline__ void w_dma(char *stage, const __amdgpu_buffer_rsrc_t *rs, int c,
-                                      int wave, int lane) {
+__device__ __forceinline__ void w_dma(char *stage, const __amdgpu_buffer_rsrc_t *rs, bool real,
+                                      __amdgpu_buffer_rsrc_t none, int c, int wave, int lane) {
   using T = LTile<NB>;
 #pragma unroll
   for (int j = 0; j < T::WLOADS; ++j) {
     const int t = j * T::WAVES + wave;  // instruction index: slab t / 4, step t % 4
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[t / 4], TT_LDS_PTR(stage + t * 1024), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(real ? rs[t / 4] : none, TT_LDS_PTR(stage + t * 1024), 16,
                                              lane * 16, c * 4096 + (t % 4) * 1024, 0,
                                              kNonTemporal);
   }
@@ -317,16 +318,20 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void *>(p.x), (short)0, p.M * p.K * 2, 0x00020000);
   // Every step issues the same DMA: W(c) (c = step + WST - 1) and X(c') (c' = step + XST - 1).
-  // Chunks past the end are still loaded ("phantom" loads of the last W chunk and of a harmless X
-  // range) into the stage they would occupy, which nobody reads again; so the number of DMA
-  // instructions issued after X(i) when chunk i is due is always T::AFTER and one vmcnt immediate
-  // serves every step. W(i) is issued before X(i) (WST >= XST), so the wait covers both.
+  // Chunks past the end are still "loaded" (phantom loads that move no data, into the stage they
+  // would occupy, which nobody reads again); so the number of DMA instructions issued after X(i)
+  // when chunk i is due is always T::AFTER and one vmcnt immediate serves every step. W(i) is
+  // issued before X(i) (WST >= XST), so the wait covers both.
+  // Phantom loads go through a resource of zero records: out of range, so they move no data
+  // (the LDS stage gets zeros) while still counting as issued loads.
+  const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void *>(p.x), (short)0, 0, 0x00020000);
   auto w_issue = [&](int c) {
-    w_dma<NB>(wring + (c % T::WST) * T::WBYTES, rs, c0 + min(c, n - 1), wave, lane);
+    w_dma<NB>(wring + (c % T::WST) * T::WBYTES, rs, c < n, none, c0 + min(c, n - 1), wave, lane);
   };
   auto x_issue = [&](int c) {
-    x_dma<NB>(xring + (c % T::XST) * T::XBYTES, xr, p, m0, c < n_dma_x ? (c0 + c) * kLK : 0, wave,
-              lane);
+    x_dma<NB>(xring + (c % T::XST) * T::XBYTES, c < n_dma_x ? xr : none, p, m0,
+              c < n_dma_x ? (c0 + c) * kLK : 0, wave, lane);
   };
   if (n > 0) {
     // Prologue: W(0 .. WST-XST-1), then the pairs W(WST-XST+j), X(j) for j < XST-1, so that
@@ -359,8 +364,8 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
   // thread handles 4 consecutive features of one row, consecutive threads along the row: the global
   // stores cover whole rows instead of 32-byte pieces of 32 rows.
   constexpr int NCH = T::N / 4;  // 16-byte chunks per tile row
-  // The last steps issued phantom loads into the rings; they must land before the rings are
-  // reused for the output tile.
+  // The last steps issued phantom loads into the rings (zeros); they must land before the rings
+  // are reused for the output tile.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   lds_barrier();                 // every wave is done with the rings
   float *tile = reinterpret_cast<float *>(smem);
