@@ -225,11 +225,13 @@ __device__ __forceinline__ void linear_chunk(const char *ws, const char *xs, f32
 
 // Fused lm-head epilogue feeding the unmasking: the fp32 tile [128 rows][256 features] is in LDS
 // (16-byte chunk c of row r at chunk slot c ^ (r & 63)). Optionally stores it as logits; then
-// four threads per row each take 64 consecutive features in increasing order (first maximum by a
-// strict '>', then the sum of exp(y - max)), merge their triples with two lane exchanges, and the
-// first writes the row's triple for this tile. Rows committed already (masked == 0) write nothing.
+// four threads per row each reduce 64 consecutive features to (maximum, its first position, sum
+// of exp(y - max)), merge their triples with two lane exchanges, and the first writes the row's
+// triple for this tile. Rows committed already (masked == 0, read at kernel start into `live`)
+// write nothing. A thread whose features run past the vocabulary takes them one by one.
 template <int NB>
-__device__ void unmask_epilogue(const LinearParams &p, const float *tile, int m0, int n0, int tid) {
+__device__ void unmask_epilogue(const LinearParams &p, const float *tile, int m0, int n0, int tid,
+                                bool live) {
   using T = LTile<NB>;
   static_assert(T::THREADS == 4 * kLM, "four threads per row");
   constexpr int NCH = T::N / 4;
@@ -244,9 +246,42 @@ __device__ void unmask_epilogue(const LinearParams &p, const float *tile, int m0
   }
   const int r = tid >> 2, q = tid & 3;
   const int m = m0 + r;
-  const bool live = m < p.M && p.masked[m] != 0;
   Triple t = empty_triple();
-  if (live) {
+  const int nq = n0 + q * (NCH / 4) * 4;  // first feature of this thread's 64
+  if (live && nq + (NCH / 4) * 4 <= p.N) {
+    // All 64 features inside the vocabulary: the maximum by a max tree, its first position by a
+    // backward scan, then the sum of exp2(y log2 e - max log2 e) in four independent chains.
+    f32x4 v[NCH / 4];
+    float m4[NCH / 4];
+#pragma unroll
+    for (int j = 0; j < NCH / 4; ++j) {
+      const int c = q * (NCH / 4) + j;
+      v[j] = *reinterpret_cast<const f32x4 *>(tile + r * T::N + ((c ^ (r & (NCH - 1))) << 2));
+      m4[j] = fmaxf(fmaxf(v[j][0], v[j][1]), fmaxf(v[j][2], v[j][3]));
+    }
+#pragma unroll
+    for (int w = NCH / 8; w >= 1; w /= 2)
+#pragma unroll
+      for (int j = 0; j < w; ++j) m4[j] = fmaxf(m4[j], m4[j + w]);
+    const float mx = m4[0];
+    if (mx > -INFINITY) {  // else no feature is above -inf (or all are NaN): the empty triple
+      int idx = 0;
+#pragma unroll
+      for (int j = NCH / 4 - 1; j >= 0; --j)
+#pragma unroll
+        for (int e = 3; e >= 0; --e) idx = v[j][e] == mx ? j * 4 + e : idx;
+      constexpr float kLog2e = 1.4426950408889634f;
+      const float mc = mx * kLog2e;
+      float z[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NCH / 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[e] += __builtin_amdgcn_exp2f(fmaf(v[j][e], kLog2e, -mc));
+      t.m = mx;
+      t.idx = nq + idx;
+      t.z = (z[0] + z[1]) + (z[2] + z[3]);
+    }
+  } else if (live) {
     f32x4 v[NCH / 4];
 #pragma unroll
     for (int j = 0; j < NCH / 4; ++j) {
@@ -297,6 +332,13 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
   const int col = lane & 31, hh = lane >> 5;
   const int slab = NB == 2 ? (wave & 1) : wave;
   const int mrow0 = NB == 2 ? (wave >> 1) * 32 : 0;
+  // Fused unmasking: whether this thread's epilogue row (m0 + tid / 4) is still masked, read now
+  // so that the load is long done when the epilogue needs it.
+  bool live_row = false;
+  if (NB == 8 && p.epi == EPI_UNMASK) {
+    const int mr = m0 + (tid >> 2);
+    live_row = mr < p.M && p.masked[min(mr, p.M - 1)] != 0;
+  }
 
   const int nch = (p.K + kLK - 1) / kLK;
   const int Ks = (p.K + 15) / 16;
@@ -384,7 +426,7 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
   const int n0 = nb0 * 32;
   if constexpr (NB == 8) {
     if (p.epi == EPI_UNMASK) {
-      unmask_epilogue<NB>(p, tile, m0, n0, tid);
+      unmask_epilogue<NB>(p, tile, m0, n0, tid, live_row);
       return;
     }
   }
