@@ -180,17 +180,23 @@ def checksum(ts):
     return [int(t.view(torch.int16).to(torch.int64).sum().item()) for t in ts]
 
 
-def run_block(m, step, threshold=0.9):
+def run_block(m, step, threshold=0.9, count_slices=False):
+    """One block of T steps. With count_slices every step writes its commit counts into its own
+    row of a [T, B] tensor (as the benchmark does) instead of the step's own buffer."""
     masked = torch.ones((m.B, m.S), dtype=torch.uint8, device=DEV)
     tokens = torch.full((m.B, m.S), -1, dtype=torch.int32, device=DEV)
+    counts = torch.full((m.T, m.B), -7, dtype=torch.int32, device=DEV)
     per_step, history = [], []
     for t in range(m.T):
         _, n = step(m.h_steps[t], masked, tokens, threshold=threshold, min_commit=True,
-                    commit_all=(t == m.T - 1))
+                    commit_all=(t == m.T - 1), n_committed=counts[t] if count_slices else None)
         per_step.append(n.clone())
         history.append(masked.clone())
     torch.cuda.synchronize()
-    return masked, tokens, torch.stack(per_step).cpu().numpy(), [h.cpu().numpy() for h in history]
+    per_step = torch.stack(per_step).cpu().numpy()
+    if count_slices:
+        assert np.array_equal(per_step, counts.cpu().numpy())
+    return masked, tokens, per_step, [h.cpu().numpy() for h in history]
 
 
 def test_block_loop_invariants_small():
@@ -211,7 +217,7 @@ def test_full_size_loop_32k_one_block():
     m = loop_model(5, device=DEV)
     step = make_step(m, keep_logits=True)
     before = checksum(m.k_pages[:1] + m.v_pages[-1:])
-    masked, tokens, per_step, hist = run_block(m, step)
+    masked, tokens, per_step, hist = run_block(m, step, count_slices=True)
     # near-uniform logits of a random model: exactly one commit per step per sequence
     assert (per_step == 1).all()
     assert not masked.any()

@@ -445,11 +445,20 @@ class DenoiseStep:
         self._ws_n = C.c_size_t(0)
 
     def __call__(self, h_in, masked, tokens, *, threshold, min_commit=True, commit_all=False,
-                 timing_events=None):
-        """Enqueue one step; updates masked/tokens in place, fills confidence/n_committed."""
+                 timing_events=None, n_committed=None):
+        """Enqueue one step; updates masked/tokens in place, fills confidence and the per-sequence
+        commit counts (into `n_committed`, an int32 [batch] device tensor, when given, else into
+        self.n_committed, which is returned)."""
         a = self.args
         a.h_in = _p(h_in)
         a.unmask.masked, a.unmask.tokens = _p(masked), _p(tokens)
+        if n_committed is None:
+            n_committed = self.n_committed
+        else:
+            _check(n_committed, "n_committed", self.device, torch.int32)
+            if n_committed.numel() != self.n_committed.numel() or not n_committed.is_contiguous():
+                raise ValueError("n_committed must be a contiguous int32 tensor of batch elements")
+        a.unmask.n_committed = _p(n_committed)
         a.unmask.threshold = float(threshold)
         a.unmask.min_commit, a.unmask.commit_all = int(bool(min_commit)), int(bool(commit_all))
         if timing_events is not None:
@@ -467,4 +476,4 @@ class DenoiseStep:
         st = _lib.call("twotower_denoise_step", a, _p(self._ws), self._ws_n, _stream())
         if st != _lib.TT_OK:
             raise TwoTowerError("twotower_denoise_step", st)
-        return self.confidence, self.n_committed
+        return self.confidence, n_committed
