@@ -56,6 +56,20 @@ __device__ __forceinline__ u32x4 ld_global_16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// Stores of results that a later kernel reads (from any XCD) go through a buffer resource over a
+// wave-uniform base with the write-through policy (sc1): they reach memory while the kernel runs
+// instead of staying dirty in this XCD's L2 until the write-back at the kernel's end (a plain
+// 256 x 32 KB store kernel: 2.8 instead of 3.3 us).
+constexpr int kWriteThrough = 16;  // cache-policy operand: sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void st_wt_16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kWriteThrough);
+}
+
 __device__ __forceinline__ u32x4 ld_lds_16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }

@@ -430,13 +430,16 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
       return;
     }
   }
+  // K partials: rows m0 .. of partition kz, written through (the reduce reads them from any XCD)
+  const __amdgpu_buffer_rsrc_t pr =
+      buf_rsrc(p.part + ((size_t)kz * p.M + m0) * p.N, (uint32_t)(min(kLM, p.M - m0) * p.N * 4));
   for (int u = tid; u < kLM * NCH; u += T::THREADS) {
     const int r = u / NCH, c = u % NCH;
     const int m = m0 + r, nn = n0 + c * 4;
     if (m >= p.M || nn >= p.N) continue;
     const f32x4 v = *reinterpret_cast<const f32x4 *>(tile + r * T::N + ((c ^ (r & (NCH - 1))) << 2));
     if (p.ksplit > 1)
-      *reinterpret_cast<f32x4 *>(p.part + ((size_t)kz * p.M + m) * p.N + nn) = v;
+      st_wt_16(pr, (uint32_t)((r * p.N + nn) * 4), __builtin_bit_cast(u32x4, v));
     else
       epilogue4(p, m, nn, v);
   }
