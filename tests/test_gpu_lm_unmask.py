@@ -61,6 +61,7 @@ CASES = [
     (4, 16, 264, 4096, 5.0, 0.5, 0.5, False, False),
     (2, 64, 128, 2048, 2.0, 0.3, 0.2, True, True),       # commit-all, 64 positions
     (2, 128, 256, 2048, 3.0, 0.2, 0.3, True, False),     # block size 128 (two row tiles)
+    (2, 16, 128, 1100, 3.0, 0.2, 0.0, True, False),      # 35 slabs: last tile past the weight
 ]
 
 

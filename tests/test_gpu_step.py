@@ -90,7 +90,10 @@ def test_out_projection(rows, hidden, inf):
     assert torch.equal(h2, out)
 
 
-@pytest.mark.parametrize("rows,hidden,V", [(32, 512, 8192), (128, 2048, 131072), (7, 136, 1004)])
+# (96: 3 slabs of 32 features in 64-feature tiles; 70000: 2188 slabs in 256-feature tiles: the last
+# tile of each reaches past the packed weight and must read nothing there)
+@pytest.mark.parametrize("rows,hidden,V", [(32, 512, 8192), (128, 2048, 131072), (7, 136, 1004),
+                                           (5, 128, 96), (128, 256, 70000)])
 def test_lm_head(rows, hidden, V):
     g = torch.Generator(device=DEV).manual_seed(13)
     h = torch.randn((rows, hidden), generator=g, device=DEV).to(torch.bfloat16)

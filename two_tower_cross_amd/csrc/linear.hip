@@ -347,9 +347,15 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
   const bool tail = p.K % kLK != 0 && c0 + n == nch;  // its last chunk is partial
   const int n_dma_x = tail ? n - 1 : n;            // chunks whose X comes by DMA
 
+  // Slabs past the packed weight's ceil(N / 32) (the last tile of an N that is not a multiple of
+  // the tile width) get a resource with no records: their loads return zeros and touch no memory.
+  const int nslabs = (p.N + 31) / 32;
   __amdgpu_buffer_rsrc_t rs[NB];
 #pragma unroll
-  for (int j = 0; j < NB; ++j) rs[j] = slab_rsrc(p.w, nb0 + j, Ks);
+  for (int j = 0; j < NB; ++j)
+    rs[j] = nb0 + j < nslabs ? slab_rsrc(p.w, nb0 + j, Ks)
+                             : __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p.w), (short)0,
+                                                                 0, 0x00020000);
 
   f32x16 acc[T::MB];
 #pragma unroll
