@@ -65,14 +65,22 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("keep", [True, False], ids=["logits", "no-logits"])
 @pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}S{c[1]}V{c[3]}" for c in CASES])
-def test_fused_matches_two_call_path_and_oracle(case):
+def test_fused_matches_two_call_path_and_oracle(case, keep):
+    """keep: the call also stores the logits (and unmask runs on them); else the logits come from
+    a second, storing call (the same products in the same order, so the same fp32 values)."""
     B, S, hidden, V, sigma, gamma, frac, min_commit, commit_all = case
     h, w, masked, tokens = make(17 + V % 97, B, S, hidden, V, sigma, frac)
     m0, t0 = masked.cpu().numpy().copy(), tokens.cpu().numpy().copy()
     m1, t1 = masked.clone(), tokens.clone()
     conf, n, logits = tt.lm_head_unmask(h, w, masked, tokens, gamma, min_commit=min_commit,
-                                        commit_all=commit_all, keep_logits=True)
+                                        commit_all=commit_all, keep_logits=keep)
+    if not keep:
+        assert logits is None
+        _, _, logits = tt.lm_head_unmask(h, w, masked.new_tensor(m0), tokens.new_tensor(t0), gamma,
+                                         min_commit=min_commit, commit_all=commit_all,
+                                         keep_logits=True)
     ref_logits = tt.lm_head(h, w)
     conf2, n2 = tt.unmask(logits, m1, t1, gamma, min_commit=min_commit, commit_all=commit_all)
     torch.cuda.synchronize()
@@ -113,7 +121,11 @@ def test_logits_not_stored_gives_the_same_decisions():
     torch.cuda.synchronize()
     assert logits is None and logits2 is not None
     assert torch.equal(masked, m1) and torch.equal(tokens, t1) and torch.equal(n, n2)
-    assert torch.equal(torch.nan_to_num(conf, nan=-1.0), torch.nan_to_num(conf2, nan=-1.0))
+    # the two reduce the sums of exponentials in different orders (fp32 rounding)
+    c, c2 = conf.cpu().numpy(), conf2.cpu().numpy()
+    assert np.array_equal(np.isnan(c), np.isnan(c2))
+    ok = ~np.isnan(c)
+    assert np.all(np.abs(c[ok] - c2[ok]) <= CONF_RTOL * np.abs(c2[ok]))
 
 
 def test_fully_committed_block_is_left_alone():

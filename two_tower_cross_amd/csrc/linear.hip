@@ -17,6 +17,7 @@
 // one reduce pass, fixed summation order, no atomics).
 // Epilogues: fp32 store (logits), Q/K/V scatter into the attention layouts (bf16), and residual
 // add (bf16).
+#include <algorithm>
 #include <math.h>
 
 #include "common.hpp"
@@ -451,6 +452,173 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
   }
 }
 
+// ---------------------------------------------------------------- lm-head fused with unmasking
+// The step's lm-head when its logits are not kept. Persistent: work-group g of a 128-row block
+// takes the 256-feature tiles g, g + G, g + 2G, ... (G = gridDim.x) and streams their K chunks
+// through the ring as one sequence, so the first chunks of its next tile are in flight while the
+// (max, first argmax, sum of exp) of the previous tile are reduced. The reduction reads the
+// accumulators in registers (no staging of the fp32 tile): each lane's 16 features of a row, the
+// lane pair (the other 16 of the wave's 32-feature slab), then the 8 slabs through a 12 KB LDS
+// area after the rings.
+constexpr int kRedBytes = 8 * kLM * 3 * 4;  // [slab][row] (m, idx, z)
+
+// (max, first argmax, sum of exp(y - max)) of the 16 accumulator values a lane holds for one
+// row: register i is feature f0 + (i / 4) * 8 + i % 4; features at or past N are left out.
+__device__ __forceinline__ Triple lane_triple(const f32x16 &a, int f0, int N) {
+  float v[16];
+  const bool full = f0 + 28 < N;  // (the lane's last feature is f0 + 27)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = full || f0 + (i / 4) * 8 + i % 4 < N ? a[i] : -INFINITY;
+  float m4[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) m4[j] = fmaxf(fmaxf(v[4 * j], v[4 * j + 1]), fmaxf(v[4 * j + 2], v[4 * j + 3]));
+  const float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+  Triple t = empty_triple();
+  if (mx > -INFINITY) {
+    int idx = 0;
+#pragma unroll
+    for (int i = 15; i >= 0; --i) idx = v[i] == mx ? (i / 4) * 8 + i % 4 : idx;
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float mc = mx * kLog2e;
+    float z0 = 0.f, z1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      z0 += __builtin_amdgcn_exp2f(fmaf(v[i], kLog2e, -mc));
+      z1 += __builtin_amdgcn_exp2f(fmaf(v[i + 1], kLog2e, -mc));
+    }
+    t.m = mx;
+    t.idx = f0 + idx;
+    t.z = z0 + z1;
+  }
+  return t;
+}
+
+// W chunk c of 256-feature tile `tile` -> W stage (as w_dma<8>); slabs past the packed weight,
+// and every load when real is false, go through `none` (no records: nothing moves).
+__device__ __forceinline__ void w_dma_tile(char *stage, const void *w, int tile, int nslabs, int Ks,
+                                           bool real, __amdgpu_buffer_rsrc_t none, int c, int wave,
+                                           int lane) {
+  using T = LTile<8>;
+#pragma unroll
+  for (int j = 0; j < T::WLOADS; ++j) {
+    const int t = j * T::WAVES + wave;  // instruction index: slab t / 4, step t % 4
+    const int nb = tile * 8 + t / 4;
+    const __amdgpu_buffer_rsrc_t r = real && nb < nslabs ? slab_rsrc(w, nb, Ks) : none;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, TT_LDS_PTR(stage + t * 1024), 16, lane * 16,
+                                             c * 4096 + (t % 4) * 1024, 0, kNonTemporal);
+  }
+}
+
+__global__ __launch_bounds__(LTile<8>::THREADS) void lm_unmask_kernel(LinearParams p, int ntiles) {
+  using T = LTile<8>;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int m0 = blockIdx.y * kLM;
+  const int G = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, hh = lane >> 5;
+  // the final merge: four threads per row; whether the row is still masked, read now
+  const int rr = tid >> 2, q = tid & 3;
+  const bool live = m0 + rr < p.M && p.masked[min(m0 + rr, p.M - 1)] != 0;
+
+  const int mine = (ntiles - (int)blockIdx.x + G - 1) / G;  // tiles of this work-group
+  const int nch = (p.K + kLK - 1) / kLK;
+  const int Ks = (p.K + 15) / 16;
+  const int nslabs = (p.N + 31) / 32;
+  const bool tail = p.K % kLK != 0;  // the last chunk of every tile is partial
+  const int total = mine * nch;
+
+  f32x16 acc[T::MB];
+#pragma unroll
+  for (int mb = 0; mb < T::MB; ++mb) acc[mb] = f32x16{};
+
+  char *wring = smem;
+  char *xring = smem + T::XBASE;
+  float *red = reinterpret_cast<float *>(smem + T::LDS);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void *>(p.x), (short)0, p.M * p.K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void *>(p.x), (short)0, 0, 0x00020000);
+  // Chunk g of the sequence is chunk g % nch of tile blockIdx.x + (g / nch) * G. As in
+  // linear_kernel every step issues the same DMA (phantom loads past the end), so T::AFTER is
+  // exact for every chunk whose X comes by DMA.
+  auto w_issue = [&](int g) {
+    const int gg = min(g, total - 1);
+    w_dma_tile(wring + (g % T::WST) * T::WBYTES, p.w, (int)blockIdx.x + (gg / nch) * G, nslabs,
+               Ks, g < total, none, gg % nch, wave, lane);
+  };
+  auto x_issue = [&](int g) {
+    const int c = g % nch;
+    const bool real = g < total && !(tail && c == nch - 1);
+    x_dma<8>(xring + (g % T::XST) * T::XBYTES, real ? xr : none, p, m0, real ? c * kLK : 0, wave,
+             lane);
+  };
+  if (total > 0) {
+#pragma unroll
+    for (int c = 0; c < T::WST - T::XST; ++c) w_issue(c);
+#pragma unroll
+    for (int j = 0; j < T::XST - 1; ++j) {
+      w_issue(T::WST - T::XST + j);
+      x_issue(j);
+    }
+  }
+  for (int g = 0; g < total; ++g) {
+    const int c = g % nch;
+    const bool x_by_regs = tail && c == nch - 1;
+    if (!x_by_regs) __builtin_amdgcn_s_waitcnt(waitcnt_vm(T::AFTER));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    lds_barrier();  // chunk g is in LDS for every wave; the stages of chunk g - 1 are free
+    w_issue(g + T::WST - 1);
+    x_issue(g + T::XST - 1);
+    char *xs = xring + (g % T::XST) * T::XBYTES;
+    if (x_by_regs) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no DMA into this stage is still in flight
+      x_tail<8>(xs, p, m0, c * kLK, p.K, tid);
+      lds_barrier();
+    }
+    linear_chunk<8>(wring + (g % T::WST) * T::WBYTES, xs, acc, wave, 0, lane);
+    if (c == nch - 1) {
+      // Tile done: this wave's slab, per row: lane triple, lane pair, then the 8 slabs.
+      const int tile = (int)blockIdx.x + (g / nch) * G;
+      const int f0 = tile * T::N + wave * 32 + hh * 4;
+#pragma unroll
+      for (int mb = 0; mb < T::MB; ++mb) {
+        Triple t = lane_triple(acc[mb], f0, p.N);
+        t = merge(t, shfl_xor_triple(t, 32));
+        if (hh == 0) {
+          float *o = red + (wave * kLM + mb * 32 + col) * 3;
+          o[0] = t.m;
+          o[1] = __int_as_float(t.idx);
+          o[2] = t.z;
+        }
+        acc[mb] = f32x16{};
+      }
+      lds_barrier();
+      Triple t, u;
+      const float *a = red + ((2 * q) * kLM + rr) * 3, *b = red + ((2 * q + 1) * kLM + rr) * 3;
+      t.m = a[0];
+      t.idx = __float_as_int(a[1]);
+      t.z = a[2];
+      u.m = b[0];
+      u.idx = __float_as_int(b[1]);
+      u.z = b[2];
+      t = merge(t, u);
+      t = merge(t, shfl_xor_triple(t, 1));
+      t = merge(t, shfl_xor_triple(t, 2));
+      if (q == 0 && live) {
+        float *o = p.triples + ((size_t)(m0 + rr) * ntiles + tile) * 4;
+        o[0] = t.m;
+        o[1] = __int_as_float(t.idx);
+        o[2] = t.z;
+      }
+      // (the next write of `red` follows at least one more ring barrier)
+    }
+  }
+  // The last steps issued phantom loads into the rings; they must land before the work-group
+  // ends and its LDS is handed to another.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+}
+
 // Sum of the K partials in partition order, 8 partials requested at a time (clamped loads, no
 // branches, so that they are all in flight together).
 __global__ __launch_bounds__(256) void linear_reduce_kernel(LinearParams p) {
@@ -488,7 +656,35 @@ static hipError_t launch_tile(const LinearParams &p, hipStream_t stream, int cpz
   return hipGetLastError();
 }
 
+// Persistent fused lm-head: as many work-groups as compute units (or tiles, if fewer), spread
+// over the 128-row blocks.
+static hipError_t launch_lm_unmask(const LinearParams &p, hipStream_t stream) {
+  using T = LTile<8>;
+  constexpr int kBytes = T::LDS + kRedBytes;
+  static_assert(kBytes <= 160 * 1024, "LDS");
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&lm_unmask_kernel),
+      hipFuncAttributeMaxDynamicSharedMemorySize, kBytes);
+  if (attr != hipSuccess) return attr;
+  static int cu_count[64] = {};  // per device, queried once
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int cus = dev < 64 ? cu_count[dev] : 0;
+  if (cus == 0) {
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (dev < 64) cu_count[dev] = cus;
+  }
+  const int ntiles = (p.N + T::N - 1) / T::N;
+  const int rows = (p.M + kLM - 1) / kLM;
+  const int G = std::max(1, std::min(ntiles, cus / rows));
+  hipLaunchKernelGGL(lm_unmask_kernel, dim3(G, rows), dim3(T::THREADS), kBytes, stream, p, ntiles);
+  return hipGetLastError();
+}
+
 hipError_t launch_linear(const LinearParams &p, hipStream_t stream) {
+  if (p.epi == EPI_UNMASK && p.y == nullptr) return launch_lm_unmask(p, stream);
   const int nch = (p.K + kLK - 1) / kLK;
   const int cpz = (nch + p.ksplit - 1) / p.ksplit;
   hipError_t e = p.wide ? launch_tile<8>(p, stream, cpz) : launch_tile<2>(p, stream, cpz);
