@@ -45,8 +45,8 @@ struct LTile {
   static constexpr int WAVES = 8;
   static constexpr int THREADS = WAVES * 64;
   static constexpr int MB = NB == 2 ? 1 : 4;              // 32-row blocks per wave
-  static constexpr int WST = NB == 2 ? 8 : 3;             // W ring depth
-  static constexpr int XST = NB == 2 ? 6 : 3;             // X ring depth (<= WST)
+  static constexpr int WST = NB == 2 ? 6 : 3;             // W ring depth
+  static constexpr int XST = NB == 2 ? 4 : 3;             // X ring depth (<= WST)
   static constexpr int WBYTES = NB * 4096;                // one W chunk
   static constexpr int XBYTES = kLM * kLK * 2;            // one X chunk
   static constexpr int XBASE = WST * WBYTES;
