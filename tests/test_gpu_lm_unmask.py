@@ -62,6 +62,8 @@ CASES = [
     (2, 64, 128, 2048, 2.0, 0.3, 0.2, True, True),       # commit-all, 64 positions
     (2, 128, 256, 2048, 3.0, 0.2, 0.3, True, False),     # block size 128 (two row tiles)
     (2, 16, 128, 1100, 3.0, 0.2, 0.0, True, False),      # 35 slabs: last tile past the weight
+    # two row blocks, 300 tiles over 128 persistent work-groups (2 or 3 each), K tail
+    (16, 16, 136, 76800, 2.0, 0.3, 0.2, True, False),
 ]
 
 
