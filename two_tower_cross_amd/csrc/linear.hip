@@ -6,17 +6,18 @@
 // 32-feature x 16-column block is 1 KB, lane-contiguous, and the blocks of one 32-feature slab
 // follow each other along K. A work-group owns NB such slabs (64 or 256 features) and all rows of
 // an M tile, and walks its K range in chunks of 64 columns:
-//   * W chunks (NB x 4 KB of contiguous runs) stream into a deep LDS ring with non-temporal
-//     direct-to-LDS loads (several chunks in flight: a compute unit keeps ~56-64 KB of weights in
-//     flight, enough to cover the memory latency at full bandwidth);
+//   * W chunks (NB x 4 KB of contiguous runs) stream into an LDS ring with non-temporal
+//     direct-to-LDS loads (several chunks in flight: a compute unit keeps ~64 KB of loads in
+//     flight, and deeper rings only queue behind that limit);
 //   * X chunks (128 rows x 64 columns, re-read by every work-group, so served by L2) go through a
 //     second ring, 16-byte chunks XOR-swizzled per 128-byte row, deep enough to cover the L2
 //     latency under load;
 //   * Y^T = W X^T with 32x32x16 bf16 MFMA in fp32; the W operand reads are lane-contiguous.
-// When N alone gives too few work-groups to fill the GPU, K is also partitioned (fp32 partials +
-// one reduce pass, fixed summation order, no atomics).
-// Epilogues: fp32 store (logits), Q/K/V scatter into the attention layouts (bf16), and residual
-// add (bf16).
+// When N alone gives too few work-groups to fill the GPU, K is also partitioned (fp32 partials,
+// written through to memory, + one reduce pass, fixed summation order, no atomics).
+// Epilogues: fp32 store (logits), Q/K/V scatter into the attention layouts (bf16), residual add
+// (bf16), and the unmasking triples of the lm-head (lm_unmask_kernel when the logits are not
+// kept: persistent, one ring stream over several tiles).
 #include <algorithm>
 #include <math.h>
 
@@ -35,8 +36,8 @@ constexpr int kNonTemporal = 2;
 
 // Two tile shapes, 8 waves each (a wave issues a 1 KB load only every ~100 cycles and stalls
 // meanwhile, so the ring's loads are spread over as many waves as possible). NB = 2: 64 output
-// features, the waves are 2 slabs x 4 blocks of 32 rows, an 8-deep W ring (64 KB) and a 6-deep X
-// ring (96 KB) -- for the projections, with K partitioned across work-groups. NB = 8: 256 output
+// features, the waves are 2 slabs x 4 blocks of 32 rows, a 6-deep W ring (48 KB) and a 4-deep X
+// ring (64 KB) -- for the projections, with K partitioned across work-groups. NB = 8: 256 output
 // features, 8 waves of one slab x all 128 rows, 3-deep rings (96 + 48 KB) -- for the lm-head,
 // where each X chunk read through L2 then serves 4x more weights.
 template <int NB>
