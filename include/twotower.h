@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define TWOTOWER_ABI_VERSION 5
+#define TWOTOWER_ABI_VERSION 6
 
 typedef enum {
   TT_OK = 0,
@@ -201,11 +201,15 @@ typedef struct {
  * step because the block changes (explainer, "Generierungsprozess").
  * Products accumulate in fp32 and are rounded once to the output type.
  *
- * Packed weight layout (the A-operand order of the 32x32x16 bf16 matrix instruction): with
- * Ks = ceil(in_features / 16), the bf16 element at
- *   ((nb * Ks + s) * 64 + lane) * 8 + e     (nb < ceil(out_features / 32), s < Ks, lane < 64, e < 8)
- * is W[nb * 32 + lane % 32][s * 16 + (lane / 32) * 8 + e], and 0 where that is outside W.
- * Size: twotower_packed_weight_bytes(out_features, in_features) bytes.
+ * Packed weight layout (the A-operand order of the 32x32x16 bf16 matrix instruction): W is cut
+ * into slabs of 32 output features (nb < NS = ceil(out_features / 32)) and K steps of 16 inputs
+ * (s < Ks = ceil(in_features / 16)); a (slab, step) block is one 1 KB unit, and the slabs are
+ * grouped by 8 (group gi = nb / 8 holds gsize = min(8, NS - 8 gi) slabs) with the units of a group
+ * ordered step-major, so that the 64 inputs of 8 slabs are one contiguous 32 KB run:
+ *   unit U = 8 * gi * Ks + s * gsize + nb % 8,
+ * and the bf16 element at (U * 64 + lane) * 8 + e (lane < 64, e < 8) is
+ * W[nb * 32 + lane % 32][s * 16 + (lane / 32) * 8 + e], 0 where that is outside W.
+ * Size: twotower_packed_weight_bytes(out_features, in_features) bytes (NS * Ks KB).
  */
 typedef struct {
   int32_t batch, S, hidden, num_q_heads, num_kv_heads, head_dim;

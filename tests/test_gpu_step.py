@@ -42,11 +42,14 @@ def pack_reference(w):
     nbk, ks = -(-N // 32), -(-K // 16)
     wp = np.zeros((nbk * 32, ks * 16), dtype=w.dtype)
     wp[:N, :K] = w
-    # [nb, r, s, hh, e] -> [nb, s, hh, r, e]: lane = hh * 32 + r
-    return wp.reshape(nbk, 32, ks, 2, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
+    # [nb, r, s, hh, e] -> [nb, s, hh, r, e]: lane = hh * 32 + r; one 1 KB unit per (nb, s)
+    units = wp.reshape(nbk, 32, ks, 2, 8).transpose(0, 2, 3, 1, 4).reshape(nbk, ks, 512)
+    # groups of 8 slabs, each group's units step-major: unit 8 gi ks + s gsize + nb % 8
+    return np.concatenate([units[g:g + 8].transpose(1, 0, 2).reshape(-1)
+                           for g in range(0, nbk, 8)])
 
 
-@pytest.mark.parametrize("N,K", [(64, 64), (1004, 136), (4608, 2048), (37, 8)])
+@pytest.mark.parametrize("N,K", [(64, 64), (1004, 136), (4608, 2048), (37, 8), (300, 40)])
 def test_pack_weight_matches_the_documented_layout(N, K):
     g = torch.Generator(device=DEV).manual_seed(15)
     w = torch.randn((N, K), generator=g, device=DEV).to(torch.bfloat16)

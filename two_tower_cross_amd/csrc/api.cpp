@@ -188,9 +188,10 @@ hipError_t run_unmask(UnmaskPlan &pl, void *ws, hipStream_t stream) {
 // Tile shape and K partitions of a skinny product: 256-feature tiles once N alone yields a full
 // wave of work-groups (one per compute unit); otherwise 64-feature tiles with K split so that up
 // to one work-group per compute unit runs, each over at least 4 chunks of 64 along K.
-// X is addressed through a buffer resource with 32-bit byte offsets, and a packed weight slab too.
+// X is addressed through a buffer resource with 32-bit byte offsets, and a group of 8 packed
+// weight slabs too.
 bool linear_fits(int64_t M, int64_t K) {
-  return M * K * 2 <= INT32_MAX && cdiv(K, 16) * 1024 <= INT32_MAX;
+  return M * K * 2 <= INT32_MAX && 8 * cdiv(K, 16) * 1024 <= INT32_MAX;
 }
 
 void choose_tiling(int M, int N, int K, tt::LinearParams *p) {
@@ -410,8 +411,8 @@ tt_status twotower_pack_weight(const void *w, int32_t out_features, int32_t in_f
                                void *packed, void *stream) {
   if (out_features < 1 || in_features < 1) return TT_EINVAL;
   if (in_features % 8 != 0) return TT_ENOTSUP;
-  // one packed 32-feature slab is addressed with 32-bit byte offsets
-  if ((int64_t)cdiv(in_features, 16) * 1024 > INT32_MAX) return TT_ENOTSUP;
+  // one packed group of 8 slabs is addressed with 32-bit byte offsets
+  if ((int64_t)8 * cdiv(in_features, 16) * 1024 > INT32_MAX) return TT_ENOTSUP;
   if (!w || !packed || !aligned(w, 16) || !aligned(packed, 16)) return TT_EINVAL;
   return hip_status(
       tt::launch_pack_weight(w, out_features, in_features, packed, static_cast<hipStream_t>(stream)));

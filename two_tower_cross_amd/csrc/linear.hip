@@ -59,17 +59,23 @@ struct LTile {
 };
 
 // ----------------------------------------------------------------------------- weight packing
-// P[((nb * Ks + s) * 64 + lane) * 8 + e] = W[nb * 32 + lane % 32][s * 16 + (lane / 32) * 8 + e],
-// zero outside W; Ks = ceil(K / 16), nb < ceil(N / 32). One thread per 16-byte unit.
+// Packed layout: slabs of 32 features, grouped by 8 (group gi = nb / 8 of gsize = min(8, NS - 8 gi)
+// slabs, NS = ceil(N / 32)); 1 KB unit U = 8 gi Ks + s gsize + nb % 8 holds the 32 x 16 block
+// (slab nb, K step s), Ks = ceil(K / 16):
+// P[(U * 64 + lane) * 8 + e] = W[nb * 32 + lane % 32][s * 16 + (lane / 32) * 8 + e], zero outside W.
+// One thread per 16-byte piece, read in slab order.
 __global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t *w, int N, int K,
                                                           uint16_t *out, int64_t units) {
   const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (u >= units) return;
   const int Ks = (K + 15) / 16;
+  const int NS = (N + 31) / 32;
   const int lane = (int)(u % 64);
   const int64_t blk = u / 64;
   const int s = (int)(blk % Ks);
   const int nb = (int)(blk / Ks);
+  const int gi = nb / 8, gsize = min(8, NS - 8 * gi);
+  const int64_t unit = (int64_t)8 * gi * Ks + (int64_t)s * gsize + nb % 8;
   const int n = nb * 32 + lane % 32;
   const int k0 = s * 16 + (lane / 32) * 8;
   u32x4 v = {0u, 0u, 0u, 0u};
@@ -85,7 +91,7 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t *w, int
       for (int i = 0; i < 4; ++i) v[i] = (uint32_t)e[2 * i] | ((uint32_t)e[2 * i + 1] << 16);
     }
   }
-  *reinterpret_cast<u32x4 *>(out + (size_t)u * 8) = v;
+  *reinterpret_cast<u32x4 *>(out + ((size_t)unit * 64 + lane) * 8) = v;
 }
 
 hipError_t launch_pack_weight(const void *w, int N, int K, void *out, hipStream_t stream) {
@@ -141,25 +147,31 @@ __device__ __forceinline__ void epilogue4(const LinearParams &p, int m, int n, f
 }
 
 // ------------------------------------------------------------------------------------ loads
-// Buffer resource over one packed 32-feature slab (Ks KB); loads past it return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void *w, int nb, int Ks) {
-  const char *base = static_cast<const char *>(w) + (size_t)nb * Ks * 1024;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, Ks * 1024,
+// Buffer resource over the packed block of slab group gi (gsize x Ks KB); loads past it return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t group_rsrc(const void *w, int gi, int gsize,
+                                                             int Ks) {
+  const char *base = static_cast<const char *>(w) + (size_t)8 * gi * Ks * 1024;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, gsize * Ks * 1024,
                                            0x00020000);
 }
 
-// W chunk c (K columns 64c .. 64c + 63) of this work-group's NB slabs -> W stage (block-major:
-// slab j at j * 4 KB, 16-column step i at i * 1 KB; a straight copy of the packed bytes). With
-// real false every load goes through `none` instead (a resource with no records: nothing moves).
+// W chunk c (K columns 64c .. 64c + 63, steps 4c .. 4c + 3) of this work-group's NB slabs, slots
+// gs0 .. gs0 + NB - 1 of the group behind `gr` -> W stage (block-major: slab j at j * 4 KB, step i
+// at i * 1 KB). For a whole group (NB = 8) the chunk is one contiguous 32 KB run of the packed
+// weight. Slots past the group's gsize (features past N), and every load when real is false, go
+// through `none` (a resource with no records: nothing moves); steps past Ks fall outside `gr`.
 template <int NB>
-__device__ __forceinline__ void w_dma(char *stage, const __amdgpu_buffer_rsrc_t *rs, bool real,
-                                      __amdgpu_buffer_rsrc_t none, int c, int wave, int lane) {
+__device__ __forceinline__ void w_dma(char *stage, __amdgpu_buffer_rsrc_t gr, int gsize, int gs0,
+                                      bool real, __amdgpu_buffer_rsrc_t none, int c, int wave,
+                                      int lane) {
   using T = LTile<NB>;
 #pragma unroll
   for (int j = 0; j < T::WLOADS; ++j) {
     const int t = j * T::WAVES + wave;  // instruction index: slab t / 4, step t % 4
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(real ? rs[t / 4] : none, TT_LDS_PTR(stage + t * 1024), 16,
-                                             lane * 16, c * 4096 + (t % 4) * 1024, 0,
+    const int gs = gs0 + t / 4;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(real && gs < gsize ? gr : none,
+                                             TT_LDS_PTR(stage + t * 1024), 16, lane * 16,
+                                             ((4 * c + t % 4) * gsize + gs) * 1024, 0,
                                              kNonTemporal);
   }
 }
@@ -349,15 +361,11 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
   const bool tail = p.K % kLK != 0 && c0 + n == nch;  // its last chunk is partial
   const int n_dma_x = tail ? n - 1 : n;            // chunks whose X comes by DMA
 
-  // Slabs past the packed weight's ceil(N / 32) (the last tile of an N that is not a multiple of
-  // the tile width) get a resource with no records: their loads return zeros and touch no memory.
+  // This tile's slabs are slots nb0 % 8 .. of slab group nb0 / 8 (8 % NB == 0); slots past the
+  // group's size (the last tile of an N that is not a multiple of the tile width) load nothing.
   const int nslabs = (p.N + 31) / 32;
-  __amdgpu_buffer_rsrc_t rs[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j)
-    rs[j] = nb0 + j < nslabs ? slab_rsrc(p.w, nb0 + j, Ks)
-                             : __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p.w), (short)0,
-                                                                 0, 0x00020000);
+  const int gi = nb0 / 8, gs0 = nb0 % 8, gsize = min(8, nslabs - 8 * gi);
+  const __amdgpu_buffer_rsrc_t gr = group_rsrc(p.w, gi, gsize, Ks);
 
   f32x16 acc[T::MB];
 #pragma unroll
@@ -377,7 +385,8 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
   const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void *>(p.x), (short)0, 0, 0x00020000);
   auto w_issue = [&](int c) {
-    w_dma<NB>(wring + (c % T::WST) * T::WBYTES, rs, c < n, none, c0 + min(c, n - 1), wave, lane);
+    w_dma<NB>(wring + (c % T::WST) * T::WBYTES, gr, gsize, gs0, c < n, none, c0 + min(c, n - 1),
+              wave, lane);
   };
   auto x_issue = [&](int c) {
     x_dma<NB>(xring + (c % T::XST) * T::XBYTES, c < n_dma_x ? xr : none, p, m0,
@@ -494,22 +503,6 @@ __device__ __forceinline__ Triple lane_triple(const f32x16 &a, int f0, int N) {
   return t;
 }
 
-// W chunk c of 256-feature tile `tile` -> W stage (as w_dma<8>); slabs past the packed weight,
-// and every load when real is false, go through `none` (no records: nothing moves).
-__device__ __forceinline__ void w_dma_tile(char *stage, const void *w, int tile, int nslabs, int Ks,
-                                           bool real, __amdgpu_buffer_rsrc_t none, int c, int wave,
-                                           int lane) {
-  using T = LTile<8>;
-#pragma unroll
-  for (int j = 0; j < T::WLOADS; ++j) {
-    const int t = j * T::WAVES + wave;  // instruction index: slab t / 4, step t % 4
-    const int nb = tile * 8 + t / 4;
-    const __amdgpu_buffer_rsrc_t r = real && nb < nslabs ? slab_rsrc(w, nb, Ks) : none;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, TT_LDS_PTR(stage + t * 1024), 16, lane * 16,
-                                             c * 4096 + (t % 4) * 1024, 0, kNonTemporal);
-  }
-}
-
 __global__ __launch_bounds__(LTile<8>::THREADS) void lm_unmask_kernel(LinearParams p, int ntiles) {
   using T = LTile<8>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -543,10 +536,13 @@ __global__ __launch_bounds__(LTile<8>::THREADS) void lm_unmask_kernel(LinearPara
   // Chunk g of the sequence is chunk g % nch of tile blockIdx.x + (g / nch) * G. As in
   // linear_kernel every step issues the same DMA (phantom loads past the end), so T::AFTER is
   // exact for every chunk whose X comes by DMA.
+  // (a 256-feature tile is one whole slab group)
   auto w_issue = [&](int g) {
     const int gg = min(g, total - 1);
-    w_dma_tile(wring + (g % T::WST) * T::WBYTES, p.w, (int)blockIdx.x + (gg / nch) * G, nslabs,
-               Ks, g < total, none, gg % nch, wave, lane);
+    const int tile = (int)blockIdx.x + (gg / nch) * G;
+    const int gsize = min(8, nslabs - 8 * tile);
+    w_dma<8>(wring + (g % T::WST) * T::WBYTES, group_rsrc(p.w, tile, gsize, Ks), gsize, 0,
+             g < total, none, gg % nch, wave, lane);
   };
   auto x_issue = [&](int g) {
     const int c = g % nch;
@@ -663,6 +659,7 @@ static hipError_t launch_lm_unmask(const LinearParams &p, hipStream_t stream) {
   using T = LTile<8>;
   constexpr int kBytes = T::LDS + kRedBytes;
   static_assert(kBytes <= 160 * 1024, "LDS");
+  static_assert(8 % 2 == 0, "a 64-feature tile lies inside one slab group");
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(&lm_unmask_kernel),
       hipFuncAttributeMaxDynamicSharedMemorySize, kBytes);
