@@ -3,10 +3,12 @@
 //
 // The weights dominate the bytes (M = 128 against N, K in the thousands) and are read once per
 // product, so they are stored pre-packed in the A-operand order of v_mfma_f32_32x32x16_bf16: a
-// 32-feature x 16-column block is 1 KB, lane-contiguous, and the blocks of one 32-feature slab
-// follow each other along K. A work-group owns NB such slabs (64 or 256 features) and all rows of
-// an M tile, and walks its K range in chunks of 64 columns:
-//   * W chunks (NB x 4 KB of contiguous runs) stream into an LDS ring with non-temporal
+// 32-feature x 16-column block is 1 KB, lane-contiguous; 32-feature slabs are grouped by 8 and a
+// group's blocks are stored step-major (see pack_weight_kernel). A work-group owns NB slabs of one
+// group (64 or 256 features) and all rows of an M tile, and walks its K range in chunks of 64
+// columns:
+//   * W chunks (one 32 KB run for 256 features, four 2 KB runs for 64) stream into an LDS ring
+//     with non-temporal
 //     direct-to-LDS loads (several chunks in flight: a compute unit keeps ~64 KB of loads in
 //     flight, and deeper rings only queue behind that limit);
 //   * X chunks (128 rows x 64 columns, re-read by every work-group, so served by L2) go through a
