@@ -248,6 +248,18 @@ def test_full_size_loop_32k_one_block():
     assert max_abs(got, ref) <= 1e-4 + 1e-5 * np.abs(ref).max()
 
 
+def test_full_size_loop_32k_as_benchmarked():
+    """The benchmark's exact step (logits not kept: the persistent fused lm-head) commits the same
+    tokens at the same steps as the step that keeps its logits (checked against the oracle
+    above); the two differ only in the fp32 order of the sums of exponentials."""
+    m = loop_model(5, device=DEV)
+    _, tok_kept, per_kept, _ = run_block(m, make_step(m, keep_logits=True))
+    masked, tok, per, _ = run_block(m, make_step(m), count_slices=True)
+    assert not masked.any()
+    assert np.array_equal(per, per_kept)
+    assert torch.equal(tok, tok_kept)
+
+
 @pytest.mark.parametrize("S", [32, 128])
 def test_block_sizes_of_the_pages(S):
     """The block sizes the pages train and sample with besides 16 (32 in training, 128 at
