@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define TWOTOWER_ABI_VERSION 6
+#define TWOTOWER_ABI_VERSION 7
 
 typedef enum {
   TT_OK = 0,
@@ -68,14 +68,18 @@ typedef enum { TT_FP32 = 0, TT_BF16 = 1 } tt_dtype;
  *
  * Layouts (elements of `dtype`, innermost last, all contiguous):
  *   q        [batch, S, num_q_heads, head_dim]
- *   k_pages  [num_pages, num_kv_heads, page_size, head_dim]     token-major pages
- *   v_pages  [num_pages, num_kv_heads, page_size/64, head_dim, 64]  dim-major 64-token tiles:
- *            row o of a page is at [page, g, o / 64, :, o % 64]
+ *   k_pages  [num_pages, num_kv_heads, page_size/64, head_dim/8, 64, 8]   64-token tiles of
+ *            8-element chunks, chunk-major: element (row o of the page, dimension d) is at
+ *            [page, g, o / 64, d / 8, o % 64, d % 8]
+ *   v_pages  [num_pages, num_kv_heads, page_size/64, 8, head_dim, 8]        64-token tiles of
+ *            8-token chunks: element (o, d) is at [page, g, o / 64, (o % 64) / 8, d, o % 8]
+ *            (a tile of either is contiguous: head_dim * 64 elements; the 32 lanes of a matrix
+ *            operand read 32 consecutive 16-byte chunks of it)
  *   block_table [batch, max_pages_per_seq] int32: context row t of sequence b is in page
  *            block_table[b, t / page_size] at offset t % page_size
  *   ctx_lens [batch] int32, 0 <= ctx_lens[b] <= max_ctx_len
  *   k_blk    [batch, num_kv_heads, S, head_dim]
- *   v_blk    [batch, num_kv_heads, head_dim, S]                 dim-major, like v_pages
+ *   v_blk    [batch, num_kv_heads, head_dim, S]                 dim-major
  *   out      [batch, S, num_q_heads, head_dim] in `out_dtype`
  *   lse      [batch, num_q_heads, S] fp32, natural log; optional (NULL = not written)
  * A contiguous cache is the case page_size >= max_ctx_len, block_table[b] = {b}.

@@ -20,10 +20,13 @@ K_blk(b, g)], values V_cat likewise:
     o   = sum_j w_j V_cat[j] / sum_j w_j,   lse = m + ln(sum_j w_j)
 
 Context row t of sequence b sits in page block_table[b, t // page_size] at offset
-o = t % page_size. K pages are [pool, Hkv, page_size, D] (row o at [page, g, o, :]). V pages
-hold dim-major tiles of T tokens, [pool, Hkv, page_size // T, D, T] (row o at
-[page, g, o // T, :, o % T]); T = 64 when page_size is a multiple of 64, else T = page_size. The
-block's V is [B, Hkv, D, S]. Only rows t < ctx_lens[b] are read.
+o = t % page_size. A page holds tiles of T tokens made of element chunks (the cache layout this
+build chooses; the pages prescribe none): K pages are [pool, Hkv, page_size // T, D // CK, T, CK]
+(element (o, d) at [page, g, o // T, d // CK, o % T, d % CK]), V pages
+[pool, Hkv, page_size // T, T // CV, D, CV] (element (o, d) at [page, g, o // T, (o % T) // CV,
+d, o % CV]). The library uses T = CK = ... = 64, 8, 8; the tile and chunk widths are read from the
+array shapes here, so that small cases can use pages of a few tokens. The block's V is
+[B, Hkv, D, S]. Only rows t < ctx_lens[b] are read.
 """
 from __future__ import annotations
 
@@ -32,16 +35,21 @@ import numpy as np
 
 def gather_context(k_pages, v_pages, block_table, ctx_len, b, g):
     """Rows 0..ctx_len-1 of sequence b, KV head g, as float64 [L, D] keys and [L, D] values."""
-    page_size = k_pages.shape[2]
-    n_tiles, D, T = v_pages.shape[2:]
-    if n_tiles * T != page_size:
-        raise ValueError("K and V pages disagree on the page size")
+    n_tiles, nck, T, CK = k_pages.shape[2:]
+    n_tiles_v, ncv, D, CV = v_pages.shape[2:]
+    if n_tiles_v != n_tiles or ncv * CV != T or nck * CK != D:
+        raise ValueError("K and V pages disagree on the page or tile shape")
+    page_size = n_tiles * T
     t = np.arange(int(ctx_len))
     page = np.asarray(block_table)[b, t // page_size]
-    off = t % page_size
-    keys = np.asarray(k_pages[:, g], dtype=np.float64)[page, off, :]                 # [L, D]
-    vals = np.asarray(v_pages[:, g], dtype=np.float64)[page, off // T, :, off % T]   # [L, D]
-    return keys, vals
+    o = t % page_size
+    kp = np.asarray(k_pages[:, g], dtype=np.float64)   # [pool, tiles, D // CK, T, CK]
+    vp = np.asarray(v_pages[:, g], dtype=np.float64)   # [pool, tiles, T // CV, D, CV]
+    d = np.arange(D)
+    keys = kp[page[:, None], (o // T)[:, None], d[None, :] // CK, (o % T)[:, None], d[None, :] % CK]
+    vals = vp[page[:, None], (o // T)[:, None], ((o % T) // CV)[:, None], d[None, :],
+              (o % CV)[:, None]]
+    return keys, vals                                   # [L, D] each
 
 
 def _softmax_attend(qrows, keys, vals, scale):

@@ -11,8 +11,10 @@ allocator):
 * the block's S rows of every layer go to context positions L .. L+S-1 of the sequence, L being
   its length before the append, which then becomes L+S;
 * a row t lives in page block_table[b, t // page_size] at offset t % page_size (the same paging
-  as the attention's context reads); K pages are token-major [pool, Hkv, page, D], V pages hold
-  dim-major 64-token tiles [pool, Hkv, page // 64, D, 64];
+  as the attention's context reads), stored in the tiled page layouts the attention oracle
+  decodes: K [pool, Hkv, page // T, D // CK, T, CK] with element (o, d) at
+  [page, g, o // T, d // CK, o % T, d % CK], V [pool, Hkv, page // T, T // CV, D, CV] with
+  element (o, d) at [page, g, o // T, (o % T) // CV, d, o % CV] (widths read from the shapes);
 * new pages come from the top of a free-page stack (the last valid entry first), sequences
   served in order b = 0, 1, ...; a sequence that does not fit (its table is too short, the stack
   runs out, or a page id it would write is outside the pool) is left untouched and flagged.
@@ -40,7 +42,9 @@ def append_block(k_pages, v_pages, block_table, ctx_lens, free_pages, free_count
     free = np.asarray(free_pages, dtype=np.int32)
     top = int(free_count)
     status = 0
-    pool, _, page, _ = k_pages[0].shape
+    pool, _, n_tiles, _, T, CK = k_pages[0].shape
+    CV = v_pages[0].shape[-1]
+    page = n_tiles * T
     B, max_pages = table.shape
     S = k_new[0].shape[2]
     for b in range(B):
@@ -64,8 +68,10 @@ def append_block(k_pages, v_pages, block_table, ctx_lens, free_pages, free_count
         for i in range(S):
             t = L + i
             pg, off = int(table[b, t // page]), t % page
+            tile, o = off // T, off % T
             for layer in range(len(k_pages)):
-                k_pages[layer][pg, :, off, :] = k_new[layer][b, :, i, :]
-                v_pages[layer][pg, :, off // 64, :, off % 64] = v_new[layer][b, :, :, i]
+                for d in range(k_new[layer].shape[3]):
+                    k_pages[layer][pg, :, tile, d // CK, o, d % CK] = k_new[layer][b, :, i, d]
+                v_pages[layer][pg, :, tile, o // CV, :, o % CV] = v_new[layer][b, :, :, i]
         lens[b] = L + S
     return k_pages, v_pages, table, lens, top, status

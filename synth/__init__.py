@@ -9,9 +9,14 @@ every machine.
 Layouts produced here (the library's layouts, documented in ``include/twotower.h``):
 
 * ``q``        ``[B, S, Hq, D]``
-* ``k_pages``  ``[num_pages, Hkv, page_size, D]``   (token-major pages)
-* ``v_pages``  ``[num_pages, Hkv, page_size // T, D, T]`` (dim-major tiles of T tokens; T = 64
-  when page_size is a multiple of 64, else T = page_size)
+* ``k_pages``  ``[num_pages, Hkv, page_size // T, D // CK, T, CK]`` (tiles of T tokens made of
+  CK-element chunks: element (o, d) at [page, g, o // T, d // CK, o % T, d % CK])
+* ``v_pages``  ``[num_pages, Hkv, page_size // T, T // CV, D, CV]`` (tiles of T tokens made of
+  CV-token chunks: element (o, d) at [page, g, o // T, (o % T) // CV, d, o % CV])
+
+  (T, CK, CV) = (64, 8, 8), the library's widths, whenever page_size is a multiple of 64 and D
+  of 8; otherwise a width falls back to the whole extent (T = page_size, CK = D, CV = T), which
+  only the oracle reads (small hand-sized cases).
 * ``k_blk``    ``[B, Hkv, S, D]``
 * ``v_blk``    ``[B, Hkv, D, S]``
 * ``block_table`` ``[B, max_pages]`` int32, ``ctx_lens`` ``[B]`` int32
@@ -29,7 +34,8 @@ import math
 import numpy as np
 
 __all__ = [
-    "rng", "round_to_bf16", "bf16_bits", "bits_to_f32", "v_tile_width", "tile_v", "AttnCase",
+    "rng", "round_to_bf16", "bf16_bits", "bits_to_f32", "tile_widths", "tile_k", "untile_k",
+    "tile_v", "untile_v", "AttnCase",
     "attn_case",
     "logits_normal", "logits_planted", "config_attn", "config_logits",
 ]
@@ -60,17 +66,46 @@ def bf16_bits(x_bf16_exact: np.ndarray) -> np.ndarray:
     return (u >> 16).astype(np.uint16)
 
 
-def v_tile_width(page_size: int) -> int:
-    return 64 if page_size % 64 == 0 else page_size
+def tile_widths(page_size: int, D: int) -> tuple[int, int, int]:
+    """(T, CK, CV): tokens per tile, K elements per chunk, V tokens per chunk."""
+    T = 64 if page_size % 64 == 0 else page_size
+    CK = 8 if D % 8 == 0 else D
+    CV = 8 if T % 8 == 0 else T
+    return T, CK, CV
+
+
+def tile_k(k: np.ndarray) -> np.ndarray:
+    """[..., page, D] (token-major page) -> [..., page // T, D // CK, T, CK] (the K page layout)."""
+    *lead, P, D = k.shape
+    T, CK, _ = tile_widths(P, D)
+    nd = len(lead)
+    x = k.reshape(*lead, P // T, T, D // CK, CK)
+    return np.ascontiguousarray(np.swapaxes(x, nd + 1, nd + 2))
+
+
+def untile_k(kt: np.ndarray) -> np.ndarray:
+    """Inverse of tile_k."""
+    *lead, nt, nck, T, CK = kt.shape
+    nd = len(lead)
+    return np.ascontiguousarray(np.swapaxes(kt, nd + 1, nd + 2)).reshape(*lead, nt * T, nck * CK)
 
 
 def tile_v(v_dim_major: np.ndarray) -> np.ndarray:
-    """[..., D, page] (dim-major page) -> [..., page // T, D, T] (the V page layout)."""
+    """[..., D, page] (dim-major page) -> [..., page // T, T // CV, D, CV] (the V page layout)."""
     *lead, D, P = v_dim_major.shape
-    T = v_tile_width(P)
-    x = v_dim_major.reshape(*lead, D, P // T, T)
+    T, _, CV = tile_widths(P, D)
     nd = len(lead)
-    return np.ascontiguousarray(np.moveaxis(x, nd + 1, nd))
+    x = v_dim_major.reshape(*lead, D, P // T, T // CV, CV)
+    perm = list(range(nd)) + [nd + 1, nd + 2, nd, nd + 3]
+    return np.ascontiguousarray(x.transpose(perm))
+
+
+def untile_v(vt: np.ndarray) -> np.ndarray:
+    """Inverse of tile_v: [..., page // T, T // CV, D, CV] -> [..., D, page]."""
+    *lead, nt, ncv, D, CV = vt.shape
+    nd = len(lead)
+    perm = list(range(nd)) + [nd + 2, nd, nd + 1, nd + 3]
+    return np.ascontiguousarray(vt.transpose(perm)).reshape(*lead, D, nt * ncv * CV)
 
 
 def bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -106,7 +141,7 @@ class AttnCase:
     def Hkv(self): return self.k_pages.shape[1]
 
     @property
-    def page_size(self): return self.k_pages.shape[2]
+    def page_size(self): return self.k_pages.shape[2] * self.k_pages.shape[4]
 
 
 def _store(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -152,8 +187,8 @@ def attn_case(seed: int, *, B: int, S: int, Hq: int, Hkv: int, D: int, ctx_lens,
         seqs.append((_store(k, dtype), _store(v, dtype)))
 
     fill = np.float32("nan") if nan_poison else np.float32(0.0)
-    k_pages = np.full((n_pool, Hkv, page_size, D), fill, dtype=np.float32)
-    v_pages = np.full((n_pool, Hkv, D, page_size), fill, dtype=np.float32)   # dim-major, tiled below
+    k_pages = np.full((n_pool, Hkv, page_size, D), fill, dtype=np.float32)   # both tiled below
+    v_pages = np.full((n_pool, Hkv, D, page_size), fill, dtype=np.float32)
     order = g.permutation(n_pool) if shuffle_pages else np.arange(n_pool)
     block_table = np.zeros((B, max_pages), dtype=np.int32)
     nxt = 0
@@ -167,7 +202,7 @@ def attn_case(seed: int, *, B: int, S: int, Hq: int, Hkv: int, D: int, ctx_lens,
             n = t1 - t0
             k_pages[slot, :, :n, :] = k[t0:t1].transpose(1, 0, 2)
             v_pages[slot, :, :, :n] = v[t0:t1].transpose(1, 2, 0)
-    v_pages = tile_v(v_pages)
+    k_pages, v_pages = tile_k(k_pages), tile_v(v_pages)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     return AttnCase(dtype, q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, float(scale))

@@ -4,7 +4,8 @@ generate on the host). Distributions and layouts only; no method arithmetic.
 Model (one reading, stated with the library): residual stream H [B, S, hidden]; per layer
 W_qkv [(Hq + 2 Hkv) D, hidden] and W_o [hidden, Hq D] ~ N(0, 1/fan_in); lm-head W_lm
 [V, hidden] ~ N(0, 1/hidden); context KV per layer ~ N(0, 1) as a contiguous cache (one page per
-sequence: k [B, Hkv, L, D], v [B, Hkv, L/64, D, 64]); a fresh H ~ N(0, 1) per denoise step.
+sequence, in the library's tiled page layouts: k [B, Hkv, L/64, D/8, 64, 8], v [B, Hkv, L/64, 8,
+D, 8]); a fresh H ~ N(0, 1) per denoise step.
 """
 from __future__ import annotations
 
@@ -63,8 +64,8 @@ def loop_model(seed: int = 5, *, B=8, S=16, L=32768, layers=6, Hq=32, Hkv=2, D=1
         pool = B * n + spare_pages
     k_pages, v_pages, w_qkv, w_o = [], [], [], []
     for _ in range(layers):
-        k_pages.append(_randn((pool, Hkv, P, D), g, dev))
-        v_pages.append(_randn((pool, Hkv, P // 64, D, 64), g, dev))
+        k_pages.append(_randn((pool, Hkv, P // 64, D // 8, 64, 8), g, dev))
+        v_pages.append(_randn((pool, Hkv, P // 64, 8, D, 8), g, dev))
         w_qkv.append(_randn(((Hq + 2 * Hkv) * D, hidden), g, dev, 1.0 / math.sqrt(hidden)))
         w_o.append(_randn((hidden, Hq * D), g, dev, 1.0 / math.sqrt(Hq * D)))
     w_lm = _randn((vocab, hidden), g, dev, 1.0 / math.sqrt(hidden))

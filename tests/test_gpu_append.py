@@ -32,8 +32,8 @@ def setup_case(seed, *, B, Hkv, D, S, page, lens, layers, pool, max_pages, dtype
     r = synth.rng(seed)
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
     mk = lambda shape: torch.from_numpy(r.standard_normal(shape).astype(np.float32)).to(DEV).to(dt)
-    k = [mk((pool, Hkv, page, D)) for _ in range(layers)]
-    v = [mk((pool, Hkv, page // 64, D, 64)) for _ in range(layers)]
+    k = [mk(tt.k_pages_shape(pool, Hkv, page, D)) for _ in range(layers)]
+    v = [mk(tt.v_pages_shape(pool, Hkv, page, D)) for _ in range(layers)]
     kn = [mk((B, Hkv, S, D)) for _ in range(layers)]
     vn = [mk((B, Hkv, D, S)) for _ in range(layers)]
     # pages in use: a random permutation of the pool (minus an explicit free stack), the rest free
@@ -133,7 +133,7 @@ def test_two_blocks_at_a_growing_context():
             kc[b, g, :Lc] = np.concatenate([ok, to_np(kb1)[b, g]])
             vc[b, g, :Lc] = np.concatenate([ov, to_np(vb1)[b, g].T])
     vtiles = synth.tile_v(vc.transpose(0, 1, 3, 2))
-    ref, _ = oattn.block_attention(to_np(step.q), kc, vtiles,
+    ref, _ = oattn.block_attention(to_np(step.q), synth.tile_k(kc), vtiles,
                                    np.arange(m.B, dtype=np.int32).reshape(m.B, 1),
                                    np.full(m.B, Lc, np.int32), to_np(step.k_blk[l]),
                                    to_np(step.v_blk[l]), 1.0 / math.sqrt(m.D))

@@ -115,10 +115,12 @@ def test_single_dominant_key_returns_its_value():
     case.q[..., 0] = 8.0
     case.k_pages[...] = synth.round_to_bf16(case.k_pages * 0.01)
     case.k_blk[...] = synth.round_to_bf16(case.k_blk * 0.01)
-    case.k_pages[case.block_table[0, 0], 0, 300, :] = 0.0
-    case.k_pages[case.block_table[0, 0], 0, 300, 0] = 64.0
+    k = synth.untile_k(case.k_pages)                      # [pool, Hkv, page, D]
+    k[case.block_table[0, 0], 0, 300, :] = 0.0
+    k[case.block_table[0, 0], 0, 300, 0] = 64.0
+    case.k_pages = synth.tile_k(k)
     out, lse = gpu_attn(case)
-    v = case.v_pages[case.block_table[0, 0], 0, 300 // 64, :, 300 % 64]
+    v = synth.untile_v(case.v_pages)[case.block_table[0, 0], 0, :, 300]
     for h in range(2):
         np.testing.assert_allclose(out[0, :, h, :], np.broadcast_to(v, (16, 128)), atol=1e-5)
 

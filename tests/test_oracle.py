@@ -58,7 +58,7 @@ def test_single_key_returns_its_value():
     out, lse = run(c, k_blk=c.k_blk[:, :, :0], v_blk=c.v_blk[:, :, :, :0])
     G = c.Hq // c.Hkv
     for h in range(c.Hq):
-        v = c.v_pages[c.block_table[0, 0], h // G, 0, :, 0]
+        v = synth.untile_v(c.v_pages)[c.block_table[0, 0], h // G, :, 0]
         np.testing.assert_allclose(out[0, :, h, :], np.broadcast_to(v, (2, c.D)), atol=1e-15)
     # empty context, one block key
     c = small_case(3, B=1, lens=(0,), S=1)
@@ -107,7 +107,7 @@ def test_permutation_invariance_block_context_and_pages():
             kc, vc = attention.gather_context(c.k_pages, c.v_pages, c.block_table, L, b, h)
             kp[b, h, :L] = kc[p]
             vp[b, h, :, :L] = vc[p].T
-    out, _ = run(c, k_pages=kp, v_pages=synth.tile_v(vp),
+    out, _ = run(c, k_pages=synth.tile_k(kp), v_pages=synth.tile_v(vp),
                  block_table=np.arange(B, dtype=np.int32)[:, None])
     np.testing.assert_allclose(out, ref, atol=1e-13)
 
@@ -140,7 +140,7 @@ def test_key_shift_invariance():
     c = small_case(6)
     ref, _ = run(c)
     u = synth.rng(7).standard_normal((c.Hkv, c.D)).astype(np.float32)
-    kp = c.k_pages + u[None, :, None, :]
+    kp = synth.tile_k(synth.untile_k(c.k_pages) + u[None, :, None, :])
     kb = c.k_blk + u[None, :, None, :]
     out, _ = run(c, k_pages=kp, k_blk=kb)
     np.testing.assert_allclose(out, ref, atol=1e-6)
@@ -178,7 +178,7 @@ def test_affine_values():
     ref, _ = run(c)
     alpha = -1.75
     beta = synth.rng(11).standard_normal(c.D).astype(np.float32)
-    vp = alpha * c.v_pages + beta[None, None, None, :, None]
+    vp = alpha * c.v_pages + beta[None, None, None, None, :, None]
     vb = alpha * c.v_blk + beta[None, None, :, None]
     out, _ = run(c, v_pages=vp.astype(np.float32), v_blk=vb.astype(np.float32))
     np.testing.assert_allclose(out, alpha * ref + beta, atol=1e-5)
@@ -203,18 +203,27 @@ def test_matches_torch_sdpa_float64():
         np.testing.assert_allclose(out[b], ref.permute(1, 0, 2).numpy(), atol=1e-12)
 
 
-def test_v_tile_layout_addresses():
-    """Row o of a 128-token page sits at [page, g, o // 64, :, o % 64] of the V pages."""
-    c = small_case(14, B=1, Hq=2, Hkv=1, D=3, lens=(150,), page_size=128)
+def test_tile_layout_addresses():
+    """Element (o, d) of a 128-token page sits at [page, g, o // 64, d // 8, o % 64, d % 8] of the
+    K pages and at [page, g, o // 64, (o % 64) // 8, d, o % 8] of the V pages."""
+    c = small_case(14, B=1, Hq=2, Hkv=1, D=16, lens=(150,), page_size=128)
     L = 150
-    _, vc = attention.gather_context(c.k_pages, c.v_pages, c.block_table, L, 0, 0)
-    for t in (0, 63, 64, 127, 128, 149):
-        page = c.block_table[0, t // 128]
-        np.testing.assert_array_equal(vc[t], c.v_pages[page, 0, (t % 128) // 64, :, t % 64])
+    kc, vc = attention.gather_context(c.k_pages, c.v_pages, c.block_table, L, 0, 0)
+    for t in (0, 7, 8, 63, 64, 127, 128, 149):
+        page, o = c.block_table[0, t // 128], t % 128
+        for d in (0, 7, 8, 15):
+            assert kc[t, d] == c.k_pages[page, 0, o // 64, d // 8, o % 64, d % 8]
+            assert vc[t, d] == c.v_pages[page, 0, o // 64, (o % 64) // 8, d, o % 8]
     dm = synth.rng(1).standard_normal((2, 3, 5, 192))
     tv = synth.tile_v(dm)
-    assert tv.shape == (2, 3, 3, 5, 64)
-    assert tv[1, 2, 2, 4, 7] == dm[1, 2, 4, 2 * 64 + 7]
+    assert tv.shape == (2, 3, 3, 8, 5, 8)
+    assert tv[1, 2, 2, 3, 4, 7] == dm[1, 2, 4, 2 * 64 + 3 * 8 + 7]
+    np.testing.assert_array_equal(synth.untile_v(tv), dm)
+    tm = synth.rng(2).standard_normal((2, 3, 192, 24))
+    tk = synth.tile_k(tm)
+    assert tk.shape == (2, 3, 3, 3, 64, 8)
+    assert tk[1, 2, 2, 1, 5, 6] == tm[1, 2, 2 * 64 + 5, 8 + 6]
+    np.testing.assert_array_equal(synth.untile_k(tk), tm)
 
 
 def test_paged_layout_equals_contiguous():
@@ -239,11 +248,11 @@ def test_golden_attention_closed_form():
     sec = [float(x) for x in rows["ctx_key_second"].split()]
     vals = [[float(x) for x in part.split()] for part in rows["ctx_values"].split("|")]
     L = len(w)
-    k_pages = np.zeros((L, 1, 1, 2)); v_pages = np.zeros((L, 1, 1, 2, 1))
+    k_pages = np.zeros((L, 1, 1, 1, 1, 2)); v_pages = np.zeros((L, 1, 1, 1, 2, 1))   # 1-token pages
     order = [1, 0]  # token 0 in pool page 1, token 1 in pool page 0
     for t in range(L):
-        k_pages[order[t], 0, 0] = [math.log(w[t]), sec[t]]
-        v_pages[order[t], 0, 0, :, 0] = vals[t]
+        k_pages[order[t], 0, 0, 0, 0] = [math.log(w[t]), sec[t]]
+        v_pages[order[t], 0, 0, 0, :, 0] = vals[t]
     bw = float(rows["blk_key_weights"]); bs = float(rows["blk_key_second"])
     k_blk = np.array([math.log(bw), bs]).reshape(1, 1, 1, 2)
     v_blk = np.array([float(x) for x in rows["blk_values"].split()]).reshape(1, 1, 2, 1)
@@ -515,15 +524,16 @@ def test_paged_generator_places_tokens_where_the_table_says():
     spare = [p for p in range(c.k_pages.shape[0]) if p not in used]
     assert spare and all(np.isnan(c.k_pages[p]).all() for p in spare)
     # tail of the last page of sequence 0 (length 5, page 2) is poisoned
-    assert np.isnan(c.k_pages[c.block_table[0, 2], 0, 1]).all()
+    assert np.isnan(synth.untile_k(c.k_pages)[c.block_table[0, 2], 0, 1]).all()
 
 
 # ------------------------------------------------------------------------------ cache append
 
 def _paged_cache(seed, pool, Hkv, page, D, layers=2):
     r = synth.rng(seed)
-    k = [r.standard_normal((pool, Hkv, page, D)) for _ in range(layers)]
-    v = [r.standard_normal((pool, Hkv, page // 64, D, 64)) for _ in range(layers)]
+    T, CK, CV = synth.tile_widths(page, D)
+    k = [r.standard_normal((pool, Hkv, page // T, D // CK, T, CK)) for _ in range(layers)]
+    v = [r.standard_normal((pool, Hkv, page // T, T // CV, D, CV)) for _ in range(layers)]
     return k, v
 
 

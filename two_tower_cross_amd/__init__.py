@@ -21,7 +21,7 @@ from ._lib import LibraryNotBuilt, TwoTowerError, TT_BF16, TT_FP32  # noqa: F401
 
 __all__ = ["block_attn", "unmask", "qkv_projection", "out_projection", "lm_head",
            "lm_head_unmask", "kv_append", "mask_corrupt", "masked_nll", "DenoiseStep",
-           "PackedWeight", "pack_weight",
+           "PackedWeight", "pack_weight", "k_pages_shape", "v_pages_shape",
            "LibraryNotBuilt", "TwoTowerError", "library_path"]
 
 
@@ -72,10 +72,30 @@ def _run(name: str, args, device) -> None:
         raise TwoTowerError(name, st)
 
 
+def k_pages_shape(num_pages, num_kv_heads, page_size, head_dim):
+    """Shape of a K cache in the library's layout: 64-token tiles of 8-element chunks,
+    chunk-major ([..., page_size / 64, head_dim / 8, 64, 8]; see include/twotower.h)."""
+    return (num_pages, num_kv_heads, page_size // 64, head_dim // 8, 64, 8)
+
+
+def v_pages_shape(num_pages, num_kv_heads, page_size, head_dim):
+    """Shape of a V cache: 64-token tiles of 8-token chunks ([..., page_size / 64, 8, head_dim,
+    8])."""
+    return (num_pages, num_kv_heads, page_size // 64, 8, head_dim, 8)
+
+
+def _cache_dims(k_pages):
+    """(num_pages, num_kv_heads, page_size, head_dim) of a K cache tensor."""
+    if k_pages.dim() != 6 or tuple(k_pages.shape[4:]) != (64, 8):
+        raise ValueError("k_pages must have the shape k_pages_shape(...)")
+    P, Hkv, tiles, chunks = k_pages.shape[:4]
+    return P, Hkv, tiles * 64, chunks * 8
+
+
 def _attn_struct(q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, out, lse, scale,
                  max_ctx_len, num_splits):
     B, S, Hq, D = q.shape
-    P, Hkv, page, _ = k_pages.shape
+    P, Hkv, page, _ = _cache_dims(k_pages)
     a = _lib.BlockAttnArgs()
     a.batch, a.S, a.num_q_heads, a.num_kv_heads, a.head_dim = B, S, Hq, Hkv, D
     a.dtype = _dt(q)
@@ -102,14 +122,14 @@ def block_attn(q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, *, scal
     dev = q.device
     _check(q, "q", dev, ndim=4)
     B, S, Hq, D = q.shape
-    _check(k_pages, "k_pages", dev, q.dtype, 4)
-    _check(v_pages, "v_pages", dev, q.dtype, 5)
+    _check(k_pages, "k_pages", dev, q.dtype, 6)
+    _check(v_pages, "v_pages", dev, q.dtype, 6)
     _check(k_blk, "k_blk", dev, q.dtype, 4)
     _check(v_blk, "v_blk", dev, q.dtype, 4)
     _check(block_table, "block_table", dev, torch.int32, 2)
     _check(ctx_lens, "ctx_lens", dev, torch.int32, 1)
-    P, Hkv, page, Dk = k_pages.shape
-    if (Dk != D or page % 64 or tuple(v_pages.shape) != (P, Hkv, page // 64, D, 64)
+    P, Hkv, page, Dk = _cache_dims(k_pages)
+    if (Dk != D or tuple(v_pages.shape) != v_pages_shape(P, Hkv, page, D)
             or tuple(k_blk.shape) != (B, Hkv, S, D) or tuple(v_blk.shape) != (B, Hkv, D, S)
             or block_table.shape[0] != B or ctx_lens.shape[0] != B):
         raise ValueError("inconsistent attention shapes")
@@ -293,16 +313,16 @@ def kv_append(k_pages, v_pages, k_new, v_new, block_table, ctx_lens, free_pages,
     L = len(k_pages)
     if not (len(v_pages) == len(k_new) == len(v_new) == L) or L == 0:
         raise ValueError("one k_pages / v_pages / k_new / v_new tensor per layer")
-    P, Hkv, page, D = k_pages[0].shape
+    P, Hkv, page, D = _cache_dims(k_pages[0])
     B, _, S, _ = k_new[0].shape
     dt = k_pages[0].dtype
     for t in k_pages:
-        _check(t, "k_pages", dev, dt, 4)
-        if tuple(t.shape) != (P, Hkv, page, D):
+        _check(t, "k_pages", dev, dt, 6)
+        if tuple(t.shape) != k_pages_shape(P, Hkv, page, D):
             raise ValueError("k_pages shape mismatch")
     for t in v_pages:
-        _check(t, "v_pages", dev, dt, 5)
-        if tuple(t.shape) != (P, Hkv, page // 64, D, 64):
+        _check(t, "v_pages", dev, dt, 6)
+        if tuple(t.shape) != v_pages_shape(P, Hkv, page, D):
             raise ValueError("v_pages shape mismatch")
     for t in k_new:
         _check(t, "k_new", dev, dt, 4)
@@ -423,7 +443,7 @@ class DenoiseStep:
                       arr([w.data for w in w_o]), arr(self.k_blk), arr(self.v_blk)]
         a = _lib.DenoiseStepArgs()
         a.num_layers, a.hidden, a.vocab = self.L, hidden, vocab
-        P, _, page, _ = k_pages[0].shape
+        P, _, page, _ = _cache_dims(k_pages[0])
         a.attn.batch, a.attn.S = batch, S
         a.attn.num_q_heads, a.attn.num_kv_heads, a.attn.head_dim = num_q_heads, num_kv_heads, head_dim
         a.attn.dtype = a.attn.out_dtype = TT_BF16

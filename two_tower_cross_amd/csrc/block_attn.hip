@@ -8,10 +8,10 @@
 //
 // bf16 path (one work-group = 8 waves = up to 256 query rows of one (b, g), one context
 // partition):
-//   * K tiles [64 tokens][D] and V tiles [D][64 tokens] (V pages are stored as contiguous
-//     dim-major 64-token tiles, so both are single 16 KB blocks in memory) are staged in LDS
-//     with 16-byte loads; chunks are XOR-swizzled by (row & 7) so the MFMA operand reads of 32
-//     different rows hit distinct banks.
+//   * 64-token K and V tiles are contiguous 16 KB blocks of 16-byte chunks in HBM, K as
+//     [D/8 dimension chunks][64 tokens][8] and V as [8 token chunks][D][8], the order in which
+//     the MFMA operands read them; they are copied into LDS unchanged with 16-byte loads, and the
+//     operand reads of 32 lanes touch 32 consecutive chunks (no bank conflict).
 //   * Each wave owns 32 query rows and computes S^T = K Q^T with 32x32x16 bf16 MFMA: a lane then
 //     holds one query column and 16 token rows, so the softmax max/sum is in-lane plus one swap
 //     between the two wave halves. The token order inside a 32-token sub-tile is permuted (bits 2
@@ -45,15 +45,6 @@ __device__ __forceinline__ int swap_bits23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
-// XOR keys of the 16-byte chunk swizzle. K rows (one token, D*2 bytes): the 32 lanes that read
-// one MFMA operand hold tokens swap_bits23(lane) of a 32-token sub-tile, so keying on
-// swap_bits23(token) gives every group of 8 (and of 16) consecutive lanes distinct chunk slots.
-// V rows (one dimension, 128 bytes): distinct slots for 8 consecutive rows and, within each row
-// parity, for 16 consecutive rows. Both hold for 32 and for 64 LDS banks.
-template <int D>
-__device__ __forceinline__ int kkey(int t) { return swap_bits23(t & 15) & (D / 8 - 1); }
-__device__ __forceinline__ int vkey(int d) { return key128(d); }
-
 // Keep the first n (0..8) bf16 elements of a 16-byte chunk, zero the rest.
 __device__ __forceinline__ u32x4 keep_first(u32x4 v, int n) {
   u32x4 r;
@@ -65,11 +56,11 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int n) {
   return r;
 }
 
-// LDS map of the bf16 kernel: K stages [kStages][64 tokens][D], then V stages
-// [kStages][D][64 tokens], then the partition's tile indices. Every K offset, and every V offset
-// relative to VBASE (which the lanes' V offsets include), stays within the 16-bit immediate of
-// ds_read, so with the stage known at compile time each operand read is one VGPR plus an
-// immediate.
+// LDS map of the bf16 kernel: K stages, then V stages, each a 64-token tile in the cache's own
+// 16-byte-chunk order (K [D/8][64 tokens][8], V [8 token chunks][D][8]), then the partition's
+// tile indices. Every K offset, and every V offset relative to VBASE (which the lanes' V offsets
+// include), stays within the 16-bit immediate of ds_read, so with the stage known at compile time
+// each operand read is one VGPR plus an immediate.
 template <int D>
 struct Geom {
   static constexpr int KBYTES = kTile * D * 2;
@@ -85,12 +76,14 @@ struct Geom {
   static __device__ __forceinline__ constexpr int voff(int s) { return VBASE + s * VBYTES; }
 };
 
-// Per-lane constants of one wave. MFMA operand reads: the K operand for K-step kk of sub-tile 0 of
-// a stage is at kb ^ (kk * 32), the V operand for (sub-tile sub, 16-token half kc) at
-// vb ^ (sub * 64 + kc * 32) (these XORs only touch the chunk bits below the row bits, so they
-// commute with adding stage, sub-tile and 32-row block offsets). DMA: this lane's j-th 16-byte
-// chunk of a 16 KB tile comes from byte kdma (vdma) + j * kThreads * 16 of the source and goes to
-// LDS byte (j * kWaves + wave) * 1024 of the stage (the swizzle keys repeat with that step).
+// Per-lane constants of one wave. The tiles are chunk-major in HBM and in LDS, so an operand read
+// of 32 lanes (32 tokens of one 8-dimension chunk for K, 32 dimensions of one 8-token chunk for V)
+// covers 32 consecutive 16-byte slots (no bank conflict, no swizzle) and every address is one
+// register plus an immediate: the K operand of K-step kk of the sub-tile in tokens 32h .. 32h + 31
+// of a stage is at kb + kk * 2048 + h * 512; the V operand of (sub-tile sub, 16-token half kc) for
+// dimensions 32mb .. 32mb + 31 at vb + (4 sub + 2 kc) * D * 16 + mb * 512. The DMA is a straight
+// copy: a lane's j-th 16-byte chunk of a tile is byte (j * kThreads + wave * 64 + lane) * 16 of
+// the source and of the stage.
 template <int D>
 struct LaneMap {
   int kb, vb;
@@ -101,16 +94,12 @@ struct LaneMap {
     wave = wave_;
     const int col = lane & 31, hh = lane >> 5;
     const int tok = swap_bits23(col);
-    kb = tok * D * 2 + ((hh ^ kkey<D>(tok)) << 4);
-    vb = Geom<D>::VBASE + col * kTile * 2 + ((hh ^ vkey(col)) << 4);
-    const int f = wave * 64 + lane;
-    const int r = f / (D / 8), pk = f % (D / 8);
-    kdma = (uint32_t)(r * D + ((pk ^ kkey<D>(r)) << 3)) * 2u;
-    const int d = f / 8, pv = f % 8;
-    vdma = (uint32_t)(d * kTile + ((pv ^ vkey(d)) << 3)) * 2u;
+    kb = hh * 1024 + tok * 16;                   // chunk 2kk + hh of token tok
+    vb = Geom<D>::VBASE + hh * D * 16 + col * 16;  // token chunk 4sub + 2kc + hh of dimension col
+    kdma = vdma = (uint32_t)(wave * 64 + lane) * 16u;
   }
-  __device__ __forceinline__ int k(int kk) const { return kb ^ (kk * 32); }
-  __device__ __forceinline__ int v(int sub, int kc) const { return vb ^ (sub * 64 + kc * 32); }
+  __device__ __forceinline__ int k(int kk) const { return kb + kk * 2048; }
+  __device__ __forceinline__ int v(int sub, int kc) const { return vb + (sub * 4 + kc * 2) * D * 16; }
 };
 
 // Cache policy of the streaming loads: non-temporal (the KV caches are read once per step; the
@@ -124,9 +113,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *base, in
 }
 
 // Full 64-token context tile -> LDS stage s, asynchronously (buffer_load ... lds, 16 B per lane).
-// Each instruction fills 1024 contiguous LDS bytes lane by lane; the source of each lane is the
-// logical chunk that the swizzle places in that slot. The tile base goes into the (scalar) buffer
-// resource, so a lane's source is a 32-bit offset.
+// Each instruction fills 1024 contiguous LDS bytes lane by lane from the same 1024 bytes of the
+// tile. The tile base goes into the (scalar) buffer resource, so a lane's source is a 32-bit
+// offset.
 template <int D>
 __device__ __forceinline__ void dma_tile(char *smem, int s, const char *kb, const char *vb,
                                          const LaneMap<D> &lm) {
@@ -145,37 +134,29 @@ __device__ __forceinline__ void dma_tile(char *smem, int s, const char *kb, cons
 }
 
 // Partial context tile (`valid` < 64 tokens) -> LDS stage s through registers, zero-filling the
-// tokens past the end so that whatever the page holds there never reaches the MFMA. All of a
+// tokens past the end so that whatever the page holds there never reaches the MFMA. The tile is
+// copied in its own chunk order (16-byte unit u: K token u % 64, V tokens 8 (u / D) ..); all of a
 // thread's loads are issued before its first store, so the tile costs one memory round trip.
 template <int D>
 __device__ void load_tail_tile(char *smem, int s, const uint16_t *kbase, const uint16_t *vbase,
                                int valid, int tid) {
-  constexpr int KC = D / 8;
-  constexpr int NK = kTile * KC / kThreads, NV = D * 8 / kThreads;
-  uint16_t *ks = reinterpret_cast<uint16_t *>(smem + Geom<D>::koff(s));
-  uint16_t *vs = reinterpret_cast<uint16_t *>(smem + Geom<D>::voff(s));
+  constexpr int NU = kTile * D / 8 / kThreads;  // 16-byte units per thread (K and V alike)
+  char *ks = smem + Geom<D>::koff(s);
+  char *vs = smem + Geom<D>::voff(s);
   const u32x4 z = {0u, 0u, 0u, 0u};
-  u32x4 xk[NK], xv[NV];
+  u32x4 xk[NU], xv[NU];
 #pragma unroll
-  for (int j = 0; j < NK; ++j) {
-    const int f = tid + j * kThreads, r = f / KC, c = f % KC;
-    xk[j] = r < valid ? ld_global_16(kbase + (size_t)r * D + c * 8) : z;
+  for (int j = 0; j < NU; ++j) {
+    const int u = tid + j * kThreads;
+    xk[j] = (u & 63) < valid ? ld_global_16(kbase + (size_t)u * 8) : z;
+    xv[j] = (u / D) * 8 < valid ? ld_global_16(vbase + (size_t)u * 8) : z;
   }
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int f = tid + j * kThreads, d = f / 8, c = f % 8;
-    xv[j] = c * 8 < valid ? ld_global_16(vbase + (size_t)d * kTile + c * 8) : z;
-  }
-#pragma unroll
-  for (int j = 0; j < NK; ++j) {
-    const int f = tid + j * kThreads, r = f / KC, c = f % KC;
-    st_lds_16(ks + r * D + ((c ^ kkey<D>(r)) << 3), xk[j]);
-  }
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int f = tid + j * kThreads, d = f / 8, c = f % 8;
-    const int n = valid - c * 8;
-    st_lds_16(vs + d * kTile + ((c ^ vkey(d)) << 3), keep_first(xv[j], n < 0 ? 0 : (n > 8 ? 8 : n)));
+  for (int j = 0; j < NU; ++j) {
+    const int u = tid + j * kThreads;
+    const int n = valid - (u / D) * 8;
+    st_lds_16(ks + u * 16, xk[j]);
+    st_lds_16(vs + u * 16, keep_first(xv[j], n < 0 ? 0 : (n > 8 ? 8 : n)));
   }
 }
 
@@ -222,23 +203,23 @@ __device__ __forceinline__ void fetch_block_tile(BlockRegs<D> &br, const uint16_
   }
 }
 
-// ... then into LDS stage s (swizzled like the ring's tiles).
+// ... then into LDS stage s (in the chunk-major order of the ring's tiles).
 template <int D>
 __device__ __forceinline__ void store_block_tile(char *smem, int s, const BlockRegs<D> &br, int tid) {
   constexpr int KC = D / 8;
   constexpr int NK = BlockRegs<D>::NK, NV = BlockRegs<D>::NV;
-  uint16_t *ks = reinterpret_cast<uint16_t *>(smem + Geom<D>::koff(s));
-  uint16_t *vs = reinterpret_cast<uint16_t *>(smem + Geom<D>::voff(s));
+  char *ks = smem + Geom<D>::koff(s);
+  char *vs = smem + Geom<D>::voff(s);
   const u32x4 *xk = br.xk, *xv = br.xv;
 #pragma unroll
-  for (int j = 0; j < NK; ++j) {
+  for (int j = 0; j < NK; ++j) {  // chunk c of row r -> K unit c * 64 + r
     const int f = tid + j * kThreads, r = f / KC, c = f % KC;
-    st_lds_16(ks + r * D + ((c ^ kkey<D>(r)) << 3), xk[j]);
+    st_lds_16(ks + (c * kTile + r) * 16, xk[j]);
   }
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
+  for (int j = 0; j < NV; ++j) {  // tokens 8c .. of dimension d -> V unit c * D + d
     const int f = tid + j * kThreads, d = f / 8, c = f % 8;
-    st_lds_16(vs + d * kTile + ((c ^ vkey(d)) << 3), xv[j]);
+    st_lds_16(vs + (c * D + d) * 16, xv[j]);
   }
 }
 
@@ -268,7 +249,7 @@ __device__ __forceinline__ void attend_tile(const char *smem, int kst, int vst, 
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     a0[kk] = ld_lds_16(smem + kst + lm.k(kk));
-    a1[kk] = ld_lds_16(smem + kst + 32 * D * 2 + lm.k(kk));
+    a1[kk] = ld_lds_16(smem + kst + 32 * 16 + lm.k(kk));
   }
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
@@ -319,13 +300,13 @@ __device__ __forceinline__ void attend_tile(const char *smem, int kst, int vst, 
   u32x4 v0[D / 16], v1[D / 16];
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) {
-    v0[2 * mb] = ld_lds_16(smem + vst + mb * 32 * kTile * 2 + lm.v(0, 0));
-    v0[2 * mb + 1] = ld_lds_16(smem + vst + mb * 32 * kTile * 2 + lm.v(0, 1));
+    v0[2 * mb] = ld_lds_16(smem + vst + mb * 32 * 16 + lm.v(0, 0));
+    v0[2 * mb + 1] = ld_lds_16(smem + vst + mb * 32 * 16 + lm.v(0, 1));
   }
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) {
-    v1[2 * mb] = ld_lds_16(smem + vst + mb * 32 * kTile * 2 + lm.v(1, 0));
-    v1[2 * mb + 1] = ld_lds_16(smem + vst + mb * 32 * kTile * 2 + lm.v(1, 1));
+    v1[2 * mb] = ld_lds_16(smem + vst + mb * 32 * 16 + lm.v(1, 0));
+    v1[2 * mb + 1] = ld_lds_16(smem + vst + mb * 32 * 16 + lm.v(1, 1));
   }
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) {
@@ -390,10 +371,10 @@ __device__ __forceinline__ void pipe_mma(const char *smem, const LaneMap<D> &lm,
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
       r.v[2 * mb + kc] = ld_lds_16(smem + (Geom<D>::voff(VS) - Geom<D>::VBASE) +
-                                   mb * 32 * kTile * 2 + lm.v(VH, kc));
+                                   mb * 32 * 16 + lm.v(VH, kc));
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
-    r.k[kk] = ld_lds_16(smem + Geom<D>::koff(KS) + KH * 32 * D * 2 + lm.k(kk));
+    r.k[kk] = ld_lds_16(smem + Geom<D>::koff(KS) + KH * 32 * 16 + lm.k(kk));
   // Each operand read follows the MFMA that last used its registers.
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -464,7 +445,7 @@ __device__ __forceinline__ void pipe_start(const char *smem, const LaneMap<D> &l
   for (int kk = 0; kk < D / 16; ++kk) k0[kk] = ld_lds_16(smem + Geom<D>::koff(0) + lm.k(kk));
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
-    r.k[kk] = ld_lds_16(smem + Geom<D>::koff(0) + 32 * D * 2 + lm.k(kk));
+    r.k[kk] = ld_lds_16(smem + Geom<D>::koff(0) + 32 * 16 + lm.k(kk));
   r.s = f32x16{};
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) r.s = mfma32x32x16(k0[kk], qreg[kk], r.s);
@@ -871,13 +852,15 @@ __global__ __launch_bounds__(256) void block_attn_f32_kernel(AttnParams p) {
         if (page < 0 || page >= p.num_pages) {
           key = nullptr;
         } else {
-          key = kp + (((size_t)page * p.Hkv + g) * p.page_size + t % p.page_size) * D;
+          key = kp + ((size_t)page * p.Hkv + g) * p.page_size * D;  // the (page, head) block
         }
       }
       if (key) {
         float acc = 0.f;
+        const int o = (j - p.S) % p.page_size;
         for (int d = 0; d < D; d += 4) {
-          const f32x4 kv = *reinterpret_cast<const f32x4 *>(key + d);
+          const f32x4 kv = *reinterpret_cast<const f32x4 *>(
+              key + (j < p.S ? (size_t)d : k_elem(o, d, D)));
           acc = fmaf(qs[d], kv[0], acc);
           acc = fmaf(qs[d + 1], kv[1], acc);
           acc = fmaf(qs[d + 2], kv[2], acc);
@@ -911,8 +894,7 @@ __global__ __launch_bounds__(256) void block_attn_f32_kernel(AttnParams p) {
           const int page = btab[tt / p.page_size];
           const int off = tt % p.page_size;
           v = (page >= 0 && page < p.num_pages)
-                  ? vp[((((size_t)page * p.Hkv + g) * (p.page_size / kTile) + off / kTile) * D + tid) *
-                           kTile + off % kTile]
+                  ? vp[((size_t)page * p.Hkv + g) * p.page_size * D + v_elem(off, tid, D)]
                   : 0.f;
         }
         acc = fmaf(pw[t], v, acc);

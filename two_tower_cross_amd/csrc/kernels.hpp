@@ -7,6 +7,18 @@
 
 namespace tt {
 
+// Context cache layout. A (page, KV head) block holds page_size tokens x D elements as 64-token
+// tiles; a tile is made of 8-element chunks (16 bytes in bf16) in chunk-major order:
+//   K tile [D / 8][64 tokens][8 dims]      (the 64 tokens of one 8-dimension chunk together)
+//   V tile [8 token chunks][D][8 tokens]   (8 consecutive tokens of one dimension together)
+// Element offsets of (token o of the page, dimension d) within the block:
+__host__ __device__ inline size_t k_elem(int o, int d, int D) {
+  return ((size_t)(o >> 6) * (D >> 3) + (d >> 3)) * 512 + (size_t)(o & 63) * 8 + (d & 7);
+}
+__host__ __device__ inline size_t v_elem(int o, int d, int D) {
+  return (((size_t)(o >> 6) * 8 + ((o & 63) >> 3)) * D + d) * 8 + (o & 7);
+}
+
 // ---------------------------------------------------------------------------- block attention
 struct AttnParams {
   const void *q, *k_pages, *v_pages, *k_blk, *v_blk;

@@ -8,7 +8,7 @@
 //   block table too short, a length outside the cache, or a page id outside the pools) is skipped
 //   and flagged in *status, so the copy below never writes outside the pools.
 // kv_write_kernel: one work-group per (sequence, KV head, layer) copies the block's S key rows
-//   (token-major pages) and value rows (dim-major 64-token tiles) to their cache slots.
+//   and value rows to their cache slots (the chunk-major 64-token tiles of k_elem / v_elem).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -66,12 +66,12 @@ __global__ __launch_bounds__(256) void kv_write_kernel(AppendParams p) {
   for (int e = threadIdx.x; e < S * D; e += 256) {
     const int i = e / D, d = e % D;               // key row i, dimension d (rows contiguous)
     const int t = L + i, page = table[t / P], off = t % P;
-    kp[(((size_t)page * Hkv + g) * P + off) * D + d] = kn[e];
+    kp[((size_t)page * Hkv + g) * P * D + k_elem(off, d, D)] = kn[e];
   }
   for (int e = threadIdx.x; e < S * D; e += 256) {
     const int d = e / S, i = e % S;               // value dimension d, row i (rows contiguous)
     const int t = L + i, page = table[t / P], off = t % P;
-    vp[((((size_t)page * Hkv + g) * (P / 64) + off / 64) * D + d) * 64 + off % 64] = vn[e];
+    vp[((size_t)page * Hkv + g) * P * D + v_elem(off, d, D)] = vn[e];
   }
 }
 

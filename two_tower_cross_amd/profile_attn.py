@@ -18,8 +18,8 @@ def main(launches: int = 4) -> None:
     g = torch.Generator(device=dev).manual_seed(1)
     B, S, Hq, Hkv, D, L = 8, 16, 32, 2, 128, 32768
     bf = torch.bfloat16
-    k = torch.randn((B, Hkv, L, D), generator=g, device=dev).to(bf)
-    v = torch.randn((B, Hkv, L // 64, D, 64), generator=g, device=dev).to(bf)
+    k = torch.randn(tt.k_pages_shape(B, Hkv, L, D), generator=g, device=dev).to(bf)
+    v = torch.randn(tt.v_pages_shape(B, Hkv, L, D), generator=g, device=dev).to(bf)
     q = torch.randn((B, S, Hq, D), generator=g, device=dev).to(bf)
     kb = torch.randn((B, Hkv, S, D), generator=g, device=dev).to(bf)
     vb = torch.randn((B, Hkv, D, S), generator=g, device=dev).to(bf)
