@@ -514,8 +514,12 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   if (has_block) fetch_block_tile<D>(br, kblk, vblk, min(p.S, kTile), p.S, tid);
   const int32_t *btab = p.block_table + (size_t)b * p.max_pages;
   const int n_spec = p.chunk / kTile;               // tiles of a full partition
+  // Up to 64 tiles, every wave requests all of the pages (lane i: tile i) and keeps the tile
+  // indices in a register; beyond, the work-group requests them once and stages them in LDS.
+  const bool ids_in_regs = n_spec <= 64;
+  const int li = ids_in_regs ? lane : tid;
   int spec_page = 0;
-  if (tid < n_spec) spec_page = btab[min((t_begin + tid * kTile) / p.page_size, p.max_pages - 1)];
+  if (li < n_spec) spec_page = btab[min((t_begin + li * kTile) / p.page_size, p.max_pages - 1)];
 
   bool bad = L < 0 || L > p.max_ctx_len;
   const int Lc = bad ? 0 : L;
@@ -526,22 +530,32 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   const int n_full = n_ctx / kTile;            // full tiles: asynchronous ring
   const int tail = n_ctx - n_full * kTile;     // tokens of the last, partial tile
 
-  // K and V pools are both sequences of 16 KB tiles (K [64 tokens][D], V [D][64 tokens]); context
-  // tile n of this partition (tokens t_begin + 64n ...) is tile (page * Hkv + g) * (page_size / 64)
-  // + (offset in page) / 64 of either pool. The partition's tile indices are staged in LDS once, so
-  // the ring issues no vector load of its own besides the DMA. A page id outside the pool makes the
-  // sequence bad: nothing is loaded through it and its outputs become NaN.
+  // K and V pools are both sequences of 16 KB tiles (chunk-major 64-token tiles); context tile n of
+  // this partition (tokens t_begin + 64n ...) is tile (page * Hkv + g) * (page_size / 64) + (offset
+  // in page) / 64 of either pool. The partition's tile indices are computed once (in a register of
+  // every wave up to 64 tiles, else in LDS), so the ring issues no vector load of its own besides
+  // the DMA. A page id outside the pool makes the sequence bad: nothing is loaded through it and
+  // its outputs become NaN.
   int *tile_ids = reinterpret_cast<int *>(smem + Geom<D>::IDS);
   const int n_tiles = (n_ctx + kTile - 1) / kTile;
   const int tpp = p.page_size / kTile;
-  int page_bad = 0;
-  for (int i = tid; i < n_tiles; i += kThreads) {
-    const int t = t_begin + i * kTile;
-    const int page = i < kThreads ? spec_page : btab[t / p.page_size];
-    page_bad |= page < 0 || page >= p.num_pages;
-    tile_ids[i] = (page * p.Hkv + g) * tpp + (t % p.page_size) / kTile;
-  }
-  {
+  int my_tile = 0;  // register path: the index of tile `lane`
+  if (ids_in_regs) {
+    // Every wave sees every page, so each reaches the same verdict without a barrier.
+    int page_bad = 0;
+    if (lane < n_tiles) {
+      page_bad = spec_page < 0 || spec_page >= p.num_pages;
+      my_tile = (spec_page * p.Hkv + g) * tpp + ((t_begin + lane * kTile) % p.page_size) / kTile;
+    }
+    if (__ballot(page_bad) != 0) bad = true;
+  } else {
+    int page_bad = 0;
+    for (int i = tid; i < n_tiles; i += kThreads) {
+      const int t = t_begin + i * kTile;
+      const int page = i < kThreads ? spec_page : btab[t / p.page_size];
+      page_bad |= page < 0 || page >= p.num_pages;
+      tile_ids[i] = (page * p.Hkv + g) * tpp + (t % p.page_size) / kTile;
+    }
     int *flags = reinterpret_cast<int *>(smem + Geom<D>::FLAGS);
     const bool wave_bad = __ballot(page_bad) != 0;
     if (lane == 0) flags[wave] = wave_bad;
@@ -551,6 +565,12 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
     for (int w = 0; w < kWaves; ++w) any |= flags[w];
     if (any) bad = true;
   }
+  // Index of context tile n (n uniform); on the LDS path it is read after a barrier, when this
+  // wave has no LDS read in flight.
+  auto tile_index = [&](int n) {
+    return ids_in_regs ? __builtin_amdgcn_readlane(my_tile, n)
+                       : __builtin_amdgcn_readfirstlane(tile_ids[n]);
+  };
   const int n_full_ok = bad ? 0 : n_full;
   const int tail_ok = bad ? 0 : tail;
   const char *kpool = static_cast<const char *>(p.k_pages);
@@ -559,10 +579,9 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
 
   LaneMap<D> lm;
   lm.init(lane, wave);
-  // DMA of context tile n into stage n % kStages (tile indices are read after a barrier, when this
-  // wave has no LDS read in flight).
+  // DMA of context tile n into stage n % kStages.
   auto dma_ctx_tile = [&](int n, int stage) {
-    const size_t off = (size_t)__builtin_amdgcn_readfirstlane(tile_ids[n]) * kTileBytes;
+    const size_t off = (size_t)tile_index(n) * kTileBytes;
     dma_tile<D>(smem, stage, kpool + off, vpool + off, lm);
   };
 
@@ -631,7 +650,7 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   if (tail_ok > 0) {
     lds_barrier();  // every wave is done with the ring before a stage is overwritten
     const int st = n_full_ok % kStages;
-    const size_t off = (size_t)__builtin_amdgcn_readfirstlane(tile_ids[n_full_ok]) * kTileBytes;
+    const size_t off = (size_t)tile_index(n_full_ok) * kTileBytes;
     load_tail_tile<D>(smem, st, reinterpret_cast<const uint16_t *>(kpool + off),
                       reinterpret_cast<const uint16_t *>(vpool + off), tail_ok, tid);
     lds_barrier();
