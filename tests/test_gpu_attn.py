@@ -206,6 +206,23 @@ def test_bad_lengths_and_pages_give_nan_rows_only():
         assert max_abs(out[0], ref[0]) <= TOL_BF16
 
 
+@pytest.mark.parametrize("L", [4096, 4160])
+def test_partition_tile_index_paths(L):
+    """One partition of 64 tiles keeps its tile indices in registers and one of 65 stages them in
+    LDS. Both must match the oracle, and both must catch a bad page in the partition's last tile."""
+    case = synth.attn_case(83, B=2, S=16, Hq=8, Hkv=2, D=128, ctx_lens=[L, L - 100], page_size=64,
+                           dtype="bf16")
+    out, lse = gpu_attn(case, num_splits=1, max_ctx_len=L)
+    ref = check(case, out, lse, TOL_BF16)
+    d = dev_case(case)
+    bt = d["block_table"].clone()
+    bt[0, L // 64 - 1] = 10_000           # the last page of sequence 0, outside the pool
+    d.update(block_table=bt)
+    out, lse = gpu_attn(case, d, num_splits=1, max_ctx_len=L)
+    assert np.isnan(out[0]).all() and np.isnan(lse[0]).all()
+    assert max_abs(out[1], ref[1]) <= TOL_BF16
+
+
 def test_deterministic_and_outputs_stay_in_bounds():
     case = synth.config_attn("ctx4k_bf16", ctx_len=3000)
     d = dev_case(case)
