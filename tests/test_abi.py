@@ -257,3 +257,25 @@ def test_loss_entry_points_validate_and_size():
         for k, v in over.items():
             setattr(b, k, v)
         assert query("twotower_masked_nll", b)[0] == code, over
+
+
+def test_cache_shape_helpers_match_the_tiled_layouts():
+    """k_pages_shape / v_pages_shape are the shapes of the header's tiled caches: a token-major
+    [pages, Hkv, page, D] K cache tiled by synth.tile_k and a dim-major V cache tiled by
+    synth.tile_v (64-token tiles of 8-wide chunks) land exactly there, and the binding's shape
+    check accepts them and refuses the untiled layouts."""
+    import numpy as np
+    import torch
+
+    import synth
+    import two_tower_cross_amd as tt
+
+    P, Hkv, page, D = 3, 2, 128, 64
+    k = np.zeros((P, Hkv, page, D), np.float32)
+    v = np.zeros((P, Hkv, D, page), np.float32)
+    assert synth.tile_k(k).shape == tt.k_pages_shape(P, Hkv, page, D)
+    assert synth.tile_v(v).shape == tt.v_pages_shape(P, Hkv, page, D)
+    assert tt._cache_dims(torch.empty(tt.k_pages_shape(P, Hkv, page, D))) == (P, Hkv, page, D)
+    for bad in [(P, Hkv, page, D), (P, Hkv, page // 64, D, 64), (P, Hkv, 2, 8, 32, 8)]:
+        with pytest.raises(ValueError):
+            tt._cache_dims(torch.empty(bad))
