@@ -1,17 +1,25 @@
-"""Benchmark: committed tokens/s of the TwoTower denoise-step block loop on one MI355X.
+"""Benchmark: committed tokens/s of the TwoTower denoise-step block loop on one MI355X, plus the
+attention and unmasking workloads at their own shapes.
 
-Workload (one "step" of this benchmark = one block): batch 8, 6 attention layers, context 32768
-tokens per sequence (resident bf16 KV caches, 1.61 GB), block S = 16, T = 16 denoise steps, hidden
-2048, Hq = 32 / Hkv = 2, head_dim 128, vocab 131072, threshold 0.9 with the one-commit fallback and
-commit-all at the last step. Every denoise step rewrites the block KV of every layer (QKV
-projection), runs the block attention over [context KV ; block KV] of the same layer, the output
-projection with the residual add, the lm-head to fp32 logits and the confidence unmasking.
-Inputs are synthetic (seeded on-device draws) and resident in HBM before timing starts.
+Headline workload (one "step" of this benchmark = one block): batch 8, 6 attention layers, context
+32768 tokens per sequence (resident bf16 KV caches, 1.61 GB), block S = 16, T = 16 denoise steps,
+hidden 2048, Hq = 32 / Hkv = 2, head_dim 128, vocab 131072, threshold 0.9 with the one-commit
+fallback and commit-all at the last step. Every denoise step rewrites the block KV of every layer
+(QKV projection), runs the block attention over [context KV ; block KV] of the same layer, the
+output projection with the residual add, the lm-head and the confidence unmasking. Inputs are
+synthetic (seeded on-device draws) and resident in HBM before timing starts.
 
-Prints one JSON line. ``value`` is committed tokens/s over the timed blocks; ``roofline``
-reports the block-attention kernel (the dominant kernel) as algorithmic HBM bytes per launch over
-its average launch duration, taken from HIP events recorded around every launch of it inside the
-timed region; ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same workload.
+Prints one JSON line. ``value`` is committed tokens/s over the timed blocks. ``roofline`` reports
+the block-attention call of the loop (main kernel + partition merge, the dominant work of a step)
+as algorithmic HBM bytes per call (context K+V, block K+V, Q read, O write) over the call's mean
+duration, from HIP events that the library records around both kernels of every call inside the
+timed region; ``roofline.kernel_only`` gives the main kernel alone. ``workloads`` holds the other
+shapes (tiny fp32; 4K context with the 16 x 131072 unmasking; a ragged paged batch of 32; a 131072-
+token context at 64/128/256/auto partitions), each timed over 50 calls with a 1 GiB write between
+calls (outside the timed events) so that no input is served from the 256 MB last-level cache, as
+median and minimum, with the fp64 CPU oracle's time and its max-abs deviation on the same inputs.
+``stream_read_ceiling_GBps`` is a plain streaming read of 2 GiB measured in the same run.
+``cpu_baseline`` times the oracle on a bounded sample of the headline workload.
 """
 from __future__ import annotations
 
@@ -19,6 +27,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -29,25 +38,49 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0   # dense bf16
 THRESHOLD = 0.9
-ATTN_SOURCE = os.path.join(ROOT, "two_tower_cross_amd", "csrc", "block_attn.hip")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "block_attn_bf16_128_loop32k_traffic.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "step_kernels_loop32k_traffic.md")
+TIMED_CALLS = 50
+SCRUB_BYTES = 1 << 30
 
 
-def attn_bytes_per_launch(B, L, S, Hq, Hkv, D, e=2):
-    """Algorithmic bytes the block-attention kernel must move per launch: context K+V, block K+V
-    and Q (its reads; the output is written by the partition merge)."""
-    ctx = 2 * B * Hkv * L * D * e
-    blk = 2 * B * Hkv * S * D * e
-    q = B * S * Hq * D * e
-    return ctx + blk + q
+def attn_bytes(ctx_lens, S, Hq, Hkv, D, e=2):
+    """Algorithmic bytes of one attention call: context K+V of every sequence, block K+V, the Q
+    read and the O write."""
+    B = len(ctx_lens)
+    ctx = sum(2 * Hkv * int(L) * D * e for L in ctx_lens)
+    return ctx + 2 * B * Hkv * S * D * e + 2 * B * S * Hq * D * e
 
 
-def attn_flops_per_launch(B, L, S, Hq, D):
+def attn_flops(ctx_lens, S, Hq, D):
     """QK^T and PV over every (context + block) key of every query row: 4 flops per row, key, dim."""
-    return 4 * B * Hq * S * (L + S) * D
+    return sum(4 * Hq * S * (int(L) + S) * D for L in ctx_lens)
 
 
-def cpu_baseline(m, threads_note, steps=2):
+def stats_us(xs):
+    return {"median": round(statistics.median(xs), 2), "min": round(min(xs), 2),
+            "n": len(xs)}
+
+
+def host_description():
+    return {"sched_getaffinity": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count(),
+            "blas_threads": blas_threads()}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    for var in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS"):
+        if os.environ.get(var, "").isdigit():
+            return int(os.environ[var])
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(m, steps=2):
     """The fp64 oracle on the whole batch for the first ``steps`` denoise steps of a block (each:
     6 layers of QKV projection, block attention and output projection; lm-head; unmasking with
     the one-commit fallback). tokens/s = tokens committed / seconds."""
@@ -71,32 +104,197 @@ def cpu_baseline(m, threads_note, steps=2):
             scale=1.0 / math.sqrt(m.D), threshold=THRESHOLD, min_commit=True)
         n_tok += int(n.sum())
     dt = time.perf_counter() - t0
-    return {"value": n_tok / dt, "unit": "committed tokens/s", "cores": threads_note,
+    host = host_description()
+    return {"value": n_tok / dt, "unit": "committed tokens/s", "cores": host["blas_threads"],
             "kind": "oracle",
             "sample": f"the first {steps} of {m.T} denoise steps of one block, whole batch of "
                       f"{m.B} at context {m.L} (6 layers, lm-head {m.vocab}, unmask): "
-                      f"{dt:.2f} s for {n_tok} committed tokens"}
+                      f"{dt:.2f} s for {n_tok} committed tokens",
+            "host": host}
 
 
-def measured_traffic():
-    """HBM bytes per launch of the attention kernel from the committed counter summary, or None
+def measured_traffic(kernels):
+    """HBM bytes per call summed over ``kernels`` from the committed counter summary, or None
     when there is none or the kernel source changed since the counters were taken."""
     try:
         from two_tower_cross_amd import traffic
-        return traffic.bytes_per_launch(TRAFFIC_SUMMARY, ATTN_SOURCE)
+        return traffic.bytes_per_launch(TRAFFIC_SUMMARY, kernels)
     except Exception:
         return None
 
 
-def blas_threads():
-    try:
-        from threadpoolctl import threadpool_info
-        n = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
-        if n:
-            return int(max(n))
-    except Exception:
-        pass
-    return len(os.sched_getaffinity(0))
+class Timer:
+    """Timed calls of a workload, each preceded by a 1 GiB write (outside the events)."""
+
+    def __init__(self, torch, dev):
+        self.torch = torch
+        self.scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device=dev)
+
+    def events(self, n):
+        evs = [self.torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record()          # materialize the underlying hipEvent_t
+        return evs
+
+    def run(self, call, *, calls=TIMED_CALLS, warmup=3, n_events=3, reset=None):
+        """call(events) enqueues one call and records the events; returns per-call lists of
+        elapsed microseconds between event 0 and every later event."""
+        torch = self.torch
+        for _ in range(warmup):
+            if reset:
+                reset()
+            call(None)
+        torch.cuda.synchronize()
+        evs = [self.events(n_events) for _ in range(calls)]
+        torch.cuda.synchronize()
+        for i in range(calls):
+            if reset:
+                reset()
+            self.scrub.fill_(i & 0xFF)
+            call(evs[i])
+        torch.cuda.synchronize()
+        return [[1e3 * e[0].elapsed_time(e[k]) for e in evs] for k in range(1, n_events)]
+
+
+def attention_workload(name, case, timer, splits_list, *, out_dtype, oracle_time=True):
+    """Times twotower_block_attn on ``case`` for each partition count; oracle time and max-abs
+    deviation of the last GPU output."""
+    import numpy as np
+    import torch
+    import two_tower_cross_amd as tt
+    from oracle import attention as oattn
+
+    dev = torch.device("cuda", 0)
+    dt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+    f = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt)
+    d = dict(q=f(case.q), k_pages=f(case.k_pages), v_pages=f(case.v_pages),
+             block_table=torch.from_numpy(case.block_table).to(dev),
+             ctx_lens=torch.from_numpy(case.ctx_lens).to(dev), k_blk=f(case.k_blk),
+             v_blk=f(case.v_blk))
+    lens = [int(x) for x in case.ctx_lens]
+    e = 2 if case.dtype == "bf16" else 4
+    nbytes = attn_bytes(lens, case.S, case.Hq, case.Hkv, case.D, e)
+    flops = attn_flops(lens, case.S, case.Hq, case.D)
+    out = torch.empty((case.B, case.S, case.Hq, case.D), dtype=out_dtype, device=dev)
+    res = {"bytes": nbytes, "flops": flops, "calls": {}}
+    for splits in splits_list:
+        def call(evs, splits=splits):
+            tt.block_attn(d["q"], d["k_pages"], d["v_pages"], d["block_table"], d["ctx_lens"],
+                          d["k_blk"], d["v_blk"], scale=case.scale, max_ctx_len=max(lens),
+                          num_splits=splits, out=out,
+                          timing_events=None if evs is None else [x.cuda_event for x in evs])
+        kern, whole = timer.run(call)
+        med = statistics.median(whole)
+        res["calls"]["auto" if splits == 0 else str(splits)] = {
+            "us": stats_us(whole), "kernel_us": stats_us(kern),
+            "GBps": round(nbytes / med / 1e3, 1),
+            "frac": round(nbytes / med / 1e3 / HBM_PEAK_GBPS, 4),
+            "kernel_frac": round(nbytes / statistics.median(kern) / 1e3 / HBM_PEAK_GBPS, 4),
+            "TFLOPs": round(flops / med / 1e6, 1)}
+    if oracle_time:
+        t0 = time.perf_counter()
+        ref, _ = oattn.block_attention_case(case)
+        res["oracle_s"] = round(time.perf_counter() - t0, 3)
+        res["max_abs_err_last_call"] = float(np.abs(out.float().cpu().numpy() - ref).max())
+    res["workload"] = name
+    return res
+
+
+def unmask_workload(name, logits_np, timer):
+    import numpy as np
+    import torch
+    import two_tower_cross_amd as tt
+    from oracle import unmask as ounmask
+
+    dev = torch.device("cuda", 0)
+    B, S, V = logits_np.shape
+    logits = torch.from_numpy(logits_np).to(dev)
+    masked = torch.ones((B, S), dtype=torch.uint8, device=dev)
+    tokens = torch.full((B, S), -1, dtype=torch.int32, device=dev)
+    conf = torch.empty((B, S), dtype=torch.float32, device=dev)
+    ncom = torch.empty((B,), dtype=torch.int32, device=dev)
+
+    def reset():
+        masked.fill_(1)
+        tokens.fill_(-1)
+
+    def call(evs):
+        if evs is not None:
+            evs[0].record()
+        tt.unmask(logits, masked, tokens, THRESHOLD, min_commit=True, confidence=conf,
+                  n_committed=ncom)
+        if evs is not None:
+            evs[1].record()
+
+    (whole,) = timer.run(call, reset=reset, n_events=2)
+    nbytes = B * S * V * 4
+    med = statistics.median(whole)
+    t0 = time.perf_counter()
+    ot, om, _, _ = ounmask.confidence_unmask(logits_np, np.ones((B, S), np.uint8),
+                                             np.full((B, S), -1, np.int32), np.float32(THRESHOLD),
+                                             min_commit=True)
+    oracle_s = time.perf_counter() - t0
+    same = bool(np.array_equal(tokens.cpu().numpy(), ot) and np.array_equal(masked.cpu().numpy(), om))
+    return {"workload": name, "bytes": nbytes, "us": stats_us(whole),
+            "GBps": round(nbytes / med / 1e3, 1),
+            "frac": round(nbytes / med / 1e3 / HBM_PEAK_GBPS, 4),
+            "oracle_s": round(oracle_s, 3), "commits_equal_oracle": same}
+
+
+def stream_ceiling(timer, dev):
+    import torch
+    import two_tower_cross_amd as tt
+
+    nbytes = 2 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(3)
+    sink = torch.zeros(65536, dtype=torch.int32, device=dev)
+    best = None
+    for wg in (256, 512, 1024, 2048, 4096):
+        def call(evs, wg=wg):
+            if evs is not None:
+                evs[0].record()
+            tt.probe_stream_read(src, wg, sink)
+            if evs is not None:
+                evs[1].record()
+        (us,) = timer.run(call, calls=10, n_events=2)
+        gbps = nbytes / statistics.median(us) / 1e3
+        if best is None or gbps > best[0]:
+            best = (gbps, wg)
+    del src
+    return {"GBps": round(best[0], 1), "frac_of_peak": round(best[0] / HBM_PEAK_GBPS, 4),
+            "workgroups": best[1], "bytes": nbytes}
+
+
+def workloads(dev):
+    import synth
+    import torch
+
+    timer = Timer(torch, dev)
+    out = {}
+    out["stream_read_ceiling"] = stream_ceiling(timer, dev)
+    print("bench: stream ceiling done", file=sys.stderr, flush=True)
+    out["tiny_fp32"] = attention_workload(
+        "tiny fp32: L 256, S 16, Hq 4 / Hkv 1, head_dim 64", synth.config_attn("tiny_fp32"),
+        timer, [0], out_dtype=torch.float32)
+    out["tiny_fp32_unmask"] = unmask_workload("tiny fp32 unmask: 16 x 1024 logits ~ N(0, 3)",
+                                              synth.config_logits("tiny_fp32"), timer)
+    out["ctx4k"] = attention_workload(
+        "4K context bf16: B 1, L 4096, S 16, Hq 32 / Hkv 2, head_dim 128",
+        synth.config_attn("ctx4k_bf16"), timer, [0], out_dtype=torch.bfloat16)
+    out["ctx4k_unmask"] = unmask_workload(
+        "4K-context unmask: 16 x 131072 logits ~ N(0, 4) + one planted peak per row",
+        synth.config_logits("ctx4k_bf16"), timer)
+    print("bench: tiny and 4K workloads done", file=sys.stderr, flush=True)
+    out["ragged32"] = attention_workload(
+        "ragged paged batch bf16: B 32, L ~ U[1024, 8192], 256-token pages in random order",
+        synth.config_attn("ragged32_paged"), timer, [0], out_dtype=torch.bfloat16)
+    print("bench: ragged workload done", file=sys.stderr, flush=True)
+    out["ctx128k"] = attention_workload(
+        "131072-token context bf16: B 1, S 16, Hq 32 / Hkv 2, head_dim 128, 1% outlier keys x8",
+        synth.config_attn("long128k"), timer, [64, 128, 256, 0], out_dtype=torch.bfloat16)
+    print("bench: 128K workload done", file=sys.stderr, flush=True)
+    del timer
+    return out
 
 
 def main():
@@ -105,8 +303,10 @@ def main():
     ap.add_argument("--steps", type=int, default=10, help="timed blocks (T denoise steps each)")
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the tiny / 4K / ragged / 128K workloads after the block loop")
     ap.add_argument("--no-events", action="store_true",
-                    help="do not record per-launch attention events")
+                    help="do not record per-call attention events")
     ap.add_argument("--block-size", type=int, default=16, metavar="S",
                     help="block size S (16 is the benchmark's workload; the pages also use 32 and "
                          "128)")
@@ -141,14 +341,16 @@ def main():
             e.record()          # materialize the underlying hipEvent_t
         return evs
 
+    ev_per_step = 3 * m.layers
+
     def run_block(events=None, k=None):
         masked.fill_(1)
         tokens.fill_(-1)
         for t in range(m.T):
             ev = None
             if events is not None:
-                base = t * 2 * m.layers
-                ev = [events[base + i].cuda_event for i in range(2 * m.layers)]
+                base = t * ev_per_step
+                ev = [events[base + i].cuda_event for i in range(ev_per_step)]
             step(m.h_steps[t], masked, tokens, threshold=THRESHOLD, min_commit=True,
                  commit_all=(t == m.T - 1), timing_events=ev,
                  n_committed=None if k is None else counts[k, t])
@@ -157,7 +359,7 @@ def main():
         run_block()
     torch.cuda.synchronize()
 
-    per_block = 2 * m.layers * m.T
+    per_block = ev_per_step * m.T
     events = None if args.no_events else make_events(per_block * args.steps)
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -172,27 +374,37 @@ def main():
     assert not masked.any().item(), "a block ended with masked positions"
     ms_per_block = ms_total / args.steps
     value = n_tokens / (ms_total / 1e3)
+    print(f"bench: block loop timed, {value:.1f} committed tokens/s", file=sys.stderr, flush=True)
 
     roofline = None
-    attn_us = None
     if events is not None:
-        durs = [events[2 * i].elapsed_time(events[2 * i + 1]) for i in range(len(events) // 2)]
-        attn_us = 1e3 * sum(durs) / len(durs)
-        nbytes = attn_bytes_per_launch(m.B, m.L, m.S, m.Hq, m.Hkv, m.D)
-        flops = attn_flops_per_launch(m.B, m.L, m.S, m.Hq, m.D)
+        n_calls = len(events) // 3
+        kern = [1e3 * events[3 * i].elapsed_time(events[3 * i + 1]) for i in range(n_calls)]
+        whole = [1e3 * events[3 * i].elapsed_time(events[3 * i + 2]) for i in range(n_calls)]
+        lens = [m.L] * m.B
+        nbytes = attn_bytes(lens, m.S, m.Hq, m.Hkv, m.D)
+        flops = attn_flops(lens, m.S, m.Hq, m.D)
+        call_us, kern_us = sum(whole) / n_calls, sum(kern) / n_calls
+        kernels = ["block_attn_bf16_kernel<128>", "attn_reduce_kernel<128>"]
         if flops / nbytes <= MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
-            achieved = nbytes / (attn_us * 1e-6) / 1e9
+            achieved = nbytes / call_us / 1e3
             roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                        "traffic": measured_traffic() if m.S == 16 else None,
-                        "kernel": "block_attn_bf16_kernel<128>", "launch_us": round(attn_us, 2),
-                        "bytes_per_launch": nbytes}
-        else:   # past the ridge (larger blocks): the matrix cores bound the kernel
-            achieved = flops / (attn_us * 1e-6) / 1e12
+                        "traffic": measured_traffic(kernels) if m.S == 16 else None,
+                        "kernel": " + ".join(kernels), "call_us": round(call_us, 2),
+                        "call_us_median_min": stats_us(whole), "bytes_per_call": nbytes,
+                        "kernel_only": {"kernel": kernels[0], "launch_us": round(kern_us, 2),
+                                        "launch_us_median_min": stats_us(kern),
+                                        "achieved": round(nbytes / kern_us / 1e3, 1),
+                                        "frac": round(nbytes / kern_us / 1e3 / HBM_PEAK_GBPS, 4)}}
+        else:   # past the ridge (larger blocks): the matrix cores bound the attention
+            achieved = flops / call_us / 1e6
             roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
-                        "traffic": None, "kernel": "block_attn_bf16_kernel<128>",
-                        "launch_us": round(attn_us, 2), "flops_per_launch": flops}
+                        "traffic": None, "kernel": " + ".join(kernels),
+                        "call_us": round(call_us, 2), "flops_per_call": flops,
+                        "kernel_only": {"kernel": kernels[0], "launch_us": round(kern_us, 2),
+                                        "frac": round(flops / kern_us / 1e6 / MFMA_PEAK_TFLOPS, 4)}}
 
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
@@ -205,7 +417,13 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(m, blas_threads())
+        cpu = cpu_baseline(m)
+        print("bench: cpu baseline done", file=sys.stderr, flush=True)
+
+    extra = None
+    if not args.no_workloads:
+        del step
+        extra = workloads(dev)
 
     line = {
         "metric": "denoise-step attn HBM GB/s (% of peak) + committed tokens/s at 32K ctx",
@@ -219,18 +437,18 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded on-device N(0,1) KV caches, hidden states and scaled weights)",
+        "data": "synthetic (seeded on-device N(0,1) KV caches, hidden states and scaled weights; "
+                "seeded host draws for the other workloads)",
         "config": {"workload": f"block loop: batch 8, 6 attention layers, context 32768, S={m.S}, "
                                "T=16, hidden 2048, Hq 32 / Hkv 2, head_dim 128, vocab 131072, "
                                "threshold 0.9", "global_batch": m.B, "seq_len": m.L,
                    "parallelism": "single GPU"},
-        "attn_GBps": (None if roofline is None else
-                      round(attn_bytes_per_launch(m.B, m.L, m.S, m.Hq, m.Hkv, m.D) / attn_us / 1e3, 1)),
-        "attn_frac_of_hbm_peak": (None if roofline is None else
-                                  round(attn_bytes_per_launch(m.B, m.L, m.S, m.Hq, m.Hkv, m.D)
-                                        / attn_us / 1e3 / HBM_PEAK_GBPS, 4)),
+        "attn_GBps": None if roofline is None or roofline["bound"] != "hbm" else roofline["achieved"],
+        "attn_frac_of_hbm_peak": (None if roofline is None or roofline["bound"] != "hbm"
+                                  else roofline["frac"]),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "workloads": extra,
     }
     print(json.dumps(line), flush=True)
 

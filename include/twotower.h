@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define TWOTOWER_ABI_VERSION 7
+#define TWOTOWER_ABI_VERSION 8
 
 typedef enum {
   TT_OK = 0,
@@ -97,6 +97,17 @@ typedef enum { TT_FP32 = 0, TT_BF16 = 1 } tt_dtype;
  * num_splits: number of context partitions per (sequence, KV head) at max_ctx_len (0 = chosen
  * by the library to fill the GPU). Partitions are merged exactly with their log-sum-exp weights;
  * the result depends on num_splits only through floating-point rounding.
+ *
+ * Value range: any finite inputs. With several partitions each partition's normalized output row
+ * is kept in the workspace as fp16 scaled by a power of two chosen per row (its largest magnitude
+ * in [2^14, 2^15)), so no bf16 value overflows and rows of small values keep fp16's relative
+ * precision (2^-11); the bf16 path's error is relative to max|V| (P is rounded to bf16 once,
+ * relative 2^-8; the fp16 partial adds 2^-12 of the row's largest magnitude).
+ *
+ * timing_events: optional host array of 3 hipEvent_t (NULL in normal use): events[0] and
+ * events[1] are recorded on `stream` immediately before and after the main attention kernel,
+ * events[2] after the partition merge (equal in time to events[1] when there is one partition).
+ * A profiling hook; the events must have been created by the caller.
  */
 typedef struct {
   int32_t batch, S, num_q_heads, num_kv_heads, head_dim;
@@ -115,6 +126,7 @@ typedef struct {
   float *lse;
   int32_t num_splits;
   int32_t reserved0;
+  void *const *timing_events;  /* host array [3] of hipEvent_t, optional */
 } tt_block_attn_args;
 
 /*
@@ -271,13 +283,13 @@ typedef struct {
  * context tower's layer l, gotburnout.io "2. Denoiser Tower") -> twotower_out_projection; then
  * twotower_lm_head_unmask. Layer 0 reads h_in; the residual stream is kept in h_work.
  * All layers share batch, S, heads, head_dim, block_table, ctx_lens and page geometry (taken from
- * `attn`; attn.q/k_pages/v_pages/k_blk/v_blk/out/lse are ignored). The context caches are only
- * read. Sequences with no masked position left still run the dense math (their results are
- * discarded by the unmasking, which reads no committed row).
+ * `attn`; attn.q/k_pages/v_pages/k_blk/v_blk/out/lse/timing_events are ignored). The context
+ * caches are only read. Sequences with no masked position left still run the dense math (their
+ * results are discarded by the unmasking, which reads no committed row).
  *
- * timing_events: optional host array of 2*num_layers hipEvent_t; if not NULL, events[2l] and
- * events[2l+1] are recorded on `stream` immediately before and after the main attention kernel
- * of layer l (profiling hook, NULL in normal use).
+ * timing_events: optional host array of 3*num_layers hipEvent_t; if not NULL, events[3l] and
+ * events[3l+1] are recorded on `stream` immediately before and after the main attention kernel
+ * of layer l and events[3l+2] after its partition merge (profiling hook, NULL in normal use).
  */
 typedef struct {
   int32_t num_layers, hidden, vocab;
@@ -373,6 +385,18 @@ size_t twotower_packed_weight_bytes(int32_t out_features, int32_t in_features);
  * 16-byte aligned and in_features % 8 == 0 (else TT_EINVAL / TT_ENOTSUP); no workspace. */
 tt_status twotower_pack_weight(const void *w, int32_t out_features, int32_t in_features,
                                void *packed, void *stream);
+
+/*
+ * Measurement probe (not part of the method): reads `bytes` of device memory at `src` with
+ * 16-byte non-temporal loads, `workgroups` work-groups of 256 threads in a grid-stride loop, the
+ * practical streaming-read ceiling that the bandwidth-bound kernels are reported against next to
+ * the nominal HBM peak. `sink` (device, `workgroups` uint32 words) is written only in the
+ * practically never taken case that a work-group's XOR of the data equals 0x9E3779B9, so the
+ * probe normally writes nothing. bytes a positive multiple of 16, src 16-byte aligned,
+ * 1 <= workgroups <= 65536 (else TT_EINVAL).
+ */
+tt_status twotower_probe_stream_read(const void *src, size_t bytes, int32_t workgroups,
+                                     uint32_t *sink, void *stream);
 
 /* Static string for a status code ("TT_OK", ...); never NULL. */
 const char *twotower_status_string(int32_t status);

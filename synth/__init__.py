@@ -152,7 +152,8 @@ def _store(x: np.ndarray, dtype: str) -> np.ndarray:
 def attn_case(seed: int, *, B: int, S: int, Hq: int, Hkv: int, D: int, ctx_lens,
               page_size: int | None = None, dtype: str = "bf16", shuffle_pages: bool = True,
               spare_frac: float = 0.0, nan_poison: bool = False, outlier_frac: float = 0.0,
-              outlier_scale: float = 8.0, scale: float | None = None) -> AttnCase:
+              outlier_scale: float = 8.0, scale: float | None = None, q_scale: float = 1.0,
+              v_scale: float = 1.0) -> AttnCase:
     """Q/K/V ~ N(0, 1) in the paged layout.
 
     ``ctx_lens``: sequence of B context lengths. ``page_size`` None means one page per sequence
@@ -160,7 +161,9 @@ def attn_case(seed: int, *, B: int, S: int, Hq: int, Hkv: int, D: int, ctx_lens,
     pages of all sequences sit in the pool in a random order. ``spare_frac`` adds unused pool
     pages; ``nan_poison`` fills unused pages and the tail of every last page with NaN.
     ``outlier_frac`` of the context positions, drawn independently per KV head, get their whole
-    key vector multiplied by ``outlier_scale`` before rounding.
+    key vector multiplied by ``outlier_scale`` before rounding. ``q_scale`` / ``v_scale`` multiply
+    the queries / all values (context and block) before rounding: Q ~ N(0, q_scale^2),
+    V ~ N(0, v_scale^2).
     """
     g = rng(seed)
     ctx_lens = np.asarray(ctx_lens, dtype=np.int32).reshape(B)
@@ -172,15 +175,16 @@ def attn_case(seed: int, *, B: int, S: int, Hq: int, Hkv: int, D: int, ctx_lens,
     n_pool = max(1, n_used + int(math.ceil(spare_frac * n_used)))
     max_pages = max(1, max(pages_per_seq) if B else 1)
 
-    q = _store(g.standard_normal((B, S, Hq, D), dtype=np.float32), dtype)
+    qs, vs = np.float32(q_scale), np.float32(v_scale)
+    q = _store(g.standard_normal((B, S, Hq, D), dtype=np.float32) * qs, dtype)
     k_blk = _store(g.standard_normal((B, Hkv, S, D), dtype=np.float32), dtype)
-    v_blk = _store(g.standard_normal((B, Hkv, D, S), dtype=np.float32), dtype)
+    v_blk = _store(g.standard_normal((B, Hkv, D, S), dtype=np.float32) * vs, dtype)
 
     seqs = []
     for b in range(B):
         L = int(ctx_lens[b])
         k = g.standard_normal((L, Hkv, D), dtype=np.float32)
-        v = g.standard_normal((L, Hkv, D), dtype=np.float32)
+        v = g.standard_normal((L, Hkv, D), dtype=np.float32) * vs
         if outlier_frac > 0.0:
             hit = g.random((L, Hkv)) < outlier_frac
             k = np.where(hit[:, :, None], k * np.float32(outlier_scale), k)

@@ -72,9 +72,10 @@ def query(name, a):
 def test_attention_workspace_query_and_plan():
     st, n = query("twotower_block_attn", attn_args())
     assert st == _lib.TT_OK
-    # auto plan at B*Hkv = 16 units: 16 partitions of 2048 tokens, 256-row fp16 partials + fp32 lse
+    # auto plan at B*Hkv = 16 units: 16 partitions of 2048 tokens, 256-row fp16 partials + an
+    # fp32 (lse, scale exponent) pair per row
     items = 8 * 2 * 16
-    expect = -(-items * 256 * 128 * 2 // 256) * 256 + -(-items * 256 * 4 // 256) * 256
+    expect = -(-items * 256 * 128 * 2 // 256) * 256 + -(-items * 256 * 8 // 256) * 256
     assert n == expect
     # one partition needs no workspace
     st, n = query("twotower_block_attn", attn_args(num_splits=1))
@@ -279,3 +280,14 @@ def test_cache_shape_helpers_match_the_tiled_layouts():
     for bad in [(P, Hkv, page, D), (P, Hkv, page // 64, D, 64), (P, Hkv, 2, 8, 32, 8)]:
         with pytest.raises(ValueError):
             tt._cache_dims(torch.empty(bad))
+
+
+def test_stream_read_probe_validation(L):
+    f = L.twotower_probe_stream_read
+    assert f(None, 1 << 20, 256, C.c_void_p(FAKE), None) == _lib.TT_EINVAL
+    assert f(C.c_void_p(FAKE), 0, 256, C.c_void_p(FAKE), None) == _lib.TT_EINVAL
+    assert f(C.c_void_p(FAKE), 1000, 256, C.c_void_p(FAKE), None) == _lib.TT_EINVAL   # not x16
+    assert f(C.c_void_p(FAKE + 8), 1 << 20, 256, C.c_void_p(FAKE), None) == _lib.TT_EINVAL
+    assert f(C.c_void_p(FAKE), 1 << 20, 0, C.c_void_p(FAKE), None) == _lib.TT_EINVAL
+    assert f(C.c_void_p(FAKE), 1 << 20, 65537, C.c_void_p(FAKE), None) == _lib.TT_EINVAL
+    assert f(C.c_void_p(FAKE), 1 << 20, 256, None, None) == _lib.TT_EINVAL

@@ -81,6 +81,36 @@ def test_loop32k_layer_shape():
     check(case, out, lse, TOL_BF16)
 
 
+# ----------------------------------------------------------------------------- value range
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("splits", [1, 16, 64])
+@pytest.mark.parametrize("v_scale", [1e5, 1e-6])
+def test_value_range(v_scale, splits, out_dtype):
+    """The output is defined for any bf16 values: V ~ N(0, v_scale^2) far above fp16's largest
+    value (65504) and far below its smallest normal (6.1e-5). The queries are scaled by 4 so that
+    the softmax concentrates on a few keys and the partition outputs reach max|V|. Attention is
+    linear in V, so the bf16 tolerance scales with v_scale; a bf16 output adds its own rounding
+    (2^-8 relative)."""
+    case = synth.attn_case(60, B=1, S=16, Hq=32, Hkv=2, D=128, ctx_lens=[4096], dtype="bf16",
+                           q_scale=4.0, v_scale=v_scale)
+    ref, ref_lse = oattn.block_attention_case(case)
+    if v_scale > 1.0:
+        # each output row is a convex combination of the partitions' rows, so some partition
+        # row exceeds fp16's range wherever the result does
+        assert np.abs(ref).max() > 65504.0
+    out, lse = gpu_attn(case, num_splits=splits, out_dtype=out_dtype)
+    assert np.isfinite(out).all()
+    tol = TOL_BF16 * v_scale
+    if out_dtype == torch.float32:
+        err = max_abs(out, ref)
+        assert err <= tol, f"max-abs {err:.3g} > {tol:.3g}"
+    else:
+        excess = np.abs(out - ref) - (tol + 2.0 ** -8 * np.abs(ref))
+        assert excess.max() <= 0.0, f"bf16 output off by {excess.max():.3g} beyond the bound"
+    assert max_abs(lse, ref_lse) <= TOL_BF16
+
+
 # ------------------------------------------------------------------------ closed forms on the GPU
 
 def test_identical_keys_give_mean_of_values():

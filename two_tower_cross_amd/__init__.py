@@ -6,7 +6,8 @@ tensor metadata, build the C argument structs and size the workspace. If the sha
 is missing, every call raises ``LibraryNotBuilt`` (there is no fallback).
 
 Layouts follow ``include/twotower.h``:
-q [B,S,Hq,D]; k_pages [P,Hkv,page,D]; v_pages [P,Hkv,page/64,D,64]; k_blk [B,Hkv,S,D];
+q [B,S,Hq,D]; k_pages [P,Hkv,page/64,D/8,64,8] (64-token tiles of 8-dimension chunks);
+v_pages [P,Hkv,page/64,8,D,8] (64-token tiles of 8-token chunks); k_blk [B,Hkv,S,D];
 v_blk [B,Hkv,D,S]; block_table [B,max_pages] int32; ctx_lens [B] int32; logits [B,S,V] fp32.
 """
 from __future__ import annotations
@@ -21,7 +22,7 @@ from ._lib import LibraryNotBuilt, TwoTowerError, TT_BF16, TT_FP32  # noqa: F401
 
 __all__ = ["block_attn", "unmask", "qkv_projection", "out_projection", "lm_head",
            "lm_head_unmask", "kv_append", "mask_corrupt", "masked_nll", "DenoiseStep",
-           "PackedWeight", "pack_weight", "k_pages_shape", "v_pages_shape",
+           "PackedWeight", "pack_weight", "k_pages_shape", "v_pages_shape", "probe_stream_read",
            "LibraryNotBuilt", "TwoTowerError", "library_path"]
 
 
@@ -113,11 +114,14 @@ def _attn_struct(q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, out, 
 
 
 def block_attn(q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, *, scale=None,
-               max_ctx_len=None, out_dtype=None, return_lse=False, num_splits=0, out=None):
+               max_ctx_len=None, out_dtype=None, return_lse=False, num_splits=0, out=None,
+               timing_events=None):
     """Denoiser block attention at one layer; returns ``out`` (and ``lse`` [B,Hq,S] fp32).
 
     ``max_ctx_len`` bounds ctx_lens (used to plan the context partitions; default: the page
     table's capacity). ``num_splits`` 0 lets the library choose the partition count.
+    ``timing_events``: optional 3 hipEvent_t handles (``torch.cuda.Event(...).cuda_event``),
+    recorded before and after the main kernel and after the partition merge.
     """
     dev = q.device
     _check(q, "q", dev, ndim=4)
@@ -145,14 +149,21 @@ def block_attn(q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, *, scal
         max_ctx_len = block_table.shape[1] * page
     a = _attn_struct(q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, out, lse, scale,
                      max_ctx_len, num_splits)
+    if timing_events is not None:
+        if len(timing_events) != 3:
+            raise ValueError("timing_events takes 3 events")
+        ev = (C.c_void_p * 3)(*timing_events)
+        a.timing_events = C.cast(ev, C.POINTER(C.c_void_p))
     _run("twotower_block_attn", a, dev)
     return (out, lse) if return_lse else out
 
 
-def unmask(logits, masked, tokens, threshold, *, min_commit=False, commit_all=False):
+def unmask(logits, masked, tokens, threshold, *, min_commit=False, commit_all=False,
+           confidence=None, n_committed=None):
     """Confidence unmasking; updates ``masked`` and ``tokens`` in place.
 
-    Returns (confidence [B,S] fp32, written where masked on entry; n_committed [B] int32).
+    Returns (confidence [B,S] fp32, written where masked on entry; n_committed [B] int32), into
+    the given ``confidence`` / ``n_committed`` tensors when passed (else new ones, NaN / 0).
     """
     dev = logits.device
     _check(masked, "masked", dev, torch.uint8, 2)
@@ -162,8 +173,18 @@ def unmask(logits, masked, tokens, threshold, *, min_commit=False, commit_all=Fa
     B, S, V = logits.shape
     if logits.stride(0) != S * logits.stride(1):
         raise ValueError("logits rows must be evenly strided")
-    conf = torch.full((B, S), float("nan"), dtype=torch.float32, device=dev)
-    ncom = torch.zeros((B,), dtype=torch.int32, device=dev)
+    if confidence is None:
+        conf = torch.full((B, S), float("nan"), dtype=torch.float32, device=dev)
+    else:
+        _check(confidence, "confidence", dev, torch.float32, 2)
+        conf = confidence
+    if n_committed is None:
+        ncom = torch.zeros((B,), dtype=torch.int32, device=dev)
+    else:
+        _check(n_committed, "n_committed", dev, torch.int32, 1)
+        ncom = n_committed
+    if tuple(conf.shape) != (B, S) or tuple(ncom.shape) != (B,):
+        raise ValueError("confidence / n_committed shape mismatch")
     a = _lib.UnmaskArgs()
     a.batch, a.S, a.vocab, a.ld = B, S, V, logits.stride(1)
     a.logits, a.masked, a.tokens = _p(logits), _p(masked), _p(tokens)
@@ -468,7 +489,8 @@ class DenoiseStep:
                  timing_events=None, n_committed=None):
         """Enqueue one step; updates masked/tokens in place, fills confidence and the per-sequence
         commit counts (into `n_committed`, an int32 [batch] device tensor, when given, else into
-        self.n_committed, which is returned)."""
+        self.n_committed, which is returned). ``timing_events``: optional 3 * layers hipEvent_t
+        handles, recorded around each layer's attention kernel and after its merge."""
         a = self.args
         a.h_in = _p(h_in)
         a.unmask.masked, a.unmask.tokens = _p(masked), _p(tokens)
@@ -482,6 +504,8 @@ class DenoiseStep:
         a.unmask.threshold = float(threshold)
         a.unmask.min_commit, a.unmask.commit_all = int(bool(min_commit)), int(bool(commit_all))
         if timing_events is not None:
+            if len(timing_events) != 3 * self.L:
+                raise ValueError("timing_events takes 3 events per layer")
             self._ev = (C.c_void_p * len(timing_events))(*timing_events)
             a.timing_events = C.cast(self._ev, C.POINTER(C.c_void_p))
         else:
@@ -497,3 +521,16 @@ class DenoiseStep:
         if st != _lib.TT_OK:
             raise TwoTowerError("twotower_denoise_step", st)
         return self.confidence, n_committed
+
+
+def probe_stream_read(src, workgroups, sink):
+    """Measurement probe: stream-read the bytes of ``src`` (a contiguous device tensor whose size
+    is a multiple of 16 bytes) with ``workgroups`` work-groups; ``sink`` is an int32 device tensor
+    of at least ``workgroups`` elements (normally left untouched)."""
+    nbytes = src.numel() * src.element_size()
+    if not src.is_contiguous() or sink.numel() < workgroups or sink.element_size() != 4:
+        raise ValueError("probe_stream_read: contiguous source, sink of >= workgroups words")
+    st = _lib.lib().twotower_probe_stream_read(_p(src), nbytes, int(workgroups), _p(sink),
+                                                _stream())
+    if st != _lib.TT_OK:
+        raise TwoTowerError("twotower_probe_stream_read", st)

@@ -15,7 +15,7 @@ LIB_PATH = os.environ.get("TWOTOWER_LIB", os.path.join(HERE, "libtwotower.so"))
 TT_OK, TT_EINVAL, TT_ENOTSUP, TT_ENOSPACE, TT_EHIP = range(5)
 TT_FP32, TT_BF16 = 0, 1
 TT_APPEND_OUT_OF_PAGES, TT_APPEND_NO_ROOM_IN_TABLE, TT_APPEND_BAD_PAGE = 1, 2, 4
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 i32, i64, f32, vp = C.c_int32, C.c_int64, C.c_float, C.c_void_p
 
@@ -27,7 +27,8 @@ class BlockAttnArgs(C.Structure):
                 ("num_pages", i32), ("page_size", i32), ("max_pages_per_seq", i32),
                 ("max_ctx_len", i32),
                 ("block_table", vp), ("ctx_lens", vp), ("k_blk", vp), ("v_blk", vp),
-                ("out", vp), ("lse", vp), ("num_splits", i32), ("reserved0", i32)]
+                ("out", vp), ("lse", vp), ("num_splits", i32), ("reserved0", i32),
+                ("timing_events", C.POINTER(vp))]
 
 
 class UnmaskArgs(C.Structure):
@@ -145,6 +146,8 @@ def lib():
         L.twotower_packed_weight_bytes.argtypes = [i32, i32]
         L.twotower_pack_weight.restype = i32
         L.twotower_pack_weight.argtypes = [vp, i32, i32, vp, vp]
+        L.twotower_probe_stream_read.restype = i32
+        L.twotower_probe_stream_read.argtypes = [vp, C.c_size_t, i32, vp, vp]
         if L.twotower_abi_version() != ABI_VERSION:
             raise RuntimeError("libtwotower ABI version mismatch")
         _lib = L

@@ -105,24 +105,32 @@ tt_status plan_attn(const tt_block_attn_args *a, bool check_pointers, AttnPlan *
   if (p.splits > 1) {
     const size_t items = (size_t)p.B * p.Hkv * p.row_groups * p.splits;
     out->ws_bytes = align_up(items * p.rows_per_group * p.D * sizeof(uint16_t)) +
-                    align_up(items * p.rows_per_group * sizeof(float));
+                    align_up(items * p.rows_per_group * 2 * sizeof(float));
   }
   return TT_OK;
 }
 
-hipError_t run_attn(AttnPlan &pl, void *ws, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+// e0 / e1: recorded before / after the main kernel, e2 after the merge (each may be null).
+hipError_t run_attn(AttnPlan &pl, void *ws, hipStream_t stream, hipEvent_t e0, hipEvent_t e1,
+                    hipEvent_t e2) {
   tt::AttnParams &p = pl.p;
   if (p.B == 0) return hipSuccess;
-  if (!pl.use_bf16) return tt::launch_block_attn_f32(p, stream, e0, e1);
+  hipError_t e;
+  if (!pl.use_bf16) {
+    e = tt::launch_block_attn_f32(p, stream, e0, e1);
+    if (e == hipSuccess && e2) e = hipEventRecord(e2, stream);
+    return e;
+  }
   if (p.splits > 1) {
     const size_t items = (size_t)p.B * p.Hkv * p.row_groups * p.splits;
     char *w = static_cast<char *>(ws);
     p.part_o = w;
     p.part_lse = reinterpret_cast<float *>(w + align_up(items * p.rows_per_group * p.D * sizeof(uint16_t)));
   }
-  hipError_t e = tt::launch_block_attn_bf16(p, stream, e0, e1);
-  if (e != hipSuccess || p.splits == 1) return e;
-  return tt::launch_attn_reduce(p, stream);
+  e = tt::launch_block_attn_bf16(p, stream, e0, e1);
+  if (e == hipSuccess && p.splits > 1) e = tt::launch_attn_reduce(p, stream);
+  if (e == hipSuccess && e2) e = hipEventRecord(e2, stream);
+  return e;
 }
 
 tt_status ws_protocol(size_t need, void *ws, size_t *ws_bytes, bool *launch) {
@@ -426,7 +434,10 @@ tt_status twotower_block_attn(const tt_block_attn_args *args, void *ws, size_t *
   bool launch;
   st = ws_protocol(pl.ws_bytes, ws, ws_bytes, &launch);
   if (st != TT_OK || !launch) return st;
-  return hip_status(run_attn(pl, ws, static_cast<hipStream_t>(stream), nullptr, nullptr));
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  if (args->timing_events)
+    for (int i = 0; i < 3; ++i) ev[i] = static_cast<hipEvent_t>(args->timing_events[i]);
+  return hip_status(run_attn(pl, ws, static_cast<hipStream_t>(stream), ev[0], ev[1], ev[2]));
 }
 
 tt_status twotower_unmask(const tt_unmask_args *args, void *ws, size_t *ws_bytes, void *stream) {
@@ -646,18 +657,28 @@ tt_status twotower_denoise_step(const tt_denoise_step_args *a, void *ws, size_t 
     al.p.v_pages = a->v_pages[l];
     al.p.k_blk = a->k_blk[l];
     al.p.v_blk = a->v_blk[l];
-    hipEvent_t e0 = nullptr, e1 = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr, e2 = nullptr;
     if (a->timing_events) {
-      e0 = static_cast<hipEvent_t>(a->timing_events[2 * l]);
-      e1 = static_cast<hipEvent_t>(a->timing_events[2 * l + 1]);
+      e0 = static_cast<hipEvent_t>(a->timing_events[3 * l]);
+      e1 = static_cast<hipEvent_t>(a->timing_events[3 * l + 1]);
+      e2 = static_cast<hipEvent_t>(a->timing_events[3 * l + 2]);
     }
-    if ((e = run_attn(al, ws, s, e0, e1)) != hipSuccess) return TT_EHIP;
+    if ((e = run_attn(al, ws, s, e0, e1, e2)) != hipSuccess) return TT_EHIP;
     op.residual = h_prev;
     op.w = a->w_o[l];
     if ((e = run_linear(op, ws, s)) != hipSuccess) return TT_EHIP;
   }
   if (run_lm_unmask(lup, ws, s) != hipSuccess) return TT_EHIP;
   return TT_OK;
+}
+
+tt_status twotower_probe_stream_read(const void *src, size_t bytes, int32_t workgroups,
+                                     uint32_t *sink, void *stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 != 0 || !aligned(src, 16) || !aligned(sink, 4))
+    return TT_EINVAL;
+  if (workgroups < 1 || workgroups > 65536) return TT_EINVAL;
+  return hip_status(
+      tt::launch_stream_read(src, bytes, workgroups, sink, static_cast<hipStream_t>(stream)));
 }
 
 const char *twotower_status_string(int32_t status) {
@@ -703,7 +724,7 @@ int64_t twotower_struct_offset(int32_t which, int32_t field) {
       TT_OFF(tt_block_attn_args, ctx_lens), TT_OFF(tt_block_attn_args, k_blk),
       TT_OFF(tt_block_attn_args, v_blk), TT_OFF(tt_block_attn_args, out),
       TT_OFF(tt_block_attn_args, lse), TT_OFF(tt_block_attn_args, num_splits),
-      TT_OFF(tt_block_attn_args, reserved0)};
+      TT_OFF(tt_block_attn_args, reserved0), TT_OFF(tt_block_attn_args, timing_events)};
   static const int64_t unm[] = {
       TT_OFF(tt_unmask_args, batch), TT_OFF(tt_unmask_args, S), TT_OFF(tt_unmask_args, vocab),
       TT_OFF(tt_unmask_args, reserved0), TT_OFF(tt_unmask_args, ld),

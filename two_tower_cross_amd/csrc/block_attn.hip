@@ -19,8 +19,11 @@
 //     the next product O^T += V^T P^T, with no LDS round trip for P.
 //   * Online softmax in base 2 with the scale folded into one FMA; O^T is rescaled only when a
 //     row maximum moved.
-//   * Partition 0 also folds in the S block keys; with several partitions each one writes a
-//     normalized fp32 partial and its log-sum-exp, merged exactly by attn_reduce_kernel.
+//   * Partition 0 also folds in the S block keys; with several partitions each one writes its
+//     normalized output rows in fp16, each row scaled by a power of two 2^k that puts its largest
+//     magnitude in [2^14, 2^15) (so no finite bf16 value overflows and small rows keep fp16's
+//     relative precision), with (log-sum-exp, k) beside it; attn_reduce_kernel merges them
+//     exactly.
 // fp32 path: one work-group per (b, query head, block position), plain fp32 arithmetic.
 #include <math.h>
 
@@ -669,6 +672,22 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   const float inv = bad ? NAN : 1.0f / l;
   const float lse_val = bad ? NAN : m * p.scale + logf(l);
   const bool to_part = p.splits > 1;
+  // Partial rows go out in fp16 scaled by 2^kexp, kexp chosen so that the row's largest |O_p|
+  // lands in [2^14, 2^15): |O_p| <= max|V| may be any finite bf16 value, far outside fp16's range
+  // without the scale. The row's 2 x D/2 values sit in the lane pair (col, col + 32).
+  int kexp = 0;
+  float fac = inv;
+  if (to_part) {
+    float amax = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(oacc[mb][i]));
+    amax = pair_max(amax) * inv;
+    if (amax > 0.f) kexp = 15 - __builtin_amdgcn_frexp_expf(amax);  // amax in [2^(e-1), 2^e)
+    kexp = min(max(kexp, -126), 126);  // inv <= 1, so inv * 2^kexp stays finite
+    fac = __builtin_amdgcn_ldexpf(inv, kexp);
+  }
   const bool half_out = to_part || p.out_bf16;     // 2-byte elements (fp16 partial / bf16 out)
   const int row_bytes = D * (half_out ? 2 : 4);
   const int cpr = row_bytes / 16;                 // 16-byte chunks per row (a power of two)
@@ -680,8 +699,8 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = mb * 32 + q4 * 8 + hh * 4;
-        const float o0 = oacc[mb][q4 * 4 + 0] * inv, o1 = oacc[mb][q4 * 4 + 1] * inv;
-        const float o2 = oacc[mb][q4 * 4 + 2] * inv, o3 = oacc[mb][q4 * 4 + 3] * inv;
+        const float o0 = oacc[mb][q4 * 4 + 0] * fac, o1 = oacc[mb][q4 * 4 + 1] * fac;
+        const float o2 = oacc[mb][q4 * 4 + 2] * fac, o3 = oacc[mb][q4 * 4 + 3] * fac;
         uint2 pk;
         if (to_part) {
           pk.x = pack_f16x2(o0, o1);
@@ -719,7 +738,8 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
     for (int f = lane; f < nrows * cpr; f += 64)
       *reinterpret_cast<u32x4 *>(dst + (size_t)f * 16) = slice_chunk(f / cpr, f % cpr);
     if (hh == 0 && r_local < p.rows_per_group)
-      p.part_lse[item * p.rows_per_group + r_local] = lse_val;
+      reinterpret_cast<float2 *>(p.part_lse)[item * p.rows_per_group + r_local] =
+          make_float2(lse_val, (float)kexp);
   } else {
     char *obase = static_cast<char *>(p.out);
     for (int f = lane; f < 32 * cpr; f += 64) {
@@ -736,6 +756,8 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
 
 // Exact merge of the partitions of each query row: with lse* = max_p lse_p and
 // w_p = exp(lse_p - lse*), out = sum_p w_p O_p / sum_p w_p and lse = lse* + ln(sum_p w_p).
+// A partition's row is stored as fp16 O_p * 2^k_p with (lse_p, k_p) beside it, so its term is
+// (w_p * 2^-k_p) times the stored value (the power of two is exact).
 // One work-group = 16 query rows of one (b, KV head, row group); 16 threads per row, 8 dims each.
 // Each thread requests its row's LSE and its 16-byte partial chunk of every partition of a batch
 // (up to 16) together with the sequence length, before any of them is used: one memory round trip
@@ -764,12 +786,12 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnParams p) {
   bool bad = false;
   for (int s0 = 0; s0 < p.splits; s0 += kRedBatch) {
     const int nb = min(kRedBatch, p.splits - s0);
-    float ls[kRedBatch];
+    float2 ls[kRedBatch];
     u32x4 v[kRedBatch];
 #pragma unroll
     for (int sp = 0; sp < kRedBatch; ++sp) {  // unconditional loads (clamped), no branches
       const size_t it = (item0 + s0 + min(sp, nb - 1)) * p.rows_per_group + r_local;
-      ls[sp] = p.part_lse[it];
+      ls[sp] = reinterpret_cast<const float2 *>(p.part_lse)[it];
       v[sp] = ld_global_16(part + it * D + d8 * 8);
     }
     asm volatile("" ::: "memory");  // keeps the length load behind the batch's loads
@@ -781,7 +803,7 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnParams p) {
     float bmx = mx;
 #pragma unroll
     for (int sp = 0; sp < kRedBatch; ++sp)
-      if (sp < ns) bmx = fmaxf(bmx, ls[sp]);
+      if (sp < ns) bmx = fmaxf(bmx, ls[sp].x);
     const float rescale = __expf(mx - bmx);   // 0 for the first batch (mx = -inf)
     wsum *= rescale;
 #pragma unroll
@@ -790,12 +812,13 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnParams p) {
 #pragma unroll
     for (int sp = 0; sp < kRedBatch; ++sp) {
       if (sp < ns) {
-        const float w = __expf(ls[sp] - mx);
+        const float w = __expf(ls[sp].x - mx);
         wsum += w;
+        const float wk = __builtin_amdgcn_ldexpf(w, -(int)ls[sp].y);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += w * f16_to_f32(v[sp][e] & 0xFFFFu);
-          acc[2 * e + 1] += w * f16_to_f32(v[sp][e] >> 16);
+          acc[2 * e] += wk * f16_to_f32(v[sp][e] & 0xFFFFu);
+          acc[2 * e + 1] += wk * f16_to_f32(v[sp][e] >> 16);
         }
       }
     }

@@ -25,8 +25,9 @@ struct AttnParams {
   const int32_t *block_table, *ctx_lens;
   void *out;
   float *lse;
-  void *part_o;     // [items, rows_per_group, D] fp16 normalized partial outputs (splits > 1)
-  float *part_lse;  // [items, rows_per_group]
+  void *part_o;     // [items, rows_per_group, D] fp16 normalized partial rows, row r scaled by
+                    // 2^k_r (splits > 1)
+  float *part_lse;  // [items, rows_per_group, 2]: (log-sum-exp, k_r) of each partial row
   int B, S, Hq, Hkv, G, D;
   int rows;            // G * S query rows per (sequence, KV head)
   int rows_per_group;  // rows handled by one work-group (multiple of 32, <= 256)
@@ -91,8 +92,8 @@ constexpr int kAppendNoRoomInTable = 2;
 constexpr int kAppendBadPage = 4;
 
 struct AppendParams {
-  void *k_pages[kMaxAppendLayers];      // [num_pages, Hkv, page_size, D]
-  void *v_pages[kMaxAppendLayers];      // [num_pages, Hkv, page_size / 64, D, 64]
+  void *k_pages[kMaxAppendLayers];      // [num_pages, Hkv, page_size / 64, D / 8, 64, 8]
+  void *v_pages[kMaxAppendLayers];      // [num_pages, Hkv, page_size / 64, 8, D, 8]
   const void *k_new[kMaxAppendLayers];  // [B, Hkv, S, D]
   const void *v_new[kMaxAppendLayers];  // [B, Hkv, D, S]
   int32_t *block_table;                 // [B, max_pages]
@@ -142,5 +143,10 @@ hipError_t launch_linear(const LinearParams &p, hipStream_t stream);
 
 // Packed weight layout of the linear kernels (see twotower_pack_weight).
 hipError_t launch_pack_weight(const void *w, int N, int K, void *out, hipStream_t stream);
+
+// --------------------------------------------------------------------------- measurement
+// Streaming read of `bytes` (a multiple of 16) from src with `workgroups` work-groups of 256.
+hipError_t launch_stream_read(const void *src, size_t bytes, int workgroups, uint32_t *sink,
+                              hipStream_t stream);
 
 }  // namespace tt

@@ -1,13 +1,18 @@
-"""HBM traffic of the block-attention kernel from rocprofv3 byte counters.
+"""HBM traffic of the step's kernels from rocprofv3 byte counters.
 
 Two counter runs of the same command (``--pmc FETCH_SIZE``, then ``--pmc WRITE_SIZE``; the counters
 report KiB per dispatch) are scaled by what the same counter reads for a plain device copy of known
 size in the same run (``bench.py --copy-calibration MIB``): factor = true bytes / counted bytes.
+Optionally the kernel trace of the same command (``--kernel-trace``; its kernel_trace CSV, or
+the kernel_stats CSV of ``--stats``) adds each kernel's mean duration, so that counted bytes per
+second can be put next to the algorithmic rate.
 
-    python -m two_tower_cross_amd.traffic FETCH_CSV WRITE_CSV COPY_MIB OUT_MD "COMMAND"
+    python -m two_tower_cross_amd.traffic FETCH_CSV WRITE_CSV COPY_MIB OUT_MD "COMMAND" [TRACE_CSV]
 
-writes a short summary (text plus one JSON line) that ``bench.py`` reads back; the JSON records the
-SHA-256 of the kernel source so that a stale measurement is never reported for a changed kernel.
+writes a short summary (a table plus one JSON line) that ``bench.py`` reads back. Kernels are keyed
+by name and grid size (the two projections of a layer are the same kernel on different grids);
+the JSON records the SHA-256 of each kernel's source file, so that a stale measurement is never
+reported for a changed kernel.
 """
 from __future__ import annotations
 
@@ -15,22 +20,48 @@ import csv
 import hashlib
 import json
 import os
+import statistics
 import sys
 
-KERNEL = "block_attn_bf16_kernel<128>"
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "two_tower_cross_amd", "csrc")
+
+# kernel name prefix -> source file
+SOURCES = [("block_attn", "block_attn.hip"), ("attn_reduce", "block_attn.hip"),
+           ("linear", "linear.hip"), ("lm_unmask", "linear.hip"), ("pack_weight", "linear.hip"),
+           ("unmask", "unmask.hip"), ("nll", "unmask.hip"), ("mask_corrupt", "unmask.hip"),
+           ("kv_", "kv_append.hip"), ("stream_read", "probe.hip")]
+
+# Algorithmic bytes per dispatch of the 32K-context block loop (batch 8, S 16, Hq 32 / Hkv 2,
+# head_dim 128, hidden 2048, vocab 131072, L 32768), by (kernel, grid size in work-items):
+# what the method itself must move through that kernel (inputs read once, outputs written once);
+# split partials and re-reads are overhead, counted by the counters but not here.
+_B, _S, _HQ, _HKV, _D, _H, _V, _L = 8, 16, 32, 2, 128, 2048, 131072, 32768
+_M = _B * _S
+ALGORITHMIC_LOOP32K = {
+    # context K+V, block K+V and Q (the O write is the merge's)
+    "block_attn_bf16_kernel<128>": 2 * _B * _HKV * _L * _D * 2 + 2 * _B * _HKV * _S * _D * 2
+    + _B * _S * _HQ * _D * 2,
+    "attn_reduce_kernel<128>": _B * _S * _HQ * _D * 2,                     # O write
+    # QKV product: W_qkv + H (its fp32 K partials are overhead); the reduce writes Q, K_blk, V_blk
+    "linear_kernel<2>@qkv": (_HQ + 2 * _HKV) * _D * _H * 2 + _M * _H * 2,
+    "linear_reduce_kernel@qkv": _M * (_HQ + 2 * _HKV) * _D * 2,
+    # output product: W_o + O; the reduce reads the residual and writes H
+    "linear_kernel<2>@out": _H * _HQ * _D * 2 + _M * _HQ * _D * 2,
+    "linear_reduce_kernel@out": 2 * _M * _H * 2,
+    # fused lm-head: W_lm + H_final, then 12-byte row triples per 256-logit tile (their round trip
+    # is the fused path's own overhead, not counted)
+    "lm_unmask_kernel": _V * _H * 2 + _M * _H * 2,
+    "unmask_tiles_finalize_kernel": 0,
+}
 
 
-def _per_dispatch(path, counter):
-    """{dispatch id: (kernel name, value)} for one counter of a counter_collection CSV."""
-    out = {}
-    with open(path) as f:
-        for r in csv.DictReader(f):
-            if r["Counter_Name"] != counter:
-                continue
-            d = int(r["Dispatch_Id"])
-            name, v = out.get(d, (r["Kernel_Name"], 0.0))
-            out[d] = (name, v + float(r["Counter_Value"]))
-    return out
+def source_of(kernel):
+    k = kernel.replace("tt::", "")
+    for prefix, src in SOURCES:
+        if k.startswith(prefix):
+            return src
+    return None
 
 
 def source_hash(path):
@@ -38,55 +69,165 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def summarize(fetch_csv, write_csv, copy_mib, kernel_source):
+def short_name(kernel):
+    """`tt::block_attn_bf16_kernel<128>(tt::AttnParams)` -> `block_attn_bf16_kernel<128>`."""
+    k = kernel.replace("tt::", "").replace(" ", "")
+    depth, out = 0, []
+    for ch in k:
+        if ch == "(" and depth == 0:
+            break
+        out.append(ch)
+        depth += ch == "<"
+        depth -= ch == ">"
+    return "".join(out)
+
+
+def _grid(r):
+    """Total work-items of a CSV row (one Grid_Size column, or one per dimension)."""
+    if r.get("Grid_Size"):
+        return int(r["Grid_Size"])
+    n = 1
+    for ax in ("X", "Y", "Z"):
+        n *= int(r.get(f"Grid_Size_{ax}", 1) or 1)
+    return n
+
+
+def _per_dispatch(path, counter):
+    """{dispatch id: (kernel name, grid size, value)} for one counter of a counter CSV."""
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            name, _, v = out.get(d, (short_name(r["Kernel_Name"]), _grid(r), 0.0))
+            out[d] = (name, _grid(r), v + float(r["Counter_Value"]))
+    return out
+
+
+def _durations(trace_csv):
+    """{kernel key: mean duration in us} from a rocprofv3 kernel_trace CSV of the same command
+    (keys as for the counters), or from a kernel_stats CSV (by name only)."""
+    if not trace_csv:
+        return {}
+    with open(trace_csv) as f:
+        rows = list(csv.DictReader(f))
+    if rows and "AverageNs" in rows[0]:
+        return {short_name(r["Name"]): float(r["AverageNs"]) / 1e3 for r in rows}
+    grids = {}
+    for r in rows:
+        grids.setdefault(short_name(r["Kernel_Name"]), set()).add(_grid(r))
+    durs = {}
+    for r in rows:
+        name = short_name(r["Kernel_Name"])
+        k = _key(name, _grid(r), grids)
+        durs.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return {k: statistics.mean(v) for k, v in durs.items()}
+
+
+def _key(name, grid, grids):
+    """Kernel key: the name, with the projection's role when one name runs on several grids."""
+    if name in ("linear_kernel<2>", "linear_reduce_kernel") and len(grids[name]) == 2:
+        # at this workload the QKV product runs on the smaller grid (72 feature tiles x 3 K
+        # partitions against 32 x 8) and its reduce on the larger one (4608 against 2048 features)
+        qkv = min(grids[name]) if name == "linear_kernel<2>" else max(grids[name])
+        return name + ("@qkv" if grid == qkv else "@out")
+    return name
+
+
+def summarize(fetch_csv, write_csv, copy_mib, stats_csv=None):
     copy_bytes = copy_mib << 20
-    res = {}
+    per = {}
+    factors = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         disp = _per_dispatch(path, counter)
-        attn = [v for n, v in disp.values() if KERNEL in n.replace(" ", "")]
-        # the calibration copy: the last dispatch of the run
-        last = disp[max(disp)]
-        factor = copy_bytes / (last[1] * 1024.0)
-        kib = sum(attn) / len(attn)
-        res[counter] = {"dispatches": len(attn), "kib_per_dispatch": round(kib, 1),
-                        "copy_kernel": last[0][:80], "copy_counted_kib": round(last[1], 1),
-                        "factor": round(factor, 4), "bytes_per_launch": int(kib * 1024 * factor)}
-    total = res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]
-    return {"kernel": KERNEL, "source_sha256": source_hash(kernel_source), "copy_mib": copy_mib,
-            "fetch": res["FETCH_SIZE"], "write": res["WRITE_SIZE"], "traffic_bytes": total}
+        last = disp[max(disp)]                      # the calibration copy: the run's last dispatch
+        factor = copy_bytes / (last[2] * 1024.0)
+        factors[counter] = {"copy_kernel": last[0][:60], "copy_counted_kib": round(last[2], 1),
+                            "factor": round(factor, 4)}
+        grids = {}
+        for name, grid, _ in disp.values():
+            grids.setdefault(name, set()).add(grid)
+        vals = {}
+        for d, (name, grid, v) in disp.items():
+            if d == max(disp) or source_of(name) is None:
+                continue
+            vals.setdefault(_key(name, grid, grids), []).append(v)
+        for k, vs in vals.items():
+            e = per.setdefault(k, {"dispatches": len(vs)})
+            e[counter] = int(statistics.mean(vs) * 1024 * factor)
+    dur = _durations(stats_csv)
+    hashes = {}
+    for k, e in per.items():
+        src = source_of(k)
+        hashes[src] = source_hash(os.path.join(CSRC, src))
+        e["source"] = src
+        e["traffic_bytes"] = e.get("FETCH_SIZE", 0) + e.get("WRITE_SIZE", 0)
+        alg = ALGORITHMIC_LOOP32K.get(k)
+        if alg is not None:
+            e["algorithmic_bytes"] = alg
+            if alg:
+                e["traffic_over_algorithmic"] = round(e["traffic_bytes"] / alg, 3)
+        base = k if k in dur else k.split("@")[0]
+        if base in dur:
+            e["mean_us"] = round(dur[base], 2)
+            if alg:
+                e["algorithmic_GBps"] = round(alg / dur[base] / 1e3, 1)
+                e["algorithmic_frac_of_8TBps"] = round(alg / dur[base] / 1e3 / 8000.0, 4)
+            e["counted_GBps"] = round(e["traffic_bytes"] / dur[base] / 1e3, 1)
+    return {"kernels": per, "source_sha256": hashes, "copy_mib": copy_mib, "calibration": factors}
 
 
-def bytes_per_launch(summary_md, kernel_source):
-    """Scaled fetch + write bytes per launch, or None (no summary / different kernel source)."""
+def bytes_per_launch(summary_md, kernels):
+    """Scaled fetch + write bytes per call summed over ``kernels`` (short names), or None (no
+    summary, a kernel missing, or a changed source file)."""
     if not os.path.exists(summary_md):
         return None
     with open(summary_md) as f:
         for line in f:
             line = line.strip()
-            if line.startswith("{") and '"traffic_bytes"' in line:
+            if line.startswith("{") and '"kernels"' in line:
                 s = json.loads(line)
-                if s.get("source_sha256") == source_hash(kernel_source):
-                    return int(s["traffic_bytes"])
+                total = 0
+                for k in kernels:
+                    e = s["kernels"].get(k)
+                    if e is None:
+                        return None
+                    src = e["source"]
+                    if s["source_sha256"].get(src) != source_hash(os.path.join(CSRC, src)):
+                        return None
+                    total += e["traffic_bytes"]
+                return total
     return None
 
 
 def main(argv):
     fetch_csv, write_csv, copy_mib, out_md, command = argv[1:6]
-    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    src = os.path.join(root, "two_tower_cross_amd", "csrc", "block_attn.hip")
-    s = summarize(fetch_csv, write_csv, int(copy_mib), src)
+    stats_csv = argv[6] if len(argv) > 6 else None
+    s = summarize(fetch_csv, write_csv, int(copy_mib), stats_csv)
     with open(out_md, "w") as f:
-        f.write(f"# HBM traffic of {KERNEL}, 32K-context block loop\n\n")
-        f.write("Counters: rocprofv3 `--pmc FETCH_SIZE` and `--pmc WRITE_SIZE`, one run each, of\n\n")
+        f.write("# HBM traffic of the denoise-step kernels, 32K-context block loop\n\n")
+        f.write("Counters: rocprofv3 `--pmc FETCH_SIZE` and `--pmc WRITE_SIZE`, one run each"
+                + (", and a `--kernel-trace --stats` run for durations" if stats_csv else "")
+                + ", of\n\n")
         f.write(f"    {command}\n\n")
-        for k in ("fetch", "write"):
-            r = s[k]
-            f.write(f"- {k.upper()}: {r['kib_per_dispatch']} KiB counted per dispatch over "
-                    f"{r['dispatches']} dispatches; plain copy of {s['copy_mib']} MiB "
-                    f"(`{r['copy_kernel']}`) counted {r['copy_counted_kib']} KiB -> factor "
-                    f"{r['factor']}; scaled: {r['bytes_per_launch']} bytes per launch\n")
-        f.write(f"- traffic (fetch + write, scaled): {s['traffic_bytes']} bytes per launch\n\n")
-        f.write("Machine-readable (bench.py reports it only while the kernel source hash matches):\n\n")
+        for c, r in s["calibration"].items():
+            f.write(f"- {c}: a plain copy of {s['copy_mib']} MiB (`{r['copy_kernel']}`) counted "
+                    f"{r['copy_counted_kib']} KiB -> scale factor {r['factor']}\n")
+        f.write("\nBytes per dispatch, scaled; algorithmic = what the method itself moves through "
+                "the kernel at this workload.\n\n")
+        f.write("| kernel | dispatches | fetch B | write B | traffic B | algorithmic B | "
+                "traffic / alg. | mean us | alg. GB/s | alg. % of 8 TB/s |\n")
+        f.write("|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|\n")
+        for k, e in sorted(s["kernels"].items(), key=lambda kv: -kv[1]["traffic_bytes"]):
+            f.write(f"| `{k}` | {e['dispatches']} | {e.get('FETCH_SIZE', 0):,} | "
+                    f"{e.get('WRITE_SIZE', 0):,} | {e['traffic_bytes']:,} | "
+                    f"{e.get('algorithmic_bytes', '-') if 'algorithmic_bytes' not in e else format(e['algorithmic_bytes'], ',')} | "
+                    f"{e.get('traffic_over_algorithmic', '-')} | {e.get('mean_us', '-')} | "
+                    f"{e.get('algorithmic_GBps', '-')} | "
+                    f"{round(100 * e['algorithmic_frac_of_8TBps'], 1) if 'algorithmic_frac_of_8TBps' in e else '-'} |\n")
+        f.write("\nMachine-readable (bench.py reports a kernel's traffic only while the hash of "
+                "its source file matches):\n\n")
         f.write(json.dumps(s) + "\n")
     print(json.dumps(s))
 
