@@ -81,6 +81,25 @@ def test_loop32k_layer_shape():
     check(case, out, lse, TOL_BF16)
 
 
+# ------------------------------------------------------------------------------- the merge
+
+@pytest.mark.parametrize("B,Hkv,D,lens,splits", [
+    (32, 2, 128, (2048, 1500), 16),      # 64 (b, g) units: one partition group per row
+    (64, 2, 64, (1024, 700), 16),        # head_dim 64, one partition group
+    (8, 2, 128, (4096, 3000), 40),       # 4 partition groups, partitions past a short sequence
+    (1, 2, 128, (40960,), 600),          # 16 groups, 320 partitions: two load batches per thread
+    (2, 1, 64, (20000, 9000), 313),      # 16 groups at head_dim 64, 313 partitions, ragged
+])
+def test_merge_partition_groups(B, Hkv, D, lens, splits):
+    """The partition merge spreads a row's partitions over 1, 4 or 16 thread groups depending on
+    the number of rows and partitions; every variant must give the oracle's result."""
+    ctx = [lens[b % len(lens)] for b in range(B)]
+    case = synth.attn_case(61 + B, B=B, S=16, Hq=16 * Hkv, Hkv=Hkv, D=D, ctx_lens=ctx,
+                           page_size=None if B == 1 else 512, dtype="bf16")
+    out, lse = gpu_attn(case, num_splits=splits)
+    check(case, out, lse, TOL_BF16)
+
+
 # ----------------------------------------------------------------------------- value range
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])

@@ -758,17 +758,22 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
 // w_p = exp(lse_p - lse*), out = sum_p w_p O_p / sum_p w_p and lse = lse* + ln(sum_p w_p).
 // A partition's row is stored as fp16 O_p * 2^k_p with (lse_p, k_p) beside it, so its term is
 // (w_p * 2^-k_p) times the stored value (the power of two is exact).
-// One work-group = 16 query rows of one (b, KV head, row group); 16 threads per row, 8 dims each.
-// Each thread requests its row's LSE and its 16-byte partial chunk of every partition of a batch
-// (up to 16) together with the sequence length, before any of them is used: one memory round trip
-// per batch. Partitions past the sequence's last one are loaded (the workspace holds them) but
-// not used.
+//
+// A work-group of 256 threads covers RPB query rows of one (b, KV head, row group); a row's D
+// outputs are spread over TPR = D/8 threads (8 dimensions each) and its partitions over PG thread
+// groups (group pg takes partitions pg, pg + PG, ...), so that the grid grows with the partition
+// count and not only with the rows (a single 131072-token sequence has only 2 x 256 rows). Each
+// thread requests the LSE pair and the 16-byte chunk of its next kRedBatch partitions together with
+// the sequence length before using any of them (one memory round trip per batch); partitions past
+// the sequence's last one are loaded (the workspace holds them) but not used. The PG groups'
+// (max, sum, 8 accumulators) are combined through LDS in a fixed order.
 constexpr int kRedBatch = 16;
 
-template <int D>
+template <int D, int PG>
 __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnParams p) {
-  constexpr int TPR = D / 8;                 // threads per row
-  constexpr int RPB = 256 / TPR;             // rows per pass of the block (16 or 32)
+  constexpr int TPR = D / 8;                 // threads per row and partition group
+  constexpr int RPB = 256 / (TPR * PG);      // rows per work-group
+  __shared__ float red[PG > 1 ? 256 * 10 : 1];
   const int item_bgr = blockIdx.x;
   const int rg = item_bgr % p.row_groups;
   const int g = (item_bgr / p.row_groups) % p.Hkv;
@@ -776,42 +781,48 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnParams p) {
   const int tid = threadIdx.x;
   const size_t item0 = (size_t)item_bgr * p.splits;
   const uint16_t *part = static_cast<const uint16_t *>(p.part_o);
-  const int rr = tid / TPR, d8 = tid % TPR;
+  const int d8 = tid % TPR, pg = (tid / TPR) % PG, rr = tid / (TPR * PG);
   const int r_local = blockIdx.y * RPB + rr;
   const bool live = r_local < p.rows_per_group && rg * p.rows_per_group + r_local < p.rows;
-  if (!live) return;
+  const int r_ld = live ? r_local : 0;       // rows past the end load row 0 (never stored)
 
   float mx = -INFINITY, wsum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   bool bad = false;
-  for (int s0 = 0; s0 < p.splits; s0 += kRedBatch) {
-    const int nb = min(kRedBatch, p.splits - s0);
+  for (int s0 = 0; s0 < p.splits; s0 += kRedBatch * PG) {
+    // partitions per thread in this batch (the same for the whole work-group); a group whose
+    // last one lies past the end loads the batch's last partition instead (never used)
+    const int nb = min(kRedBatch, (p.splits - s0 + PG - 1) / PG);
     float2 ls[kRedBatch];
     u32x4 v[kRedBatch];
 #pragma unroll
-    for (int sp = 0; sp < kRedBatch; ++sp) {  // unconditional loads (clamped), no branches
-      const size_t it = (item0 + s0 + min(sp, nb - 1)) * p.rows_per_group + r_local;
-      ls[sp] = reinterpret_cast<const float2 *>(p.part_lse)[it];
-      v[sp] = ld_global_16(part + it * D + d8 * 8);
+    for (int sp = 0; sp < kRedBatch; ++sp) {
+      if (sp < nb) {
+        const int sidx = min(s0 + pg + sp * PG, p.splits - 1);
+        const size_t it = (item0 + sidx) * p.rows_per_group + r_ld;
+        ls[sp] = reinterpret_cast<const float2 *>(p.part_lse)[it];
+        v[sp] = ld_global_16(part + it * D + d8 * 8);
+      }
     }
     asm volatile("" ::: "memory");  // keeps the length load behind the batch's loads
     const int L = p.ctx_lens[b];    // so that one round trip serves all of them
     bad = L < 0 || L > p.max_ctx_len;
     const int nact = min(bad || L == 0 ? 1 : (L + p.chunk - 1) / p.chunk, p.splits);
-    if (s0 >= nact) break;
-    const int ns = min(nb, nact - s0);
+    if (s0 >= nact) break;          // uniform: s0 and b are the same for the whole work-group
     float bmx = mx;
 #pragma unroll
     for (int sp = 0; sp < kRedBatch; ++sp)
-      if (sp < ns) bmx = fmaxf(bmx, ls[sp].x);
-    const float rescale = __expf(mx - bmx);   // 0 for the first batch (mx = -inf)
-    wsum *= rescale;
+      if (s0 + pg + sp * PG < nact) bmx = fmaxf(bmx, ls[sp].x);
+    if (bmx > mx) {                 // first active partition: mx = -inf, the factor is 0
+      const float rescale = __expf(mx - bmx);
+      wsum *= rescale;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= rescale;
-    mx = bmx;
+      for (int e = 0; e < 8; ++e) acc[e] *= rescale;
+      mx = bmx;
+    }
 #pragma unroll
     for (int sp = 0; sp < kRedBatch; ++sp) {
-      if (sp < ns) {
+      if (s0 + pg + sp * PG < nact) {
         const float w = __expf(ls[sp].x - mx);
         wsum += w;
         const float wk = __builtin_amdgcn_ldexpf(w, -(int)ls[sp].y);
@@ -823,6 +834,33 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnParams p) {
       }
     }
   }
+  if (PG > 1) {
+    // groups 1 .. PG-1 hand (max, sum, accumulators) to group 0 of the same row and dimensions
+    float *mine = red + tid * 10;
+    mine[0] = mx;
+    mine[1] = wsum;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mine[2 + e] = acc[e];
+    __syncthreads();
+    if (pg != 0) return;
+    float gm = mx;
+#pragma unroll
+    for (int q = 1; q < PG; ++q) gm = fmaxf(gm, red[(tid + q * TPR) * 10]);
+    const float f0 = __expf(mx - gm);
+    wsum *= f0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= f0;
+#pragma unroll
+    for (int q = 1; q < PG; ++q) {
+      const float *o = red + (tid + q * TPR) * 10;
+      const float f = o[0] > -INFINITY ? __expf(o[0] - gm) : 0.f;  // a group with no partition
+      wsum += f * o[1];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += f * o[2 + e];
+    }
+    mx = gm;
+  }
+  if (!live) return;
   const float inv = bad ? NAN : 1.0f / wsum;
   const int r = rg * p.rows_per_group + r_local;
   const int jq = r / p.S, iq = r % p.S, h = g * p.G + jq;
@@ -998,13 +1036,30 @@ hipError_t launch_block_attn_f32(const AttnParams &p, hipStream_t stream, hipEve
   return e;
 }
 
-hipError_t launch_attn_reduce(const AttnParams &p, hipStream_t stream) {
-  const int rpb = 256 / (p.D / 8);
+// The merge's partition groups: the fewest (1, 4 or 16) that give >= 1024 work-groups and at
+// most kRedBatch partitions per thread, else 16.
+template <int D, int PG>
+static void launch_reduce_pg(const AttnParams &p, hipStream_t stream) {
+  constexpr int rpb = 256 / (D / 8 * PG);
   dim3 grid(p.B * p.Hkv * p.row_groups, (p.rows_per_group + rpb - 1) / rpb);
-  if (p.D == 128)
-    hipLaunchKernelGGL(attn_reduce_kernel<128>, grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(attn_reduce_kernel<64>, grid, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((attn_reduce_kernel<D, PG>), grid, dim3(256), 0, stream, p);
+}
+
+template <int D>
+static void launch_reduce_d(const AttnParams &p, hipStream_t stream) {
+  const int64_t units = (int64_t)p.B * p.Hkv * p.row_groups;
+  auto groups = [&](int pg) {
+    const int rpb = 256 / (D / 8 * pg);
+    return units * ((p.rows_per_group + rpb - 1) / rpb);
+  };
+  if (p.splits <= kRedBatch && groups(1) >= 1024) launch_reduce_pg<D, 1>(p, stream);
+  else if (p.splits <= 4 * kRedBatch && groups(4) >= 1024) launch_reduce_pg<D, 4>(p, stream);
+  else launch_reduce_pg<D, 16>(p, stream);
+}
+
+hipError_t launch_attn_reduce(const AttnParams &p, hipStream_t stream) {
+  if (p.D == 128) launch_reduce_d<128>(p, stream);
+  else launch_reduce_d<64>(p, stream);
   return hipGetLastError();
 }
 
