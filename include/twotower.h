@@ -360,6 +360,22 @@ typedef struct {
 
 tt_status twotower_block_attn(const tt_block_attn_args *args, void *ws, size_t *ws_bytes,
                               void *stream);
+
+/*
+ * twotower_block_attn without a workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * operation, kernels and arguments as twotower_block_attn, with the split-KV partials kept in a
+ * scratch array of TWOTOWER_STATIC_SCRATCH_BYTES that the library holds per device (in its code
+ * object, from the first call on a device until the process ends). Nothing is allocated or freed.
+ * num_splits == 0: the library's partition count, lowered if needed until the partials fit the
+ * scratch; an explicit num_splits whose partials do not fit returns TT_ENOSPACE (nothing is
+ * launched). Every call on one device shares that device's scratch: calls that may overlap on one
+ * device (different streams, or host threads without ordering) race and give wrong results;
+ * order them on one stream. The scratch needs no initial content (every value read is written
+ * first by the same call). TT_EHIP if the scratch's device address cannot be obtained.
+ */
+#define TWOTOWER_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+tt_status twotower_block_attn_static(const tt_block_attn_args *args, void *stream);
 tt_status twotower_kv_append(const tt_kv_append_args *args, void *ws, size_t *ws_bytes,
                              void *stream);
 tt_status twotower_mask_corrupt(const tt_mask_corrupt_args *args, void *ws, size_t *ws_bytes,

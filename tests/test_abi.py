@@ -291,3 +291,16 @@ def test_stream_read_probe_validation(L):
     assert f(C.c_void_p(FAKE), 1 << 20, 0, C.c_void_p(FAKE), None) == _lib.TT_EINVAL
     assert f(C.c_void_p(FAKE), 1 << 20, 65537, C.c_void_p(FAKE), None) == _lib.TT_EINVAL
     assert f(C.c_void_p(FAKE), 1 << 20, 256, None, None) == _lib.TT_EINVAL
+
+
+def test_static_attention_entry_validates_before_touching_the_device(L):
+    """The no-allocation entry point checks its arguments and the scratch size on the host first
+    (here no device is ever touched): bad arguments give TT_EINVAL, an explicit partition count
+    whose partials exceed the 32 MiB scratch TT_ENOSPACE."""
+    f = L.twotower_block_attn_static
+    assert f(None, None) == _lib.TT_EINVAL
+    assert f(C.byref(attn_args(head_dim=96)), None) == _lib.TT_ENOTSUP
+    assert f(C.byref(attn_args(q=FAKE + 8)), None) == _lib.TT_EINVAL
+    # 8 x 2 units x 256 partitions x 256 rows x (256 + 8) B = 276 MB of partials
+    assert f(C.byref(attn_args(num_splits=256)), None) == _lib.TT_ENOSPACE
+    assert _lib.STATIC_SCRATCH_BYTES == 32 << 20

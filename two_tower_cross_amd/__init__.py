@@ -115,13 +115,16 @@ def _attn_struct(q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, out, 
 
 def block_attn(q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, *, scale=None,
                max_ctx_len=None, out_dtype=None, return_lse=False, num_splits=0, out=None,
-               timing_events=None):
+               lse_out=None, timing_events=None, no_alloc=False):
     """Denoiser block attention at one layer; returns ``out`` (and ``lse`` [B,Hq,S] fp32).
 
     ``max_ctx_len`` bounds ctx_lens (used to plan the context partitions; default: the page
     table's capacity). ``num_splits`` 0 lets the library choose the partition count.
     ``timing_events``: optional 3 hipEvent_t handles (``torch.cuda.Event(...).cuda_event``),
     recorded before and after the main kernel and after the partition merge.
+    ``no_alloc``: call twotower_block_attn_static (no workspace; the library's per-device scratch);
+    nothing is allocated here either, so ``out`` (and ``lse_out`` with ``return_lse``) must be
+    given.
     """
     dev = q.device
     _check(q, "q", dev, ndim=4)
@@ -137,12 +140,22 @@ def block_attn(q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, *, scal
             or tuple(k_blk.shape) != (B, Hkv, S, D) or tuple(v_blk.shape) != (B, Hkv, D, S)
             or block_table.shape[0] != B or ctx_lens.shape[0] != B):
         raise ValueError("inconsistent attention shapes")
+    if no_alloc and (out is None or (return_lse and lse_out is None)):
+        raise ValueError("no_alloc: pass out (and lse_out to return the log-sum-exp)")
     if out is None:
         od = q.dtype if out_dtype is None else out_dtype
         out = torch.empty((B, S, Hq, D), dtype=od, device=dev)
     else:
         _check(out, "out", dev, None, 4)
-    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev) if return_lse else None
+    lse = None
+    if return_lse:
+        if lse_out is None:
+            lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+        else:
+            _check(lse_out, "lse_out", dev, torch.float32, 3)
+            if tuple(lse_out.shape) != (B, Hq, S):
+                raise ValueError("lse_out must be [B, Hq, S]")
+            lse = lse_out
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if max_ctx_len is None:
@@ -154,7 +167,12 @@ def block_attn(q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, *, scal
             raise ValueError("timing_events takes 3 events")
         ev = (C.c_void_p * 3)(*timing_events)
         a.timing_events = C.cast(ev, C.POINTER(C.c_void_p))
-    _run("twotower_block_attn", a, dev)
+    if no_alloc:
+        st = _lib.lib().twotower_block_attn_static(C.byref(a), _stream())
+        if st != _lib.TT_OK:
+            raise TwoTowerError("twotower_block_attn_static", st)
+    else:
+        _run("twotower_block_attn", a, dev)
     return (out, lse) if return_lse else out
 
 

@@ -15,6 +15,7 @@ LIB_PATH = os.environ.get("TWOTOWER_LIB", os.path.join(HERE, "libtwotower.so"))
 TT_OK, TT_EINVAL, TT_ENOTSUP, TT_ENOSPACE, TT_EHIP = range(5)
 TT_FP32, TT_BF16 = 0, 1
 TT_APPEND_OUT_OF_PAGES, TT_APPEND_NO_ROOM_IN_TABLE, TT_APPEND_BAD_PAGE = 1, 2, 4
+STATIC_SCRATCH_BYTES = 32 << 20
 ABI_VERSION = 8
 
 i32, i64, f32, vp = C.c_int32, C.c_int64, C.c_float, C.c_void_p
@@ -146,6 +147,8 @@ def lib():
         L.twotower_packed_weight_bytes.argtypes = [i32, i32]
         L.twotower_pack_weight.restype = i32
         L.twotower_pack_weight.argtypes = [vp, i32, i32, vp, vp]
+        L.twotower_block_attn_static.restype = i32
+        L.twotower_block_attn_static.argtypes = [C.POINTER(BlockAttnArgs), vp]
         L.twotower_probe_stream_read.restype = i32
         L.twotower_probe_stream_read.argtypes = [vp, C.c_size_t, i32, vp, vp]
         if L.twotower_abi_version() != ABI_VERSION:

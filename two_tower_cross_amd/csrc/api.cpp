@@ -440,6 +440,31 @@ tt_status twotower_block_attn(const tt_block_attn_args *args, void *ws, size_t *
   return hip_status(run_attn(pl, ws, static_cast<hipStream_t>(stream), ev[0], ev[1], ev[2]));
 }
 
+static_assert(TWOTOWER_STATIC_SCRATCH_BYTES == tt::kStaticScratchBytes, "static scratch size");
+
+tt_status twotower_block_attn_static(const tt_block_attn_args *args, void *stream) {
+  AttnPlan pl;
+  tt_status st = plan_attn(args, true, &pl);
+  if (st != TT_OK) return st;
+  if (pl.ws_bytes > tt::kStaticScratchBytes) {
+    if (args->num_splits != 0) return TT_ENOSPACE;
+    // the library's own partition count, lowered until the partials fit the scratch
+    const tt::AttnParams &p = pl.p;
+    const size_t per_split = (size_t)p.B * p.Hkv * p.row_groups * p.rows_per_group *
+                             (p.D * sizeof(uint16_t) + 2 * sizeof(float));
+    tt_block_attn_args a = *args;
+    a.num_splits = (int32_t)std::max<size_t>(1, (tt::kStaticScratchBytes - 2 * kAlign) / per_split);
+    if ((st = plan_attn(&a, true, &pl)) != TT_OK) return st;
+    if (pl.ws_bytes > tt::kStaticScratchBytes) return TT_ENOSPACE;
+  }
+  void *scratch = nullptr;
+  if (pl.ws_bytes > 0 && tt::static_scratch_address(&scratch) != hipSuccess) return TT_EHIP;
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  if (args->timing_events)
+    for (int i = 0; i < 3; ++i) ev[i] = static_cast<hipEvent_t>(args->timing_events[i]);
+  return hip_status(run_attn(pl, scratch, static_cast<hipStream_t>(stream), ev[0], ev[1], ev[2]));
+}
+
 tt_status twotower_unmask(const tt_unmask_args *args, void *ws, size_t *ws_bytes, void *stream) {
   UnmaskPlan pl;
   tt_status st = plan_unmask(args, true, &pl);

@@ -27,6 +27,7 @@
 // fp32 path: one work-group per (b, query head, block position), plain fp32 arithmetic.
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -1055,6 +1056,33 @@ static void launch_reduce_d(const AttnParams &p, hipStream_t stream) {
   if (p.splits <= kRedBatch && groups(1) >= 1024) launch_reduce_pg<D, 1>(p, stream);
   else if (p.splits <= 4 * kRedBatch && groups(4) >= 1024) launch_reduce_pg<D, 4>(p, stream);
   else launch_reduce_pg<D, 16>(p, stream);
+}
+
+// Scratch of the no-allocation attention entry point: the split-KV partials live in this
+// file-scope array instead of a caller workspace. Each device that loads the library holds its own
+// copy until the process ends. Host code never uses the array's name as an address: the device
+// address is looked up once per device with hipGetSymbolAddress (with that device current) and
+// only that pointer is handed to the kernels.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch_address(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_attn_reduce(const AttnParams &p, hipStream_t stream) {

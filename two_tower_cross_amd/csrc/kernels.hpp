@@ -45,6 +45,11 @@ hipError_t launch_block_attn_f32(const AttnParams &p, hipStream_t stream, hipEve
                                  hipEvent_t ev_end);
 hipError_t launch_attn_reduce(const AttnParams &p, hipStream_t stream);
 
+// Static scratch of the no-allocation attention entry point (32 MiB per device): the device
+// address of the current device's copy, looked up on the first call on that device.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+hipError_t static_scratch_address(void **ptr);
+
 // ------------------------------------------------------------------------------------ unmask
 struct UnmaskParams {
   const float *logits;
