@@ -94,9 +94,13 @@ typedef enum { TT_FP32 = 0, TT_BF16 = 1 } tt_dtype;
  * needed block_table entries lie outside [0, num_pages), gets NaN in all its outputs (nothing out
  * of bounds is read). Page slots past ctx_lens[b] are never used, so they may hold anything.
  *
- * num_splits: number of context partitions per (sequence, KV head) at max_ctx_len (0 = chosen
- * by the library to fill the GPU). Partitions are merged exactly with their log-sum-exp weights;
- * the result depends on num_splits only through floating-point rounding.
+ * num_splits: number of context partitions per (sequence, KV head) at max_ctx_len; 0 = chosen
+ * by the library: for up to 256 sequences the partitions are sized on the device from the actual
+ * lengths, nearly equal across the whole batch and about one per compute unit (sequence b's
+ * ceil(ctx_lens[b] / 64) tiles in nearly equal parts of at most c tiles, c the smallest size that
+ * keeps the total near the GPU's compute units), so ragged batches keep every compute unit busy.
+ * Partitions are merged exactly with their log-sum-exp weights; the result depends on the
+ * partitioning only through floating-point rounding.
  *
  * Value range: any finite inputs. With several partitions each partition's normalized output row
  * is kept in the workspace as fp16 scaled by a power of two chosen per row (its largest magnitude
@@ -284,8 +288,11 @@ typedef struct {
  * twotower_lm_head_unmask. Layer 0 reads h_in; the residual stream is kept in h_work.
  * All layers share batch, S, heads, head_dim, block_table, ctx_lens and page geometry (taken from
  * `attn`; attn.q/k_pages/v_pages/k_blk/v_blk/out/lse/timing_events are ignored). The context
- * caches are only read. Sequences with no masked position left still run the dense math (their
- * results are discarded by the unmasking, which reads no committed row).
+ * caches are only read. A sequence with no masked position left gets no attention work (with the
+ * automatic partition count its context is left out of the partition plan, so the live
+ * sequences' contexts spread over the whole GPU, and its attn_out rows are not written); the
+ * row-wise projections still run over its rows (their weights are streamed for the live rows
+ * anyway) and their results are discarded by the unmasking, which reads no committed row.
  *
  * timing_events: optional host array of 3*num_layers hipEvent_t; if not NULL, events[3l] and
  * events[3l+1] are recorded on `stream` immediately before and after the main attention kernel

@@ -72,10 +72,12 @@ def query(name, a):
 def test_attention_workspace_query_and_plan():
     st, n = query("twotower_block_attn", attn_args())
     assert st == _lib.TT_OK
-    # auto plan at B*Hkv = 16 units: 16 partitions of 2048 tokens, 256-row fp16 partials + an
-    # fp32 (lse, scale exponent) pair per row
+    # automatic (balanced) plan for 8 sequences x 2 KV heads at 32768 tokens: 128 partitions per KV
+    # head (16 per sequence), 256-row fp16 partials + an fp32 (lse, scale exponent) pair per row,
+    # plus the plan record (2 int32) of every sequence
     items = 8 * 2 * 16
-    expect = -(-items * 256 * 128 * 2 // 256) * 256 + -(-items * 256 * 8 // 256) * 256
+    expect = (-(-items * 256 * 128 * 2 // 256) * 256 + -(-items * 256 * 8 // 256) * 256
+              + -(-8 * 2 * 4 // 256) * 256)
     assert n == expect
     # one partition needs no workspace
     st, n = query("twotower_block_attn", attn_args(num_splits=1))

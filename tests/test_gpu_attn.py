@@ -100,6 +100,25 @@ def test_merge_partition_groups(B, Hkv, D, lens, splits):
     check(case, out, lse, TOL_BF16)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,hi", [
+    (100, 8, 2, 3000),   # two lanes' worth of sequences per wave in the plan
+    (256, 4, 1, 1500),   # the largest batch the balanced plan takes (four per lane)
+    (300, 4, 1, 600),    # beyond it: the uniform split by the longest context
+])
+def test_balanced_plan_batches(B, Hq, Hkv, hi):
+    """The automatic partition count cuts every sequence's context from the actual lengths so
+    that the work-groups get nearly equal shares: empty, one-token, tile-boundary and random
+    lengths, against the oracle."""
+    g = synth.rng(70 + B)
+    lens = g.integers(0, hi + 1, size=B)
+    lens[:6] = [0, 1, 63, 64, 65, hi]
+    case = synth.attn_case(71 + B, B=B, S=16, Hq=Hq, Hkv=Hkv, D=128, ctx_lens=lens,
+                           page_size=256, dtype="bf16", nan_poison=True, spare_frac=0.05)
+    out, lse = gpu_attn(case)
+    assert not np.isnan(out).any()
+    check(case, out, lse, TOL_BF16)
+
+
 # ----------------------------------------------------------------------------- value range
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])

@@ -182,6 +182,48 @@ def test_step_stages_against_oracle():
             assert gn[b] == 1 and m0[b].sum() - gm[b].sum() == 1
 
 
+def test_finished_sequences_get_no_attention_work():
+    """A sequence with no masked position left gets no attention work in the step (the live
+    sequences' context is re-planned over the whole GPU): its state and its attention output rows
+    are untouched, and the live sequences' attention and decisions still match the oracle on the
+    step's own inputs."""
+    m = small_model(seed=8, B=4, L=1500)
+    step = make_step(m, keep_logits=True)
+    masked = torch.ones((m.B, m.S), dtype=torch.uint8, device=DEV)
+    tokens = torch.full((m.B, m.S), -1, dtype=torch.int32, device=DEV)
+    for b in (1, 3):
+        masked[b] = 0
+        tokens[b] = 10 + b
+    m0, t0 = masked.clone(), tokens.clone()
+    step.attn_out.fill_(7.0)
+    conf, n = step(m.h_steps[0], masked, tokens, threshold=0.9, min_commit=True)
+    torch.cuda.synchronize()
+    for b in (1, 3):
+        assert torch.equal(masked[b], m0[b]) and torch.equal(tokens[b], t0[b]) and int(n[b]) == 0
+        assert bool((step.attn_out[b] == 7.0).all())       # no attention work for it
+    l = m.layers - 1
+    G = m.Hq // m.Hkv
+    for b in (0, 2):
+        for g in range(m.Hkv):
+            heads = slice(g * G, (g + 1) * G)
+            ref, _ = oattn.block_attention(
+                f64(step.q[b:b + 1, :, heads]), f64(m.k_pages[l][b:b + 1, g:g + 1]),
+                f64(m.v_pages[l][b:b + 1, g:g + 1]), np.zeros((1, 1), np.int32),
+                np.array([m.L], np.int32), f64(step.k_blk[l][b:b + 1, g:g + 1]),
+                f64(step.v_blk[l][b:b + 1, g:g + 1]), 1.0 / math.sqrt(m.D))
+            ref16 = torch.from_numpy(ref).to(torch.bfloat16).double().numpy()
+            assert max_abs(f64(step.attn_out[b:b + 1, :, heads]), ref16) <= TOL_BF16
+    ot, om, oc, on = ounmask.confidence_unmask(step.logits.cpu().numpy(), m0.cpu().numpy(),
+                                               t0.cpu().numpy(), np.float32(0.9), min_commit=True)
+    gm, gt = masked.cpu().numpy(), tokens.cpu().numpy()
+    for b in (0, 2):
+        c = np.sort(oc[b])[::-1]
+        if c[0] - c[1] >= 1e-4 * c[0]:
+            assert np.array_equal(gm[b], om[b]) and np.array_equal(gt[b], ot[b])
+        else:
+            assert int(n[b]) == 1
+
+
 def checksum(ts):
     return [int(t.view(torch.int16).to(torch.int64).sum().item()) for t in ts]
 

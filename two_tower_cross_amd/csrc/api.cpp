@@ -16,6 +16,8 @@ namespace {
 constexpr int kTargetWorkgroups = 256;  // one work-group per compute unit on MI355X
 constexpr int kMinChunk = 256;          // context tokens per partition, lower bound
 constexpr int kMaxPartitionTiles = 4096;  // 64-token tile indices one attention work-group stages in LDS
+constexpr int kMinPartTiles = 4;          // the balanced plan's smallest partition (256 tokens)
+constexpr int kPlanMaxB = 256;            // sequences the balanced plan handles
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -30,6 +32,33 @@ struct AttnPlan {
   size_t ws_bytes = 0;
   bool use_bf16 = false;
 };
+
+// Balanced plan (see block_attn.hip): the smallest partition size c >= kMinPartTiles (in 64-token
+// tiles) for which B sequences of t tiles need at most `parts` partitions, n = max(1, ceil(t / c))
+// each; kMaxPartitionTiles when one partition per sequence is already too many. The device
+// computes the same from the actual lengths; for equal lengths both agree.
+int64_t balanced_tiles(int64_t B, int64_t t, int64_t parts) {
+  auto count = [&](int64_t c) { return B * std::max<int64_t>(1, cdiv(t, c)); };
+  int64_t lo = std::min<int64_t>(std::max<int64_t>(kMinPartTiles, cdiv(B * t, parts)),
+                                 kMaxPartitionTiles);
+  if (count(lo) <= parts) return lo;
+  if (B >= parts) return kMaxPartitionTiles;
+  int64_t hi = std::min<int64_t>(kMaxPartitionTiles,
+                                 std::max<int64_t>(lo + 1, cdiv(B * t, parts - B)));
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) / 2;
+    if (count(mid) <= parts) hi = mid;
+    else lo = mid;
+  }
+  return hi;
+}
+
+// Partial slots of a call (per row-group row block) and whether the merge runs.
+size_t attn_slots(const tt::AttnParams &p) {
+  return p.balanced ? (size_t)p.items * p.Hkv * p.row_groups
+                    : (size_t)p.B * p.Hkv * p.row_groups * p.splits;
+}
+bool attn_needs_merge(const tt::AttnParams &p) { return p.balanced ? p.max_parts > 1 : p.splits > 1; }
 
 tt_status plan_attn(const tt_block_attn_args *a, bool check_pointers, AttnPlan *out) {
   if (!a) return TT_EINVAL;
@@ -85,9 +114,24 @@ tt_status plan_attn(const tt_block_attn_args *a, bool check_pointers, AttnPlan *
   const int rows_pad = (int)cdiv(rows, 32) * 32;
   p.rows_per_group = std::min(rows_pad, 256);
   p.row_groups = (int)cdiv(rows_pad, p.rows_per_group);
+  const int64_t t_max = cdiv(a->max_ctx_len, 64);
+  const int64_t groups = (int64_t)p.Hkv * p.row_groups;
   if (!out->use_bf16 || a->max_ctx_len == 0) {
     p.splits = 1;
     p.chunk = std::max(64, (int)cdiv(std::max(a->max_ctx_len, 1), 64) * 64);
+  } else if (a->num_splits == 0 && p.B <= kPlanMaxB && t_max < (1 << 24) &&
+             (int64_t)p.B * t_max < INT32_MAX) {
+    // Balanced plan: the kernels size the partitions from the actual lengths; here the case of
+    // every sequence at max_ctx_len (the same search as on the device) gives the speculative
+    // split, and the bounds give the grid and the workspace.
+    const int64_t parts = std::max<int64_t>(1, kTargetWorkgroups / groups);
+    const int64_t c = balanced_tiles(p.B, t_max, parts);
+    p.balanced = 1;
+    p.parts = (int)parts;
+    p.splits = (int)std::max<int64_t>(1, cdiv(t_max, c));
+    p.chunk = (int)(c * 64);
+    p.items = (int)std::max<int64_t>(parts, (int64_t)p.B * cdiv(t_max, kMaxPartitionTiles));
+    p.max_parts = (int)std::min<int64_t>(p.items, cdiv(t_max, kMinPartTiles));
   } else {
     const int64_t units = std::max<int64_t>(1, (int64_t)p.B * p.Hkv * p.row_groups);
     int64_t want = a->num_splits > 0 ? a->num_splits : cdiv(kTargetWorkgroups, units);
@@ -101,11 +145,13 @@ tt_status plan_attn(const tt_block_attn_args *a, bool check_pointers, AttnPlan *
     p.splits = (int)cdiv(a->max_ctx_len, chunk);
   }
   if (p.splits > 65535 || (int64_t)p.B * p.Hkv * p.row_groups > 65535) return TT_ENOTSUP;
+  if (p.balanced && (int64_t)p.items * groups * 8 > INT32_MAX) return TT_ENOTSUP;
   out->ws_bytes = 0;
-  if (p.splits > 1) {
-    const size_t items = (size_t)p.B * p.Hkv * p.row_groups * p.splits;
+  if (attn_needs_merge(p)) {
+    const size_t items = attn_slots(p);
     out->ws_bytes = align_up(items * p.rows_per_group * p.D * sizeof(uint16_t)) +
-                    align_up(items * p.rows_per_group * 2 * sizeof(float));
+                    align_up(items * p.rows_per_group * 2 * sizeof(float)) +
+                    (p.balanced ? align_up((size_t)p.B * 2 * sizeof(int32_t)) : 0);
   }
   return TT_OK;
 }
@@ -121,14 +167,17 @@ hipError_t run_attn(AttnPlan &pl, void *ws, hipStream_t stream, hipEvent_t e0, h
     if (e == hipSuccess && e2) e = hipEventRecord(e2, stream);
     return e;
   }
-  if (p.splits > 1) {
-    const size_t items = (size_t)p.B * p.Hkv * p.row_groups * p.splits;
+  if (attn_needs_merge(p)) {
+    const size_t items = attn_slots(p);
     char *w = static_cast<char *>(ws);
+    const size_t o_bytes = align_up(items * p.rows_per_group * p.D * sizeof(uint16_t));
+    const size_t l_bytes = align_up(items * p.rows_per_group * 2 * sizeof(float));
     p.part_o = w;
-    p.part_lse = reinterpret_cast<float *>(w + align_up(items * p.rows_per_group * p.D * sizeof(uint16_t)));
+    p.part_lse = reinterpret_cast<float *>(w + o_bytes);
+    p.plan_rec = p.balanced ? reinterpret_cast<int32_t *>(w + o_bytes + l_bytes) : nullptr;
   }
   e = tt::launch_block_attn_bf16(p, stream, e0, e1);
-  if (e == hipSuccess && p.splits > 1) e = tt::launch_attn_reduce(p, stream);
+  if (e == hipSuccess && attn_needs_merge(p)) e = tt::launch_attn_reduce(p, stream);
   if (e == hipSuccess && e2) e = hipEventRecord(e2, stream);
   return e;
 }
@@ -613,6 +662,8 @@ tt_status twotower_denoise_step(const tt_denoise_step_args *a, void *ws, size_t 
   AttnPlan ap;
   tt_status st = plan_attn(&ga, true, &ap);
   if (st != TT_OK) return st;
+  // sequences with no masked position left get no attention work (balanced plan)
+  ap.p.active = a->unmask.masked;
 
   tt_qkv_args qa{};
   qa.batch = g.batch;

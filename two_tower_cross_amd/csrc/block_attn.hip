@@ -470,6 +470,167 @@ __device__ __forceinline__ void pipe_finish(const PipeRegs<D> &r, f32x16 *oacc) 
       oacc[mb] = mfma32x32x16(r.v[2 * mb + kc], kc ? r.pb : r.pa, oacc[mb]);
 }
 
+// ------------------------------------------------------------------ balanced partition plan
+// With the automatic partition count the context of each (sequence, KV head) is cut so that the
+// work-groups get nearly equal shares whatever the mix of lengths: sequence b's T_b =
+// ceil(L_b / 64) tiles go into n_b = max(1, ceil(T_b / c)) partitions of nearly equal size
+// (partition s holds tiles floor(s T_b / n_b) .. floor((s + 1) T_b / n_b) - 1; partition 0 also
+// takes the block keys), with c the smallest tile count >= kMinPartTiles for which
+// sum_b n_b <= p.parts (the host's target per KV head and row group: one work-group per compute
+// unit); when one partition per sequence already exceeds the target, c = kMaxPartTiles. A
+// sequence that the caller marks finished (p.active given and no nonzero flag of the sequence)
+// gets no partition; one with an invalid length counts as empty (its outputs become NaN). Work
+// item k of a KV head and row group is partition k - E_b of the sequence b with E_b <= k <
+// E_b + n_b (E_b = sum of n over the sequences before b), ordered (b, KV head, partition) so that
+// equal lengths give the same items, in the same order, as a uniform split. Every wave of the
+// attention kernel and of the merge computes the plan from the lengths (at most kPlanMaxB
+// sequences, kPlanPerLane per lane).
+constexpr int kPlanMaxB = 256;
+constexpr int kPlanPerLane = kPlanMaxB / 64;
+constexpr int kMinPartTiles = 4;
+
+// Inclusive prefix sum over the 64 lanes of a wave: sums of 4 within each row of 16 lanes by row
+// shifts, then rows completed with shifts by 4 and 8, then carried across rows by the row
+// broadcasts of lanes 15 and 31.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  int v = x + __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);         // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, x, 0x113, 0xf, 0xf, true);         // row_shr:3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xe, true);         // row_shr:4, lanes 4-15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xc, true);         // row_shr:8, lanes 8-15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, true);         // row_bcast:15, rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, true);         // row_bcast:31, rows 2, 3
+  return v;
+}
+
+__device__ __forceinline__ int wave_total(int x) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
+}
+
+// ceil(a / c) for 0 <= a < 2^24, 1 <= c < 2^24: a float estimate, then corrected exactly.
+__device__ __forceinline__ int ceil_div24(int a, int c) {
+  int q = (int)ceilf((float)a / (float)c);
+  while (q > 0 && (q - 1) * c >= a) --q;
+  while (q * c < a) ++q;
+  return q;
+}
+
+// Lane l's sequences b = l + 64 j: their tile counts, activity, and (after plan_partitions)
+// partition counts and exclusive prefix sums.
+struct PlanLanes {
+  int T[kPlanPerLane];
+  int n[kPlanPerLane];
+  int excl[kPlanPerLane];
+  bool act[kPlanPerLane];
+};
+
+// A sequence counts as active unless the caller's flags say it has no masked position left.
+__device__ __forceinline__ bool seq_active(const AttnParams &p, int b) {
+  if (!p.active) return true;
+  const uint8_t *m = p.active + (size_t)b * p.S;
+  uint32_t any = 0;
+  if ((p.S & 3) == 0 && (reinterpret_cast<uintptr_t>(p.active) & 3) == 0) {
+    for (int i = 0; i < p.S; i += 4) any |= *reinterpret_cast<const uint32_t *>(m + i);
+  } else {
+    for (int i = 0; i < p.S; ++i) any |= m[i];
+  }
+  return any != 0;
+}
+
+// Requests the lengths (and activity flags) of lane's sequences; nothing is used yet.
+__device__ __forceinline__ void plan_load(const AttnParams &p, int lane, int (&L)[kPlanPerLane],
+                                          bool (&act)[kPlanPerLane]) {
+#pragma unroll
+  for (int j = 0; j < kPlanPerLane; ++j) {
+    const int b = lane + 64 * j;
+    L[j] = b < p.B ? p.ctx_lens[b] : 0;
+    act[j] = b < p.B && seq_active(p, b);
+  }
+}
+
+__device__ __forceinline__ int plan_count(const PlanLanes &pl, int c) {
+  int s = 0;
+#pragma unroll
+  for (int j = 0; j < kPlanPerLane; ++j)
+    if (pl.act[j]) s += max(1, ceil_div24(pl.T[j], c));
+  return wave_total(s);
+}
+
+// The partition size c (tiles) and every lane's n and exclusive prefix; returns the total count.
+__device__ int plan_partitions(const AttnParams &p, const int (&L)[kPlanPerLane],
+                               const bool (&act)[kPlanPerLane], PlanLanes &pl) {
+  int tot = 0, nact = 0;
+#pragma unroll
+  for (int j = 0; j < kPlanPerLane; ++j) {
+    const bool ok = L[j] >= 0 && L[j] <= p.max_ctx_len;
+    pl.T[j] = ok ? (L[j] + kTile - 1) / kTile : 0;
+    pl.act[j] = act[j];
+    if (act[j]) {
+      tot += pl.T[j];
+      ++nact;
+    }
+  }
+  tot = wave_total(tot);
+  nact = wave_total(nact);
+  int lo = min(max(kMinPartTiles, (tot + p.parts - 1) / p.parts), kMaxPartTiles);
+  int c = lo;
+  if (plan_count(pl, lo) > p.parts) {
+    if (nact >= p.parts) {
+      c = kMaxPartTiles;
+    } else {
+      // feasible: sum_b n_b <= tot / hi + nact <= parts (or hi is the largest partition allowed)
+      int hi = min(kMaxPartTiles, max(lo + 1, (tot + p.parts - nact - 1) / (p.parts - nact)));
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (plan_count(pl, mid) <= p.parts) hi = mid;
+        else lo = mid;
+      }
+      c = hi;
+    }
+  }
+  int carry = 0;
+#pragma unroll
+  for (int j = 0; j < kPlanPerLane; ++j) {
+    pl.n[j] = pl.act[j] ? max(1, ceil_div24(pl.T[j], c)) : 0;
+    const int incl = wave_incl_scan(pl.n[j]) + carry;
+    pl.excl[j] = incl - pl.n[j];
+    carry = __builtin_amdgcn_readlane(incl, 63);
+  }
+  return carry;
+}
+
+// The sequence, KV head and partition of work unit q (units ordered (b, KV head, partition)), or
+// b = -1 when q lies past the last one.
+struct PlanItem {
+  int b, g, split, n, excl;
+};
+
+__device__ __forceinline__ PlanItem plan_item(const AttnParams &p, const PlanLanes &pl, int q) {
+  PlanItem it = {-1, 0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < kPlanPerLane; ++j) {
+    const bool mine = q >= pl.excl[j] * p.Hkv && q < (pl.excl[j] + pl.n[j]) * p.Hkv;
+    const uint64_t hit = __ballot(mine);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      it.b = l + 64 * j;
+      it.n = __builtin_amdgcn_readlane(pl.n[j], l);
+      it.excl = __builtin_amdgcn_readlane(pl.excl[j], l);
+      const int r = q - it.excl * p.Hkv;
+      it.g = r / it.n;
+      it.split = r - it.g * it.n;
+    }
+  }
+  return it;
+}
+
+// Tokens [t_begin, t_end) of partition s of n over a sequence of L tokens (T tiles).
+__device__ __forceinline__ void part_range(int s, int n, int L, int &t_begin, int &t_end) {
+  const int T = (L + kTile - 1) / kTile;
+  t_begin = (int)(((int64_t)s * T) / n) * kTile;
+  t_end = min(L, (int)(((int64_t)(s + 1) * T) / n) * kTile);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -478,23 +639,31 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   // in its dispatch order, one L2 serving them all.
   const int id = blockIdx.x, R = p.row_groups;
   const int q = (id >> 3) / R * 8 + (id & 7);  // (sequence, KV head, partition) unit
-  if (q >= p.B * p.Hkv * p.splits) return;
-  const int split = q % p.splits;
-  const int item_bgr = q / p.splits * R + (id >> 3) % R;
-  const int rg = item_bgr % p.row_groups;
-  const int g = (item_bgr / p.row_groups) % p.Hkv;
-  const int b = item_bgr / (p.row_groups * p.Hkv);
+  const int rg = (id >> 3) % R;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int per_b = p.Hkv * p.splits;
+  if (!p.balanced && q >= p.B * per_b) return;
 
-  const bool has_block = split == 0;
-  const int t_begin = split * p.chunk;
+  // The unit's sequence, KV head and partition, first as if every sequence had max_ctx_len tokens
+  // (and were active): the uniform split, and with the balanced plan the plan of that case, which
+  // is the actual one whenever the lengths are equal. Everything that depends on them is requested
+  // at once with the lengths (one memory round trip): this wave's query rows, the first block
+  // tile (partition 0) and the page of every tile the partition can hold (clamped to the table;
+  // entries past the sequence's end are loaded but not used). With the balanced plan the actual
+  // unit follows from the lengths, and what differs is requested again.
+  int b = min(q / per_b, p.B - 1);
+  int g = (q % per_b) / p.splits, split = q % p.splits;
+  int t_begin, t_end_b;
+  if (p.balanced) part_range(split, p.splits, p.max_ctx_len, t_begin, t_end_b);
+  else t_begin = split * p.chunk;
+  int n_b = p.splits, excl_b = b * p.splits;  // the sequence's partitions, and those before it
+  int Lp[kPlanPerLane];
+  bool actp[kPlanPerLane];
+  int L = 0;
+  if (p.balanced) plan_load(p, lane, Lp, actp);
+  else L = p.ctx_lens[b];
 
-  // Everything that does not depend on the sequence length is requested at once with it (one
-  // memory round trip): the length, this wave's query rows, the first block tile (partition 0)
-  // and the page of every tile the partition can hold (clamped to the table; entries past the
-  // sequence's end are loaded but not used).
-  const int L = p.ctx_lens[b];
   const int col = lane & 31, hh = lane >> 5;
   const int r_local = wave * 32 + col;
   const int r = rg * p.rows_per_group + r_local;
@@ -502,33 +671,71 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   const bool wave_active =
       wave * 32 < p.rows_per_group && rg * p.rows_per_group + wave * 32 < p.rows;
   const int jq = row_ok ? r / p.S : 0, iq = row_ok ? r % p.S : 0;
-  const int h = g * p.G + jq;
   u32x4 qreg[D / 16];
-  {
-    const uint16_t *qrow =
-        static_cast<const uint16_t *>(p.q) + (((size_t)b * p.S + iq) * p.Hq + h) * D;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = row_ok ? ld_global_16(qrow + kk * 16 + hh * 8) : z;
-  }
-  const size_t bg = (size_t)b * p.Hkv + g;
-  const uint16_t *kblk = static_cast<const uint16_t *>(p.k_blk) + bg * p.S * D;
-  const uint16_t *vblk = static_cast<const uint16_t *>(p.v_blk) + bg * D * p.S;
   BlockRegs<D> br;
-  if (has_block) fetch_block_tile<D>(br, kblk, vblk, min(p.S, kTile), p.S, tid);
-  const int32_t *btab = p.block_table + (size_t)b * p.max_pages;
-  const int n_spec = p.chunk / kTile;               // tiles of a full partition
+  const int n_spec = p.chunk / kTile;               // tiles of the largest partition
   // Up to 64 tiles, every wave requests all of the pages (lane i: tile i) and keeps the tile
   // indices in a register; beyond, the work-group requests them once and stages them in LDS.
   const bool ids_in_regs = n_spec <= 64;
   const int li = ids_in_regs ? lane : tid;
   int spec_page = 0;
-  if (li < n_spec) spec_page = btab[min((t_begin + li * kTile) / p.page_size, p.max_pages - 1)];
+  auto load_unit = [&]() {
+    const uint16_t *qrow =
+        static_cast<const uint16_t *>(p.q) + (((size_t)b * p.S + iq) * p.Hq + g * p.G + jq) * D;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      qreg[kk] = row_ok ? ld_global_16(qrow + kk * 16 + hh * 8) : z;
+    const size_t bg = (size_t)b * p.Hkv + g;
+    if (split == 0)
+      fetch_block_tile<D>(br, static_cast<const uint16_t *>(p.k_blk) + bg * p.S * D,
+                          static_cast<const uint16_t *>(p.v_blk) + bg * D * p.S, min(p.S, kTile),
+                          p.S, tid);
+    const int32_t *btab = p.block_table + (size_t)b * p.max_pages;
+    if (li < n_spec) spec_page = btab[min((t_begin + li * kTile) / p.page_size, p.max_pages - 1)];
+  };
+  load_unit();
+
+  if (p.balanced) {
+    PlanLanes pl;
+    plan_partitions(p, Lp, actp, pl);
+    if (id == 0 && wave == 0 && p.plan_rec) {  // the merge reads the plan instead of recomputing it
+#pragma unroll
+      for (int j = 0; j < kPlanPerLane; ++j) {
+        const int bb = lane + 64 * j;
+        if (bb < p.B) *reinterpret_cast<int2 *>(p.plan_rec + 2 * bb) = make_int2(pl.n[j], pl.excl[j]);
+      }
+    }
+    const PlanItem it = plan_item(p, pl, q);
+    if (it.b < 0) return;                        // past the last unit (the same for every wave)
+#pragma unroll
+    for (int j = 0; j < kPlanPerLane; ++j)
+      if (it.b >= 64 * j && it.b < 64 * (j + 1)) L = __builtin_amdgcn_readlane(Lp[j], it.b - 64 * j);
+    const bool ok = L >= 0 && L <= p.max_ctx_len;
+    int tb, te;
+    part_range(it.split, it.n, ok ? L : 0, tb, te);
+    n_b = it.n;
+    excl_b = it.excl;
+    if (it.b != b || it.g != g || it.split != split || tb != t_begin) {
+      b = it.b;
+      g = it.g;
+      split = it.split;
+      t_begin = tb;
+      load_unit();
+    }
+    t_end_b = te;
+  }
+  const int h = g * p.G + jq;
+  const bool has_block = split == 0;
+  const size_t bg = (size_t)b * p.Hkv + g;
+  const uint16_t *kblk = static_cast<const uint16_t *>(p.k_blk) + bg * p.S * D;
+  const uint16_t *vblk = static_cast<const uint16_t *>(p.v_blk) + bg * D * p.S;
+  const int32_t *btab = p.block_table + (size_t)b * p.max_pages;
 
   bool bad = L < 0 || L > p.max_ctx_len;
   const int Lc = bad ? 0 : L;
-  const int t_end = min(Lc, t_begin + p.chunk);
-  if (!has_block && t_begin >= Lc && !bad) return;  // partition past this sequence's context
+  const int t_end = p.balanced ? t_end_b : min(Lc, t_begin + p.chunk);
+  if (!p.balanced && !has_block && t_begin >= Lc && !bad) return;  // partition past the context
 
   const int n_ctx = t_end > t_begin ? t_end - t_begin : 0;
   const int n_full = n_ctx / kTile;            // full tiles: asynchronous ring
@@ -672,7 +879,7 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   const float l = pair_sum(lpart);
   const float inv = bad ? NAN : 1.0f / l;
   const float lse_val = bad ? NAN : m * p.scale + logf(l);
-  const bool to_part = p.splits > 1;
+  const bool to_part = n_b > 1;
   // Partial rows go out in fp16 scaled by 2^kexp, kexp chosen so that the row's largest |O_p|
   // lands in [2^14, 2^15): |O_p| <= max|V| may be any finite bf16 value, far outside fp16's range
   // without the scale. The row's 2 x D/2 values sit in the lane pair (col, col + 32).
@@ -732,7 +939,10 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
     return ld_lds_16(slice + rr * row_bytes + ((cc ^ (rr & (cpr - 1))) << 4));
   };
   if (to_part) {
-    const size_t item = (size_t)item_bgr * p.splits + split;
+    // partial slot: the sequence's partitions sit together, per (KV head, row group)
+    const size_t item = (size_t)excl_b * p.Hkv * R + (size_t)(g * R + rg) * n_b + split;
+    const size_t slots = p.balanced ? (size_t)p.items * p.Hkv * R : (size_t)p.B * p.Hkv * R * p.splits;
+    if (item >= slots) return;  // never taken: the plan keeps every slot inside the workspace
     // rows wave*32 .. wave*32+31 of this partition are contiguous in the partial buffer
     char *dst = reinterpret_cast<char *>(p.part_o) + (item * p.rows_per_group + wave * 32) * (size_t)row_bytes;
     const int nrows = min(32, p.rows_per_group - wave * 32);
@@ -764,9 +974,9 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
 // outputs are spread over TPR = D/8 threads (8 dimensions each) and its partitions over PG thread
 // groups (group pg takes partitions pg, pg + PG, ...), so that the grid grows with the partition
 // count and not only with the rows (a single 131072-token sequence has only 2 x 256 rows). Each
-// thread requests the LSE pair and the 16-byte chunk of its next kRedBatch partitions together with
-// the sequence length before using any of them (one memory round trip per batch); partitions past
-// the sequence's last one are loaded (the workspace holds them) but not used. The PG groups'
+// thread requests the LSE pair and the 16-byte chunk of its first kRedBatch partitions together
+// with the lengths before using any of them (one memory round trip); partitions past the
+// sequence's last one are loaded (the workspace holds them) but not used. The PG groups'
 // (max, sum, 8 accumulators) are combined through LDS in a fixed order.
 constexpr int kRedBatch = 16;
 
@@ -779,37 +989,63 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnParams p) {
   const int rg = item_bgr % p.row_groups;
   const int g = (item_bgr / p.row_groups) % p.Hkv;
   const int b = item_bgr / (p.row_groups * p.Hkv);
-  const int tid = threadIdx.x;
-  const size_t item0 = (size_t)item_bgr * p.splits;
+  const int tid = threadIdx.x, lane = tid & 63;
   const uint16_t *part = static_cast<const uint16_t *>(p.part_o);
   const int d8 = tid % TPR, pg = (tid / TPR) % PG, rr = tid / (TPR * PG);
   const int r_local = blockIdx.y * RPB + rr;
   const bool live = r_local < p.rows_per_group && rg * p.rows_per_group + r_local < p.rows;
   const int r_ld = live ? r_local : 0;       // rows past the end load row 0 (never stored)
 
-  float mx = -INFINITY, wsum = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  bool bad = false;
-  for (int s0 = 0; s0 < p.splits; s0 += kRedBatch * PG) {
+  // This (sequence, KV head, row group)'s partials: slots item0 .. item0 + n - 1, first as in the
+  // case that every sequence has max_ctx_len tokens (the uniform split); with the balanced plan
+  // the actual slots follow from the sequence's plan record (written by the attention kernel,
+  // requested in the same round trip), and the first batch is requested again if they differ.
+  size_t item0 = (size_t)item_bgr * p.splits;
+  int n = p.splits;
+  int2 rec = make_int2(0, 0);
+  if (p.balanced) rec = *reinterpret_cast<const int2 *>(p.plan_rec + 2 * b);
+  float2 ls[kRedBatch];
+  u32x4 v[kRedBatch];
+  auto batch_loads = [&](int s0) {
     // partitions per thread in this batch (the same for the whole work-group); a group whose
-    // last one lies past the end loads the batch's last partition instead (never used)
-    const int nb = min(kRedBatch, (p.splits - s0 + PG - 1) / PG);
-    float2 ls[kRedBatch];
-    u32x4 v[kRedBatch];
+    // last one lies past the end loads the sequence's last partition instead (never used)
+    const int nb = min(kRedBatch, (n - s0 + PG - 1) / PG);
 #pragma unroll
     for (int sp = 0; sp < kRedBatch; ++sp) {
       if (sp < nb) {
-        const int sidx = min(s0 + pg + sp * PG, p.splits - 1);
+        const int sidx = min(s0 + pg + sp * PG, n - 1);
         const size_t it = (item0 + sidx) * p.rows_per_group + r_ld;
         ls[sp] = reinterpret_cast<const float2 *>(p.part_lse)[it];
         v[sp] = ld_global_16(part + it * D + d8 * 8);
       }
     }
-    asm volatile("" ::: "memory");  // keeps the length load behind the batch's loads
-    const int L = p.ctx_lens[b];    // so that one round trip serves all of them
-    bad = L < 0 || L > p.max_ctx_len;
-    const int nact = min(bad || L == 0 ? 1 : (L + p.chunk - 1) / p.chunk, p.splits);
-    if (s0 >= nact) break;          // uniform: s0 and b are the same for the whole work-group
+  };
+  batch_loads(0);
+  asm volatile("" ::: "memory");  // keeps the length loads behind the batch's loads
+  const int L = p.ctx_lens[b];
+  const bool bad = L < 0 || L > p.max_ctx_len;
+  int nact;                       // partitions of this sequence that hold context
+  if (p.balanced) {
+    const int nb = __builtin_amdgcn_readfirstlane(rec.x), ex = __builtin_amdgcn_readfirstlane(rec.y);
+    // one partition: the attention kernel wrote the output itself; none: a finished sequence
+    if (nb <= 1) return;
+    const size_t real0 = (size_t)ex * p.Hkv * p.row_groups + (size_t)(g * p.row_groups + rg) * nb;
+    // never taken: the plan keeps every slot inside the workspace
+    if (real0 + nb > (size_t)p.items * p.Hkv * p.row_groups) return;
+    if (real0 != item0 || nb != n) {
+      item0 = real0;
+      n = nb;
+      batch_loads(0);
+    }
+    nact = n;
+  } else {
+    nact = min(bad || L == 0 ? 1 : (L + p.chunk - 1) / p.chunk, p.splits);
+  }
+
+  float mx = -INFINITY, wsum = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nact; s0 += kRedBatch * PG) {
+    if (s0 > 0) batch_loads(s0);
     float bmx = mx;
 #pragma unroll
     for (int sp = 0; sp < kRedBatch; ++sp)
@@ -999,7 +1235,7 @@ __global__ __launch_bounds__(256) void block_attn_f32_kernel(AttnParams p) {
 
 hipError_t launch_block_attn_bf16(const AttnParams &p, hipStream_t stream, hipEvent_t ev_begin,
                                   hipEvent_t ev_end) {
-  const int units = p.B * p.Hkv * p.splits;
+  const int units = p.balanced ? p.Hkv * p.items : p.B * p.Hkv * p.splits;
   dim3 grid((unsigned)((units + 7) / 8 * 8 * p.row_groups));
   hipError_t e = hipSuccess;
   if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess) return e;
@@ -1053,8 +1289,11 @@ static void launch_reduce_d(const AttnParams &p, hipStream_t stream) {
     const int rpb = 256 / (D / 8 * pg);
     return units * ((p.rows_per_group + rpb - 1) / rpb);
   };
-  if (p.splits <= kRedBatch && groups(1) >= 1024) launch_reduce_pg<D, 1>(p, stream);
-  else if (p.splits <= 4 * kRedBatch && groups(4) >= 1024) launch_reduce_pg<D, 4>(p, stream);
+  // partitions of a sequence (with the balanced plan: when all lengths are equal; a sequence
+  // with more takes more load batches)
+  const int parts = p.splits;
+  if (parts <= kRedBatch && groups(1) >= 1024) launch_reduce_pg<D, 1>(p, stream);
+  else if (parts <= 4 * kRedBatch && groups(4) >= 1024) launch_reduce_pg<D, 4>(p, stream);
   else launch_reduce_pg<D, 16>(p, stream);
 }
 

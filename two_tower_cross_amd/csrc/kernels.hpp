@@ -33,10 +33,20 @@ struct AttnParams {
   int rows_per_group;  // rows handled by one work-group (multiple of 32, <= 256)
   int row_groups;
   int num_pages, page_size, max_pages, max_ctx_len;
-  int chunk;   // context tokens per partition (multiple of 64)
-  int splits;  // partitions per (sequence, KV head, row group)
+  int chunk;   // context tokens per partition (multiple of 64); balanced plan: the largest
+               // partition when every sequence has max_ctx_len tokens and is active
+  int splits;  // partitions per (sequence, KV head, row group); balanced plan: the same case
   float scale;
   int out_bf16;
+  // Balanced plan (automatic partition count): partitions are sized on the device from the
+  // actual lengths so that every work-group gets a nearly equal share (see block_attn.hip).
+  int balanced;
+  int parts;      // target partitions per (KV head, row group) over the whole batch
+  int max_parts;  // bound on the partitions of one sequence
+  int items;      // work items per (KV head, row group) the grid and the workspace hold
+  const uint8_t *active;  // optional [B, S]: a sequence with no nonzero flag has no work
+  int *plan_rec;  // balanced plan with a merge: [B, 2] (partitions, partitions before) of every
+                  // sequence, written by work-group 0 of the attention kernel for the merge
 };
 
 hipError_t launch_block_attn_bf16(const AttnParams &p, hipStream_t stream, hipEvent_t ev_begin,
