@@ -425,6 +425,15 @@ def main():
         del step
         extra = workloads(dev)
 
+    if args.copy_calibration > 0 and not args.no_workloads:
+        n = args.copy_calibration << 20   # again: the calibration must be the run's last dispatch
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     line = {
         "metric": "denoise-step attn HBM GB/s (% of peak) + committed tokens/s at 32K ctx",
         "value": round(value, 1),

@@ -351,7 +351,7 @@ typedef struct {
 #define TT_APPEND_BAD_PAGE 4
 typedef struct {
   int32_t num_layers, batch, num_kv_heads, head_dim, S;
-  tt_dtype dtype;
+  int32_t dtype;                 /* tt_dtype of the caches and the new rows */
   int32_t num_pages, page_size, max_pages_per_seq;
   int32_t reserved0;
   void *const *k_pages;          /* host array [num_layers] of device pointers */

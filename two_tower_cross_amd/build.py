@@ -67,5 +67,28 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SANITIZED_LIB = os.path.join(OBJ, "libtwotower_hostsan.so")
+
+
+def build_host_sanitized() -> str:
+    """The C ABI's host code (api.cpp: argument checks, planning, workspace sizing) built with g++
+    under AddressSanitizer and UndefinedBehaviorSanitizer, the device launchers replaced by stubs
+    that report no device (csrc/host_stubs.cpp). Load it with the sanitizer runtime preloaded
+    (LD_PRELOAD of gcc's libasan) and TWOTOWER_LIB pointing to it. Returns its path."""
+    os.makedirs(OBJ, exist_ok=True)
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    tmp = SANITIZED_LIB + ".tmp"
+    _run(["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-D__HIP_PLATFORM_AMD__",
+          "-fsanitize=address,undefined", "-fno-omit-frame-pointer",
+          "-fno-sanitize-recover=undefined", f"-I{rocm}/include", f"-I{CSRC}",
+          os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "host_stubs.cpp"),
+          f"-L{rocm}/lib", "-lamdhip64", f"-Wl,-rpath,{rocm}/lib", "-o", tmp])
+    os.replace(tmp, SANITIZED_LIB)
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-sanitized" in sys.argv:
+        print(build_host_sanitized())
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -1273,8 +1273,9 @@ hipError_t launch_block_attn_f32(const AttnParams &p, hipStream_t stream, hipEve
   return e;
 }
 
-// The merge's partition groups: the fewest (1, 4 or 16) that give >= 1024 work-groups and at
-// most kRedBatch partitions per thread, else 16.
+// The merge's partition groups: one while a row has at most kRedBatch partitions (at 256 rows of
+// 16 partitions, 256 work-groups of one round trip each were faster than 1024 of 4 groups: 6.5
+// against 8.6 us); else the fewest (4 or 16) with at most kRedBatch partitions per thread.
 template <int D, int PG>
 static void launch_reduce_pg(const AttnParams &p, hipStream_t stream) {
   constexpr int rpb = 256 / (D / 8 * PG);
@@ -1292,8 +1293,8 @@ static void launch_reduce_d(const AttnParams &p, hipStream_t stream) {
   // partitions of a sequence (with the balanced plan: when all lengths are equal; a sequence
   // with more takes more load batches)
   const int parts = p.splits;
-  if (parts <= kRedBatch && groups(1) >= 1024) launch_reduce_pg<D, 1>(p, stream);
-  else if (parts <= 4 * kRedBatch && groups(4) >= 1024) launch_reduce_pg<D, 4>(p, stream);
+  if (parts <= kRedBatch) launch_reduce_pg<D, 1>(p, stream);
+  else if (parts <= 4 * kRedBatch && groups(4) >= 256) launch_reduce_pg<D, 4>(p, stream);
   else launch_reduce_pg<D, 16>(p, stream);
 }
 

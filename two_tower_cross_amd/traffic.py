@@ -7,7 +7,8 @@ Optionally the kernel trace of the same command (``--kernel-trace``; its kernel_
 the kernel_stats CSV of ``--stats``) adds each kernel's mean duration, so that counted bytes per
 second can be put next to the algorithmic rate.
 
-    python -m two_tower_cross_amd.traffic FETCH_CSV WRITE_CSV COPY_MIB OUT_MD "COMMAND" [TRACE_CSV]
+    python -m two_tower_cross_amd.traffic [--by-grid] FETCH_CSV WRITE_CSV COPY_MIB OUT_MD "COMMAND" [TRACE_CSV]
+    python -m two_tower_cross_amd.traffic --sq SQ_CSV_1 SQ_CSV_2 TRACE_CSV OUT_MD "COMMAND"
 
 writes a short summary (a table plus one JSON line) that ``bench.py`` reads back. Kernels are keyed
 by name and grid size (the two projections of a layer are the same kernel on different grids);
@@ -70,8 +71,11 @@ def source_hash(path):
 
 
 def short_name(kernel):
-    """`tt::block_attn_bf16_kernel<128>(tt::AttnParams)` -> `block_attn_bf16_kernel<128>`."""
-    k = kernel.replace("tt::", "").replace(" ", "")
+    """`void tt::block_attn_bf16_kernel<128>(tt::AttnParams)` -> `block_attn_bf16_kernel<128>`."""
+    k = kernel.strip()
+    if k.startswith("void "):
+        k = k[5:]
+    k = k.replace("tt::", "").replace(" ", "")
     depth, out = 0, []
     for ch in k:
         if ch == "(" and depth == 0:
@@ -125,8 +129,13 @@ def _durations(trace_csv):
     return {k: statistics.mean(v) for k, v in durs.items()}
 
 
+BY_GRID = False   # key every kernel by name and grid (several workloads in one run)
+
+
 def _key(name, grid, grids):
     """Kernel key: the name, with the projection's role when one name runs on several grids."""
+    if BY_GRID:
+        return f"{name}@{grid}" if len(grids[name]) > 1 else name
     if name in ("linear_kernel<2>", "linear_reduce_kernel") and len(grids[name]) == 2:
         # at this workload the QKV product runs on the smaller grid (72 feature tiles x 3 K
         # partitions against 32 x 8) and its reduce on the larger one (4608 against 2048 features)
@@ -201,12 +210,102 @@ def bytes_per_launch(summary_md, kernels):
     return None
 
 
+# SQ counters: units as read on gfx950 (each checked against a known quantity): SQ_BUSY_CYCLES
+# sums the shader clock over the 32 shader engines (8 XCDs x 4), so /32 gives the kernel's cycles;
+# SQ_VALU_MFMA_BUSY_CYCLES and SQ_VALU_MFMA_COEXEC_CYCLES sum cycles over the 1024 SIMDs (busy =
+# MFMA instructions x 32 cycles for 32x32x16 bf16); SQ_WAVE_CYCLES, SQ_ACTIVE_INST_* and SQ_WAIT_*
+# are in 4-cycle units summed over waves.
+N_SE, N_SIMD, MFMA_FLOPS, PEAK_TFLOPS = 32, 1024, 32 * 32 * 16 * 2, 2500.0
+
+
+def sq_summary(csvs, trace_csv):
+    vals = {}
+    for path in csvs:
+        per = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = short_name(r["Kernel_Name"])
+                if source_of(name) is None:
+                    continue
+                d = (name, _grid(r), int(r["Dispatch_Id"]))
+                c = per.setdefault(d, {})
+                c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        grids = {}
+        for name, grid, _ in per:
+            grids.setdefault(name, set()).add(grid)
+        for (name, grid, _), c in per.items():
+            e = vals.setdefault(_key(name, grid, grids), {})
+            for k, v in c.items():
+                e.setdefault(k, []).append(v)
+    dur = _durations(trace_csv)
+    out = {}
+    for k, cs in vals.items():
+        m = {c: statistics.mean(v) for c, v in cs.items()}
+        e = {"counters": {c: round(v) for c, v in m.items()}}
+        us = dur.get(k, dur.get(k.split("@")[0]))
+        cyc = m.get("SQ_BUSY_CYCLES", 0) / N_SE
+        if us:
+            e["mean_us"] = round(us, 2)
+            if cyc:
+                e["clock_GHz"] = round(cyc / us / 1e3, 3)
+            if m.get("SQ_INSTS_MFMA"):
+                tf = m["SQ_INSTS_MFMA"] * MFMA_FLOPS / us / 1e6
+                e["mfma_TFLOPs"] = round(tf, 1)
+                e["mfma_frac_of_peak"] = round(tf / PEAK_TFLOPS, 4)
+        if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            e["mfma_busy_frac"] = round(m["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMD / cyc, 4)
+        valu = m.get("SQ_ACTIVE_INST_VALU", 0) * 4 / N_SIMD
+        if valu and "SQ_VALU_MFMA_COEXEC_CYCLES" in m:
+            e["valu_cycles_per_simd"] = round(valu)
+            e["valu_coexec_frac"] = round(m["SQ_VALU_MFMA_COEXEC_CYCLES"] / N_SIMD / valu, 4)
+        if m.get("SQ_WAVE_CYCLES"):
+            e["wait_frac"] = round(m.get("SQ_WAIT_ANY", 0) / m["SQ_WAVE_CYCLES"], 4)
+            e["issue_blocked_frac"] = round(m.get("SQ_WAIT_INST_ANY", 0) / m["SQ_WAVE_CYCLES"], 4)
+        out[k] = e
+    return out
+
+
+def main_sq(argv):
+    sq1, sq2, trace_csv, out_md, command = argv[:5]
+    s = sq_summary([sq1, sq2], trace_csv)
+    with open(out_md, "w") as f:
+        f.write("# SQ counters of the denoise-step kernels, 32K-context block loop\n\n")
+        f.write("Two counter passes (8 SQ counters each) and a kernel trace for durations, of\n\n")
+        f.write(f"    {command}\n\n")
+        f.write("Units: SQ_BUSY_CYCLES / 32 shader engines = the kernel's cycles (so clock = that "
+                "/ mean duration); SQ_VALU_MFMA_BUSY / COEXEC cycles summed over 1024 SIMDs; "
+                "SQ_WAVE_CYCLES, SQ_ACTIVE_INST_* and SQ_WAIT_* in 4-cycle units summed over "
+                "waves. MFMA TFLOP/s = SQ_INSTS_MFMA x 32768 flops (32x32x16 bf16) / mean "
+                "duration, against 2.5 PFLOP/s dense bf16.\n\n")
+        f.write("| kernel | mean us | clock GHz | MFMA busy | MFMA TFLOP/s (% peak) | VALU cycles / SIMD "
+                "| VALU co-exec with MFMA | waves waiting | issue-blocked |\n")
+        f.write("|---|---:|---:|---:|---:|---:|---:|---:|---:|\n")
+        pct = lambda x: "-" if x is None else f"{100 * x:.1f}%"
+        for k, e in sorted(s.items(), key=lambda kv: -kv[1].get("mean_us", 0)):
+            tf = (f"{e['mfma_TFLOPs']} ({100 * e['mfma_frac_of_peak']:.1f}%)"
+                  if "mfma_TFLOPs" in e else "-")
+            f.write(f"| `{k}` | {e.get('mean_us', '-')} | {e.get('clock_GHz', '-')} | "
+                    f"{pct(e.get('mfma_busy_frac')) if e.get('counters', {}).get('SQ_INSTS_MFMA') else '-'} | {tf} | "
+                    f"{e.get('valu_cycles_per_simd', '-')} | "
+                    f"{pct(e.get('valu_coexec_frac')) if e.get('counters', {}).get('SQ_INSTS_MFMA') else '-'} | "
+                    f"{pct(e.get('wait_frac'))} | {pct(e.get('issue_blocked_frac'))} |\n")
+        f.write("\nMachine-readable:\n\n" + json.dumps(s) + "\n")
+
+
 def main(argv):
+    global BY_GRID
+    if len(argv) > 1 and argv[1] == "--sq":
+        return main_sq(argv[2:])
+    if "--by-grid" in argv:
+        BY_GRID = True
+        argv = [a for a in argv if a != "--by-grid"]
     fetch_csv, write_csv, copy_mib, out_md, command = argv[1:6]
     stats_csv = argv[6] if len(argv) > 6 else None
     s = summarize(fetch_csv, write_csv, int(copy_mib), stats_csv)
+    title = ("the attention and unmasking workloads (kernels keyed by name and grid size in "
+             "work-items)" if BY_GRID else "the denoise-step kernels, 32K-context block loop")
     with open(out_md, "w") as f:
-        f.write("# HBM traffic of the denoise-step kernels, 32K-context block loop\n\n")
+        f.write(f"# HBM traffic of {title}\n\n")
         f.write("Counters: rocprofv3 `--pmc FETCH_SIZE` and `--pmc WRITE_SIZE`, one run each"
                 + (", and a `--kernel-trace --stats` run for durations" if stats_csv else "")
                 + ", of\n\n")
