@@ -415,6 +415,32 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # one denoise step with every sequence live, then with half of them finished (no masked
+    # position left): a finished sequence gets no attention work, the live ones spread over the GPU
+    half = None
+    if not args.no_workloads:
+        timer = Timer(torch, dev)
+        hm = torch.ones((m.B, m.S), dtype=torch.uint8, device=dev)
+        ht = torch.full((m.B, m.S), -1, dtype=torch.int32, device=dev)
+
+        def step_with(n_finished):
+            def reset():
+                hm.fill_(1)
+                hm[:n_finished] = 0
+                ht.fill_(-1)
+
+            def call(evs):
+                if evs is not None:
+                    evs[0].record()
+                step(m.h_steps[0], hm, ht, threshold=THRESHOLD, min_commit=True)
+                if evs is not None:
+                    evs[1].record()
+            (us,) = timer.run(call, calls=20, n_events=2, reset=reset)
+            return stats_us(us)
+        half = {"workload": "one denoise step of the block loop (6 layers, lm-head, unmask)",
+                "all_live_us": step_with(0), f"{m.B // 2}_of_{m.B}_finished_us": step_with(m.B // 2)}
+        del timer
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(m)
@@ -424,6 +450,7 @@ def main():
     if not args.no_workloads:
         del step
         extra = workloads(dev)
+        extra["step_half_finished"] = half
 
     if args.copy_calibration > 0 and not args.no_workloads:
         n = args.copy_calibration << 20   # again: the calibration must be the run's last dispatch

@@ -1117,7 +1117,8 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnParams p) {
   if (p.lse && d8 == 0) p.lse[((size_t)b * p.Hq + h) * p.S + iq] = bad ? NAN : mx + logf(wsum);
 }
 
-// fp32 path: one work-group per (position i, query head h, sequence b); keys in tiles of 256.
+// fp32 path: one work-group per (position i, query head h, sequence b); keys in tiles of 256,
+// each tile's values staged in LDS.
 __device__ __forceinline__ float block_max_256(float x, float *red) {
   x = wave_max(x);
   const int w = threadIdx.x >> 6;
@@ -1138,9 +1139,14 @@ __device__ __forceinline__ float block_sum_256(float x, float *red) {
 
 template <int D>
 __global__ __launch_bounds__(256) void block_attn_f32_kernel(AttnParams p) {
+  // LDS: the query, the tile's 256 weights, the reduction words, then the tile's values staged
+  // token-major [256][D] (dynamic), so that the weighted sum reads LDS instead of 256 rounds of
+  // scattered global loads.
   __shared__ float qs[D];
   __shared__ float pw[256];
   __shared__ float red[4];
+  __shared__ int vpage[256];  // page of each context key of the tile
+  extern __shared__ float vs[];
   const int iq = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int g = h / p.G;
   const float *q = static_cast<const float *>(p.q) + (((size_t)b * p.S + iq) * p.Hq + h) * D;
@@ -1157,8 +1163,11 @@ __global__ __launch_bounds__(256) void block_attn_f32_kernel(AttnParams p) {
   float m = -INFINITY, l = 0.f, o = 0.f;
   __syncthreads();
   for (int base = 0; base < N; base += 256) {
+    const int nt = min(256, N - base);
+    // this thread's key: score
     const int j = base + tid;
     float s = -INFINITY;
+    vpage[tid] = -1;
     if (j < N) {
       const float *key;
       if (j < p.S) {
@@ -1166,6 +1175,7 @@ __global__ __launch_bounds__(256) void block_attn_f32_kernel(AttnParams p) {
       } else {
         const int t = j - p.S;
         const int page = btab[t / p.page_size];
+        vpage[tid] = page;
         if (page < 0 || page >= p.num_pages) {
           key = nullptr;
         } else {
@@ -1188,6 +1198,22 @@ __global__ __launch_bounds__(256) void block_attn_f32_kernel(AttnParams p) {
         s = NAN;
       }
     }
+    // the tile's values into LDS, token-major, one independent load per element (a page id
+    // outside the pool reads nothing: 0)
+    __syncthreads();
+#pragma unroll 8
+    for (int e = tid; e < nt * D; e += 256) {
+      const int jl = e / D, d = e % D, jj = base + jl;
+      float v = 0.f;
+      if (jj < p.S) {
+        v = vb[(size_t)d * p.S + jj];
+      } else {
+        const int page = vpage[jl];
+        if (page >= 0 && page < p.num_pages)
+          v = vp[((size_t)page * p.Hkv + g) * p.page_size * D + v_elem((jj - p.S) % p.page_size, d, D)];
+      }
+      vs[e] = v;
+    }
     const bool nan_here = s != s;
     if (__syncthreads_or(nan_here)) bad = true;
     if (nan_here) s = -INFINITY;
@@ -1200,22 +1226,7 @@ __global__ __launch_bounds__(256) void block_attn_f32_kernel(AttnParams p) {
     l = l * alpha + psum;
     if (tid < D) {
       float acc = 0.f;
-      const int nt = min(256, N - base);
-      for (int t = 0; t < nt; ++t) {
-        const int jj = base + t;
-        float v;
-        if (jj < p.S) {
-          v = vb[(size_t)tid * p.S + jj];
-        } else {
-          const int tt = jj - p.S;
-          const int page = btab[tt / p.page_size];
-          const int off = tt % p.page_size;
-          v = (page >= 0 && page < p.num_pages)
-                  ? vp[((size_t)page * p.Hkv + g) * p.page_size * D + v_elem(off, tid, D)]
-                  : 0.f;
-        }
-        acc = fmaf(pw[t], v, acc);
-      }
+      for (int t = 0; t < nt; ++t) acc = fmaf(pw[t], vs[t * D + tid], acc);
       o = o * alpha + acc;
     }
     m = mnew;
@@ -1264,10 +1275,21 @@ hipError_t launch_block_attn_f32(const AttnParams &p, hipStream_t stream, hipEve
   dim3 grid(p.S, p.Hq, p.B);
   hipError_t e = hipSuccess;
   if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess) return e;
-  if (p.D == 128)
-    hipLaunchKernelGGL(block_attn_f32_kernel<128>, grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(block_attn_f32_kernel<64>, grid, dim3(256), 0, stream, p);
+  if (p.D == 128) {
+    constexpr int lds = 256 * 128 * 4;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&block_attn_f32_kernel<128>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(block_attn_f32_kernel<128>, grid, dim3(256), lds, stream, p);
+  } else {
+    constexpr int lds = 256 * 64 * 4;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&block_attn_f32_kernel<64>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(block_attn_f32_kernel<64>, grid, dim3(256), lds, stream, p);
+  }
   e = hipGetLastError();
   if (e == hipSuccess && ev_end) e = hipEventRecord(ev_end, stream);
   return e;
