@@ -9,6 +9,7 @@ second can be put next to the algorithmic rate.
 
     python -m two_tower_cross_amd.traffic [--by-grid] FETCH_CSV WRITE_CSV COPY_MIB OUT_MD "COMMAND" [TRACE_CSV]
     python -m two_tower_cross_amd.traffic --sq SQ_CSV_1 SQ_CSV_2 TRACE_CSV OUT_MD "COMMAND"
+    python -m two_tower_cross_amd.traffic --stats STATS_CSV OUT_MD "TITLE" "COMMAND"
 
 writes a short summary (a table plus one JSON line) that ``bench.py`` reads back. Kernels are keyed
 by name and grid size (the two projections of a layer are the same kernel on different grids);
@@ -55,6 +56,22 @@ ALGORITHMIC_LOOP32K = {
     "lm_unmask_kernel": _V * _H * 2 + _M * _H * 2,
     "unmask_tiles_finalize_kernel": 0,
 }
+
+
+def _algorithmic(key):
+    """Algorithmic bytes of a kernel key (the merge is one entry whatever its partition groups)."""
+    if key.startswith("attn_reduce_kernel<128,"):
+        key = "attn_reduce_kernel<128>"
+    return ALGORITHMIC_LOOP32K.get(key)
+
+
+def _lookup(kernels, name):
+    """The entry of `name`, or of the one key that starts with it followed by ',' (template
+    arguments beyond the first)."""
+    if name in kernels:
+        return kernels[name]
+    hits = [v for k, v in kernels.items() if k.startswith(name.rstrip(">") + ",")]
+    return hits[0] if len(hits) == 1 else None
 
 
 def source_of(kernel):
@@ -172,7 +189,7 @@ def summarize(fetch_csv, write_csv, copy_mib, stats_csv=None):
         hashes[src] = source_hash(os.path.join(CSRC, src))
         e["source"] = src
         e["traffic_bytes"] = e.get("FETCH_SIZE", 0) + e.get("WRITE_SIZE", 0)
-        alg = ALGORITHMIC_LOOP32K.get(k)
+        alg = _algorithmic(k)
         if alg is not None:
             e["algorithmic_bytes"] = alg
             if alg:
@@ -199,7 +216,7 @@ def bytes_per_launch(summary_md, kernels):
                 s = json.loads(line)
                 total = 0
                 for k in kernels:
-                    e = s["kernels"].get(k)
+                    e = _lookup(s["kernels"], k)
                     if e is None:
                         return None
                     src = e["source"]
@@ -292,10 +309,30 @@ def main_sq(argv):
         f.write("\nMachine-readable:\n\n" + json.dumps(s) + "\n")
 
 
+def main_stats(argv):
+    """Kernel-time table from a rocprofv3 kernel_stats CSV (the library's kernels and the rest)."""
+    stats_csv, out_md, title, command = argv[:4]
+    with open(stats_csv) as f:
+        rows = list(csv.DictReader(f))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    with open(out_md, "w") as f:
+        f.write(f"# Kernel time, {title}\n\nCommand (MI355X, one GPU):\n\n    {command}\n\n")
+        f.write("| kernel | calls | avg us | min us | max us | % of GPU time |\n")
+        f.write("|---|---:|---:|---:|---:|---:|\n")
+        for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+            name = short_name(r["Name"])
+            name = name if len(name) <= 60 else name[:57] + "..."
+            f.write(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                    f"{100 * float(r['TotalDurationNs']) / total:.2f} |\n")
+
+
 def main(argv):
     global BY_GRID
     if len(argv) > 1 and argv[1] == "--sq":
         return main_sq(argv[2:])
+    if len(argv) > 1 and argv[1] == "--stats":
+        return main_stats(argv[2:])
     if "--by-grid" in argv:
         BY_GRID = True
         argv = [a for a in argv if a != "--by-grid"]
