@@ -12,8 +12,12 @@ synthetic (seeded on-device draws) and resident in HBM before timing starts.
 Prints one JSON line. ``value`` is committed tokens/s over the timed blocks. ``roofline`` reports
 the block-attention call of the loop (main kernel + partition merge, the dominant work of a step)
 as algorithmic HBM bytes per call (context K+V, block K+V, Q read, O write) over the call's mean
-duration, from HIP events that the library records around both kernels of every call inside the
-timed region; ``roofline.kernel_only`` gives the main kernel alone. ``workloads`` holds the other
+duration, from HIP events that the library records on its launch stream in a second timed pass
+of the same K blocks (the headline pass carries no per-call events): every other denoise step
+brackets one layer's call (before the kernel, after the merge), the others one layer's main
+kernel alone (``roofline.kernel_only``), the layers rotating over the steps.
+The events are created with hipEventDisableSystemFence: a default event's record writes back and
+invalidates the caches, which costs about 5 us of idle GPU per record and slows the next kernel. ``workloads`` holds the other
 shapes (tiny fp32; 4K context with the 16 x 131072 unmasking; a ragged paged batch of 32; a 131072-
 token context at 64/128/256/auto partitions), each timed over 50 calls with a 1 GiB write between
 calls (outside the timed events) so that no input is served from the 256 MB last-level cache, as
@@ -54,6 +58,69 @@ def attn_bytes(ctx_lens, S, Hq, Hkv, D, e=2):
 def attn_flops(ctx_lens, S, Hq, D):
     """QK^T and PV over every (context + block) key of every query row: 4 flops per row, key, dim."""
     return sum(4 * Hq * S * (int(L) + S) * D for L in ctx_lens)
+
+
+class TimingEvent:
+    """A hipEvent_t for timing only, created with hipEventDisableSystemFence: recording it does
+    not write back and invalidate the caches (the default event's system-scope fence costs about
+    5 us of idle GPU time per record and leaves the next kernel with cold caches). Same interface
+    as the parts of torch.cuda.Event used here; the handle lives in the HIP runtime torch loaded."""
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+    _hip = None
+
+    @classmethod
+    def hip(cls):
+        if cls._hip is None:
+            import ctypes
+            path = None
+            with open("/proc/self/maps") as f:
+                for line in f:
+                    if "libamdhip64" in line:
+                        path = line.split()[-1]
+                        break
+            if path is None:
+                raise RuntimeError("the HIP runtime is not loaded")
+            h = ctypes.CDLL(path)
+            vp = ctypes.c_void_p
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [vp, vp]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+            h.hipEventDestroy.argtypes = [vp]
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self.cuda_event = None
+        h = ctypes.c_void_p()
+        rc = self.hip().hipEventCreateWithFlags(ctypes.byref(h), self.FLAGS)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.cuda_event = h.value
+
+    def record(self):
+        import torch
+        rc = self.hip().hipEventRecord(self.cuda_event, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, other):
+        """Milliseconds from this event to ``other`` (both recorded and complete)."""
+        import ctypes
+        ms = ctypes.c_float()
+        rc = self.hip().hipEventElapsedTime(ctypes.byref(ms), self.cuda_event, other.cuda_event)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.cuda_event:
+            self._hip.hipEventDestroy(self.cuda_event)
+
+
+def make_event(fenced=False):
+    import torch
+    return torch.cuda.Event(enable_timing=True) if fenced else TimingEvent()
 
 
 def stats_us(xs):
@@ -126,12 +193,13 @@ def measured_traffic(kernels):
 class Timer:
     """Timed calls of a workload, each preceded by a 1 GiB write (outside the events)."""
 
-    def __init__(self, torch, dev):
+    def __init__(self, torch, dev, fenced=False):
         self.torch = torch
+        self.fenced = fenced
         self.scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device=dev)
 
     def events(self, n):
-        evs = [self.torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        evs = [make_event(self.fenced) for _ in range(n)]
         for e in evs:
             e.record()          # materialize the underlying hipEvent_t
         return evs
@@ -265,11 +333,11 @@ def stream_ceiling(timer, dev):
             "workgroups": best[1], "bytes": nbytes}
 
 
-def workloads(dev):
+def workloads(dev, fenced=False):
     import synth
     import torch
 
-    timer = Timer(torch, dev)
+    timer = Timer(torch, dev, fenced)
     out = {}
     out["stream_read_ceiling"] = stream_ceiling(timer, dev)
     print("bench: stream ceiling done", file=sys.stderr, flush=True)
@@ -307,6 +375,9 @@ def main():
                     help="skip the tiny / 4K / ragged / 128K workloads after the block loop")
     ap.add_argument("--no-events", action="store_true",
                     help="do not record per-call attention events")
+    ap.add_argument("--fenced-events", action="store_true",
+                    help="time with default HIP events (a system-scope cache write-back and "
+                         "invalidate at every record) instead of fence-free timing events")
     ap.add_argument("--block-size", type=int, default=16, metavar="S",
                     help="block size S (16 is the benchmark's workload; the pages also use 32 and "
                          "128)")
@@ -335,56 +406,89 @@ def main():
     # timing, so that counting adds no work to the timed region)
     counts = torch.zeros((args.steps, m.T, m.B), dtype=torch.int32, device=dev)
 
-    def make_events(n):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-        for e in evs:
-            e.record()          # materialize the underlying hipEvent_t
-        return evs
+    L = m.layers
 
-    ev_per_step = 3 * m.layers
+    def step_events(s):
+        """Events of timed denoise step s. Even steps bracket one layer's attention call (main
+        kernel + merge), odd steps one layer's main kernel alone, the layers rotating; so each
+        sampled call carries two events and a step records two (every record still costs about
+        2 us of idle GPU, so the timing is spread thin over the timed region)."""
+        ev = [None] * (3 * L)
+        e0, e1 = make_event(args.fenced_events), make_event(args.fenced_events)
+        layer = (s // 2) % L
+        if s % 2 == 0:
+            ev[3 * layer], ev[3 * layer + 2] = e0.cuda_event, e1.cuda_event
+        else:
+            layer = (layer + L // 2) % L
+            ev[3 * layer], ev[3 * layer + 1] = e0.cuda_event, e1.cuda_event
+        return ev, s % 2, (e0, e1)
 
     def run_block(events=None, k=None):
         masked.fill_(1)
         tokens.fill_(-1)
         for t in range(m.T):
-            ev = None
-            if events is not None:
-                base = t * ev_per_step
-                ev = [events[base + i].cuda_event for i in range(ev_per_step)]
             step(m.h_steps[t], masked, tokens, threshold=THRESHOLD, min_commit=True,
-                 commit_all=(t == m.T - 1), timing_events=ev,
+                 commit_all=(t == m.T - 1), timing_events=None if events is None else events[t][0],
                  n_committed=None if k is None else counts[k, t])
 
     for _ in range(args.warmup):
         run_block()
     torch.cuda.synchronize()
 
-    per_block = ev_per_step * m.T
-    events = None if args.no_events else make_events(per_block * args.steps)
-    torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for k in range(args.steps):
-        run_block(None if events is None else events[k * per_block:(k + 1) * per_block], k)
-    stop.record()
-    torch.cuda.synchronize()
-    ms_total = start.elapsed_time(stop)
-    n_tokens = int(counts.sum().item())
-    assert not masked.any().item(), "a block ended with masked positions"
+    def timed_pass(events=None):
+        """K timed blocks (bracketed by synchronize); returns (ms total, committed tokens, ms per
+        block, host enqueue ms)."""
+        counts.zero_()
+        marks = [make_event() for _ in range(args.steps + 1)]   # block boundaries (fence-free)
+        for e in marks:
+            e.record()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_host = time.perf_counter()
+        start.record()
+        marks[0].record()
+        for k in range(args.steps):
+            run_block(None if events is None else events[k * m.T:(k + 1) * m.T], k)
+            marks[k + 1].record()
+        stop.record()
+        enqueue_ms = (time.perf_counter() - t_host) * 1e3
+        torch.cuda.synchronize()
+        total = start.elapsed_time(stop)
+        per_block = [round(marks[k].elapsed_time(marks[k + 1]), 3) for k in range(args.steps)]
+        n = int(counts.sum().item())
+        assert not masked.any().item(), "a block ended with masked positions"
+        return total, n, per_block, enqueue_ms
+
+    # The headline pass carries no per-call events (a record on the launch stream between two
+    # kernels costs idle GPU time and, now and then, a long host-side stall in the runtime).
+    ms_total, n_tokens, block_ms, host_enqueue_ms = timed_pass()
     ms_per_block = ms_total / args.steps
     value = n_tokens / (ms_total / 1e3)
     print(f"bench: block loop timed, {value:.1f} committed tokens/s", file=sys.stderr, flush=True)
 
+    # The attention roofline comes from a second timed pass of the same K blocks, with the
+    # library recording the sampled events on its launch stream.
+    events = None
+    ev_pass = None
+    if not args.no_events:
+        events = [step_events(s) for s in range(args.steps * m.T)]
+        for _, _, pair in events:
+            for e in pair:
+                e.record()      # materialize
+        torch.cuda.synchronize()
+        ev_total, ev_tokens, ev_blocks, ev_enqueue = timed_pass(events)
+        ev_pass = {"value": round(ev_tokens / (ev_total / 1e3), 1),
+                   "ms_per_timed_block": ev_blocks, "host_enqueue_ms": round(ev_enqueue, 2)}
+
     roofline = None
     if events is not None:
-        n_calls = len(events) // 3
-        kern = [1e3 * events[3 * i].elapsed_time(events[3 * i + 1]) for i in range(n_calls)]
-        whole = [1e3 * events[3 * i].elapsed_time(events[3 * i + 2]) for i in range(n_calls)]
+        whole = [1e3 * a.elapsed_time(b) for _, kind, (a, b) in events if kind == 0]
+        kern = [1e3 * a.elapsed_time(b) for _, kind, (a, b) in events if kind == 1]
+        n_calls = len(whole)
         lens = [m.L] * m.B
         nbytes = attn_bytes(lens, m.S, m.Hq, m.Hkv, m.D)
         flops = attn_flops(lens, m.S, m.Hq, m.D)
-        call_us, kern_us = sum(whole) / n_calls, sum(kern) / n_calls
+        call_us, kern_us = sum(whole) / len(whole), sum(kern) / len(kern)
         kernels = ["block_attn_bf16_kernel<128>", "attn_reduce_kernel<128>"]
         if flops / nbytes <= MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
             achieved = nbytes / call_us / 1e3
@@ -393,6 +497,12 @@ def main():
                         "traffic": measured_traffic(kernels) if m.S == 16 else None,
                         "kernel": " + ".join(kernels), "call_us": round(call_us, 2),
                         "call_us_median_min": stats_us(whole), "bytes_per_call": nbytes,
+                        "timed_calls": n_calls, "timing_pass": ev_pass,
+                        "timing": "a second timed pass of the same blocks: every other denoise "
+                        "step brackets one attention call, the others one main kernel "
+                        "(layers rotating), "
+                        + ("default" if args.fenced_events else "fence-free") + " HIP events "
+                        "recorded by the library on its launch stream",
                         "kernel_only": {"kernel": kernels[0], "launch_us": round(kern_us, 2),
                                         "launch_us_median_min": stats_us(kern),
                                         "achieved": round(nbytes / kern_us / 1e3, 1),
@@ -419,7 +529,7 @@ def main():
     # position left): a finished sequence gets no attention work, the live ones spread over the GPU
     half = None
     if not args.no_workloads:
-        timer = Timer(torch, dev)
+        timer = Timer(torch, dev, args.fenced_events)
         hm = torch.ones((m.B, m.S), dtype=torch.uint8, device=dev)
         ht = torch.full((m.B, m.S), -1, dtype=torch.int32, device=dev)
 
@@ -449,7 +559,7 @@ def main():
     extra = None
     if not args.no_workloads:
         del step
-        extra = workloads(dev)
+        extra = workloads(dev, args.fenced_events)
         extra["step_half_finished"] = half
 
     if args.copy_calibration > 0 and not args.no_workloads:
@@ -469,6 +579,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_block, 4),
+        "ms_per_timed_block": block_ms,
+        "host_enqueue_ms": round(host_enqueue_ms, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -111,7 +111,9 @@ typedef enum { TT_FP32 = 0, TT_BF16 = 1 } tt_dtype;
  * timing_events: optional host array of 3 hipEvent_t (NULL in normal use): events[0] and
  * events[1] are recorded on `stream` immediately before and after the main attention kernel,
  * events[2] after the partition merge (equal in time to events[1] when there is one partition).
- * A profiling hook; the events must have been created by the caller.
+ * A NULL entry is not recorded. A profiling hook; the events must have been created by the
+ * caller, preferably with hipEventDisableSystemFence (a default event's record writes back and
+ * invalidates the caches between the kernels it separates, which lengthens the timed interval).
  */
 typedef struct {
   int32_t batch, S, num_q_heads, num_kv_heads, head_dim;
@@ -296,7 +298,8 @@ typedef struct {
  *
  * timing_events: optional host array of 3*num_layers hipEvent_t; if not NULL, events[3l] and
  * events[3l+1] are recorded on `stream` immediately before and after the main attention kernel
- * of layer l and events[3l+2] after its partition merge (profiling hook, NULL in normal use).
+ * of layer l and events[3l+2] after its partition merge; NULL entries are skipped (profiling
+ * hook, NULL in normal use; see tt_block_attn_args for the event flags).
  */
 typedef struct {
   int32_t num_layers, hidden, vocab;

@@ -27,14 +27,15 @@ def dev_case(case):
 
 
 def gpu_attn(case, d=None, *, out_dtype=torch.float32, num_splits=0, max_ctx_len=None,
-             return_lse=True, **over):
+             return_lse=True, timing_events=None, **over):
     d = dict(dev_case(case) if d is None else d)
     d.update(over)
     if max_ctx_len is None:
         max_ctx_len = int(case.ctx_lens.max()) if case.B else 0
     r = tt.block_attn(d["q"], d["k_pages"], d["v_pages"], d["block_table"], d["ctx_lens"],
                       d["k_blk"], d["v_blk"], scale=case.scale, max_ctx_len=max_ctx_len,
-                      out_dtype=out_dtype, return_lse=return_lse, num_splits=num_splits)
+                      out_dtype=out_dtype, return_lse=return_lse, num_splits=num_splits,
+                      timing_events=timing_events)
     torch.cuda.synchronize()
     if return_lse:
         out, lse = r

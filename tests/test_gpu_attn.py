@@ -305,3 +305,22 @@ def test_deterministic_and_outputs_stay_in_bounds():
         assert (guard[0, :32] == 7.0).all() and (guard[0, -32:] == 7.0).all()
         assert (guard[1] == 7.0).all()
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+
+
+def test_timing_event_hook_skips_null_entries():
+    """The profiling hook records the events it is given around the main kernel and after the
+    merge; a None entry is skipped, and the output is the same as without events."""
+    case = synth.attn_case(81, B=2, S=16, Hq=32, Hkv=2, D=128, ctx_lens=[4096, 3000],
+                           page_size=256, dtype="bf16")
+    ref_out, _ = gpu_attn(case, num_splits=8)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in evs:
+        e.record()          # materialize the handles
+    torch.cuda.synchronize()
+    out_a, _ = gpu_attn(case, num_splits=8,
+                        timing_events=[evs[0].cuda_event, None, evs[1].cuda_event])
+    out_b, _ = gpu_attn(case, num_splits=8,
+                        timing_events=[evs[2].cuda_event, evs[3].cuda_event, None])
+    torch.cuda.synchronize()
+    assert evs[0].elapsed_time(evs[1]) > 0.0 and evs[2].elapsed_time(evs[3]) > 0.0
+    assert np.array_equal(out_a, ref_out) and np.array_equal(out_b, ref_out)

@@ -120,8 +120,9 @@ def block_attn(q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, *, scal
 
     ``max_ctx_len`` bounds ctx_lens (used to plan the context partitions; default: the page
     table's capacity). ``num_splits`` 0 lets the library choose the partition count.
-    ``timing_events``: optional 3 hipEvent_t handles (``torch.cuda.Event(...).cuda_event``),
-    recorded before and after the main kernel and after the partition merge.
+    ``timing_events``: optional 3 hipEvent_t handles (``torch.cuda.Event(...).cuda_event``, or
+    events created with hipEventDisableSystemFence), recorded before and after the main kernel and
+    after the partition merge; a None entry is not recorded.
     ``no_alloc``: call twotower_block_attn_static (no workspace; the library's per-device scratch);
     nothing is allocated here either, so ``out`` (and ``lse_out`` with ``return_lse``) must be
     given.
@@ -508,7 +509,8 @@ class DenoiseStep:
         """Enqueue one step; updates masked/tokens in place, fills confidence and the per-sequence
         commit counts (into `n_committed`, an int32 [batch] device tensor, when given, else into
         self.n_committed, which is returned). ``timing_events``: optional 3 * layers hipEvent_t
-        handles, recorded around each layer's attention kernel and after its merge."""
+        handles (None entries skipped), recorded around each layer's attention kernel and after
+        its merge."""
         a = self.args
         a.h_in = _p(h_in)
         a.unmask.masked, a.unmask.tokens = _p(masked), _p(tokens)
