@@ -22,7 +22,9 @@ shapes (tiny fp32; 4K context with the 16 x 131072 unmasking; a ragged paged bat
 token context at 64/128/256/auto partitions), each timed over 50 calls with a 1 GiB write between
 calls (outside the timed events) so that no input is served from the 256 MB last-level cache, as
 median and minimum, with the fp64 CPU oracle's time and its max-abs deviation on the same inputs.
-``stream_read_ceiling_GBps`` is a plain streaming read of 2 GiB measured in the same run.
+``stream_read_ceiling`` is a plain streaming read of 2 GiB measured in the same run, and
+``mfma_ceiling`` the issue rate of 32x32x16 bf16 MFMA chains at 2 and 4 waves per SIMD, with and
+without an LDS operand read per MFMA (both probes are part of the library).
 ``cpu_baseline`` times the oracle on a bounded sample of the headline workload.
 """
 from __future__ import annotations
@@ -333,6 +335,34 @@ def stream_ceiling(timer, dev):
             "workgroups": best[1], "bytes": nbytes}
 
 
+def mfma_ceiling(timer, dev):
+    """Issue rate of 32x32x16 bf16 MFMA chains (twotower_probe_mfma_rate) with the GPU filled at 2
+    and at 4 waves per SIMD, with and without a 1 KB LDS operand read per MFMA."""
+    import torch
+    import two_tower_cross_amd as tt
+
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(2 * cus * 512, dtype=torch.float32, device=dev)
+    iters = 2048
+    out = {"compute_units": cus, "iters": iters}
+    for name, mode in (("2_waves_per_simd", 0), ("4_waves_per_simd", 2),
+                       ("2_waves_per_simd_lds_operand", 1), ("4_waves_per_simd_lds_operand", 3)):
+        wg = cus * (2 if mode & 2 else 1)
+        flops = wg * 8 * iters * 16 * 32768
+
+        def call(evs, mode=mode, wg=wg):
+            if evs is not None:
+                evs[0].record()
+            tt.probe_mfma_rate(mode, wg, iters, sink)
+            if evs is not None:
+                evs[1].record()
+        (us,) = timer.run(call, calls=5, n_events=2)
+        tf = flops / statistics.median(us) / 1e6
+        out[name] = {"TFLOPs": round(tf, 1), "frac_of_dense_peak": round(tf / MFMA_PEAK_TFLOPS, 4),
+                     "us": round(statistics.median(us), 2)}
+    return out
+
+
 def workloads(dev, fenced=False):
     import synth
     import torch
@@ -340,7 +370,8 @@ def workloads(dev, fenced=False):
     timer = Timer(torch, dev, fenced)
     out = {}
     out["stream_read_ceiling"] = stream_ceiling(timer, dev)
-    print("bench: stream ceiling done", file=sys.stderr, flush=True)
+    out["mfma_ceiling"] = mfma_ceiling(timer, dev)
+    print("bench: stream and MFMA ceilings done", file=sys.stderr, flush=True)
     out["tiny_fp32"] = attention_workload(
         "tiny fp32: L 256, S 16, Hq 4 / Hkv 1, head_dim 64", synth.config_attn("tiny_fp32"),
         timer, [0], out_dtype=torch.float32)

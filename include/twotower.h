@@ -424,6 +424,20 @@ tt_status twotower_pack_weight(const void *w, int32_t out_features, int32_t in_f
 tt_status twotower_probe_stream_read(const void *src, size_t bytes, int32_t workgroups,
                                      uint32_t *sink, void *stream);
 
+/*
+ * Measurement probe: the issue rate of 32x32x16 bf16 MFMAs (v_mfma_f32_32x32x16_bf16, 32768 flops
+ * each) on gfx950, the compute-side ceiling next to the nominal dense bf16 peak. `workgroups`
+ * work-groups of 8 waves each run `iters` iterations of 16 MFMAs on four independent accumulators
+ * (flops per call = workgroups * 8 * iters * 16 * 32768). mode bit 0: the A operand of every MFMA
+ * is a 1 KB LDS read issued one iteration ahead (the attention's operand traffic); bit 1: two
+ * work-groups share a compute unit (4 waves per SIMD) instead of one (2 waves per SIMD), so
+ * workgroups = 2 * (or 1 *) the compute-unit count fills the GPU. sink: device float array of
+ * workgroups * 512 entries, overwritten (values have no meaning). 0 <= mode <= 3,
+ * 1 <= workgroups <= 65536, 1 <= iters <= 2^20, else TT_EINVAL.
+ */
+tt_status twotower_probe_mfma_rate(int32_t mode, int32_t workgroups, int32_t iters, float *sink,
+                                   void *stream);
+
 /* Static string for a status code ("TT_OK", ...); never NULL. */
 const char *twotower_status_string(int32_t status);
 /* TWOTOWER_ABI_VERSION of the built library. */

@@ -295,6 +295,18 @@ def test_stream_read_probe_validation(L):
     assert f(C.c_void_p(FAKE), 1 << 20, 256, None, None) == _lib.TT_EINVAL
 
 
+def test_mfma_rate_probe_validation(L):
+    f = L.twotower_probe_mfma_rate
+    assert f(0, 256, 64, None, None) == _lib.TT_EINVAL
+    assert f(0, 256, 64, C.c_void_p(FAKE + 2), None) == _lib.TT_EINVAL   # misaligned
+    assert f(-1, 256, 64, C.c_void_p(FAKE), None) == _lib.TT_EINVAL
+    assert f(4, 256, 64, C.c_void_p(FAKE), None) == _lib.TT_EINVAL
+    assert f(0, 0, 64, C.c_void_p(FAKE), None) == _lib.TT_EINVAL
+    assert f(0, 65537, 64, C.c_void_p(FAKE), None) == _lib.TT_EINVAL
+    assert f(0, 256, 0, C.c_void_p(FAKE), None) == _lib.TT_EINVAL
+    assert f(0, 256, (1 << 20) + 1, C.c_void_p(FAKE), None) == _lib.TT_EINVAL
+
+
 def test_static_attention_entry_validates_before_touching_the_device(L):
     """The no-allocation entry point checks its arguments and the scratch size on the host first
     (here no device is ever touched): bad arguments give TT_EINVAL, an explicit partition count

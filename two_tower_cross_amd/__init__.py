@@ -23,6 +23,7 @@ from ._lib import LibraryNotBuilt, TwoTowerError, TT_BF16, TT_FP32  # noqa: F401
 __all__ = ["block_attn", "unmask", "qkv_projection", "out_projection", "lm_head",
            "lm_head_unmask", "kv_append", "mask_corrupt", "masked_nll", "DenoiseStep",
            "PackedWeight", "pack_weight", "k_pages_shape", "v_pages_shape", "probe_stream_read",
+           "probe_mfma_rate",
            "LibraryNotBuilt", "TwoTowerError", "library_path"]
 
 
@@ -554,3 +555,16 @@ def probe_stream_read(src, workgroups, sink):
                                                 _stream())
     if st != _lib.TT_OK:
         raise TwoTowerError("twotower_probe_stream_read", st)
+
+def probe_mfma_rate(mode, workgroups, iters, sink):
+    """Measurement probe: ``workgroups`` x 8 waves x ``iters`` x 16 MFMAs 32x32x16 bf16 (mode bit
+    0: A operand read from LDS per MFMA; bit 1: two work-groups per compute unit). ``sink`` is a
+    float32 device tensor of at least ``workgroups * 512`` elements (overwritten). Returns the
+    flops the call performs."""
+    if sink.dtype != torch.float32 or sink.numel() < workgroups * 512 or not sink.is_contiguous():
+        raise ValueError("probe_mfma_rate: float32 sink of >= workgroups * 512 elements")
+    st = _lib.lib().twotower_probe_mfma_rate(int(mode), int(workgroups), int(iters), _p(sink),
+                                              _stream())
+    if st != _lib.TT_OK:
+        raise TwoTowerError("twotower_probe_mfma_rate", st)
+    return int(workgroups) * 8 * int(iters) * 16 * 32768

@@ -151,6 +151,8 @@ def lib():
         L.twotower_block_attn_static.argtypes = [C.POINTER(BlockAttnArgs), vp]
         L.twotower_probe_stream_read.restype = i32
         L.twotower_probe_stream_read.argtypes = [vp, C.c_size_t, i32, vp, vp]
+        L.twotower_probe_mfma_rate.restype = i32
+        L.twotower_probe_mfma_rate.argtypes = [i32, i32, i32, vp, vp]
         if L.twotower_abi_version() != ABI_VERSION:
             raise RuntimeError("libtwotower ABI version mismatch")
         _lib = L

@@ -757,6 +757,14 @@ tt_status twotower_probe_stream_read(const void *src, size_t bytes, int32_t work
       tt::launch_stream_read(src, bytes, workgroups, sink, static_cast<hipStream_t>(stream)));
 }
 
+tt_status twotower_probe_mfma_rate(int32_t mode, int32_t workgroups, int32_t iters, float *sink,
+                                   void *stream) {
+  if (!sink || !aligned(sink, 4) || mode < 0 || mode > 3) return TT_EINVAL;
+  if (workgroups < 1 || workgroups > 65536 || iters < 1 || iters > (1 << 20)) return TT_EINVAL;
+  return hip_status(tt::launch_mfma_rate(mode, workgroups, iters, sink,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 const char *twotower_status_string(int32_t status) {
   switch (status) {
     case TT_OK: return "TT_OK";

@@ -27,5 +27,6 @@ hipError_t launch_pack_weight(const void *, int, int, void *, hipStream_t) { ret
 hipError_t launch_stream_read(const void *, size_t, int, uint32_t *, hipStream_t) {
   return hipErrorNoDevice;
 }
+hipError_t launch_mfma_rate(int, int, int, float *, hipStream_t) { return hipErrorNoDevice; }
 
 }  // namespace tt

@@ -163,5 +163,8 @@ hipError_t launch_pack_weight(const void *w, int N, int K, void *out, hipStream_
 // Streaming read of `bytes` (a multiple of 16) from src with `workgroups` work-groups of 256.
 hipError_t launch_stream_read(const void *src, size_t bytes, int workgroups, uint32_t *sink,
                               hipStream_t stream);
+// MFMA issue rate: `workgroups` x 8 waves x `iters` x 16 MFMAs 32x32x16 bf16; mode bit 0: A operand
+// read from LDS per MFMA, bit 1: two work-groups per compute unit (else one). sink: workgroups x 512.
+hipError_t launch_mfma_rate(int mode, int workgroups, int iters, float *sink, hipStream_t stream);
 
 }  // namespace tt

@@ -1,5 +1,7 @@
-// Measurement probe for gfx950: a plain streaming read of device memory, the practical ceiling
-// that the bandwidth-bound kernels of this library are compared with next to the nominal HBM peak.
+// Measurement probes for gfx950: a plain streaming read of device memory, the practical ceiling
+// that the bandwidth-bound kernels of this library are compared with next to the nominal HBM peak,
+// and the issue rate of 32x32x16 bf16 MFMA chains at a given number of waves per SIMD, with and
+// without an LDS operand read per MFMA (the attention's pattern), next to the nominal MFMA peak.
 //
 // stream_read_kernel: every thread reads 16-byte words with non-temporal loads (the policy the
 // library's streaming kernels use), four independent loads in flight per iteration of a
@@ -35,6 +37,57 @@ hipError_t launch_stream_read(const void *src, size_t bytes, int workgroups, uin
                               hipStream_t stream) {
   hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)workgroups), dim3(256), 0, stream,
                      static_cast<const u32x4 *>(src), bytes / 16, sink);
+  return hipGetLastError();
+}
+
+// mfma_rate_kernel: 8 waves; every wave runs `iters` iterations of 16 MFMAs on four independent
+// accumulators. With LDS_A the A operand of every MFMA is a 1 KB ds_read (64 lanes x 16 bytes)
+// issued one iteration ahead of its use, addresses rotating over 64 KB. The dynamic LDS size
+// fixes the occupancy: one work-group per compute unit (2 waves per SIMD) or two (4 waves).
+template <bool LDS_A>
+__global__ __launch_bounds__(512) void mfma_rate_kernel(int iters, float *sink) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < 65536 / 16; i += 512) {
+    const u32x4 v = {0x3C003C00u + (uint32_t)(i & 7), 0x3C003C00u, 0x3B803B80u, 0x3C003C00u};
+    st_lds_16(smem + i * 16, v);
+  }
+  __syncthreads();
+  u32x4 a[16], b[4];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) a[j] = ld_lds_16(smem + j * 1024 + lane * 16);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b[j] = ld_lds_16(smem + 16384 + j * 1024 + lane * 16);
+  f32x16 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x16{};
+  for (int it = 0; it < iters; ++it) {
+    const int base = (((it + 1) * 16 + wave * 3) & 63) * 1024;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      acc[j & 3] = mfma32x32x16(LDS_A ? a[j] : a[j & 3], b[(j >> 2) & 3], acc[j & 3]);
+      if (LDS_A) a[j] = ld_lds_16(smem + ((base + j * 1024) & 65535) + lane * 16);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) s += acc[j][0] + acc[j][15];
+  sink[(size_t)blockIdx.x * 512 + tid] = s;
+}
+
+hipError_t launch_mfma_rate(int mode, int workgroups, int iters, float *sink, hipStream_t stream) {
+  const bool lds = (mode & 1) != 0;
+  const int bytes = (mode & 2) ? 72 * 1024 : 96 * 1024;  // 2 or 1 work-groups per compute unit
+  const void *fn = lds ? reinterpret_cast<const void *>(&mfma_rate_kernel<true>)
+                       : reinterpret_cast<const void *>(&mfma_rate_kernel<false>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+  if (e != hipSuccess) return e;
+  if (lds)
+    hipLaunchKernelGGL(mfma_rate_kernel<true>, dim3((unsigned)workgroups), dim3(512), bytes,
+                       stream, iters, sink);
+  else
+    hipLaunchKernelGGL(mfma_rate_kernel<false>, dim3((unsigned)workgroups), dim3(512), bytes,
+                       stream, iters, sink);
   return hipGetLastError();
 }
 
