@@ -466,13 +466,88 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
 
 // ---------------------------------------------------------------- lm-head fused with unmasking
 // The step's lm-head when its logits are not kept. Persistent: work-group g of a 128-row block
-// takes the 256-feature tiles g, g + G, g + 2G, ... (G = gridDim.x) and streams their K chunks
-// through the ring as one sequence, so the first chunks of its next tile are in flight while the
-// (max, first argmax, sum of exp) of the previous tile are reduced. The reduction reads the
-// accumulators in registers (no staging of the fp32 tile): each lane's 16 features of a row, the
-// lane pair (the other 16 of the wave's 32-feature slab), then the 8 slabs through a 12 KB LDS
-// area after the rings.
-constexpr int kRedBytes = 8 * kLM * 3 * 4;  // [slab][row] (m, idx, z)
+// takes the 256-feature tiles g, g + G, g + 2G, ... (G = gridDim.x) two at a time: the tiles of a
+// pair are computed together, chunk by chunk of 32 K columns, so every X chunk read through L2
+// serves both (X is re-read per tile pair instead of per tile: 1 instead of 2 X bytes per 4 weight
+// bytes), and the pairs stream through the ring as one sequence, so the first chunks of the next
+// pair are in flight while the (max, first argmax, sum of exp) of the previous one are reduced.
+// The reduction reads the accumulators in registers (no staging of the fp32 tiles): each lane's 16
+// features of a row, the lane pair (the other 16 of the wave's 32-feature slab), then the 8 slabs
+// through an LDS area after the rings.
+struct LPair {
+  static constexpr int WAVES = 8;
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int KC = 32;                      // K columns per chunk (2 MFMA K-steps)
+  static constexpr int WST = 3, XST = 3;             // ring depths
+  static constexpr int TBYTES = 8 * 2 * 1024;        // one tile's chunk: 8 slabs x 2 steps x 1 KB
+  static constexpr int WBYTES = 2 * TBYTES;          // both tiles
+  static constexpr int XBYTES = kLM * KC * 2;        // 128 rows x 64 bytes
+  static constexpr int XBASE = WST * WBYTES;
+  static constexpr int RED = XBASE + XST * XBYTES;
+  static constexpr int REDBYTES = 2 * 8 * kLM * 3 * 4;  // [tile][slab][row] (m, idx, z)
+  static constexpr int LDS = RED + REDBYTES;
+  static constexpr int WLOADS = WBYTES / 1024 / WAVES;  // DMA instructions per wave per chunk
+  static constexpr int XLOADS = XBYTES / 1024 / WAVES;
+  static constexpr int AFTER = (XST - 2) * (WLOADS + XLOADS);
+};
+static_assert(LPair::WST == LPair::XST, "the prologue issues W and X chunks in pairs");
+static_assert(LPair::LDS <= 160 * 1024, "LDS");
+
+// XOR key of the 16-byte chunk swizzle for LDS rows of 64 bytes: the 8 (32-bank) and 16 (64-bank)
+// consecutive rows read by one operand load hit distinct slots.
+__device__ __forceinline__ int key64(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// X chunk (rows m0 .. m0 + 127, columns k .. k + 31) -> X stage, direct-to-LDS through a buffer
+// resource over X (16-byte slot q of row r holds columns k + 8 (q ^ key64(r)) ..); rows past M
+// read row M - 1 (their results are never stored).
+__device__ __forceinline__ void x_dma32(char *stage, __amdgpu_buffer_rsrc_t xr, const LinearParams &p,
+                                        int m0, int k, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < LPair::XLOADS; ++j) {
+    const int seg = j * LPair::WAVES + wave, f = seg * 64 + lane;
+    const int r = f >> 2, c = (f & 3) ^ key64(r);
+    const int m = min(m0 + r, p.M - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, TT_LDS_PTR(stage + seg * 1024), 16,
+                                             (m * p.K + k + c * 8) * 2, 0, 0, 0);
+  }
+}
+
+// Partial last X chunk (k1 - k < 32 columns) through registers, zero past k1 (K % 8 == 0).
+__device__ void x_tail32(char *stage, const LinearParams &p, int m0, int k, int k1, int tid) {
+  const uint16_t *x = static_cast<const uint16_t *>(p.x);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  static_assert(kLM * 4 == LPair::THREADS, "one 16-byte slot per thread");
+  const int r = tid >> 2, q = tid & 3, c = q ^ key64(r);
+  const int m = min(m0 + r, p.M - 1);
+  const u32x4 v = k + c * 8 < k1 ? ld_global_16(x + (size_t)m * p.K + k + c * 8) : z;
+  st_lds_16(stage + r * 64 + q * 16, v);
+}
+
+// One 32-column chunk of both tiles: this wave's slab (32 features) of each tile x 128 rows;
+// the X operand fragments are read once and used for both tiles.
+__device__ __forceinline__ void pair_chunk(const char *ws, const char *xs, f32x16 (*acc)[4],
+                                           int wave, int lane) {
+  const int col = lane & 31, hh = lane >> 5;
+  u32x4 a[2][2], bx[4][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      a[t][ks] = ld_lds_16(ws + t * LPair::TBYTES + (wave * 2 + ks) * 1024 + lane * 16);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int xr = mb * 32 + col, ch = ks * 2 + hh;
+      bx[mb][ks] = ld_lds_16(xs + xr * 64 + ((ch ^ key64(xr)) << 4));
+    }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) acc[t][mb] = mfma32x32x16(a[t][ks], bx[mb][ks], acc[t][mb]);
+}
 
 // (max, first argmax, sum of exp(y - max)) of the 16 accumulator values a lane holds for one
 // row: register i is feature f0 + (i / 4) * 8 + i % 4; features at or past N are left out.
@@ -505,8 +580,8 @@ __device__ __forceinline__ Triple lane_triple(const f32x16 &a, int f0, int N) {
   return t;
 }
 
-__global__ __launch_bounds__(LTile<8>::THREADS) void lm_unmask_kernel(LinearParams p, int ntiles) {
-  using T = LTile<8>;
+__global__ __launch_bounds__(LPair::THREADS) void lm_unmask_kernel(LinearParams p, int ntiles) {
+  using T = LPair;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int m0 = blockIdx.y * kLM;
   const int G = gridDim.x;
@@ -518,46 +593,60 @@ __global__ __launch_bounds__(LTile<8>::THREADS) void lm_unmask_kernel(LinearPara
   const bool live = m0 + rr < p.M && p.masked[min(m0 + rr, p.M - 1)] != 0;
 
   const int mine = (ntiles - (int)blockIdx.x + G - 1) / G;  // tiles of this work-group
-  const int nch = (p.K + kLK - 1) / kLK;
+  const int pairs = (mine + 1) / 2;                       // pair j: tiles j-th and (j+1)-th of mine
+  const int nch = (p.K + T::KC - 1) / T::KC;
   const int Ks = (p.K + 15) / 16;
   const int nslabs = (p.N + 31) / 32;
-  const bool tail = p.K % kLK != 0;  // the last chunk of every tile is partial
-  const int total = mine * nch;
+  const bool tail = p.K % T::KC != 0;  // the last chunk of every pair is partial
+  const int total = pairs * nch;
 
-  f32x16 acc[T::MB];
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int mb = 0; mb < T::MB; ++mb) acc[mb] = f32x16{};
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[t][mb] = f32x16{};
 
   char *wring = smem;
   char *xring = smem + T::XBASE;
-  float *red = reinterpret_cast<float *>(smem + T::LDS);
+  float *red = reinterpret_cast<float *>(smem + T::RED);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void *>(p.x), (short)0, p.M * p.K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void *>(p.x), (short)0, 0, 0x00020000);
-  // Chunk g of the sequence is chunk g % nch of tile blockIdx.x + (g / nch) * G. As in
-  // linear_kernel every step issues the same DMA (phantom loads past the end), so T::AFTER is
-  // exact for every chunk whose X comes by DMA.
-  // (a 256-feature tile is one whole slab group)
+  // Tile t (0, 1) of pair j (the whole slab group of 256 features), or -1 past the last tile.
+  auto pair_tile = [&](int j, int t) {
+    const int tile = (int)blockIdx.x + (2 * j + t) * G;
+    return tile < ntiles ? tile : -1;
+  };
+  // Chunk g of the sequence is chunk g % nch of pair g / nch. As in linear_kernel every step
+  // issues the same DMA (phantom loads through `none` past the end and for a pair's missing
+  // second tile), so T::AFTER is exact for every chunk whose X comes by DMA. Instruction i of a
+  // wave loads 1 KB block (slab u / 2, step u % 2), u = (i % 2) * 8 + wave, of tile i / 2.
   auto w_issue = [&](int g) {
     const int gg = min(g, total - 1);
-    const int tile = (int)blockIdx.x + (gg / nch) * G;
-    const int gsize = min(8, nslabs - 8 * tile);
-    w_dma<8>(wring + (g % T::WST) * T::WBYTES, group_rsrc(p.w, tile, gsize, Ks), gsize, 0,
-             g < total, none, gg % nch, wave, lane);
+    const int j = gg / nch, c = gg % nch;
+#pragma unroll
+    for (int i = 0; i < T::WLOADS; ++i) {
+      const int t = i >> 1, u = (i & 1) * 8 + wave, slab = u >> 1, step = u & 1;
+      const int tile = pair_tile(j, t);
+      const int gsize = tile >= 0 ? min(8, nslabs - 8 * tile) : 0;
+      const bool real = g < total && slab < gsize;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          real ? group_rsrc(p.w, tile, gsize, Ks) : none,
+          TT_LDS_PTR(wring + (g % T::WST) * T::WBYTES + t * T::TBYTES + (slab * 2 + step) * 1024),
+          16, lane * 16, real ? ((2 * c + step) * gsize + slab) * 1024 : 0, 0, kNonTemporal);
+    }
   };
   auto x_issue = [&](int g) {
     const int c = g % nch;
     const bool real = g < total && !(tail && c == nch - 1);
-    x_dma<8>(xring + (g % T::XST) * T::XBYTES, real ? xr : none, p, m0, real ? c * kLK : 0, wave,
-             lane);
+    x_dma32(xring + (g % T::XST) * T::XBYTES, real ? xr : none, p, m0, real ? c * T::KC : 0, wave,
+            lane);
   };
   if (total > 0) {
 #pragma unroll
-    for (int c = 0; c < T::WST - T::XST; ++c) w_issue(c);
-#pragma unroll
     for (int j = 0; j < T::XST - 1; ++j) {
-      w_issue(T::WST - T::XST + j);
+      w_issue(j);
       x_issue(j);
     }
   }
@@ -572,43 +661,52 @@ __global__ __launch_bounds__(LTile<8>::THREADS) void lm_unmask_kernel(LinearPara
     char *xs = xring + (g % T::XST) * T::XBYTES;
     if (x_by_regs) {
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no DMA into this stage is still in flight
-      x_tail<8>(xs, p, m0, c * kLK, p.K, tid);
+      x_tail32(xs, p, m0, c * T::KC, p.K, tid);
       lds_barrier();
     }
-    linear_chunk<8>(wring + (g % T::WST) * T::WBYTES, xs, acc, wave, 0, lane);
+    pair_chunk(wring + (g % T::WST) * T::WBYTES, xs, acc, wave, lane);
     if (c == nch - 1) {
-      // Tile done: this wave's slab, per row: lane triple, lane pair, then the 8 slabs.
-      const int tile = (int)blockIdx.x + (g / nch) * G;
-      const int f0 = tile * T::N + wave * 32 + hh * 4;
+      // Pair done: per tile, this wave's slab, per row: lane triple, lane pair, then the 8 slabs.
+      const int j = g / nch;
 #pragma unroll
-      for (int mb = 0; mb < T::MB; ++mb) {
-        Triple t = lane_triple(acc[mb], f0, p.N);
-        t = merge(t, shfl_xor_triple(t, 32));
-        if (hh == 0) {
-          float *o = red + (wave * kLM + mb * 32 + col) * 3;
-          o[0] = t.m;
-          o[1] = __int_as_float(t.idx);
-          o[2] = t.z;
+      for (int t = 0; t < 2; ++t) {
+        const int tile = pair_tile(j, t);
+        const int f0 = max(tile, 0) * 256 + wave * 32 + hh * 4;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          Triple tr = lane_triple(acc[t][mb], f0, tile >= 0 ? p.N : 0);
+          tr = merge(tr, shfl_xor_triple(tr, 32));
+          if (hh == 0) {
+            float *o = red + ((t * 8 + wave) * kLM + mb * 32 + col) * 3;
+            o[0] = tr.m;
+            o[1] = __int_as_float(tr.idx);
+            o[2] = tr.z;
+          }
+          acc[t][mb] = f32x16{};
         }
-        acc[mb] = f32x16{};
       }
       lds_barrier();
-      Triple t, u;
-      const float *a = red + ((2 * q) * kLM + rr) * 3, *b = red + ((2 * q + 1) * kLM + rr) * 3;
-      t.m = a[0];
-      t.idx = __float_as_int(a[1]);
-      t.z = a[2];
-      u.m = b[0];
-      u.idx = __float_as_int(b[1]);
-      u.z = b[2];
-      t = merge(t, u);
-      t = merge(t, shfl_xor_triple(t, 1));
-      t = merge(t, shfl_xor_triple(t, 2));
-      if (q == 0 && live) {
-        float *o = p.triples + ((size_t)(m0 + rr) * ntiles + tile) * 4;
-        o[0] = t.m;
-        o[1] = __int_as_float(t.idx);
-        o[2] = t.z;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int tile = pair_tile(j, t);
+        Triple tr, u;
+        const float *a = red + ((t * 8 + 2 * q) * kLM + rr) * 3;
+        const float *b = red + ((t * 8 + 2 * q + 1) * kLM + rr) * 3;
+        tr.m = a[0];
+        tr.idx = __float_as_int(a[1]);
+        tr.z = a[2];
+        u.m = b[0];
+        u.idx = __float_as_int(b[1]);
+        u.z = b[2];
+        tr = merge(tr, u);
+        tr = merge(tr, shfl_xor_triple(tr, 1));
+        tr = merge(tr, shfl_xor_triple(tr, 2));
+        if (q == 0 && live && tile >= 0) {
+          float *o = p.triples + ((size_t)(m0 + rr) * ntiles + tile) * 4;
+          o[0] = tr.m;
+          o[1] = __int_as_float(tr.idx);
+          o[2] = tr.z;
+        }
       }
       // (the next write of `red` follows at least one more ring barrier)
     }
@@ -655,16 +753,13 @@ static hipError_t launch_tile(const LinearParams &p, hipStream_t stream, int cpz
   return hipGetLastError();
 }
 
-// Persistent fused lm-head: as many work-groups as compute units (or tiles, if fewer), spread
+// Persistent fused lm-head: as many work-groups as compute units (or tile pairs, if fewer), spread
 // over the 128-row blocks.
 static hipError_t launch_lm_unmask(const LinearParams &p, hipStream_t stream) {
-  using T = LTile<8>;
-  constexpr int kBytes = T::LDS + kRedBytes;
-  static_assert(kBytes <= 160 * 1024, "LDS");
-  static_assert(8 % 2 == 0, "a 64-feature tile lies inside one slab group");
+  using T = LPair;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(&lm_unmask_kernel),
-      hipFuncAttributeMaxDynamicSharedMemorySize, kBytes);
+      hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
   if (attr != hipSuccess) return attr;
   static int cu_count[64] = {};  // per device, queried once
   int dev = 0;
@@ -676,10 +771,10 @@ static hipError_t launch_lm_unmask(const LinearParams &p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     if (dev < 64) cu_count[dev] = cus;
   }
-  const int ntiles = (p.N + T::N - 1) / T::N;
+  const int ntiles = (p.N + 255) / 256;
   const int rows = (p.M + kLM - 1) / kLM;
-  const int G = std::max(1, std::min(ntiles, cus / rows));
-  hipLaunchKernelGGL(lm_unmask_kernel, dim3(G, rows), dim3(T::THREADS), kBytes, stream, p, ntiles);
+  const int G = std::max(1, std::min((ntiles + 1) / 2, cus / rows));
+  hipLaunchKernelGGL(lm_unmask_kernel, dim3(G, rows), dim3(T::THREADS), T::LDS, stream, p, ntiles);
   return hipGetLastError();
 }
 
