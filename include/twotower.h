@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define TWOTOWER_ABI_VERSION 8
+#define TWOTOWER_ABI_VERSION 9
 
 typedef enum {
   TT_OK = 0,

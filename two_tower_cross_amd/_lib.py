@@ -16,7 +16,7 @@ TT_OK, TT_EINVAL, TT_ENOTSUP, TT_ENOSPACE, TT_EHIP = range(5)
 TT_FP32, TT_BF16 = 0, 1
 TT_APPEND_OUT_OF_PAGES, TT_APPEND_NO_ROOM_IN_TABLE, TT_APPEND_BAD_PAGE = 1, 2, 4
 STATIC_SCRATCH_BYTES = 32 << 20
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 i32, i64, f32, vp = C.c_int32, C.c_int64, C.c_float, C.c_void_p
 
