@@ -1,6 +1,8 @@
 """Build ``libtwotower.so`` in-tree with hipcc for gfx950.
 
 Usage: ``python -m two_tower_cross_amd.build`` (or ``build()`` from Python). Always recompiles.
+``--host-sanitized`` builds the host code under ASan/UBSan instead, ``--phase-stamps`` the
+profiling build with per-work-group phase stamps.
 """
 from __future__ import annotations
 
@@ -67,6 +69,34 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+STAMPS_LIB = os.path.join(OBJ, "libtwotower_stamps.so")
+
+
+def build_phase_stamps() -> str:
+    """The profiling build: the same sources compiled with TT_PHASE_STAMPS, so that the attention
+    and projection kernels record per-work-group phase times (read by
+    ``python -m two_tower_cross_amd.phases``). Never loaded by the tests, the smoke run or the
+    bench. Returns its path."""
+    hipcc = _hipcc()
+    obj = os.path.join(OBJ, "stamps")
+    os.makedirs(obj, exist_ok=True)
+    jobs = []
+    for src in DEVICE_SOURCES:
+        jobs.append([hipcc, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), "-DTT_PHASE_STAMPS", "-c",
+                     os.path.join(CSRC, src), "-o", os.path.join(obj, src + ".o")])
+    for src in HOST_SOURCES:
+        jobs.append([hipcc, *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o",
+                     os.path.join(obj, src + ".o")])
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", "8"))))
+    with cf.ThreadPoolExecutor(workers) as ex:
+        list(ex.map(_run, jobs))
+    tmp = STAMPS_LIB + ".tmp"
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp,
+          *[os.path.join(obj, s + ".o") for s in DEVICE_SOURCES + HOST_SOURCES]])
+    os.replace(tmp, STAMPS_LIB)
+    return STAMPS_LIB
+
+
 SANITIZED_LIB = os.path.join(OBJ, "libtwotower_hostsan.so")
 
 
@@ -90,5 +120,7 @@ def build_host_sanitized() -> str:
 if __name__ == "__main__":
     if "--host-sanitized" in sys.argv:
         print(build_host_sanitized())
+    elif "--phase-stamps" in sys.argv:
+        print(build_phase_stamps())
     else:
         print(build(verbose="-v" in sys.argv))

@@ -35,6 +35,10 @@
 
 namespace tt {
 
+#ifdef TT_PHASE_STAMPS
+__device__ unsigned long long attn_phase_stamps[8192][8];
+#endif
+
 constexpr int kTile = 64;
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
@@ -642,6 +646,8 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   const int rg = (id >> 3) % R;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  TT_STAMPS_DECL;
+  TT_STAMP(0);  // phase stamps (profiling build): start
   const int per_b = p.Hkv * p.splits;
   if (!p.balanced && q >= p.B * per_b) return;
 
@@ -782,6 +788,7 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
     return ids_in_regs ? __builtin_amdgcn_readlane(my_tile, n)
                        : __builtin_amdgcn_readfirstlane(tile_ids[n]);
   };
+  TT_STAMP(1);  // the partition's tile indices are known
   const int n_full_ok = bad ? 0 : n_full;
   const int tail_ok = bad ? 0 : tail;
   const char *kpool = static_cast<const char *>(p.k_pages);
@@ -825,10 +832,13 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
     }
   }
 
+  TT_STAMP(2);  // the ring's first DMA is issued (and the block tile attended)
   if (n_full_ok > 0) {
     // Tile 0 is in LDS for every wave.
     wait_dma<Geom<D>::LOADS>(min(kStages - 2, n_full_ok - 1));
     lds_barrier();
+    TT_STAMP(3);  // tile 0 has landed
+    TT_CYCLES(6);
     PipeRegs<D> pr;
     if (wave_active) pipe_start<D>(smem, lm, qreg, pr);
     // Tile T is consumed by M(2T) and M(2T+1) (its V) after M(2T-2) and M(2T-1) read its K.
@@ -856,6 +866,8 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
       if (T + 3 < n_full_ok) ring_step(std::integral_constant<int, 3>{}, T + 3);
     }
     if (wave_active) pipe_finish<D>(pr, oacc);
+    TT_STAMP(4);  // the ring is done
+    TT_CYCLES(7);
   }
 
   if (tail_ok > 0) {
@@ -963,6 +975,8 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
     }
     if (p.lse && hh == 0 && row_ok) p.lse[((size_t)b * p.Hq + h) * p.S + iq] = lse_val;
   }
+  TT_STAMP_DRAINED(5);  // outputs written
+  TT_STAMPS_STORE(attn_phase_stamps, blockIdx.x);
 }
 
 // Exact merge of the partitions of each query row: with lse* = max_p lse_p and
@@ -1352,5 +1366,18 @@ hipError_t launch_attn_reduce(const AttnParams &p, hipStream_t stream) {
   else launch_reduce_d<64>(p, stream);
   return hipGetLastError();
 }
+
+#ifdef TT_PHASE_STAMPS
+// Profiling build only: copies (or, with clear != 0, zeroes) the attention kernel's phase stamps.
+extern "C" int tt_phase_stamps_attn(void *dst, size_t bytes, int clear) {
+  if (clear) {
+    static unsigned long long zero[8192][8];
+    return (int)hipMemcpyToSymbol(HIP_SYMBOL(attn_phase_stamps), zero, sizeof(zero), 0,
+                                  hipMemcpyHostToDevice);
+  }
+  return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(attn_phase_stamps), bytes, 0,
+                                  hipMemcpyDeviceToHost);
+}
+#endif
 
 }  // namespace tt

@@ -105,6 +105,25 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 #define TT_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
+// Phase stamps of the profiling build (compiled with TT_PHASE_STAMPS; the product library has
+// none): wave 0 of a work-group records wall_clock64() (a constant 100 MHz counter) at up to 6
+// phases of its kernel and clock64() (shader cycles) at 2 more points; its first lane stores the
+// 8 values in the file's stamp array, row = flat work-group id.
+#ifdef TT_PHASE_STAMPS
+#define TT_STAMPS_DECL unsigned long long tt_st_[8] = {0, 0, 0, 0, 0, 0, 0, 0}
+#define TT_STAMP(i) do { if (threadIdx.x < 64) tt_st_[i] = wall_clock64(); } while (0)
+#define TT_CYCLES(i) do { if (threadIdx.x < 64) tt_st_[i] = clock64(); } while (0)
+#define TT_STAMP_DRAINED(i) do { __builtin_amdgcn_s_waitcnt(0); TT_STAMP(i); } while (0)
+#define TT_STAMPS_STORE(arr, id) \
+  do { if (threadIdx.x == 0 && (id) < 8192) for (int i_ = 0; i_ < 8; ++i_) arr[id][i_] = tt_st_[i_]; } while (0)
+#else
+#define TT_STAMPS_DECL do {} while (0)
+#define TT_STAMP(i) do {} while (0)
+#define TT_CYCLES(i) do {} while (0)
+#define TT_STAMP_DRAINED(i) do {} while (0)
+#define TT_STAMPS_STORE(arr, id) do {} while (0)
+#endif
+
 // s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8); expcnt and
 // lgkmcnt are left at their maxima so only vector-memory operations are waited for. Issued through
 // the builtin so that the compiler's own wait insertion knows about them.

@@ -29,6 +29,10 @@
 
 namespace tt {
 
+#ifdef TT_PHASE_STAMPS
+__device__ unsigned long long linear_phase_stamps[8192][8];
+#endif
+
 constexpr int kLM = 128;         // rows per work-group
 constexpr int kLK = 64;          // K columns per chunk
 // Weights are streamed once per product: non-temporal loads (about 20% more read bandwidth than
@@ -340,6 +344,9 @@ template <int NB>
 __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams p, int cpz) {
   using T = LTile<NB>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
+  TT_STAMPS_DECL;
+  TT_STAMP(0);  // phase stamps (profiling build): start
+  TT_CYCLES(6);
   const int nb0 = blockIdx.x * NB;
   const int m0 = blockIdx.y * kLM;
   const int kz = blockIdx.z;
@@ -409,6 +416,7 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
     if (i < n_dma_x) __builtin_amdgcn_s_waitcnt(waitcnt_vm(T::AFTER));
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     lds_barrier();  // chunk i is in LDS for every wave; the stages of chunk i - 1 are free
+    if (i == 0) TT_STAMP(1);  // chunk 0 has landed
     w_issue(i + T::WST - 1);
     x_issue(i + T::XST - 1);
     char *xs = xring + (i % T::XST) * T::XBYTES;
@@ -425,10 +433,12 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
   // thread handles 4 consecutive features of one row, consecutive threads along the row: the global
   // stores cover whole rows instead of 32-byte pieces of 32 rows.
   constexpr int NCH = T::N / 4;  // 16-byte chunks per tile row
+  TT_STAMP(2);  // the K loop is done
   // The last steps issued phantom loads into the rings (zeros); they must land before the rings
   // are reused for the output tile.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   lds_barrier();                 // every wave is done with the rings
+  TT_STAMP(3);
   float *tile = reinterpret_cast<float *>(smem);
 #pragma unroll
   for (int mb = 0; mb < T::MB; ++mb) {
@@ -462,6 +472,11 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
     else
       epilogue4(p, m, nn, v);
   }
+  TT_STAMP(4);  // stores issued
+  TT_STAMP_DRAINED(5);  // stores done
+  TT_CYCLES(7);
+  TT_STAMPS_STORE(linear_phase_stamps,
+                  blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
 }
 
 // ---------------------------------------------------------------- lm-head fused with unmasking
@@ -789,5 +804,18 @@ hipError_t launch_linear(const LinearParams &p, hipStream_t stream) {
                      stream, p);
   return hipGetLastError();
 }
+
+#ifdef TT_PHASE_STAMPS
+// Profiling build only: copies (or, with clear != 0, zeroes) the projection kernel's phase stamps.
+extern "C" int tt_phase_stamps_linear(void *dst, size_t bytes, int clear) {
+  if (clear) {
+    static unsigned long long zero[8192][8];
+    return (int)hipMemcpyToSymbol(HIP_SYMBOL(linear_phase_stamps), zero, sizeof(zero), 0,
+                                  hipMemcpyHostToDevice);
+  }
+  return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(linear_phase_stamps), bytes, 0,
+                                  hipMemcpyDeviceToHost);
+}
+#endif
 
 }  // namespace tt
