@@ -1153,12 +1153,14 @@ __device__ __forceinline__ float block_sum_256(float x, float *red) {
 
 template <int D>
 __global__ __launch_bounds__(256) void block_attn_f32_kernel(AttnParams p) {
-  // LDS: the query, the tile's 256 weights, the reduction words, then the tile's values staged
-  // token-major [256][D] (dynamic), so that the weighted sum reads LDS instead of 256 rounds of
-  // scattered global loads.
+  // LDS: the query, the tile's 256 weights, the reduction words, the partial weighted sums of the
+  // key groups, then the tile's values staged token-major [256][D] (dynamic), so that the
+  // weighted sum reads LDS instead of scattered global loads.
+  constexpr int KG = 256 / D;  // key groups of the weighted sum: thread t takes dimension t % D
   __shared__ float qs[D];
   __shared__ float pw[256];
   __shared__ float red[4];
+  __shared__ float part[256];
   __shared__ int vpage[256];  // page of each context key of the tile
   extern __shared__ float vs[];
   const int iq = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
@@ -1178,55 +1180,74 @@ __global__ __launch_bounds__(256) void block_attn_f32_kernel(AttnParams p) {
   __syncthreads();
   for (int base = 0; base < N; base += 256) {
     const int nt = min(256, N - base);
-    // this thread's key: score
+    // Page of every key of the tile first (one round trip), then this thread's key row and its
+    // share of the tile's values requested together (one more), so that the tile costs two memory
+    // round trips instead of one per dependent step.
     const int j = base + tid;
-    float s = -INFINITY;
-    vpage[tid] = -1;
-    if (j < N) {
-      const float *key;
-      if (j < p.S) {
-        key = kb + (size_t)j * D;
-      } else {
-        const int t = j - p.S;
-        const int page = btab[t / p.page_size];
-        vpage[tid] = page;
-        if (page < 0 || page >= p.num_pages) {
-          key = nullptr;
+    int mypage = -1;
+    if (j >= p.S && j < N) mypage = btab[(j - p.S) / p.page_size];
+    vpage[tid] = mypage;
+    __syncthreads();
+    const bool key_ok = j < N && (j < p.S || (mypage >= 0 && mypage < p.num_pages));
+    const float *key = nullptr;
+    if (key_ok)
+      key = j < p.S ? kb + (size_t)j * D
+                    : kp + ((size_t)mypage * p.Hkv + g) * p.page_size * D;  // (page, head) block
+    const int ko = (j - p.S) % p.page_size;
+    f32x4 krow[D / 4];
+#pragma unroll
+    for (int d = 0; d < D; d += 4)
+      krow[d / 4] = key ? *reinterpret_cast<const f32x4 *>(
+                              key + (j < p.S ? (size_t)d : k_elem(ko, d, D)))
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+    // the tile's values, token-major: element e = tid + 256 i is (key e / D, dimension e % D); a
+    // page id outside the pool reads nothing (0). The first NV0 of a thread's D elements are
+    // requested with its key row, the rest (D = 128) after those are stored.
+    constexpr int NV0 = D < 64 ? D : 64;
+    auto load_v = [&](int i) {
+      const int e = tid + 256 * i, jl = e / D, d = e % D, jj = base + jl;
+      float v = 0.f;
+      if (jl < nt) {
+        if (jj < p.S) {
+          v = vb[(size_t)d * p.S + jj];
         } else {
-          key = kp + ((size_t)page * p.Hkv + g) * p.page_size * D;  // the (page, head) block
+          const int page = vpage[jl];
+          if (page >= 0 && page < p.num_pages)
+            v = vp[((size_t)page * p.Hkv + g) * p.page_size * D + v_elem((jj - p.S) % p.page_size, d, D)];
         }
       }
+      return v;
+    };
+    float vreg[NV0];
+#pragma unroll
+    for (int i = 0; i < NV0; ++i) vreg[i] = load_v(i);
+    // score (four independent partial dot products)
+    float s = -INFINITY;
+    if (j < N) {
       if (key) {
-        float acc = 0.f;
-        const int o = (j - p.S) % p.page_size;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
         for (int d = 0; d < D; d += 4) {
-          const f32x4 kv = *reinterpret_cast<const f32x4 *>(
-              key + (j < p.S ? (size_t)d : k_elem(o, d, D)));
-          acc = fmaf(qs[d], kv[0], acc);
-          acc = fmaf(qs[d + 1], kv[1], acc);
-          acc = fmaf(qs[d + 2], kv[2], acc);
-          acc = fmaf(qs[d + 3], kv[3], acc);
+          float &a = acc[(d / 4) & 3];
+          a = fmaf(qs[d], krow[d / 4][0], a);
+          a = fmaf(qs[d + 1], krow[d / 4][1], a);
+          a = fmaf(qs[d + 2], krow[d / 4][2], a);
+          a = fmaf(qs[d + 3], krow[d / 4][3], a);
         }
-        s = acc * p.scale;
+        s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * p.scale;
       } else {
         s = NAN;
       }
     }
-    // the tile's values into LDS, token-major, one independent load per element (a page id
-    // outside the pool reads nothing: 0)
-    __syncthreads();
-#pragma unroll 8
-    for (int e = tid; e < nt * D; e += 256) {
-      const int jl = e / D, d = e % D, jj = base + jl;
-      float v = 0.f;
-      if (jj < p.S) {
-        v = vb[(size_t)d * p.S + jj];
-      } else {
-        const int page = vpage[jl];
-        if (page >= 0 && page < p.num_pages)
-          v = vp[((size_t)page * p.Hkv + g) * p.page_size * D + v_elem((jj - p.S) % p.page_size, d, D)];
-      }
-      vs[e] = v;
+    __syncthreads();  // every wave is done with the previous tile's values and weights
+#pragma unroll
+    for (int i = 0; i < NV0; ++i) vs[tid + 256 * i] = vreg[i];
+#pragma unroll
+    for (int i0 = NV0; i0 < D; i0 += NV0) {
+#pragma unroll
+      for (int i = 0; i < NV0; ++i) vreg[i] = load_v(i0 + i);
+#pragma unroll
+      for (int i = 0; i < NV0; ++i) vs[tid + 256 * (i0 + i)] = vreg[i];
     }
     const bool nan_here = s != s;
     if (__syncthreads_or(nan_here)) bad = true;
@@ -1238,9 +1259,20 @@ __global__ __launch_bounds__(256) void block_attn_f32_kernel(AttnParams p) {
     pw[tid] = pj;
     const float psum = block_sum_256(pj, red);
     l = l * alpha + psum;
+    // weighted sum: thread t sums dimension t % D over keys t / D, t / D + KG, ... of the tile
+    // (four independent chains), then the KG groups are added in order
+    {
+      const int d = tid % D, kg = tid / D;
+      float a4[4] = {0.f, 0.f, 0.f, 0.f};
+      int i = 0;
+      for (int t = kg; t < nt; t += KG, ++i) a4[i & 3] = fmaf(pw[t], vs[t * D + d], a4[i & 3]);
+      part[tid] = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+    }
+    __syncthreads();
     if (tid < D) {
       float acc = 0.f;
-      for (int t = 0; t < nt; ++t) acc = fmaf(pw[t], vs[t * D + tid], acc);
+#pragma unroll
+      for (int k = 0; k < KG; ++k) acc += part[k * D + tid];
       o = o * alpha + acc;
     }
     m = mnew;
