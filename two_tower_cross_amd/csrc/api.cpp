@@ -16,7 +16,7 @@ namespace {
 constexpr int kTargetWorkgroups = 256;  // one work-group per compute unit on MI355X
 constexpr int kMinChunk = 256;          // context tokens per partition, lower bound
 constexpr int kMaxPartitionTiles = 4096;  // 64-token tile indices one attention work-group stages in LDS
-constexpr int kMinPartTiles = 4;          // the balanced plan's smallest partition (256 tokens)
+constexpr int kMinPartTiles = 1;          // the balanced plan's smallest partition (64 tokens)
 constexpr int kPlanMaxB = 256;            // sequences the balanced plan handles
 constexpr size_t kAlign = 256;
 

@@ -491,7 +491,7 @@ __device__ __forceinline__ void pipe_finish(const PipeRegs<D> &r, f32x16 *oacc) 
 // sequences, kPlanPerLane per lane).
 constexpr int kPlanMaxB = 256;
 constexpr int kPlanPerLane = kPlanMaxB / 64;
-constexpr int kMinPartTiles = 4;
+constexpr int kMinPartTiles = 1;  // short contexts: one tile per work-group, more of the GPU busy
 
 // Inclusive prefix sum over the 64 lanes of a wave: sums of 4 within each row of 16 lanes by row
 // shifts, then rows completed with shifts by 4 and 8, then carried across rows by the row
