@@ -8,9 +8,8 @@
 // group (64 or 256 features) and all rows of an M tile, and walks its K range in chunks of 64
 // columns:
 //   * W chunks (one 32 KB run for 256 features, four 2 KB runs for 64) stream into an LDS ring
-//     with non-temporal
-//     direct-to-LDS loads (several chunks in flight: a compute unit keeps ~64 KB of loads in
-//     flight, and deeper rings only queue behind that limit);
+//     with non-temporal direct-to-LDS loads (several chunks in flight: a compute unit keeps
+//     ~64 KB of loads in flight, and deeper rings only queue behind that limit);
 //   * X chunks (128 rows x 64 columns, re-read by every work-group, so served by L2) go through a
 //     second ring, 16-byte chunks XOR-swizzled per 128-byte row, deep enough to cover the L2
 //     latency under load;
@@ -19,7 +18,8 @@
 // written through to memory, + one reduce pass, fixed summation order, no atomics).
 // Epilogues: fp32 store (logits), Q/K/V scatter into the attention layouts (bf16), residual add
 // (bf16), and the unmasking triples of the lm-head (lm_unmask_kernel when the logits are not
-// kept: persistent, one ring stream over several tiles).
+// kept: persistent, 256-feature tiles computed in pairs that share each 32-column X chunk, the
+// pairs' chunks as one ring stream).
 #include <algorithm>
 #include <math.h>
 
