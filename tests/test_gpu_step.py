@@ -149,6 +149,34 @@ def test_step_equals_composition_of_stages_bit_for_bit():
     assert torch.equal(conf, conf2)
 
 
+def test_step_timing_events_change_nothing():
+    """The profiling hook of the step (events around each layer's attention, NULL entries
+    skipped; fence-free timing events as the benchmark creates them) records time and leaves every
+    output bit for bit as without events."""
+    from two_tower_cross_amd.timing import TimingEvent
+    m = small_model()
+    step = make_step(m, keep_logits=True)
+    runs = []
+    for with_events in (False, True):
+        masked = torch.ones((m.B, m.S), dtype=torch.uint8, device=DEV)
+        tokens = torch.full((m.B, m.S), -1, dtype=torch.int32, device=DEV)
+        evs, handles = None, None
+        if with_events:
+            evs = [TimingEvent() for _ in range(4)]
+            handles = [None] * (3 * m.layers)
+            handles[0], handles[2] = evs[0].cuda_event, evs[1].cuda_event        # layer 0: call
+            handles[3 * (m.layers - 1)], handles[3 * (m.layers - 1) + 1] = (
+                evs[2].cuda_event, evs[3].cuda_event)                           # last: kernel
+        conf, n = step(m.h_steps[0], masked, tokens, threshold=0.9, min_commit=True,
+                       timing_events=handles)
+        torch.cuda.synchronize()
+        runs.append((conf.clone(), n.clone(), masked.clone(), tokens.clone(), step.logits.clone()))
+        if with_events:
+            assert evs[0].elapsed_time(evs[1]) > 0.0 and evs[2].elapsed_time(evs[3]) > 0.0
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
+
+
 def test_step_stages_against_oracle():
     m = small_model(seed=4, L=777)
     masked = torch.ones((m.B, m.S), dtype=torch.uint8, device=DEV)
