@@ -487,8 +487,10 @@ __device__ __forceinline__ void pipe_finish(const PipeRegs<D> &r, f32x16 *oacc) 
 // item k of a KV head and row group is partition k - E_b of the sequence b with E_b <= k <
 // E_b + n_b (E_b = sum of n over the sequences before b), ordered (b, KV head, partition) so that
 // equal lengths give the same items, in the same order, as a uniform split. Every wave of the
-// attention kernel and of the merge computes the plan from the lengths (at most kPlanMaxB
-// sequences, kPlanPerLane per lane).
+// attention kernel computes the plan from the lengths (at most kPlanMaxB sequences, kPlanPerLane
+// per lane), except when every sequence is active at max_ctx_len: then the plan is that uniform
+// split, known beforehand, and one ballot replaces the computation. Work-group 0 writes the plan
+// record that the merge reads.
 constexpr int kPlanMaxB = 256;
 constexpr int kPlanPerLane = kPlanMaxB / 64;
 constexpr int kMinPartTiles = 1;  // short contexts: one tile per work-group, more of the GPU busy
@@ -702,7 +704,26 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   };
   load_unit();
 
+  bool spec_exact = false;
   if (p.balanced) {
+    // Every sequence active at max_ctx_len: the plan is the speculated one (the uniform split).
+    bool full = true;
+#pragma unroll
+    for (int j = 0; j < kPlanPerLane; ++j)
+      if (lane + 64 * j < p.B) full = full && actp[j] && Lp[j] == p.max_ctx_len;
+    spec_exact = __ballot(!full) == 0;
+  }
+  if (spec_exact) {
+    if (id == 0 && wave == 0 && p.plan_rec) {
+#pragma unroll
+      for (int j = 0; j < kPlanPerLane; ++j) {
+        const int bb = lane + 64 * j;
+        if (bb < p.B) *reinterpret_cast<int2 *>(p.plan_rec + 2 * bb) = make_int2(p.splits, bb * p.splits);
+      }
+    }
+    if (q >= p.B * per_b) return;  // past the last unit (the same for every wave)
+    L = p.max_ctx_len;
+  } else if (p.balanced) {
     PlanLanes pl;
     plan_partitions(p, Lp, actp, pl);
     if (id == 0 && wave == 0 && p.plan_rec) {  // the merge reads the plan instead of recomputing it
