@@ -531,14 +531,31 @@ struct PlanLanes {
 };
 
 // A sequence counts as active unless the caller's flags say it has no masked position left.
+// Whether sequence b has a nonzero flag. The flags are read in batches of 8 words (or bytes) whose
+// loads are all issued before any is used (indices clamped to the row, so a batch past its end
+// re-reads the row's last word): one memory round trip per batch, 1 for S <= 32.
 __device__ __forceinline__ bool seq_active(const AttnParams &p, int b) {
   if (!p.active) return true;
   const uint8_t *m = p.active + (size_t)b * p.S;
   uint32_t any = 0;
   if ((p.S & 3) == 0 && (reinterpret_cast<uintptr_t>(p.active) & 3) == 0) {
-    for (int i = 0; i < p.S; i += 4) any |= *reinterpret_cast<const uint32_t *>(m + i);
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(m);
+    const int nw = p.S >> 2;
+    for (int i0 = 0; i0 < nw; i0 += 8) {
+      uint32_t v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = w[min(i0 + k, nw - 1)];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) any |= v[k];
+    }
   } else {
-    for (int i = 0; i < p.S; ++i) any |= m[i];
+    for (int i0 = 0; i0 < p.S; i0 += 8) {
+      uint32_t v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = m[min(i0 + k, p.S - 1)];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) any |= v[k];
+    }
   }
   return any != 0;
 }
@@ -669,8 +686,6 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
   int Lp[kPlanPerLane];
   bool actp[kPlanPerLane];
   int L = 0;
-  if (p.balanced) plan_load(p, lane, Lp, actp);
-  else L = p.ctx_lens[b];
 
   const int col = lane & 31, hh = lane >> 5;
   const int r_local = wave * 32 + col;
@@ -702,7 +717,10 @@ __global__ __launch_bounds__(kThreads) void block_attn_bf16_kernel(AttnParams p)
     const int32_t *btab = p.block_table + (size_t)b * p.max_pages;
     if (li < n_spec) spec_page = btab[min((t_begin + li * kTile) / p.page_size, p.max_pages - 1)];
   };
+  // The unit's loads go first: the plan's lengths and flags are used (waited for) at once.
   load_unit();
+  if (p.balanced) plan_load(p, lane, Lp, actp);
+  else L = p.ctx_lens[b];
 
   bool spec_exact = false;
   if (p.balanced) {
