@@ -70,6 +70,14 @@ __device__ __forceinline__ void st_wt_16(__amdgpu_buffer_rsrc_t r, uint32_t off,
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kWriteThrough);
 }
 
+// Returns v unchanged, as the output of an (empty) asm statement at this point of the program:
+// nothing can be computed from v before it, so the wait for the load that produced v is placed
+// here and not right after the load (a flag read at kernel start and used much later).
+__device__ __forceinline__ uint32_t defer_use(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 __device__ __forceinline__ u32x4 ld_lds_16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }

@@ -357,11 +357,8 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
   const int mrow0 = NB == 2 ? (wave >> 1) * 32 : 0;
   // Fused unmasking: whether this thread's epilogue row (m0 + tid / 4) is still masked, read now
   // so that the load is long done when the epilogue needs it.
-  bool live_row = false;
-  if (NB == 8 && p.epi == EPI_UNMASK) {
-    const int mr = m0 + (tid >> 2);
-    live_row = mr < p.M && p.masked[min(mr, p.M - 1)] != 0;
-  }
+  uint32_t row_flag = 0;
+  if (NB == 8 && p.epi == EPI_UNMASK) row_flag = p.masked[min(m0 + (tid >> 2), p.M - 1)];
 
   const int nch = (p.K + kLK - 1) / kLK;
   const int Ks = (p.K + 15) / 16;
@@ -455,7 +452,7 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
   const int n0 = nb0 * 32;
   if constexpr (NB == 8) {
     if (p.epi == EPI_UNMASK) {
-      unmask_epilogue<NB>(p, tile, m0, n0, tid, live_row);
+      unmask_epilogue<NB>(p, tile, m0, n0, tid, m0 + (tid >> 2) < p.M && defer_use(row_flag) != 0);
       return;
     }
   }
@@ -603,9 +600,10 @@ __global__ __launch_bounds__(LPair::THREADS) void lm_unmask_kernel(LinearParams 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hh = lane >> 5;
-  // the final merge: four threads per row; whether the row is still masked, read now
+  // the final merge: four threads per row; whether the row is still masked, requested now and
+  // used only at the first pair's merge (the ring does not wait for it)
   const int rr = tid >> 2, q = tid & 3;
-  const bool live = m0 + rr < p.M && p.masked[min(m0 + rr, p.M - 1)] != 0;
+  const uint32_t flag = p.masked[min(m0 + rr, p.M - 1)];
 
   const int mine = (ntiles - (int)blockIdx.x + G - 1) / G;  // tiles of this work-group
   const int pairs = (mine + 1) / 2;                       // pair j: tiles j-th and (j+1)-th of mine
@@ -701,6 +699,7 @@ __global__ __launch_bounds__(LPair::THREADS) void lm_unmask_kernel(LinearParams 
         }
       }
       lds_barrier();
+      const bool live = m0 + rr < p.M && defer_use(flag) != 0;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int tile = pair_tile(j, t);

@@ -92,14 +92,15 @@ __global__ __launch_bounds__(kUThreads) void unmask_partial_kernel(UnmaskParams 
 // confidence, lowest position on ties) through per-wave reductions in LDS, then the state update.
 constexpr int kDecThreads = 256;  // largest block size S
 
-__device__ __forceinline__ void commit_decisions(const UnmaskParams &p, int b, int i, Triple t) {
+// `flag` is masked[b, i] as read at kernel start (0 for i >= S).
+__device__ __forceinline__ void commit_decisions(const UnmaskParams &p, int b, int i, Triple t,
+                                                 uint32_t flag) {
   __shared__ int any_commit_w[kDecThreads / 64], any_masked_w[kDecThreads / 64];
   __shared__ float best_c[kDecThreads / 64];
   __shared__ int best_i[kDecThreads / 64], n_w[kDecThreads / 64];
   const int lane = i & 63, w = i >> 6;
-  const bool in = i < p.S;
   const size_t row = (size_t)b * p.S + i;
-  const bool was_masked = in && p.masked[row] != 0;
+  const bool was_masked = flag != 0;
   const float conf = was_masked ? 1.0f / t.z : -1.0f;
   bool commit = was_masked && (p.commit_all || conf > p.threshold);
   // the wave's best candidate for the fallback: largest confidence, lowest position on ties
@@ -163,10 +164,11 @@ __global__ __launch_bounds__(kDecThreads) void unmask_finalize_kernel(UnmaskPara
   const int b = blockIdx.x;
   const int i = threadIdx.x;
   const size_t row = (size_t)b * p.S + i;
+  const uint32_t flag = i < p.S ? p.masked[row] : 0u;
   Triple t = empty_triple();
-  if (i < p.S && p.masked[row] != 0)
+  if (flag != 0)
     for (int c = 0; c < p.chunks; ++c) t = merge(t, load_triple(p.part + (row * p.chunks + c) * 4));
-  commit_decisions(p, b, i, t);
+  commit_decisions(p, b, i, t, flag);
 }
 
 // Many tile triples per row (one per 256-logit lm-head tile): wave w merges rows w, w + 16, ...
@@ -175,34 +177,36 @@ __global__ __launch_bounds__(1024) void unmask_tiles_finalize_kernel(UnmaskParam
   __shared__ Triple rows[kDecThreads];
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // Thread i's flag for the decisions, requested together with the triples: a row that is no
+  // longer masked has no triples of this step (what its slots hold is merged but never used), so
+  // nothing waits for a flag before the triples are requested (one memory round trip).
+  const uint32_t flag = threadIdx.x < (unsigned)p.S ? p.masked[(size_t)b * p.S + threadIdx.x] : 0u;
   for (int i = wave; i < p.S; i += 16) {
     const size_t row = (size_t)b * p.S + i;
     Triple t = empty_triple();
-    if (p.masked[row] != 0) {
-      const f32x4 *src = reinterpret_cast<const f32x4 *>(p.part) + row * p.chunks;
-      for (int c0 = 0; c0 < p.chunks; c0 += 8 * 64) {  // 8 triples per lane in flight at once
-        f32x4 v[8];
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(p.part) + row * p.chunks;
+    for (int c0 = 0; c0 < p.chunks; c0 += 8 * 64) {  // 8 triples per lane in flight at once
+      f32x4 v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int c = c0 + j * 64 + lane;
-          v[j] = c < p.chunks ? src[c] : f32x4{-INFINITY, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          Triple u;
-          u.m = v[j][0];
-          u.idx = __float_as_int(v[j][1]);
-          u.z = v[j][2];
-          t = merge(t, u);
-        }
+      for (int j = 0; j < 8; ++j) {
+        const int c = c0 + j * 64 + lane;
+        v[j] = c < p.chunks ? src[c] : f32x4{-INFINITY, 0.f, 0.f, 0.f};
       }
-      for (int o = 1; o < 64; o <<= 1) t = merge(t, shfl_xor_triple(t, o));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        Triple u;
+        u.m = v[j][0];
+        u.idx = __float_as_int(v[j][1]);
+        u.z = v[j][2];
+        t = merge(t, u);
+      }
     }
+    for (int o = 1; o < 64; o <<= 1) t = merge(t, shfl_xor_triple(t, o));
     if (lane == 0) rows[i] = t;
   }
   __syncthreads();
   const int i = threadIdx.x;
-  commit_decisions(p, b, i, i < p.S ? rows[i] : empty_triple());
+  commit_decisions(p, b, i, i < p.S ? rows[i] : empty_triple(), defer_use(flag));
 }
 
 // ------------------------------------------------------------------ masked-diffusion loss
