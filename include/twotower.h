@@ -221,7 +221,16 @@ typedef struct {
  * Weights W [out_features, in_features] (row-major bf16) are passed in the packed form written by
  * twotower_pack_weight (once, when the weights are loaded). The block's own KV is rewritten every
  * step because the block changes (explainer, "Generierungsprozess").
- * Products accumulate in fp32 and are rounded once to the output type.
+ * Products accumulate in fp32 and are rounded once to the output type. When the output features
+ * alone give too few work-groups to fill the GPU, the input features are split into partitions
+ * whose fp32 partial products are summed in partition order (a fixed order: deterministic). The
+ * sum runs inside the product's kernel when all of its work-groups can be resident on the GPU at
+ * once: the partitions of an output tile meet at an arrival counter in the workspace (a 64-bit
+ * word tagged with the launch, so any prior workspace content is accepted and nothing needs
+ * clearing; graph replays of one captured call find and restart the previous replay's count), and
+ * each then sums an equal share of the tile's rows. The wait is bounded (seconds): a partition
+ * that never arrives turns the rows it would have fed into NaN instead of hanging. Otherwise a
+ * second kernel sums them. Either way the result is the same, bit for bit.
  *
  * Packed weight layout (the A-operand order of the 32x32x16 bf16 matrix instruction): W is cut
  * into slabs of 32 output features (nb < NS = ceil(out_features / 32)) and K steps of 16 inputs

@@ -152,13 +152,14 @@ def test_packed_weight_size_and_validation(L):
 def test_projection_queries_and_errors():
     q = _lib.QkvArgs(8, 16, 2048, 32, 2, 128, FAKE, FAKE, FAKE, FAKE, FAKE)
     st, n = query("twotower_qkv_projection", q)
-    # 72 tiles of 64 features -> K in 3 partitions (one work-group per compute unit): fp32 partials
-    assert st == _lib.TT_OK and n == 3 * 128 * 4608 * 4
+    # 72 tiles of 64 features -> K in 3 partitions (one work-group per compute unit): fp32 partials,
+    # then one arrival counter (a 128-byte line) per tile for the merge inside the kernel
+    assert st == _lib.TT_OK and n == 3 * 128 * 4608 * 4 + 72 * 128
     q.hidden = 2044
     assert query("twotower_qkv_projection", q)[0] == _lib.TT_ENOTSUP
     o = _lib.OutProjArgs(128, 2048, 4096, 0, FAKE, FAKE, FAKE, FAKE)
     st, n = query("twotower_out_projection", o)
-    assert st == _lib.TT_OK and n == 8 * 128 * 2048 * 4   # 32 tiles x 8 K partitions
+    assert st == _lib.TT_OK and n == 8 * 128 * 2048 * 4 + 32 * 128   # 32 tiles x 8 K partitions
     o.o = FAKE + 4
     assert query("twotower_out_projection", o)[0] == _lib.TT_EINVAL
     lm = _lib.LmHeadArgs(128, 2048, 131072, 0, 131072, FAKE, FAKE, FAKE)

@@ -324,3 +324,73 @@ def test_timing_event_hook_skips_null_entries():
     torch.cuda.synchronize()
     assert evs[0].elapsed_time(evs[1]) > 0.0 and evs[2].elapsed_time(evs[3]) > 0.0
     assert np.array_equal(out_a, ref_out) and np.array_equal(out_b, ref_out)
+
+
+# ------------------------------------------------------------- workspace content, graph replays
+
+def _attn_into(case, d, out, lse, workspace=None, **kw):
+    tt.block_attn(d["q"], d["k_pages"], d["v_pages"], d["block_table"], d["ctx_lens"], d["k_blk"],
+                  d["v_blk"], scale=case.scale, max_ctx_len=int(case.ctx_lens.max()), out=out,
+                  return_lse=True, lse_out=lse, workspace=workspace, **kw)
+
+
+def test_attention_output_does_not_depend_on_workspace_content():
+    """The caller's workspace is never cleared: a workspace of arbitrary bytes, all ones, or left
+    over by the previous call gives the same output bit for bit, and it matches the oracle."""
+    case = synth.attn_case(91, B=4, S=16, Hq=32, Hkv=2, D=128, ctx_lens=[4096, 3000, 5000, 100],
+                           page_size=256, dtype="bf16")
+    d = dev_case(case)
+    outs = []
+    ws = torch.empty(32 << 20, dtype=torch.uint8, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(5)
+    for fill in ("random", "ones", "previous", "previous"):
+        if fill == "random":
+            ws.copy_(torch.randint(0, 256, ws.shape, generator=g, device=DEV, dtype=torch.int32)
+                     .to(torch.uint8))
+        elif fill == "ones":
+            ws.fill_(255)
+        out = torch.empty((4, 16, 32, 128), dtype=torch.float32, device=DEV)
+        lse = torch.empty((4, 32, 16), dtype=torch.float32, device=DEV)
+        _attn_into(case, d, out, lse, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)))
+    check(case, outs[0][0], outs[0][1], TOL_BF16)
+    for o, l in outs[1:]:
+        assert np.array_equal(o, outs[0][0]) and np.array_equal(l, outs[0][1])
+
+
+def test_graph_replays_of_the_attention_match_eager_calls():
+    """A captured attention call replayed several times, with eager work in between, and again
+    after the lengths changed on the device (the partitions of every sequence are planned on the
+    device, so they change without a new capture): every replay equals the eager call."""
+    case = synth.attn_case(92, B=4, S=16, Hq=32, Hkv=2, D=128, ctx_lens=[4096, 4096, 4096, 4096],
+                           page_size=256, dtype="bf16")
+    d = dev_case(case)
+    out = torch.empty((4, 16, 32, 128), dtype=torch.float32, device=DEV)
+    lse = torch.empty((4, 32, 16), dtype=torch.float32, device=DEV)
+    _attn_into(case, d, out, lse)                 # eager first: every one-time setup is done
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _attn_into(case, d, out, lse)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+    d["ctx_lens"].copy_(torch.tensor([4096, 900, 2500, 64], dtype=torch.int32, device=DEV))
+    e_out, e_lse = torch.empty_like(out), torch.empty_like(lse)
+    _attn_into(case, d, e_out, e_lse)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, e_out) and torch.equal(lse, e_lse)
+    case.ctx_lens[:] = [4096, 900, 2500, 64]
+    check(case, e_out.cpu().numpy().astype(np.float64), e_lse.cpu().numpy().astype(np.float64),
+          TOL_BF16)

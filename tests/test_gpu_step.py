@@ -93,6 +93,79 @@ def test_out_projection(rows, hidden, inf):
     assert torch.equal(h2, out)
 
 
+def test_projection_merge_needs_no_clean_workspace():
+    """The K partials of the projections are summed inside the product's kernel; its work-groups
+    meet at arrival counters kept in the caller's workspace, which nobody clears. A workspace of
+    arbitrary bytes, all ones, or left over by the previous call (complete counts of another launch)
+    gives the same outputs bit for bit, and they match the oracle."""
+    g = torch.Generator(device=DEV).manual_seed(21)
+    B, S, hidden, Hq, Hkv, D = 8, 16, 2048, 32, 2, 128
+    h = torch.randn((B, S, hidden), generator=g, device=DEV).to(torch.bfloat16)
+    wq = tt.pack_weight((torch.randn(((Hq + 2 * Hkv) * D, hidden), generator=g, device=DEV)
+                         / math.sqrt(hidden)).to(torch.bfloat16))
+    o = torch.randn((B * S, Hq * D), generator=g, device=DEV).to(torch.bfloat16)
+    wo_dense = (torch.randn((hidden, Hq * D), generator=g, device=DEV) / math.sqrt(Hq * D)).to(torch.bfloat16)
+    wo = tt.pack_weight(wo_dense)
+    ws = torch.empty(16 << 20, dtype=torch.uint8, device=DEV)
+    outs = []
+    for fill in ("random", "ones", "previous", "previous"):
+        if fill == "random":
+            ws.copy_(torch.randint(0, 256, ws.shape, generator=g, device=DEV, dtype=torch.int32)
+                     .to(torch.uint8))
+        elif fill == "ones":
+            ws.fill_(255)
+        q, kb, vb = tt.qkv_projection(h, wq, Hq, Hkv, D, workspace=ws)
+        ho = tt.out_projection(h.view(B * S, hidden), o, wo, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (q, kb, vb, ho)])
+    for later in outs[1:]:
+        for a, b in zip(outs[0], later):
+            assert torch.equal(a, b)
+    ref = ostep.residual_output(f64(h.view(B * S, hidden))[:, None], f64(o).reshape(B * S, 1, Hq * D),
+                                f64(wo_dense))[:, 0]
+    ok, err = bf16_ok(f64(outs[0][3]), ref)
+    assert ok, err
+
+
+def test_projection_graph_replays_match_eager_calls():
+    """Both projections captured in one graph (every replay of a captured product carries the same
+    launch tag, so each finds the previous replay's complete arrival counts) and replayed several
+    times, with eager work in between: every replay equals the eager calls bit for bit."""
+    g = torch.Generator(device=DEV).manual_seed(22)
+    B, S, hidden, Hq, Hkv, D = 8, 16, 2048, 32, 2, 128
+    h = torch.randn((B, S, hidden), generator=g, device=DEV).to(torch.bfloat16)
+    wq = tt.pack_weight((torch.randn(((Hq + 2 * Hkv) * D, hidden), generator=g, device=DEV)
+                         / math.sqrt(hidden)).to(torch.bfloat16))
+    o = torch.randn((B * S, Hq * D), generator=g, device=DEV).to(torch.bfloat16)
+    wo = tt.pack_weight((torch.randn((hidden, Hq * D), generator=g, device=DEV)
+                         / math.sqrt(Hq * D)).to(torch.bfloat16))
+    qkv = (torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=DEV),
+           torch.empty((B, Hkv, S, D), dtype=torch.bfloat16, device=DEV),
+           torch.empty((B, Hkv, D, S), dtype=torch.bfloat16, device=DEV))
+    ho = torch.empty((B * S, hidden), dtype=torch.bfloat16, device=DEV)
+
+    def calls():
+        tt.qkv_projection(h, wq, Hq, Hkv, D, out=qkv)
+        tt.out_projection(h.view(B * S, hidden), o, wo, out=ho)
+
+    calls()                               # eager first: every one-time setup is done
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (*qkv, ho)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    for _ in range(3):
+        for t in (*qkv, ho):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((*qkv, ho), ref):
+            assert torch.equal(a, b)
+        calls()                           # eager calls between the replays
+        torch.cuda.synchronize()
+
+
 # (96: 3 slabs of 32 features in 64-feature tiles; 70000: 2188 slabs in 256-feature tiles: the last
 # tile of each reaches past the packed weight and must read nothing there)
 @pytest.mark.parametrize("rows,hidden,V", [(32, 512, 8192), (128, 2048, 131072), (7, 136, 1004),

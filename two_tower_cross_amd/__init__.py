@@ -61,13 +61,19 @@ def _check(t: torch.Tensor, name: str, device, dtype=None, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
 
 
-def _run(name: str, args, device) -> None:
+def _run(name: str, args, device, workspace=None) -> None:
     n = C.c_size_t(0)
     st = _lib.call(name, args, None, n, None)
     if st != _lib.TT_OK:
         raise TwoTowerError(name, st)
     # ws == NULL always means "query": a call that needs no workspace still gets a buffer.
-    ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=device)
+    if workspace is None:
+        ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=device)
+    else:
+        _check(workspace, "workspace", device, torch.uint8, 1)
+        if workspace.numel() < n.value:
+            raise ValueError(f"{name} needs a workspace of {n.value} bytes, got {workspace.numel()}")
+        ws = workspace
     n = C.c_size_t(ws.numel())
     st = _lib.call(name, args, _p(ws), n, _stream())
     if st != _lib.TT_OK:
@@ -116,7 +122,7 @@ def _attn_struct(q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, out, 
 
 def block_attn(q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, *, scale=None,
                max_ctx_len=None, out_dtype=None, return_lse=False, num_splits=0, out=None,
-               lse_out=None, timing_events=None, no_alloc=False):
+               lse_out=None, timing_events=None, no_alloc=False, workspace=None):
     """Denoiser block attention at one layer; returns ``out`` (and ``lse`` [B,Hq,S] fp32).
 
     ``max_ctx_len`` bounds ctx_lens (used to plan the context partitions; default: the page
@@ -126,7 +132,8 @@ def block_attn(q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, *, scal
     after the partition merge; a None entry is not recorded.
     ``no_alloc``: call twotower_block_attn_static (no workspace; the library's per-device scratch);
     nothing is allocated here either, so ``out`` (and ``lse_out`` with ``return_lse``) must be
-    given.
+    given. ``workspace``: a uint8 device tensor used as the call's workspace instead of a new one
+    (at least the size the library asks for; its contents need no initialization).
     """
     dev = q.device
     _check(q, "q", dev, ndim=4)
@@ -174,7 +181,7 @@ def block_attn(q, k_pages, v_pages, block_table, ctx_lens, k_blk, v_blk, *, scal
         if st != _lib.TT_OK:
             raise TwoTowerError("twotower_block_attn_static", st)
     else:
-        _run("twotower_block_attn", a, dev)
+        _run("twotower_block_attn", a, dev, workspace)
     return (out, lse) if return_lse else out
 
 
@@ -254,28 +261,38 @@ def _packed(w, name, device):
     return w
 
 
-def qkv_projection(h, w_qkv, num_q_heads, num_kv_heads, head_dim):
+def qkv_projection(h, w_qkv, num_q_heads, num_kv_heads, head_dim, workspace=None, out=None):
     """[Q | K_blk | V_blk] = H W_qkv^T scattered to q [B,S,Hq,D], k_blk [B,Hkv,S,D],
-    v_blk [B,Hkv,D,S] (bf16). ``w_qkv`` is a PackedWeight or a bf16 tensor (packed here)."""
+    v_blk [B,Hkv,D,S] (bf16). ``w_qkv`` is a PackedWeight or a bf16 tensor (packed here).
+    ``workspace``: a uint8 device tensor used instead of a new one (at least the size the library
+    asks for; any content). ``out``: (q, k_blk, v_blk) tensors to write instead of new ones."""
     dev = h.device
     _check(h, "h", dev, torch.bfloat16, 3)
     w_qkv = _packed(w_qkv, "w_qkv", dev)
     B, S, hidden = h.shape
     if tuple(w_qkv.shape) != ((num_q_heads + 2 * num_kv_heads) * head_dim, hidden):
         raise ValueError("w_qkv shape mismatch")
-    q = torch.empty((B, S, num_q_heads, head_dim), dtype=torch.bfloat16, device=dev)
-    kb = torch.empty((B, num_kv_heads, S, head_dim), dtype=torch.bfloat16, device=dev)
-    vb = torch.empty((B, num_kv_heads, head_dim, S), dtype=torch.bfloat16, device=dev)
+    shapes = ((B, S, num_q_heads, head_dim), (B, num_kv_heads, S, head_dim),
+              (B, num_kv_heads, head_dim, S))
+    if out is None:
+        q, kb, vb = (torch.empty(sh, dtype=torch.bfloat16, device=dev) for sh in shapes)
+    else:
+        q, kb, vb = out
+        for t, sh, name in zip(out, shapes, ("q", "k_blk", "v_blk")):
+            _check(t, name, dev, torch.bfloat16)
+            if tuple(t.shape) != sh:
+                raise ValueError(f"{name} must be {sh}")
     a = _lib.QkvArgs()
     a.batch, a.S, a.hidden = B, S, hidden
     a.num_q_heads, a.num_kv_heads, a.head_dim = num_q_heads, num_kv_heads, head_dim
     a.h, a.w_qkv, a.q, a.k_blk, a.v_blk = _p(h), _p(w_qkv.data), _p(q), _p(kb), _p(vb)
-    _run("twotower_qkv_projection", a, dev)
+    _run("twotower_qkv_projection", a, dev, workspace)
     return q, kb, vb
 
 
-def out_projection(h_in, o, w_o, out=None):
-    """H_out = H_in + O W_o^T (bf16). ``o`` is [..., in_features] with the rows of ``h_in``."""
+def out_projection(h_in, o, w_o, out=None, workspace=None):
+    """H_out = H_in + O W_o^T (bf16). ``o`` is [..., in_features] with the rows of ``h_in``.
+    ``workspace``: as for qkv_projection."""
     dev = h_in.device
     _check(h_in, "h_in", dev, torch.bfloat16)
     _check(o, "o", dev, torch.bfloat16)
@@ -289,7 +306,7 @@ def out_projection(h_in, o, w_o, out=None):
     a = _lib.OutProjArgs()
     a.rows, a.hidden, a.in_features = rows, hidden, inf
     a.h_in, a.o, a.w_o, a.h_out = _p(h_in), _p(o), _p(w_o.data), _p(out)
-    _run("twotower_out_projection", a, dev)
+    _run("twotower_out_projection", a, dev, workspace)
     return out
 
 

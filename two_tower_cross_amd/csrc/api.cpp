@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -32,6 +34,18 @@ struct AttnPlan {
   size_t ws_bytes = 0;
   bool use_bf16 = false;
 };
+
+// Nonzero tag of one launch that merges its K partials inside the kernel (see group_arrive_wait):
+// a process-wide counter, started from the clock so that a workspace left over from another
+// process does not hold the first tags.
+uint32_t next_sync_tag() {
+  static std::atomic<uint32_t> next{
+      static_cast<uint32_t>(std::chrono::steady_clock::now().time_since_epoch().count())};
+  for (;;) {
+    const uint32_t t = next.fetch_add(1, std::memory_order_relaxed);
+    if (t != 0) return t;
+  }
+}
 
 // Balanced plan (see block_attn.hip): the smallest partition size c >= kMinPartTiles (in 64-token
 // tiles) for which B sequences of t tiles need at most `parts` partitions, n = max(1, ceil(t / c))
@@ -264,14 +278,28 @@ void choose_tiling(int M, int N, int K, tt::LinearParams *p) {
   p->ksplit = (int)std::max<int64_t>(1, ks);
 }
 
-size_t linear_ws(const tt::LinearParams &p) {
+// Workspace of a product with K partitions: the fp32 partials, then one arrival counter per output
+// tile for the merge inside the kernel.
+size_t linear_part_bytes(const tt::LinearParams &p) {
   return p.ksplit > 1 ? align_up((size_t)p.ksplit * p.M * p.N * sizeof(float)) : 0;
 }
+size_t linear_sync_bytes(const tt::LinearParams &p) {
+  if (p.ksplit <= 1) return 0;
+  const int64_t tiles = cdiv(p.N, p.wide ? 256 : 64) * cdiv(p.M, 128);
+  return align_up((size_t)tiles * tt::kSyncWords * sizeof(unsigned long long));
+}
+size_t linear_ws(const tt::LinearParams &p) { return linear_part_bytes(p) + linear_sync_bytes(p); }
 
-hipError_t run_linear(tt::LinearParams p, void *ws, hipStream_t stream) {
+// sync: the counters (linear_sync_bytes), or null for the separate merge kernel.
+hipError_t run_linear(tt::LinearParams p, void *ws, void *sync, hipStream_t stream) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
   p.part = static_cast<float *>(ws);
+  p.sync = p.ksplit > 1 ? static_cast<unsigned long long *>(sync) : nullptr;
+  if (p.sync) p.sync_tag = next_sync_tag();
   return tt::launch_linear(p, stream);
+}
+hipError_t run_linear(const tt::LinearParams &p, void *ws, hipStream_t stream) {
+  return run_linear(p, ws, static_cast<char *>(ws) + linear_part_bytes(p), stream);
 }
 
 tt_status plan_qkv(const tt_qkv_args *a, bool check_pointers, tt::LinearParams *p) {
@@ -713,7 +741,12 @@ tt_status twotower_denoise_step(const tt_denoise_step_args *a, void *ws, size_t 
       return TT_EINVAL;
   }
 
-  const size_t need = std::max({ap.ws_bytes, lup.ws_bytes, linear_ws(qp), linear_ws(op)});
+  // The stages share the workspace; the arrival counters of the two products follow everything
+  // they share, each in a region of its own, so that only the counting writes them.
+  const size_t q_sync =
+      std::max({ap.ws_bytes, lup.ws_bytes, linear_part_bytes(qp), linear_part_bytes(op)});
+  const size_t o_sync = q_sync + linear_sync_bytes(qp);
+  const size_t need = o_sync + linear_sync_bytes(op);
   bool launch;
   st = ws_protocol(need, ws, ws_bytes, &launch);
   if (st != TT_OK || !launch) return st;
@@ -726,7 +759,7 @@ tt_status twotower_denoise_step(const tt_denoise_step_args *a, void *ws, size_t 
     qp.w = a->w_qkv[l];
     qp.k_blk = a->k_blk[l];
     qp.v_blk = a->v_blk[l];
-    hipError_t e = run_linear(qp, ws, s);
+    hipError_t e = run_linear(qp, ws, static_cast<char *>(ws) + q_sync, s);
     if (e != hipSuccess) return TT_EHIP;
     AttnPlan al = ap;
     al.p.k_pages = a->k_pages[l];
@@ -742,7 +775,7 @@ tt_status twotower_denoise_step(const tt_denoise_step_args *a, void *ws, size_t 
     if ((e = run_attn(al, ws, s, e0, e1, e2)) != hipSuccess) return TT_EHIP;
     op.residual = h_prev;
     op.w = a->w_o[l];
-    if ((e = run_linear(op, ws, s)) != hipSuccess) return TT_EHIP;
+    if ((e = run_linear(op, ws, static_cast<char *>(ws) + o_sync, s)) != hipSuccess) return TT_EHIP;
   }
   if (run_lm_unmask(lup, ws, s) != hipSuccess) return TT_EHIP;
   return TT_OK;

@@ -70,6 +70,7 @@ __device__ __forceinline__ void st_wt_16(__amdgpu_buffer_rsrc_t r, uint32_t off,
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kWriteThrough);
 }
 
+
 // Returns v unchanged, as the output of an (empty) asm statement at this point of the program:
 // nothing can be computed from v before it, so the wait for the load that produced v is placed
 // here and not right after the load (a flag read at kernel start and used much later).
@@ -143,6 +144,57 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
+}
+
+// Arrival of one work-group of a group of n (1 <= n <= 65535) at the group's counter, then its
+// wait until all n have arrived; called by one thread of the work-group. The counter is a 64-bit
+// word in device memory (alone in its 128-byte line: kSyncWords apart): tag << 32 | n << 16 |
+// count, where `tag` (nonzero) identifies the launch. A word holding another tag or group size, or
+// a complete count, is left over from an earlier launch (or is arbitrary memory): the first member
+// to arrive starts a new round at count 1 with a compare-and-swap, every other member adds 1 (one
+// atomic round trip each, whatever the contention), so the word needs no reset between launches:
+// a new launch brings a new tag, and replays of one recorded launch, which share their tag, find
+// the previous replay's complete count. The member that completes the count waits for nothing;
+// the others poll about every half microsecond.
+// Visibility without cache-wide maintenance (a release or acquire fence at device scope writes back
+// or invalidates this XCD's whole L2, which costs tens of microseconds when 32 work-groups of an
+// XCD do it in turn): what the members exchange is stored write-through (sc1) and every wave of
+// the work-group has waited for its stores to complete (vmcnt 0, then a work-group barrier)
+// before the arrival; after the wait the members read it with device-coherent loads (sc1), which
+// are issued only once the complete count has been observed. The arrival and the polls are
+// device-scope atomics (relaxed: the ordering comes from those completions).
+// Every member of the group must be resident on the GPU at once (the launcher guarantees it); the
+// wait still gives up after kSyncPolls polls (seconds) and then returns false.
+constexpr int kSyncPolls = 1 << 22;
+
+__device__ __forceinline__ bool group_arrive_wait(unsigned long long *ctr, uint32_t tag, int n) {
+  const unsigned long long base =
+      ((unsigned long long)tag << 32) | ((unsigned long long)(uint32_t)n << 16);
+  const unsigned long long done = base | (unsigned long long)n;
+  unsigned long long v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    if ((v & ~0xFFFFull) == base && (v & 0xFFFFull) < (unsigned long long)n) {
+      v = __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+      break;
+    }
+    // left over from before: start this launch's round (v is reloaded when another member did)
+    if (__hip_atomic_compare_exchange_strong(ctr, &v, base + 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)) {
+      v = base + 1;
+      break;
+    }
+  }
+  for (int polls = 0; v != done && polls < kSyncPolls; ++polls) {
+    __builtin_amdgcn_s_sleep(16);
+    v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return v == done;
+}
+
+// Device-coherent (sc1) loads through a buffer resource: they do not hit lines an XCD's L2 or a
+// compute unit's cache may hold from before the data was written.
+__device__ __forceinline__ u32x4 ld_coherent_16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kWriteThrough));
 }
 
 // XOR key of the 16-byte chunk swizzle for LDS rows of 128 bytes: the 8 (32-bank) and 16

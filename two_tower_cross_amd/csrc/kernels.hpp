@@ -123,6 +123,10 @@ struct AppendParams {
 hipError_t launch_kv_append(const AppendParams &p, hipStream_t stream);
 
 // ------------------------------------------------------------------------ skinny bf16 linear
+// Arrival counters of the in-kernel merge of K partials (group_arrive_wait): one 64-bit word per
+// output tile, each in its own 128-byte line.
+constexpr int kSyncWords = 16;
+
 enum Epilogue : int {
   EPI_F32 = 0,       // y fp32 [M, ldy]
   EPI_QKV = 1,       // scatter to q [B,S,Hq,D], k_blk [B,Hkv,S,D], v_blk [B,Hkv,D,S] (bf16)
@@ -152,6 +156,11 @@ struct LinearParams {
   // triples[(m * ceil(N / 256) + t) * 4 + 0..2]; y (fp32 [M, ldy]) is also stored when not null.
   const uint8_t *masked;
   float *triples;
+  // ksplit > 1: the arrival counters of an in-kernel merge of the K partials (one per output tile,
+  // kSyncWords words each, see group_arrive_wait) and the launch's nonzero tag; null, or a grid that cannot be resident
+  // at once: linear_reduce_kernel merges them.
+  unsigned long long *sync;
+  uint32_t sync_tag;
 };
 
 hipError_t launch_linear(const LinearParams &p, hipStream_t stream);

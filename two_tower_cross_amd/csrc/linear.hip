@@ -21,6 +21,7 @@
 // kept: persistent, 256-feature tiles computed in pairs that share each 32-column X chunk, the
 // pairs' chunks as one ring stream).
 #include <algorithm>
+#include <mutex>
 #include <math.h>
 
 #include "common.hpp"
@@ -338,6 +339,39 @@ __device__ void unmask_epilogue(const LinearParams &p, const float *tile, int m0
   }
 }
 
+// Sum of the K partials of outputs (m, n .. n + 3) in partition order, 8 partials requested at a
+// time (clamped loads, no branches, so that they are all in flight together), then the epilogue.
+// With ok false (an in-kernel merge whose wait gave up) the sum is NaN.
+// COHERENT: the partials were written by other work-groups of the same kernel (the in-kernel
+// merge), so they are read with device-coherent loads (sc1) through a resource over the partials
+// (which then span less than 4 GiB).
+template <bool COHERENT>
+__device__ __forceinline__ void reduce_partials4(const LinearParams &p, int m, int n, bool ok) {
+  const float *src = p.part + (size_t)m * p.N + n;
+  const size_t zstride = (size_t)p.M * p.N;
+  const __amdgpu_buffer_rsrc_t pr =
+      buf_rsrc(p.part, COHERENT ? (uint32_t)(p.ksplit * zstride * 4) : 0u);
+  uint2 rr = {0u, 0u};
+  if (p.epi == EPI_RESIDUAL) rr = load_residual4(p, m, n);  // in flight with the partials
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int z0 = 0; z0 < p.ksplit; z0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const size_t e = (size_t)min(z0 + j, p.ksplit - 1) * zstride;
+      if (COHERENT)
+        v[j] = __builtin_bit_cast(f32x4, ld_coherent_16(pr, (uint32_t)(((size_t)m * p.N + n + e) * 4)));
+      else
+        v[j] = *reinterpret_cast<const f32x4 *>(src + e);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (z0 + j < p.ksplit) s = z0 + j == 0 ? v[j] : s + v[j];
+  }
+  if (!ok) s = f32x4{NAN, NAN, NAN, NAN};
+  epilogue4(p, m, n, s, &rr);
+}
+
 // Grid: (ceil(N / (32 NB)), ceil(M / 128), ksplit); the work-group's K range is chunks
 // [z * cpz, min(nch, (z + 1) * cpz)) of the ceil(K / 64) chunks.
 template <int NB>
@@ -468,6 +502,25 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
       st_wt_16(pr, (uint32_t)((r * p.N + nn) * 4), __builtin_bit_cast(u32x4, v));
     else
       epilogue4(p, m, nn, v);
+  }
+  if (p.ksplit > 1 && p.sync) {
+    // Merge of the K partials inside the kernel: once the tile's ksplit work-groups have stored
+    // their partials and arrived at the tile's counter, partition kz sums rows
+    // [kz * rows / ksplit, (kz + 1) * rows / ksplit) of the tile, as linear_reduce_kernel would.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's partial stores have completed
+    __syncthreads();
+    int *sync_ok = reinterpret_cast<int *>(smem + T::LDS - 4);
+    if (tid == 0)
+      sync_ok[0] = group_arrive_wait(p.sync + (blockIdx.x + gridDim.x * blockIdx.y) * kSyncWords, p.sync_tag,
+                                     p.ksplit);
+    __syncthreads();
+    const bool ok = sync_ok[0] != 0;
+    const int rows = min(kLM, p.M - m0);
+    const int lo = kz * rows / p.ksplit, hi = (kz + 1) * rows / p.ksplit;
+    for (int u = tid; u < (hi - lo) * NCH; u += T::THREADS) {
+      const int nn = n0 + (u % NCH) * 4;
+      if (nn < p.N) reduce_partials4<true>(p, m0 + lo + u / NCH, nn, ok);
+    }
   }
   TT_STAMP(4);  // stores issued
   TT_STAMP_DRAINED(5);  // stores done
@@ -730,29 +783,11 @@ __global__ __launch_bounds__(LPair::THREADS) void lm_unmask_kernel(LinearParams 
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
-// Sum of the K partials in partition order, 8 partials requested at a time (clamped loads, no
-// branches, so that they are all in flight together).
 __global__ __launch_bounds__(256) void linear_reduce_kernel(LinearParams p) {
   const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
   const size_t total = (size_t)p.M * (p.N / 4);
   if (e >= total) return;
-  const int m = (int)(e / (p.N / 4));
-  const int n = (int)(e % (p.N / 4)) * 4;
-  const float *src = p.part + (size_t)m * p.N + n;
-  const size_t zstride = (size_t)p.M * p.N;
-  uint2 rr = {0u, 0u};
-  if (p.epi == EPI_RESIDUAL) rr = load_residual4(p, m, n);  // in flight with the partials
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  for (int z0 = 0; z0 < p.ksplit; z0 += 8) {
-    f32x4 v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      v[j] = *reinterpret_cast<const f32x4 *>(src + (size_t)min(z0 + j, p.ksplit - 1) * zstride);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (z0 + j < p.ksplit) s = z0 + j == 0 ? v[j] : s + v[j];
-  }
-  epilogue4(p, m, n, s, &rr);
+  reduce_partials4<false>(p, (int)(e / (p.N / 4)), (int)(e % (p.N / 4)) * 4, true);
 }
 
 template <int NB>
@@ -792,12 +827,45 @@ static hipError_t launch_lm_unmask(const LinearParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_linear(const LinearParams &p, hipStream_t stream) {
-  if (p.epi == EPI_UNMASK && p.y == nullptr) return launch_lm_unmask(p, stream);
+// Whether every work-group of launch_tile<NB>'s grid for p can be resident on the current device at
+// once (occupancy at the tile's LDS size times the compute units): the condition for merging the K
+// partials inside the kernel.
+template <int NB>
+static bool tile_grid_resident(const LinearParams &p) {
+  using T = LTile<NB>;
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int64_t cap[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cap[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&linear_kernel<NB>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, linear_kernel<NB>, T::THREADS,
+                                                     T::LDS) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return false;
+    const int64_t c = (int64_t)per_cu * cus;
+    cap[dev] = c > 0 ? c : -1;  // -1: not even one (never merged inside)
+  }
+  const int64_t grid =
+      (int64_t)((p.N + T::N - 1) / T::N) * ((p.M + kLM - 1) / kLM) * p.ksplit;
+  return grid <= cap[dev];
+}
+
+hipError_t launch_linear(const LinearParams &p_in, hipStream_t stream) {
+  if (p_in.epi == EPI_UNMASK && p_in.y == nullptr) return launch_lm_unmask(p_in, stream);
+  LinearParams p = p_in;
+  // merged inside the kernel: the grid resident at once, the partials addressable by 32-bit offsets
+  if (p.ksplit == 1 || (size_t)p.ksplit * p.M * p.N * 4 >= ((size_t)1 << 32) ||
+      !(p.wide ? tile_grid_resident<8>(p) : tile_grid_resident<2>(p)))
+    p.sync = nullptr;
   const int nch = (p.K + kLK - 1) / kLK;
   const int cpz = (nch + p.ksplit - 1) / p.ksplit;
   hipError_t e = p.wide ? launch_tile<8>(p, stream, cpz) : launch_tile<2>(p, stream, cpz);
-  if (e != hipSuccess || p.ksplit == 1) return e;
+  if (e != hipSuccess || p.ksplit == 1 || p.sync) return e;
   const size_t total = (size_t)p.M * (p.N / 4);
   hipLaunchKernelGGL(linear_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
                      stream, p);
