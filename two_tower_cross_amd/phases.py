@@ -4,10 +4,13 @@ Loads the profiling build (``python -m two_tower_cross_amd.build --phase-stamps`
 sources compiled with TT_PHASE_STAMPS, where wave 0 of every work-group stamps the 100 MHz wall
 clock at each phase of its kernel) instead of the product library, runs the block attention at the
 32K-context layer (batch 8, Hq 32 / Hkv 2, head_dim 128, automatic partitions) and at a single
-131072-token context (automatic and 64 partitions), and the QKV and output projections at the block
-loop's shape (128 rows, hidden 2048, Q width 4096), each call after a 1 GiB write so that nothing is
-served from the last-level cache, and writes the phase percentiles over the work-groups of the
-last of six calls as markdown.
+131072-token context (automatic and 64 partitions), each call after a 1 GiB write so that nothing
+is served from the last-level cache, and the QKV and output projections at the block loop's shape
+(128 rows, hidden 2048, Q width 4096), each call after a 1 GiB non-temporal read, as in the block
+loop between two uses of a layer's weights (the KV caches and the lm-head weight are read
+non-temporally): the caches of the XCDs hold nothing useful, while the weights may stay in the
+last-level cache. Writes the phase percentiles over the work-groups of the last of six calls as
+markdown.
 
 Usage (on an MI355X): ``python -m two_tower_cross_amd.phases OUT.md 'COMMAND'``.
 """
@@ -40,7 +43,7 @@ LINEAR_PHASES = [
     ("until chunk 0 has landed", 0, 1),
     ("K loop", 1, 2),
     ("drain of the last loads, barrier", 2, 3),
-    ("issuing the stores", 3, 4),
+    ("partial stores, arrival and wait, merge of a share of the tile's rows", 3, 4),
     ("until the stores are done", 4, 5),
     ("end", None, 5),
 ]
@@ -103,16 +106,22 @@ def main(argv):
               "`python -m two_tower_cross_amd.build --phase-stamps`):", "", f"    {command}", "",
               "Phases from wall_clock64 stamps of wave 0 of every work-group, relative to the "
               "earliest work-group start of the call (the last of six calls, each right after a 1 GiB "
-              "write on the same stream); the event-timed call (fence-free events, the launch "
-              "from Python included) adds dispatch and drain.", ""]
+              "write on the same stream for the attention, a 1 GiB non-temporal read for the "
+              "projections); the event-timed call (fence-free events, the launch from Python "
+              "included) adds dispatch and drain.", ""]
 
-    def timed(call, clear):
-        # stamps cleared, then the 1 GiB write and the call back to back on the stream (the
-        # compute units are awake, as in the block loop)
+    sink = torch.zeros(2048, dtype=torch.int32, device=dev)
+
+    def timed(call, clear, nt_read=False):
+        # stamps cleared, then the 1 GiB write (or non-temporal read) and the call back to back on
+        # the stream (the compute units are awake, as in the block loop)
         us = 0.0
         for it in range(6):
             clear(None, 0, 1)
-            scrub.fill_(it)
+            if nt_read:
+                tt.probe_stream_read(scrub, 2048, sink)
+            else:
+                scrub.fill_(it)
             ev[0].record()
             call()
             ev[1].record()
@@ -153,11 +162,12 @@ def main(argv):
     wq = tt.pack_weight((torch.randn(((Hq + 2 * Hkv) * D, H), generator=g, device=dev) * 0.02).to(bf))
     wo = tt.pack_weight((torch.randn((H, Hq * D), generator=g, device=dev) * 0.02).to(bf))
     o = torch.randn((B, S, Hq, D), generator=g, device=dev).to(bf)
-    for title, call in [("QKV projection: 128 x 4608 x 2048 (K split in 3; the K-partial merge "
-                         "is a second kernel)", lambda: tt.qkv_projection(h, wq, Hq, Hkv, D)),
-                        ("Output projection: 128 x 2048 x 4096 (K split in 8; the merge with "
-                         "the residual is a second kernel)", lambda: tt.out_projection(h, o, wo))]:
-        us = timed(call, lin_f)
+    for title, call in [("QKV projection: 128 x 4608 x 2048 (K split in 3, the K partials "
+                         "merged inside the kernel)", lambda: tt.qkv_projection(h, wq, Hq, Hkv, D)),
+                        ("Output projection: 128 x 2048 x 4096 (K split in 8, the K partials "
+                         "and the residual merged inside the kernel)",
+                         lambda: tt.out_projection(h, o, wo))]:
+        us = timed(call, lin_f, nt_read=True)
         rows = _read(lin_f)
         lines, cyc, span = _table(rows, LINEAR_PHASES, title, us)
         clock = np.median(cyc / np.maximum(span[:, 5] - span[:, 0], 1e-3)) / 1e3
