@@ -230,7 +230,12 @@ typedef struct {
  * clearing; graph replays of one captured call find and restart the previous replay's count), and
  * each then sums an equal share of the tile's rows. The wait is bounded (seconds): a partition
  * that never arrives turns the rows it would have fed into NaN instead of hanging. Otherwise a
- * second kernel sums them. Either way the result is the same, bit for bit.
+ * second kernel sums them. Either way the result is the same, bit for bit. Because the merge
+ * inside the kernel needs all of the product's work-groups on the GPU at once, two such products
+ * running at the same time on one device (different streams) can each hold compute units that the
+ * other's work-groups wait for: both then stall until the wait gives up. Order the products of a
+ * device on one stream, or set the environment variable TWOTOWER_MERGE_IN_KERNEL=0 (read at every
+ * call) to have the second kernel sum the partials.
  *
  * Packed weight layout (the A-operand order of the 32x32x16 bf16 matrix instruction): W is cut
  * into slabs of 32 output features (nb < NS = ceil(out_features / 32)) and K steps of 16 inputs

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <cstdlib>
 
 #include "../../include/twotower.h"
 #include "kernels.hpp"
@@ -290,11 +291,20 @@ size_t linear_sync_bytes(const tt::LinearParams &p) {
 }
 size_t linear_ws(const tt::LinearParams &p) { return linear_part_bytes(p) + linear_sync_bytes(p); }
 
+// Whether K partials may be merged inside the product kernel: yes unless the environment sets
+// TWOTOWER_MERGE_IN_KERNEL=0 (read at every call), for processes that run products on several
+// streams of one device at once (see include/twotower.h).
+bool merge_in_kernel_allowed() {
+  const char *v = std::getenv("TWOTOWER_MERGE_IN_KERNEL");
+  return !(v && v[0] == '0' && v[1] == '\0');
+}
+
 // sync: the counters (linear_sync_bytes), or null for the separate merge kernel.
 hipError_t run_linear(tt::LinearParams p, void *ws, void *sync, hipStream_t stream) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
   p.part = static_cast<float *>(ws);
-  p.sync = p.ksplit > 1 ? static_cast<unsigned long long *>(sync) : nullptr;
+  p.sync = p.ksplit > 1 && merge_in_kernel_allowed() ? static_cast<unsigned long long *>(sync)
+                                                     : nullptr;
   if (p.sync) p.sync_tag = next_sync_tag();
   return tt::launch_linear(p, stream);
 }
