@@ -225,17 +225,16 @@ typedef struct {
  * alone give too few work-groups to fill the GPU, the input features are split into partitions
  * whose fp32 partial products are summed in partition order (a fixed order: deterministic). The
  * sum runs inside the product's kernel when all of its work-groups can be resident on the GPU at
- * once: the partitions of an output tile meet at an arrival counter in the workspace (a 64-bit
- * word tagged with the launch, so any prior workspace content is accepted and nothing needs
- * clearing; graph replays of one captured call find and restart the previous replay's count), and
- * each then sums an equal share of the tile's rows. The wait is bounded (seconds): a partition
- * that never arrives turns the rows it would have fed into NaN instead of hanging. Otherwise a
- * second kernel sums them. Either way the result is the same, bit for bit. Because the merge
- * inside the kernel needs all of the product's work-groups on the GPU at once, two such products
- * running at the same time on one device (different streams) can each hold compute units that the
- * other's work-groups wait for: both then stall until the wait gives up. Order the products of a
- * device on one stream, or set the environment variable TWOTOWER_MERGE_IN_KERNEL=0 (read at every
- * call) to have the second kernel sum the partials.
+ * once and K has at most 16 partitions: the partitions of an output tile meet at an arrival
+ * counter in the workspace (a 64-bit word tagged with the launch, so any prior workspace content is
+ * accepted and nothing needs clearing; graph replays of one captured call find and restart the
+ * previous replay's count), and each then sums an equal share of the tile's rows. A partition that
+ * has waited about 0.4 ms for the others (they cannot all be resident, e.g. while another kernel
+ * holds compute units) hands its share to the last one to arrive and leaves, so no partition
+ * waits for one that cannot run; the environment variable TWOTOWER_MERGE_WAIT_POLLS (read at every
+ * call, default 256 polls of about 1.5 us) sets that wait. Otherwise, or with
+ * TWOTOWER_MERGE_IN_KERNEL=0 in the environment (read at every call), a second kernel sums the
+ * partials. Every way gives the same result, bit for bit.
  *
  * Packed weight layout (the A-operand order of the 32x32x16 bf16 matrix instruction): W is cut
  * into slabs of 32 output features (nb < NS = ceil(out_features / 32)) and K steps of 16 inputs

@@ -128,8 +128,11 @@ def test_projection_merge_needs_no_clean_workspace():
 
 
 def test_projection_merge_inside_equals_separate_merge_kernel(monkeypatch):
-    """The K partials summed inside the product kernel and by the separate merge kernel
-    (TWOTOWER_MERGE_IN_KERNEL=0) give the same outputs bit for bit: one sum, in partition order."""
+    """The K partials summed inside the product kernel (each partition its share of the rows), by
+    the last partition to arrive after every other one handed its share over
+    (TWOTOWER_MERGE_WAIT_POLLS=0: the path taken when partitions cannot all be resident) and by the
+    separate merge kernel (TWOTOWER_MERGE_IN_KERNEL=0) give the same outputs bit for bit: one sum,
+    in partition order."""
     g = torch.Generator(device=DEV).manual_seed(23)
     for B, S, hidden, Hq, Hkv, D in ((8, 16, 2048, 32, 2, 128), (3, 5, 264, 4, 1, 64)):
         h = torch.randn((B, S, hidden), generator=g, device=DEV).to(torch.bfloat16)
@@ -139,14 +142,16 @@ def test_projection_merge_inside_equals_separate_merge_kernel(monkeypatch):
         wo = tt.pack_weight((torch.randn((hidden, Hq * D), generator=g, device=DEV)
                              / math.sqrt(Hq * D)).to(torch.bfloat16))
         outs = []
-        for flag in ("1", "0"):
-            monkeypatch.setenv("TWOTOWER_MERGE_IN_KERNEL", flag)
+        for inside, polls in (("1", "256"), ("1", "0"), ("0", "256")):
+            monkeypatch.setenv("TWOTOWER_MERGE_IN_KERNEL", inside)
+            monkeypatch.setenv("TWOTOWER_MERGE_WAIT_POLLS", polls)
             q, kb, vb = tt.qkv_projection(h, wq, Hq, Hkv, D)
             ho = tt.out_projection(h.view(B * S, hidden), o, wo)
             torch.cuda.synchronize()
             outs.append((q, kb, vb, ho))
-        for a, b in zip(*outs):
-            assert torch.equal(a, b)
+        for other in outs[1:]:
+            for a, b in zip(outs[0], other):
+                assert torch.equal(a, b)
 
 
 def test_projection_graph_replays_match_eager_calls():

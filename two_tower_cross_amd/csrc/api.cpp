@@ -36,7 +36,7 @@ struct AttnPlan {
   bool use_bf16 = false;
 };
 
-// Nonzero tag of one launch that merges its K partials inside the kernel (see group_arrive_wait):
+// Nonzero tag of one launch that merges its K partials inside the kernel (see group_arrive):
 // a process-wide counter, started from the clock so that a workspace left over from another
 // process does not hold the first tags.
 uint32_t next_sync_tag() {
@@ -292,11 +292,23 @@ size_t linear_sync_bytes(const tt::LinearParams &p) {
 size_t linear_ws(const tt::LinearParams &p) { return linear_part_bytes(p) + linear_sync_bytes(p); }
 
 // Whether K partials may be merged inside the product kernel: yes unless the environment sets
-// TWOTOWER_MERGE_IN_KERNEL=0 (read at every call), for processes that run products on several
-// streams of one device at once (see include/twotower.h).
+// TWOTOWER_MERGE_IN_KERNEL=0 (read at every call).
 bool merge_in_kernel_allowed() {
   const char *v = std::getenv("TWOTOWER_MERGE_IN_KERNEL");
   return !(v && v[0] == '0' && v[1] == '\0');
+}
+
+// Polls (about 1.5 us each) after which a partition of the in-kernel merge hands its share to the
+// last one to arrive: TWOTOWER_MERGE_WAIT_POLLS (read at every call; 0 hands every share over at
+// once), default 256. In a normal launch the partitions of a tile arrive within a few polls.
+constexpr int kDefaultMergeWaitPolls = 256;
+int merge_wait_polls() {
+  const char *v = std::getenv("TWOTOWER_MERGE_WAIT_POLLS");
+  if (!v || !*v) return kDefaultMergeWaitPolls;
+  char *end = nullptr;
+  const long n = std::strtol(v, &end, 10);
+  if (*end != '\0' || n < 0) return kDefaultMergeWaitPolls;
+  return (int)std::min<long>(n, 1L << 20);
 }
 
 // sync: the counters (linear_sync_bytes), or null for the separate merge kernel.
@@ -305,7 +317,10 @@ hipError_t run_linear(tt::LinearParams p, void *ws, void *sync, hipStream_t stre
   p.part = static_cast<float *>(ws);
   p.sync = p.ksplit > 1 && merge_in_kernel_allowed() ? static_cast<unsigned long long *>(sync)
                                                      : nullptr;
-  if (p.sync) p.sync_tag = next_sync_tag();
+  if (p.sync) {
+    p.sync_tag = next_sync_tag();
+    p.sync_polls = merge_wait_polls();
+  }
   return tt::launch_linear(p, stream);
 }
 hipError_t run_linear(const tt::LinearParams &p, void *ws, hipStream_t stream) {

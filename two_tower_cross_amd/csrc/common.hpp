@@ -146,49 +146,62 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// Arrival of one work-group of a group of n (1 <= n <= 65535) at the group's counter, then its
-// wait until all n have arrived; called by one thread of the work-group. The counter is a 64-bit
-// word in device memory (alone in its 128-byte line: kSyncWords apart): tag << 32 | n << 16 |
-// count, where `tag` (nonzero) identifies the launch. A word holding another tag or group size, or
-// a complete count, is left over from an earlier launch (or is arbitrary memory): the first member
-// to arrive starts a new round at count 1 with a compare-and-swap, every other member adds 1 (one
+// Arrival of member s of a group of n work-groups (1 <= n <= 16) at the group's counter, called by
+// one thread of the work-group once every store of the work-group that the others read has
+// completed. Returns the set of shares (bit i: share i) this work-group must merge: its own share
+// once every member has arrived, plus, for the member that completes the count, the shares of
+// members that gave up waiting; 0 when it gave up itself. No member waits for anything that might
+// never run: a member that has polled max_polls times without seeing the count complete hands its
+// share over and leaves, so the group finishes even when its members cannot all be resident at
+// once (another kernel holding compute units, on another stream), only more slowly.
+// The counter is a 64-bit word in device memory (alone in its 128-byte line): tag << 32 |
+// given-up mask << 16 | count, where `tag` (nonzero) identifies the launch. A word holding another
+// tag, or a complete count, is left over from an earlier launch (or is arbitrary memory): the first
+// member to arrive starts a new round with a compare-and-swap, every other member adds 1 (one
 // atomic round trip each, whatever the contention), so the word needs no reset between launches:
 // a new launch brings a new tag, and replays of one recorded launch, which share their tag, find
-// the previous replay's complete count. The member that completes the count waits for nothing;
-// the others poll about every half microsecond.
+// the previous replay's complete count. A member gives up with a compare-and-swap that sets its
+// bit only while the count is incomplete, so the completing member's add returns every bit set
+// before it; a give-up that loses that race finds the count complete and merges its own share.
 // Visibility without cache-wide maintenance (a release or acquire fence at device scope writes back
 // or invalidates this XCD's whole L2, which costs tens of microseconds when 32 work-groups of an
 // XCD do it in turn): what the members exchange is stored write-through (sc1) and every wave of
 // the work-group has waited for its stores to complete (vmcnt 0, then a work-group barrier)
-// before the arrival; after the wait the members read it with device-coherent loads (sc1), which
-// are issued only once the complete count has been observed. The arrival and the polls are
-// device-scope atomics (relaxed: the ordering comes from those completions).
-// Every member of the group must be resident on the GPU at once (the launcher guarantees it); the
-// wait still gives up after kSyncPolls polls (seconds) and then returns false.
-constexpr int kSyncPolls = 1 << 22;
-
-__device__ __forceinline__ bool group_arrive_wait(unsigned long long *ctr, uint32_t tag, int n) {
-  const unsigned long long base =
-      ((unsigned long long)tag << 32) | ((unsigned long long)(uint32_t)n << 16);
-  const unsigned long long done = base | (unsigned long long)n;
+// before the arrival; the merging work-groups read it with device-coherent loads (sc1), issued
+// only once the complete count has been observed. The arrival and the polls are device-scope
+// atomics (relaxed: the ordering comes from those completions).
+__device__ __forceinline__ uint32_t group_arrive(unsigned long long *ctr, uint32_t tag, int n, int s,
+                                                 int max_polls) {
+  const unsigned long long base = (unsigned long long)tag << 32;
+  const unsigned long long nn = (unsigned long long)n;
   unsigned long long v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (;;) {
-    if ((v & ~0xFFFFull) == base && (v & 0xFFFFull) < (unsigned long long)n) {
+    if ((v >> 32) == tag && (v & 0xFFFFull) < nn) {
       v = __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
       break;
     }
     // left over from before: start this launch's round (v is reloaded when another member did)
-    if (__hip_atomic_compare_exchange_strong(ctr, &v, base + 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT)) {
-      v = base + 1;
+    if (__hip_atomic_compare_exchange_strong(ctr, &v, base | 1ull, __ATOMIC_RELAXED,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+      v = base | 1ull;
       break;
     }
   }
-  for (int polls = 0; v != done && polls < kSyncPolls; ++polls) {
+  const uint32_t own = 1u << s;
+  if ((v & 0xFFFFull) == nn) return own | (uint32_t)((v >> 16) & 0xFFFFull);  // completed it
+  for (int polls = 0;;) {
+    if ((v & 0xFFFFull) == nn) return own;  // every member has arrived
+    if (polls >= max_polls) {
+      // hand the share to the member that completes the count (a failed swap reloads v)
+      if (__hip_atomic_compare_exchange_strong(ctr, &v, v | (1ull << (16 + s)), __ATOMIC_RELAXED,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        return 0;
+      continue;
+    }
     __builtin_amdgcn_s_sleep(16);
     v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ++polls;
   }
-  return v == done;
 }
 
 // Device-coherent (sc1) loads through a buffer resource: they do not hit lines an XCD's L2 or a

@@ -123,8 +123,8 @@ struct AppendParams {
 hipError_t launch_kv_append(const AppendParams &p, hipStream_t stream);
 
 // ------------------------------------------------------------------------ skinny bf16 linear
-// Arrival counters of the in-kernel merge of K partials (group_arrive_wait): one 64-bit word per
-// output tile, each in its own 128-byte line.
+// Arrival counters of the in-kernel merge of K partials (group_arrive): one 64-bit word per output
+// tile, each in its own 128-byte line.
 constexpr int kSyncWords = 16;
 
 enum Epilogue : int {
@@ -157,10 +157,12 @@ struct LinearParams {
   const uint8_t *masked;
   float *triples;
   // ksplit > 1: the arrival counters of an in-kernel merge of the K partials (one per output tile,
-  // kSyncWords words each, see group_arrive_wait) and the launch's nonzero tag; null, or a grid that cannot be resident
+  // kSyncWords words each, see group_arrive), the launch's nonzero tag and the polls after which a
+  // partition hands its share to the last one to arrive; null, or a grid that cannot be resident
   // at once: linear_reduce_kernel merges them.
   unsigned long long *sync;
   uint32_t sync_tag;
+  int sync_polls;
 };
 
 hipError_t launch_linear(const LinearParams &p, hipStream_t stream);

@@ -347,12 +347,11 @@ __device__ void unmask_epilogue(const LinearParams &p, const float *tile, int m0
 
 // Sum of the K partials of outputs (m, n .. n + 3) in partition order, 8 partials requested at a
 // time (clamped loads, no branches, so that they are all in flight together), then the epilogue.
-// With ok false (an in-kernel merge whose wait gave up) the sum is NaN.
 // COHERENT: the partials were written by other work-groups of the same kernel (the in-kernel
 // merge), so they are read with device-coherent loads (sc1) through a resource over the partials
 // (which then span less than 4 GiB).
 template <bool COHERENT>
-__device__ __forceinline__ void reduce_partials4(const LinearParams &p, int m, int n, bool ok) {
+__device__ __forceinline__ void reduce_partials4(const LinearParams &p, int m, int n) {
   const float *src = p.part + (size_t)m * p.N + n;
   const size_t zstride = (size_t)p.M * p.N;
   const __amdgpu_buffer_rsrc_t pr =
@@ -374,7 +373,6 @@ __device__ __forceinline__ void reduce_partials4(const LinearParams &p, int m, i
     for (int j = 0; j < 8; ++j)
       if (z0 + j < p.ksplit) s = z0 + j == 0 ? v[j] : s + v[j];
   }
-  if (!ok) s = f32x4{NAN, NAN, NAN, NAN};
   epilogue4(p, m, n, s, &rr);
 }
 
@@ -512,20 +510,23 @@ __global__ __launch_bounds__(LTile<NB>::THREADS) void linear_kernel(LinearParams
   if (p.ksplit > 1 && p.sync) {
     // Merge of the K partials inside the kernel: once the tile's ksplit work-groups have stored
     // their partials and arrived at the tile's counter, partition kz sums rows
-    // [kz * rows / ksplit, (kz + 1) * rows / ksplit) of the tile, as linear_reduce_kernel would.
+    // [kz * rows / ksplit, (kz + 1) * rows / ksplit) of the tile, as linear_reduce_kernel would
+    // (and the shares of partitions that gave up waiting, when it is the last to arrive).
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's partial stores have completed
     __syncthreads();
-    int *sync_ok = reinterpret_cast<int *>(smem + T::LDS - 4);
+    uint32_t *shares = reinterpret_cast<uint32_t *>(smem + T::LDS - 4);
     if (tid == 0)
-      sync_ok[0] = group_arrive_wait(p.sync + (blockIdx.x + gridDim.x * blockIdx.y) * kSyncWords, p.sync_tag,
-                                     p.ksplit);
+      shares[0] = group_arrive(p.sync + (blockIdx.x + gridDim.x * blockIdx.y) * kSyncWords,
+                               p.sync_tag, p.ksplit, kz, p.sync_polls);
     __syncthreads();
-    const bool ok = sync_ok[0] != 0;
     const int rows = min(kLM, p.M - m0);
-    const int lo = kz * rows / p.ksplit, hi = (kz + 1) * rows / p.ksplit;
-    for (int u = tid; u < (hi - lo) * NCH; u += T::THREADS) {
-      const int nn = n0 + (u % NCH) * 4;
-      if (nn < p.N) reduce_partials4<true>(p, m0 + lo + u / NCH, nn, ok);
+    for (uint32_t left = __builtin_amdgcn_readfirstlane(shares[0]); left != 0; left &= left - 1) {
+      const int sh = __builtin_ctz(left);
+      const int lo = sh * rows / p.ksplit, hi = (sh + 1) * rows / p.ksplit;
+      for (int u = tid; u < (hi - lo) * NCH; u += T::THREADS) {
+        const int nn = n0 + (u % NCH) * 4;
+        if (nn < p.N) reduce_partials4<true>(p, m0 + lo + u / NCH, nn);
+      }
     }
   }
   TT_STAMP(4);  // stores issued
@@ -793,7 +794,7 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(LinearParams p) {
   const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
   const size_t total = (size_t)p.M * (p.N / 4);
   if (e >= total) return;
-  reduce_partials4<false>(p, (int)(e / (p.N / 4)), (int)(e % (p.N / 4)) * 4, true);
+  reduce_partials4<false>(p, (int)(e / (p.N / 4)), (int)(e % (p.N / 4)) * 4);
 }
 
 template <int NB>
@@ -864,8 +865,10 @@ static bool tile_grid_resident(const LinearParams &p) {
 hipError_t launch_linear(const LinearParams &p_in, hipStream_t stream) {
   if (p_in.epi == EPI_UNMASK && p_in.y == nullptr) return launch_lm_unmask(p_in, stream);
   LinearParams p = p_in;
-  // merged inside the kernel: the grid resident at once, the partials addressable by 32-bit offsets
-  if (p.ksplit == 1 || (size_t)p.ksplit * p.M * p.N * 4 >= ((size_t)1 << 32) ||
+  // merged inside the kernel: at most 16 partitions (the counter's mask), the grid resident at
+  // once (else the partitions would mostly hand their shares over), the partials addressable by
+  // 32-bit offsets
+  if (p.ksplit == 1 || p.ksplit > 16 || (size_t)p.ksplit * p.M * p.N * 4 >= ((size_t)1 << 32) ||
       !(p.wide ? tile_grid_resident<8>(p) : tile_grid_resident<2>(p)))
     p.sync = nullptr;
   const int nch = (p.K + kLK - 1) / kLK;
