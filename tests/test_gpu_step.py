@@ -154,6 +154,32 @@ def test_projection_merge_inside_equals_separate_merge_kernel(monkeypatch):
                 assert torch.equal(a, b)
 
 
+def test_projections_on_two_streams_at_once():
+    """Two output projections launched at the same time on two streams (each grid fills the GPU,
+    so their work-groups share the compute units and a tile's partitions need not all be resident
+    at once): both finish, and each equals the same call made alone, bit for bit."""
+    g = torch.Generator(device=DEV).manual_seed(24)
+    rows, hidden, inf = 128, 2048, 4096
+    wo = tt.pack_weight((torch.randn((hidden, inf), generator=g, device=DEV) / math.sqrt(inf))
+                        .to(torch.bfloat16))
+    hs = [torch.randn((rows, hidden), generator=g, device=DEV).to(torch.bfloat16) for _ in range(2)]
+    os_ = [torch.randn((rows, inf), generator=g, device=DEV).to(torch.bfloat16) for _ in range(2)]
+    refs = [tt.out_projection(h, o, wo) for h, o in zip(hs, os_)]
+    outs = [torch.empty_like(r) for r in refs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for _ in range(5):
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        for st, h, o, out in zip(streams, hs, os_, outs):
+            with torch.cuda.stream(st):
+                tt.out_projection(h, o, wo, out=out)
+        torch.cuda.synchronize()
+        for out, ref in zip(outs, refs):
+            assert torch.equal(out, ref)
+
+
 def test_projection_graph_replays_match_eager_calls():
     """Both projections captured in one graph (every replay of a captured product carries the same
     launch tag, so each finds the previous replay's complete arrival counts) and replayed several
