@@ -14,8 +14,10 @@
 //     second ring, 16-byte chunks XOR-swizzled per 128-byte row, deep enough to cover the L2
 //     latency under load;
 //   * Y^T = W X^T with 32x32x16 bf16 MFMA in fp32; the W operand reads are lane-contiguous.
-// When N alone gives too few work-groups to fill the GPU, K is also partitioned (fp32 partials,
-// written through to memory, + one reduce pass, fixed summation order, no atomics).
+// When N alone gives too few work-groups to fill the GPU, K is also partitioned: fp32 partials,
+// written through to memory and summed in partition order (no floating-point atomics), inside the
+// product kernel once a tile's partitions have arrived at its counter (each sums a share of the
+// tile's rows), or by a second kernel.
 // Epilogues: fp32 store (logits), Q/K/V scatter into the attention layouts (bf16), residual add
 // (bf16), and the unmasking triples of the lm-head (lm_unmask_kernel when the logits are not
 // kept: persistent, 256-feature tiles computed in pairs that share each 32-column X chunk, the
