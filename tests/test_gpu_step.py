@@ -60,8 +60,10 @@ def test_pack_weight_matches_the_documented_layout(N, K):
     assert got.shape == ref.shape and np.array_equal(got, ref)
 
 
+# (3, 100, 1024, 2, 1, 48): 300 rows in three 128-row tiles, 192 features in three tiles, K in 4
+# parts merged inside the kernel
 @pytest.mark.parametrize("shape", [(2, 16, 512, 8, 2, 128), (8, 16, 2048, 32, 2, 128),
-                                   (3, 5, 264, 4, 1, 64)])
+                                   (3, 5, 264, 4, 1, 64), (3, 100, 1024, 2, 1, 48)])
 def test_qkv_projection(shape):
     B, S, hidden, Hq, Hkv, D = shape
     g = torch.Generator(device=DEV).manual_seed(11)
@@ -75,7 +77,9 @@ def test_qkv_projection(shape):
         assert ok, err
 
 
-@pytest.mark.parametrize("rows,hidden,inf", [(32, 512, 1024), (128, 2048, 4096), (80, 264, 136)])
+# (300, 200, 1024): three row tiles, the last feature tile 8 wide, K in 4 parts merged inside
+@pytest.mark.parametrize("rows,hidden,inf", [(32, 512, 1024), (128, 2048, 4096), (80, 264, 136),
+                                             (300, 200, 1024)])
 def test_out_projection(rows, hidden, inf):
     g = torch.Generator(device=DEV).manual_seed(12)
     h = torch.randn((rows, hidden), generator=g, device=DEV).to(torch.bfloat16)
