@@ -30,6 +30,12 @@
  *   TT_EHIP means a HIP launch failed; asynchronous device faults surface at the caller's next
  *   synchronization.
  * - Results are deterministic: fixed reduction order, no floating-point atomics.
+ * - An empty batch (batch = 0; rows = 0 for the row-wise products) is a valid call: the sizes are
+ *   still checked, no workspace is needed, nothing is launched (timing events included) and the
+ *   call returns TT_OK. Its device pointers may then be NULL (as PyTorch gives for empty
+ *   tensors); host arrays, such as the step's per-layer pointer arrays, must still be given.
+ *   Outputs that do not scale with the batch (twotower_masked_nll's loss and n_masked,
+ *   twotower_kv_append's free_count and status) are left as they are.
  * - Calls that share a workspace must be ordered on one stream.
  */
 #ifndef TWOTOWER_H

@@ -319,3 +319,56 @@ def test_static_attention_entry_validates_before_touching_the_device(L):
     # 8 x 2 units x 256 partitions x 256 rows x (256 + 8) B = 276 MB of partials
     assert f(C.byref(attn_args(num_splits=256)), None) == _lib.TT_ENOSPACE
     assert _lib.STATIC_SCRATCH_BYTES == 32 << 20
+
+
+def run_empty(name, a):
+    """Size query, then a run with a (never dereferenced) workspace pointer: both TT_OK with 0
+    bytes; the run returns before any HIP call, so it needs no device."""
+    st, n = query(name, a)
+    assert (st, n) == (_lib.TT_OK, 0), (name, _lib.status_string(st), n)
+    m = C.c_size_t(0)
+    st = _lib.call(name, a, C.c_void_p(FAKE), m, None)
+    assert st == _lib.TT_OK, (name, _lib.status_string(st))
+
+
+def test_empty_batch_is_a_no_op_with_null_device_pointers():
+    """batch = 0 (rows = 0): sizes still checked, no workspace, nothing launched, TT_OK, and the
+    device pointers may be NULL (as PyTorch's empty tensors give); a nonzero batch still needs
+    them."""
+    nulls = dict(q=None, k_pages=None, v_pages=None, k_blk=None, v_blk=None, out=None,
+                 block_table=None, ctx_lens=None)
+    run_empty("twotower_block_attn", attn_args(batch=0, **nulls))
+    assert _lib.lib().twotower_block_attn_static(C.byref(attn_args(batch=0, **nulls)), None) == \
+        _lib.TT_OK
+    assert query("twotower_block_attn", attn_args(batch=0, S=0, **nulls))[0] == _lib.TT_EINVAL
+    assert query("twotower_block_attn", attn_args(batch=1, **nulls))[0] == _lib.TT_EINVAL
+    run_empty("twotower_unmask", unmask_args(batch=0, logits=None, masked=None, tokens=None))
+    assert query("twotower_unmask", unmask_args(batch=1, tokens=None))[0] == _lib.TT_EINVAL
+    run_empty("twotower_qkv_projection", _lib.QkvArgs(0, 16, 2048, 32, 2, 128, None, None, None,
+                                                      None, None))
+    run_empty("twotower_out_projection", _lib.OutProjArgs(0, 2048, 4096, 0, None, None, None, None))
+    run_empty("twotower_lm_head", _lib.LmHeadArgs(0, 2048, 131072, 0, 131072, None, None, None))
+    lu = lm_unmask_args(lm__rows=0, lm__h=None, lm__w_lm=None, lm__logits=None, unmask__batch=0,
+                        unmask__masked=None, unmask__tokens=None)
+    run_empty("twotower_lm_head_unmask", lu)
+    run_empty("twotower_mask_corrupt",
+              _lib.MaskCorruptArgs(0, 16, 131071, 0, None, None, None, None, None, None))
+    run_empty("twotower_masked_nll",
+              _lib.MaskedNllArgs(0, 16, 131072, 0, 131072, None, None, None, None, None, None))
+    empty = (C.c_void_p * 6)()   # host arrays of null layer pointers
+    vpp = C.POINTER(C.c_void_p)
+    ap = append_args(batch=0, block_table=None, ctx_lens=None, free_pages=None, free_count=None,
+                     status=None, **{f: C.cast(empty, vpp) for f in ("k_pages", "v_pages", "k_new",
+                                                                    "v_new")})
+    run_empty("twotower_kv_append", ap)
+    ap.k_pages = None                        # the host arrays themselves are still required
+    assert query("twotower_kv_append", ap)[0] == _lib.TT_EINVAL
+    s = _lib.DenoiseStepArgs()
+    s.num_layers, s.hidden, s.vocab = 6, 2048, 131072
+    s.attn = attn_args(batch=0, **nulls)
+    for f in ("k_pages", "v_pages", "w_qkv", "w_o", "k_blk", "v_blk"):
+        setattr(s, f, C.cast(empty, vpp))
+    s.unmask = unmask_args(batch=0, logits=None, masked=None, tokens=None)
+    run_empty("twotower_denoise_step", s)
+    s.attn = attn_args(batch=1, **nulls)
+    assert query("twotower_denoise_step", s)[0] == _lib.TT_EINVAL

@@ -6,6 +6,7 @@ KV at every layer, attends to the resident context caches and commits confident 
 with the oracle fed the GPU's own inputs for that stage; the step is compared bit for bit with the
 composition of the per-stage entry points; the loop is checked by its invariants.
 """
+import itertools
 import math
 
 import numpy as np
@@ -430,10 +431,11 @@ def test_full_size_loop_32k_one_block():
     t = tokens.cpu().numpy()
     assert ((t >= 0) & (t < m.vocab)).all()
     assert checksum(m.k_pages[:1] + m.v_pages[-1:]) == before
-    # last layer's attention (its q and block KV are still in the step's buffers), sampled (b, g)
+    # last layer's attention (its q and block KV are still in the step's buffers), every (b, g)
     l = m.layers - 1
-    for b, g in ((0, 0), (5, 1)):
-        heads = slice(g * 16, (g + 1) * 16)
+    for b, g in itertools.product(range(m.B), range(m.Hkv)):
+        G = m.Hq // m.Hkv
+        heads = slice(g * G, (g + 1) * G)
         ref, _ = oattn.block_attention(
             f64(step.q[b:b + 1, :, heads]), f64(m.k_pages[l][b:b + 1, g:g + 1]),
             f64(m.v_pages[l][b:b + 1, g:g + 1]), np.zeros((1, 1), np.int32),
@@ -442,7 +444,7 @@ def test_full_size_loop_32k_one_block():
         ref16 = torch.from_numpy(ref).to(torch.bfloat16).double().numpy()
         assert max_abs(f64(step.attn_out[b:b + 1, :, heads]), ref16) <= TOL_BF16
     # lm-head on the final residual stream, sampled vocabulary columns
-    cols = np.sort(synth.rng(15).choice(m.vocab, size=2048, replace=False))
+    cols = np.sort(synth.rng(15).choice(m.vocab, size=8192, replace=False))
     ref = ostep.lm_head(f64(step.h_work), f64(m.w_lm[torch.from_numpy(cols).to(DEV)]))
     got = f64(step.logits)[..., cols]
     assert max_abs(got, ref) <= 1e-4 + 1e-5 * np.abs(ref).max()
@@ -479,3 +481,58 @@ def test_block_sizes_of_the_pages(S):
             f64(step.v_blk[l][b:b + 1, g:g + 1]), 1.0 / math.sqrt(m.D))
         ref16 = torch.from_numpy(ref).to(torch.bfloat16).double().numpy()
         assert max_abs(f64(step.attn_out[b:b + 1, :, heads]), ref16) <= TOL_BF16
+
+
+def test_empty_batch_through_every_entry_point():
+    """A batch of 0 sequences (PyTorch's empty tensors: null data pointers) is a no-op for every
+    call: empty results, no error, no launch; the caches and pools stay as they are."""
+    bf, i32, u8, f32 = torch.bfloat16, torch.int32, torch.uint8, torch.float32
+    S, Hq, Hkv, D, hidden, V, page = 16, 8, 2, 64, 512, 1000, 64
+    g = torch.Generator(device=DEV).manual_seed(21)
+    kp = torch.randn(tt.k_pages_shape(3, Hkv, page, D), generator=g, device=DEV).to(bf)
+    vp = torch.randn(tt.v_pages_shape(3, Hkv, page, D), generator=g, device=DEV).to(bf)
+    before = (kp.clone(), vp.clone())
+    out = tt.block_attn(torch.empty((0, S, Hq, D), dtype=bf, device=DEV), kp, vp,
+                        torch.empty((0, 2), dtype=i32, device=DEV),
+                        torch.empty((0,), dtype=i32, device=DEV),
+                        torch.empty((0, Hkv, S, D), dtype=bf, device=DEV),
+                        torch.empty((0, Hkv, D, S), dtype=bf, device=DEV))
+    assert tuple(out.shape) == (0, S, Hq, D)
+    conf, ncom = tt.unmask(torch.empty((0, S, V), dtype=f32, device=DEV),
+                           torch.empty((0, S), dtype=u8, device=DEV),
+                           torch.empty((0, S), dtype=i32, device=DEV), 0.9, min_commit=True)
+    assert conf.numel() == 0 and ncom.numel() == 0
+    w_qkv = (torch.randn(((Hq + 2 * Hkv) * D, hidden), generator=g, device=DEV) / 16).to(bf)
+    q, kb, vb = tt.qkv_projection(torch.empty((0, S, hidden), dtype=bf, device=DEV), w_qkv, Hq,
+                                  Hkv, D)
+    assert q.numel() == kb.numel() == vb.numel() == 0
+    w_o = (torch.randn((hidden, Hq * D), generator=g, device=DEV) / 16).to(bf)
+    h = tt.out_projection(torch.empty((0, hidden), dtype=bf, device=DEV),
+                          torch.empty((0, Hq * D), dtype=bf, device=DEV), w_o)
+    assert tuple(h.shape) == (0, hidden)
+    w_lm = (torch.randn((V, hidden), generator=g, device=DEV) / 16).to(bf)
+    assert tuple(tt.lm_head(torch.empty((0, S, hidden), dtype=bf, device=DEV), w_lm).shape) == \
+        (0, S, V)
+    for keep in (False, True):
+        c, n, lg = tt.lm_head_unmask(torch.empty((0, S, hidden), dtype=bf, device=DEV), w_lm,
+                                     torch.empty((0, S), dtype=u8, device=DEV),
+                                     torch.empty((0, S), dtype=i32, device=DEV), 0.9,
+                                     keep_logits=keep)
+        assert c.numel() == 0 and n.numel() == 0 and (lg is None or lg.numel() == 0)
+    noisy, masked, t = tt.mask_corrupt(torch.empty((0, S), dtype=i32, device=DEV),
+                                       torch.empty((0,), dtype=f32, device=DEV),
+                                       torch.empty((0, S), dtype=f32, device=DEV), V)
+    assert noisy.numel() == masked.numel() == t.numel() == 0
+    nll, loss, count = tt.masked_nll(torch.empty((0, S, V), dtype=f32, device=DEV),
+                                     torch.empty((0, S), dtype=i32, device=DEV),
+                                     torch.empty((0, S), dtype=u8, device=DEV))
+    assert nll.numel() == 0 and loss.item() == 0.0 and count.item() == 0
+    free_count = torch.tensor([3], dtype=i32, device=DEV)
+    status = torch.zeros((1,), dtype=i32, device=DEV)
+    tt.kv_append([kp], [vp], [torch.empty((0, Hkv, S, D), dtype=bf, device=DEV)],
+                 [torch.empty((0, Hkv, D, S), dtype=bf, device=DEV)],
+                 torch.empty((0, 2), dtype=i32, device=DEV), torch.empty((0,), dtype=i32, device=DEV),
+                 torch.arange(3, dtype=i32, device=DEV), free_count, status)
+    torch.cuda.synchronize()
+    assert free_count.item() == 3 and status.item() == 0
+    assert torch.equal(kp, before[0]) and torch.equal(vp, before[1])

@@ -446,8 +446,9 @@ def masked_nll(logits, targets, masked):
     if tuple(targets.shape) != (B, S) or tuple(masked.shape) != (B, S):
         raise ValueError("masked_nll shape mismatch")
     nll = torch.empty((B, S), dtype=torch.float32, device=dev)
-    loss = torch.empty((1,), dtype=torch.float32, device=dev)
-    count = torch.empty((1,), dtype=torch.int32, device=dev)
+    # zeros: the values of an empty batch (for which the library launches nothing)
+    loss = torch.zeros((1,), dtype=torch.float32, device=dev)
+    count = torch.zeros((1,), dtype=torch.int32, device=dev)
     a = _lib.MaskedNllArgs()
     a.batch, a.S, a.vocab, a.ld = B, S, V, logits.stride(1)
     a.logits, a.targets, a.masked = _p(logits), _p(targets), _p(masked)

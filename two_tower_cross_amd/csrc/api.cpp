@@ -92,7 +92,7 @@ tt_status plan_attn(const tt_block_attn_args *a, bool check_pointers, AttnPlan *
   // 64-token tiles of either pool are indexed with 32-bit integers
   if ((int64_t)a->num_pages * a->num_kv_heads * (a->page_size / 64) > INT32_MAX) return TT_ENOTSUP;
   if (a->out_dtype != TT_FP32 && a->out_dtype != a->dtype) return TT_ENOTSUP;
-  if (check_pointers) {
+  if (check_pointers && a->batch > 0) {  // an empty batch reads and writes nothing
     const void *p16[] = {a->q, a->k_pages, a->v_pages, a->k_blk, a->v_blk, a->out};
     for (const void *p : p16)
       if (!p || !aligned(p, 16)) return TT_EINVAL;
@@ -162,7 +162,7 @@ tt_status plan_attn(const tt_block_attn_args *a, bool check_pointers, AttnPlan *
   if (p.splits > 65535 || (int64_t)p.B * p.Hkv * p.row_groups > 65535) return TT_ENOTSUP;
   if (p.balanced && (int64_t)p.items * groups * 8 > INT32_MAX) return TT_ENOTSUP;
   out->ws_bytes = 0;
-  if (attn_needs_merge(p)) {
+  if (p.B > 0 && attn_needs_merge(p)) {
     const size_t items = attn_slots(p);
     out->ws_bytes = align_up(items * p.rows_per_group * p.D * sizeof(uint16_t)) +
                     align_up(items * p.rows_per_group * 2 * sizeof(float)) +
@@ -226,10 +226,12 @@ tt_status plan_unmask(const tt_unmask_args *a, bool check_logits, UnmaskPlan *ou
   if (a->batch < 0 || a->S < 1 || a->vocab < 1 || a->ld < a->vocab) return TT_EINVAL;
   if (std::isnan(a->threshold)) return TT_EINVAL;
   if (a->S > max_S) return TT_ENOTSUP;
-  if (check_logits && (!a->logits || !aligned(a->logits, 4))) return TT_EINVAL;
-  if (!a->masked || !a->tokens || !aligned(a->tokens, 4)) return TT_EINVAL;
-  if (a->confidence && !aligned(a->confidence, 4)) return TT_EINVAL;
-  if (a->n_committed && !aligned(a->n_committed, 4)) return TT_EINVAL;
+  if (a->batch > 0) {  // an empty batch reads and writes nothing
+    if (check_logits && (!a->logits || !aligned(a->logits, 4))) return TT_EINVAL;
+    if (!a->masked || !a->tokens || !aligned(a->tokens, 4)) return TT_EINVAL;
+    if (a->confidence && !aligned(a->confidence, 4)) return TT_EINVAL;
+    if (a->n_committed && !aligned(a->n_committed, 4)) return TT_EINVAL;
+  }
   tt::UnmaskParams &p = out->p;
   p.logits = a->logits;
   p.ld = a->ld;
@@ -268,6 +270,11 @@ bool linear_fits(int64_t M, int64_t K) {
 
 void choose_tiling(int M, int N, int K, tt::LinearParams *p) {
   const int64_t mt = cdiv(M, 128);
+  if (mt == 0) {  // no rows: nothing is launched
+    p->wide = 0;
+    p->ksplit = 1;
+    return;
+  }
   p->wide = cdiv(N, 256) * mt >= kTargetWorkgroups ? 1 : 0;
   if (p->wide) {
     p->ksplit = 1;
@@ -333,7 +340,7 @@ tt_status plan_qkv(const tt_qkv_args *a, bool check_pointers, tt::LinearParams *
       a->head_dim < 1)
     return TT_EINVAL;
   if (a->hidden % 8 != 0 || a->head_dim % 4 != 0) return TT_ENOTSUP;
-  if (check_pointers) {
+  if (check_pointers && a->batch > 0) {
     if (!a->h || !a->w_qkv || !aligned(a->h, 16) || !aligned(a->w_qkv, 16)) return TT_EINVAL;
     if (!a->q || !a->k_blk || !a->v_blk || !aligned(a->q, 8) || !aligned(a->k_blk, 8) ||
         !aligned(a->v_blk, 2))
@@ -362,7 +369,7 @@ tt_status plan_out(const tt_out_proj_args *a, bool check_pointers, tt::LinearPar
   if (!a) return TT_EINVAL;
   if (a->rows < 0 || a->hidden < 1 || a->in_features < 1) return TT_EINVAL;
   if (a->hidden % 4 != 0 || a->in_features % 8 != 0) return TT_ENOTSUP;
-  if (check_pointers) {
+  if (check_pointers && a->rows > 0) {
     if (!a->h_in || !a->o || !a->w_o || !a->h_out) return TT_EINVAL;
     if (!aligned(a->o, 16) || !aligned(a->w_o, 16) || !aligned(a->h_in, 8) || !aligned(a->h_out, 8))
       return TT_EINVAL;
@@ -385,7 +392,7 @@ tt_status plan_lm(const tt_lm_head_args *a, bool check_pointers, tt::LinearParam
   if (!a) return TT_EINVAL;
   if (a->rows < 0 || a->hidden < 1 || a->vocab < 1 || a->ld < a->vocab) return TT_EINVAL;
   if (a->hidden % 8 != 0 || a->vocab % 4 != 0 || a->ld % 4 != 0) return TT_ENOTSUP;
-  if (check_pointers) {
+  if (check_pointers && a->rows > 0) {
     if (!a->h || !a->w_lm || !a->logits) return TT_EINVAL;
     if (!aligned(a->h, 16) || !aligned(a->w_lm, 16) || !aligned(a->logits, 16)) return TT_EINVAL;
   }
@@ -417,7 +424,7 @@ tt_status plan_lm_unmask(const tt_lm_head_unmask_args *a, bool check_pointers, L
   if (l.rows < 0 || l.hidden < 1 || l.vocab < 1) return TT_EINVAL;
   if (l.hidden % 8 != 0 || l.vocab % 4 != 0) return TT_ENOTSUP;
   if (l.logits && (l.ld < l.vocab || l.ld % 4 != 0)) return l.ld < l.vocab ? TT_EINVAL : TT_ENOTSUP;
-  if (check_pointers) {
+  if (check_pointers && l.rows > 0) {
     if (!l.h || !l.w_lm || !aligned(l.h, 16) || !aligned(l.w_lm, 16)) return TT_EINVAL;
     if (l.logits && !aligned(l.logits, 16)) return TT_EINVAL;
   }
@@ -476,15 +483,17 @@ tt_status plan_append(const tt_kv_append_args *a, tt::AppendParams *p, size_t *w
   if ((int64_t)a->max_pages_per_seq * a->page_size > INT32_MAX ||
       (int64_t)a->batch * a->max_pages_per_seq > INT32_MAX || a->batch > 65535)
     return TT_ENOTSUP;
-  if (!a->k_pages || !a->v_pages || !a->k_new || !a->v_new) return TT_EINVAL;
-  if (!a->block_table || !a->ctx_lens || !a->free_pages || !a->free_count || !a->status)
+  if (!a->k_pages || !a->v_pages || !a->k_new || !a->v_new) return TT_EINVAL;  // host arrays
+  // an empty batch reads and writes nothing: its device pointers may be null
+  const bool work = a->batch > 0;
+  if (work && (!a->block_table || !a->ctx_lens || !a->free_pages || !a->free_count || !a->status))
     return TT_EINVAL;
   const uintptr_t es = a->dtype == TT_BF16 ? 2 : 4;
   *p = tt::AppendParams{};
   for (int l = 0; l < a->num_layers; ++l) {
     const void *ptrs[] = {a->k_pages[l], a->v_pages[l], a->k_new[l], a->v_new[l]};
     for (const void *q : ptrs)
-      if (!q || !aligned(q, es)) return TT_EINVAL;
+      if (work && (!q || !aligned(q, es))) return TT_EINVAL;
     p->k_pages[l] = a->k_pages[l];
     p->v_pages[l] = a->v_pages[l];
     p->k_new[l] = a->k_new[l];
@@ -504,7 +513,7 @@ tt_status plan_append(const tt_kv_append_args *a, tt::AppendParams *p, size_t *w
   p->max_pages = a->max_pages_per_seq;
   p->num_pages = a->num_pages;
   p->elem_bytes = (int)es;
-  *ws_bytes = align_up((size_t)std::max(a->batch, 1) * sizeof(int32_t));
+  *ws_bytes = align_up((size_t)a->batch * sizeof(int32_t));
   return TT_OK;
 }
 
@@ -614,11 +623,13 @@ tt_status twotower_mask_corrupt(const tt_mask_corrupt_args *a, void *ws, size_t 
   if (!a) return TT_EINVAL;
   if (a->batch < 0 || a->S < 1) return TT_EINVAL;
   if ((int64_t)a->batch * a->S > INT32_MAX / 2) return TT_ENOTSUP;
-  if (!a->clean || !a->u_time || !a->u_mask || !a->noisy || !a->masked) return TT_EINVAL;
-  const void *p4[] = {a->clean, a->u_time, a->u_mask, a->noisy};
-  for (const void *q : p4)
-    if (!aligned(q, 4)) return TT_EINVAL;
-  if (a->t_out && !aligned(a->t_out, 4)) return TT_EINVAL;
+  if (a->batch > 0) {  // an empty batch reads and writes nothing
+    if (!a->clean || !a->u_time || !a->u_mask || !a->noisy || !a->masked) return TT_EINVAL;
+    const void *p4[] = {a->clean, a->u_time, a->u_mask, a->noisy};
+    for (const void *q : p4)
+      if (!aligned(q, 4)) return TT_EINVAL;
+    if (a->t_out && !aligned(a->t_out, 4)) return TT_EINVAL;
+  }
   bool launch;
   tt_status st = ws_protocol(0, ws, ws_bytes, &launch);
   if (st != TT_OK || !launch || a->batch == 0) return st;
@@ -638,9 +649,11 @@ tt_status twotower_mask_corrupt(const tt_mask_corrupt_args *a, void *ws, size_t 
 tt_status twotower_masked_nll(const tt_masked_nll_args *a, void *ws, size_t *ws_bytes,
                               void *stream) {
   if (!a) return TT_EINVAL;
-  if (!a->targets || !a->nll || !aligned(a->targets, 4) || !aligned(a->nll, 4)) return TT_EINVAL;
-  if ((a->loss && !aligned(a->loss, 4)) || (a->n_masked && !aligned(a->n_masked, 4)))
-    return TT_EINVAL;
+  if (a->batch > 0) {  // an empty batch reads and writes nothing
+    if (!a->targets || !a->nll || !aligned(a->targets, 4) || !aligned(a->nll, 4)) return TT_EINVAL;
+    if ((a->loss && !aligned(a->loss, 4)) || (a->n_masked && !aligned(a->n_masked, 4)))
+      return TT_EINVAL;
+  }
   // the row reduction is the unmasking's: reuse its plan (masked rows, chunk triples)
   tt_unmask_args ua{};
   ua.batch = a->batch;
@@ -699,8 +712,10 @@ tt_status twotower_denoise_step(const tt_denoise_step_args *a, void *ws, size_t 
   const tt_block_attn_args &g = a->attn;
   if (g.dtype != TT_BF16) return TT_ENOTSUP;
   if (!a->k_pages || !a->v_pages || !a->w_qkv || !a->w_o || !a->k_blk || !a->v_blk)
+    return TT_EINVAL;  // host arrays
+  // an empty batch reads and writes nothing: its device pointers may be null
+  if (g.batch > 0 && (!a->w_lm || !a->h_in || !a->h_work || !a->q || !a->attn_out))
     return TT_EINVAL;
-  if (!a->w_lm || !a->h_in || !a->h_work || !a->q || !a->attn_out) return TT_EINVAL;
 
   // Plan every stage once (layer 0's pointers; the geometry is shared by all layers).
   tt_block_attn_args ga = g;
@@ -758,7 +773,7 @@ tt_status twotower_denoise_step(const tt_denoise_step_args *a, void *ws, size_t 
   LmUnmaskPlan lup;
   if ((st = plan_lm_unmask(&lu, true, &lup)) != TT_OK) return st;
 
-  for (int l = 0; l < a->num_layers; ++l) {
+  for (int l = 0; l < a->num_layers && g.batch > 0; ++l) {
     const void *p16[] = {a->k_pages[l], a->v_pages[l], a->w_qkv[l], a->w_o[l]};
     for (const void *p : p16)
       if (!p || !aligned(p, 16)) return TT_EINVAL;
