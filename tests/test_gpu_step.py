@@ -406,6 +406,53 @@ def run_block(m, step, threshold=0.9, count_slices=False):
     return masked, tokens, per_step, [h.cpu().numpy() for h in history]
 
 
+def test_block_of_steps_replays_from_a_graph_like_eager_calls():
+    """The T steps of a block captured in one graph (the library records no memset and allocates
+    nothing per call) replay bit for bit like eager calls: commits, counts, confidence and the
+    residual stream, on every replay, with the program's own eager work in between."""
+    m = small_model(seed=8)
+    step = make_step(m)
+    masked = torch.ones((m.B, m.S), dtype=torch.uint8, device=DEV)
+    tokens = torch.full((m.B, m.S), -1, dtype=torch.int32, device=DEV)
+    counts = torch.zeros((m.T, m.B), dtype=torch.int32, device=DEV)
+
+    def steps():
+        for t in range(m.T):
+            step(m.h_steps[t], masked, tokens, threshold=0.9, min_commit=True,
+                 commit_all=(t == m.T - 1), n_committed=counts[t])
+
+    def reset():
+        masked.fill_(1)
+        tokens.fill_(-1)
+        counts.fill_(-7)
+
+    def state():
+        return [x.clone() for x in (masked, tokens, counts, step.confidence, step.h_work)]
+
+    reset()
+    steps()
+    torch.cuda.synchronize()
+    ref = state()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        reset()
+        steps()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    reset()
+    with torch.cuda.graph(graph):
+        steps()
+    for _ in range(3):
+        reset()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = state()
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b)
+        assert not masked.any()
+
 def test_block_loop_invariants_small():
     m = small_model(seed=6)
     before = checksum(m.k_pages + m.v_pages)
