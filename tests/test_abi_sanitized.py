@@ -2,7 +2,7 @@
 
 api.cpp (argument checks, partition planning, workspace sizing, struct tables) is built with g++
 and both sanitizers, the device launchers replaced by stubs (csrc/host_stubs.cpp), and the whole
-host-side ABI test file runs against it in a child process with the sanitizer runtime preloaded:
+host-side ABI test files (the checks and the argument fuzzing) run against it in a child process with the sanitizer runtime preloaded:
 any out-of-bounds access, use after free or undefined behaviour in that code fails the test.
 """
 import os
@@ -34,7 +34,8 @@ def test_host_abi_under_address_and_undefined_behaviour_sanitizers():
                ASAN_OPTIONS="detect_leaks=0:halt_on_error=1:abort_on_error=0",
                UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-s", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_abi.py")],
+                        os.path.join(ROOT, "tests", "test_abi.py"),
+                        os.path.join(ROOT, "tests", "test_abi_fuzz.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     out = r.stdout + r.stderr
     assert r.returncode == 0, out[-4000:]

@@ -265,7 +265,8 @@ hipError_t run_unmask(UnmaskPlan &pl, void *ws, hipStream_t stream) {
 // X is addressed through a buffer resource with 32-bit byte offsets, and a group of 8 packed
 // weight slabs too.
 bool linear_fits(int64_t M, int64_t K) {
-  return M * K * 2 <= INT32_MAX && 8 * cdiv(K, 16) * 1024 <= INT32_MAX;
+  if (M < 0 || K < 1 || M > INT32_MAX || K > INT32_MAX) return false;
+  return M * K <= INT32_MAX / 2 && 8 * cdiv(K, 16) * 1024 <= INT32_MAX;
 }
 
 void choose_tiling(int M, int N, int K, tt::LinearParams *p) {
@@ -347,11 +348,13 @@ tt_status plan_qkv(const tt_qkv_args *a, bool check_pointers, tt::LinearParams *
       return TT_EINVAL;
   }
   if (!linear_fits((int64_t)a->batch * a->S, a->hidden)) return TT_ENOTSUP;
+  const int64_t n = ((int64_t)a->num_q_heads + 2 * (int64_t)a->num_kv_heads) * a->head_dim;
+  if (n > INT32_MAX) return TT_ENOTSUP;
   *p = tt::LinearParams{};
   p->x = a->h;
   p->w = a->w_qkv;
   p->M = a->batch * a->S;
-  p->N = (a->num_q_heads + 2 * a->num_kv_heads) * a->head_dim;
+  p->N = (int)n;
   p->K = a->hidden;
   p->epi = tt::EPI_QKV;
   p->q = a->q;
