@@ -250,6 +250,32 @@ def test_shapes_fp32(S, Hq, Hkv, D):
     check(case, out, lse, TOL_FP32)
 
 
+def _random_attn(seed):
+    """A seeded random configuration within the documented limits: ragged paged contexts
+    (empty ones included), any block size up to 256, GQA groups, both head sizes, page sizes that
+    are multiples of 64, and a partition count."""
+    g = np.random.default_rng(seed)
+    hkv = int(g.integers(1, 4))
+    B = int(g.integers(1, 7))
+    return dict(B=B, S=int(g.choice([1, 2, 5, 16, 17, 31, 48, 64, 100, 128, 200, 256])),
+                Hq=hkv * int(g.integers(1, 9)), Hkv=hkv, D=int(g.choice([64, 128])),
+                ctx_lens=[int(x) for x in g.integers(0, 1500, size=B)],
+                page_size=int(g.choice([64, 128, 192, 256, 512])),
+                dtype="bf16" if g.random() < 0.75 else "fp32",
+                splits=int(g.choice([0, 1, 2, 5])))
+
+
+@pytest.mark.parametrize("seed", range(90, 102))
+def test_random_shapes_within_the_limits(seed):
+    cfg = _random_attn(seed)
+    splits = cfg.pop("splits")
+    dtype = cfg["dtype"]
+    case = synth.attn_case(seed, shuffle_pages=True, spare_frac=0.25, **cfg)
+    for s in sorted({0, splits}):
+        out, lse = gpu_attn(case, num_splits=s)
+        check(case, out, lse, TOL_BF16 if dtype == "bf16" else TOL_FP32)
+
+
 def test_empty_context_and_tiny_tails():
     case = synth.attn_case(80, B=4, S=16, Hq=32, Hkv=2, D=128, ctx_lens=[0, 1, 63, 65],
                            page_size=64, dtype="bf16", nan_poison=True, spare_frac=1.0)

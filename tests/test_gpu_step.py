@@ -61,10 +61,32 @@ def test_pack_weight_matches_the_documented_layout(N, K):
     assert got.shape == ref.shape and np.array_equal(got, ref)
 
 
+def random_shapes(seed, n, draw):
+    """n shapes drawn by draw(generator), seeded: the same every run."""
+    g = np.random.default_rng(seed)
+    return [draw(g) for _ in range(n)]
+
+
+def _ri(g, lo, hi):
+    return int(g.integers(lo, hi + 1))
+
+
+# batch, S, hidden (multiple of 8), Hq = G Hkv, Hkv, head_dim (multiple of 4)
+RANDOM_QKV = random_shapes(31, 6, lambda g: (lambda hkv: (_ri(g, 1, 4), _ri(g, 1, 40),
+                                                          8 * _ri(g, 1, 160), hkv * _ri(g, 1, 8),
+                                                          hkv, 4 * _ri(g, 1, 32)))(_ri(g, 1, 3)))
+# rows, hidden (multiple of 4), in_features (multiple of 8)
+RANDOM_OUT = random_shapes(32, 6, lambda g: (_ri(g, 1, 300), 4 * _ri(g, 1, 300),
+                                             8 * _ri(g, 1, 200)))
+# rows, hidden (multiple of 8), vocab (multiple of 4)
+RANDOM_LM = random_shapes(33, 6, lambda g: (_ri(g, 1, 200), 8 * _ri(g, 1, 100),
+                                            4 * _ri(g, 1, 5000)))
+
+
 # (3, 100, 1024, 2, 1, 48): 300 rows in three 128-row tiles, 192 features in three tiles, K in 4
-# parts merged inside the kernel
+# parts merged inside the kernel; then seeded random shapes within the documented limits
 @pytest.mark.parametrize("shape", [(2, 16, 512, 8, 2, 128), (8, 16, 2048, 32, 2, 128),
-                                   (3, 5, 264, 4, 1, 64), (3, 100, 1024, 2, 1, 48)])
+                                   (3, 5, 264, 4, 1, 64), (3, 100, 1024, 2, 1, 48)] + RANDOM_QKV)
 def test_qkv_projection(shape):
     B, S, hidden, Hq, Hkv, D = shape
     g = torch.Generator(device=DEV).manual_seed(11)
@@ -80,7 +102,7 @@ def test_qkv_projection(shape):
 
 # (300, 200, 1024): three row tiles, the last feature tile 8 wide, K in 4 parts merged inside
 @pytest.mark.parametrize("rows,hidden,inf", [(32, 512, 1024), (128, 2048, 4096), (80, 264, 136),
-                                             (300, 200, 1024)])
+                                             (300, 200, 1024)] + RANDOM_OUT)
 def test_out_projection(rows, hidden, inf):
     g = torch.Generator(device=DEV).manual_seed(12)
     h = torch.randn((rows, hidden), generator=g, device=DEV).to(torch.bfloat16)
@@ -227,7 +249,7 @@ def test_projection_graph_replays_match_eager_calls():
 # (96: 3 slabs of 32 features in 64-feature tiles; 70000: 2188 slabs in 256-feature tiles: the last
 # tile of each reaches past the packed weight and must read nothing there)
 @pytest.mark.parametrize("rows,hidden,V", [(32, 512, 8192), (128, 2048, 131072), (7, 136, 1004),
-                                           (5, 128, 96), (128, 256, 70000)])
+                                           (5, 128, 96), (128, 256, 70000)] + RANDOM_LM)
 def test_lm_head(rows, hidden, V):
     g = torch.Generator(device=DEV).manual_seed(13)
     h = torch.randn((rows, hidden), generator=g, device=DEV).to(torch.bfloat16)
