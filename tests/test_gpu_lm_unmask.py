@@ -102,6 +102,23 @@ CASES = [
 ]
 
 
+def _random_cases(seed, n):
+    """Seeded random cases within the documented limits (the same every run)."""
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        out.append((int(g.integers(1, 9)), int(g.choice([1, 5, 16, 33, 64, 100])),
+                    8 * int(g.integers(8, 65)), 4 * int(g.integers(25, 5001)),
+                    float(g.choice([2.0, 3.0, 4.0, 5.0])),
+                    float(g.choice([0.05, 0.1, 0.2, 0.3, 0.5, 0.9])),
+                    float(g.choice([0.0, 0.2, 0.5])), bool(g.random() < 0.8),
+                    bool(g.random() < 0.15)))
+    return out
+
+
+CASES += _random_cases(41, 6)
+
+
 @pytest.mark.parametrize("keep", [True, False], ids=["logits", "no-logits"])
 @pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}S{c[1]}V{c[3]}" for c in CASES])
 def test_fused_matches_two_call_path_and_oracle(case, keep):

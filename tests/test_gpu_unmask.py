@@ -105,7 +105,14 @@ def test_exact_ties_inside_a_row_pick_lowest_index():
     assert gt[0].tolist() == [3, 9000, 8191, 0]
 
 
-@pytest.mark.parametrize("V,pad", [(1000, 0), (1003, 0), (8192, 4), (12345, 7), (1, 3)])
+def _random_vocab(seed, n):
+    """Seeded random vocabulary sizes and row paddings (the same every run)."""
+    g = np.random.default_rng(seed)
+    return [(int(g.integers(1, 200001)), int(g.integers(0, 17))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("V,pad", [(1000, 0), (1003, 0), (8192, 4), (12345, 7), (1, 3)]
+                         + _random_vocab(51, 5))
 def test_vocab_sizes_and_row_strides(V, pad):
     B, S = 2, 5
     base = synth.logits_normal(11 + V, B, S, V + pad, 2.0)
