@@ -82,6 +82,29 @@ def test_append_matches_the_oracle(dtype, D, page):
     assert run_both(c) == 0
 
 
+def _random_append(seed):
+    """A seeded random append within the documented limits: block sizes up to 128, both head
+    sizes, pages of 64 to 256 tokens, random lengths that leave room in each table, and a pool
+    whose free stack covers every sequence (so every append goes through)."""
+    g = np.random.default_rng(seed)
+    page = int(g.choice([64, 128, 192, 256]))
+    S = int(g.choice([1, 5, 16, 32, 100, 128]))
+    max_pages = int(g.integers(-(-S // page) + 1, 7))
+    B = int(g.integers(1, 7))
+    lens = [int(x) for x in g.integers(0, max_pages * page - S + 1, size=B)]
+    used = sum(-(-L // page) for L in lens)
+    need = sum(-(-(L + S) // page) - (-(-L // page)) for L in lens)
+    return dict(B=B, Hkv=int(g.integers(1, 4)), D=int(g.choice([64, 128])), S=S, page=page,
+                lens=lens, layers=int(g.integers(1, 4)), pool=used + need + int(g.integers(0, 4)),
+                max_pages=max_pages, dtype="bf16" if g.random() < 0.7 else "fp32")
+
+
+@pytest.mark.parametrize("seed", range(110, 118))
+def test_random_appends_match_the_oracle(seed):
+    c = setup_case(seed, **_random_append(seed))
+    assert run_both(c) == 0
+
+
 def test_append_flags_and_skips_like_the_oracle():
     # stack of 2 pages for 3 sequences that each need one; the last table is too short
     c = setup_case(70, B=4, Hkv=1, D=64, S=16, page=64, lens=[64, 64, 60, 120], layers=2,
