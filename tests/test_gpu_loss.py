@@ -38,12 +38,43 @@ def test_corruption_matches_the_oracle():
     assert masked[2, 5].item() == 0 and not masked[0].any()
 
 
+@pytest.mark.parametrize("seed", range(84, 88))
+def test_random_corruptions_match_the_oracle(seed):
+    """Seeded random batch and block sizes (up to 300 positions), vocabularies and mask ids."""
+    r = synth.rng(seed)
+    B, S, V = int(r.integers(1, 65)), int(r.integers(1, 301)), int(r.integers(2, 200001))
+    clean = r.integers(0, V - 1, (B, S)).astype(np.int32)
+    u_t = r.random(B).astype(np.float32)
+    u_m = r.random((B, S)).astype(np.float32)
+    d = lambda x: torch.from_numpy(x).to(DEV)
+    noisy, masked, t = tt.mask_corrupt(d(clean), d(u_t), d(u_m), mask_id=V - 1)
+    torch.cuda.synchronize()
+    rn, rm, rt = oloss.corrupt(clean, u_t, u_m, V - 1)
+    assert np.array_equal(noisy.cpu().numpy(), rn) and np.array_equal(masked.cpu().numpy(), rm)
+    assert np.array_equal(t.cpu().numpy(), rt)
+
+
 CASES = [  # B, S, V, ld, sigma, masked fraction
     (8, 16, 131072, 131072, 2.0, 0.5),
     (3, 5, 1004, 1010, 4.0, 0.7),        # ragged vocabulary, padded rows
     (2, 100, 8192, 8192, 1.0, 0.3),      # more than 64 positions
     (4, 16, 4096, 4096, 3.0, 0.0),       # nothing masked
 ]
+
+
+def _random_cases(seed, n):
+    """Seeded random cases (the same every run): batch, block size up to 300, vocabulary and row
+    padding, logit scale and masked fraction."""
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        V = int(g.integers(1, 60001))
+        out.append((int(g.integers(1, 9)), int(g.integers(1, 301)), V, V + int(g.integers(0, 9)),
+                    float(g.choice([0.5, 1.0, 2.0, 4.0])), float(g.choice([0.1, 0.5, 0.9, 1.0]))))
+    return out
+
+
+CASES += _random_cases(61, 5)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}S{c[1]}V{c[2]}" for c in CASES])
