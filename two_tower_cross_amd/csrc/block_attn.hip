@@ -32,6 +32,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "launch_util.hpp"
 
 namespace tt {
 
@@ -1337,16 +1338,14 @@ hipError_t launch_block_attn_bf16(const AttnParams &p, hipStream_t stream, hipEv
   if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess) return e;
   if (p.D == 128) {
     constexpr int lds = Geom<128>::LDS;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&block_attn_bf16_kernel<128>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    const hipError_t attr =
+        allow_dynamic_lds(reinterpret_cast<const void *>(&block_attn_bf16_kernel<128>), lds);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL(block_attn_bf16_kernel<128>, grid, dim3(kThreads), lds, stream, p);
   } else {
     constexpr int lds = Geom<64>::LDS;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&block_attn_bf16_kernel<64>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    const hipError_t attr =
+        allow_dynamic_lds(reinterpret_cast<const void *>(&block_attn_bf16_kernel<64>), lds);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL(block_attn_bf16_kernel<64>, grid, dim3(kThreads), lds, stream, p);
   }
@@ -1362,16 +1361,14 @@ hipError_t launch_block_attn_f32(const AttnParams &p, hipStream_t stream, hipEve
   if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess) return e;
   if (p.D == 128) {
     constexpr int lds = 256 * 128 * 4;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&block_attn_f32_kernel<128>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    const hipError_t attr =
+        allow_dynamic_lds(reinterpret_cast<const void *>(&block_attn_f32_kernel<128>), lds);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL(block_attn_f32_kernel<128>, grid, dim3(256), lds, stream, p);
   } else {
     constexpr int lds = 256 * 64 * 4;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&block_attn_f32_kernel<64>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    const hipError_t attr =
+        allow_dynamic_lds(reinterpret_cast<const void *>(&block_attn_f32_kernel<64>), lds);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL(block_attn_f32_kernel<64>, grid, dim3(256), lds, stream, p);
   }

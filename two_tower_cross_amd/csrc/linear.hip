@@ -28,6 +28,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "launch_util.hpp"
 #include "triple.hpp"
 
 namespace tt {
@@ -803,9 +804,8 @@ template <int NB>
 static hipError_t launch_tile(const LinearParams &p, hipStream_t stream, int cpz) {
   using T = LTile<NB>;
   dim3 grid((p.N + T::N - 1) / T::N, (p.M + kLM - 1) / kLM, p.ksplit);
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&linear_kernel<NB>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
+  const hipError_t attr =
+      allow_dynamic_lds(reinterpret_cast<const void *>(&linear_kernel<NB>), T::LDS);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(linear_kernel<NB>, grid, dim3(T::THREADS), T::LDS, stream, p, cpz);
   return hipGetLastError();
@@ -815,20 +815,11 @@ static hipError_t launch_tile(const LinearParams &p, hipStream_t stream, int cpz
 // over the 128-row blocks.
 static hipError_t launch_lm_unmask(const LinearParams &p, hipStream_t stream) {
   using T = LPair;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&lm_unmask_kernel),
-      hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
+  const hipError_t attr =
+      allow_dynamic_lds(reinterpret_cast<const void *>(&lm_unmask_kernel), T::LDS);
   if (attr != hipSuccess) return attr;
-  static int cu_count[64] = {};  // per device, queried once
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  int cus = dev < 64 ? cu_count[dev] : 0;
-  if (cus == 0) {
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    if (dev < 64) cu_count[dev] = cus;
-  }
+  const int cus = current_device_cus();
+  if (cus < 1) return hipErrorInvalidDevice;
   const int ntiles = (p.N + 255) / 256;
   const int rows = (p.M + kLM - 1) / kLM;
   const int G = std::max(1, std::min((ntiles + 1) / 2, cus / rows));
@@ -849,12 +840,13 @@ static bool tile_grid_resident(const LinearParams &p) {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
   std::lock_guard<std::mutex> lock(mu);
   if (cap[dev] == 0) {
-    int per_cu = 0, cus = 0;
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&linear_kernel<NB>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS) != hipSuccess ||
+    int per_cu = 0;
+    const int cus = current_device_cus();
+    if (cus < 1 ||
+        allow_dynamic_lds(reinterpret_cast<const void *>(&linear_kernel<NB>), T::LDS) !=
+            hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, linear_kernel<NB>, T::THREADS,
-                                                     T::LDS) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+                                                     T::LDS) != hipSuccess)
       return false;
     const int64_t c = (int64_t)per_cu * cus;
     cap[dev] = c > 0 ? c : -1;  // -1: not even one (never merged inside)
