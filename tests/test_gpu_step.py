@@ -207,6 +207,50 @@ def test_projections_on_two_streams_at_once():
             assert torch.equal(out, ref)
 
 
+def test_stages_from_several_host_threads_at_once():
+    """Four host threads, each with its own stream (and the binding's own workspaces), run QKV,
+    attention and the output projection concurrently (the ctypes calls release the interpreter
+    lock): the library's per-device caches are shared by all of them, and every thread's results
+    equal the same calls made from one thread, bit for bit."""
+    import threading
+    m = small_model(seed=9)
+    l = 0
+    hs = [m.h_steps[t] for t in range(4)]
+
+    def stages(h):
+        q, kb, vb = tt.qkv_projection(h, m.w_qkv[l], m.Hq, m.Hkv, m.D)
+        o = tt.block_attn(q, m.k_pages[l], m.v_pages[l], m.block_table, m.ctx_lens, kb, vb,
+                          max_ctx_len=m.L, out_dtype=torch.bfloat16)
+        return q, o, tt.out_projection(h, o, m.w_o[l])
+
+    refs = [stages(h) for h in hs]
+    torch.cuda.synchronize()
+    results, errors = [None] * len(hs), []
+    barrier = threading.Barrier(len(hs))
+
+    def worker(i):
+        try:
+            stream = torch.cuda.Stream()
+            barrier.wait()
+            with torch.cuda.stream(stream):
+                outs = [stages(hs[i]) for _ in range(3)]
+            stream.synchronize()
+            results[i] = outs
+        except Exception as e:  # reported below, in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(hs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    assert all(not t.is_alive() for t in threads)
+    for outs, ref in zip(results, refs):
+        for got in outs:
+            for a, b in zip(got, ref):
+                assert torch.equal(a, b)
+
 def test_projection_graph_replays_match_eager_calls():
     """Both projections captured in one graph (every replay of a captured product carries the same
     launch tag, so each finds the previous replay's complete arrival counts) and replayed several
