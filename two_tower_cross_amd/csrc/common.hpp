@@ -13,10 +13,6 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
-  return __uint_as_float(static_cast<uint32_t>(u) << 16);
-}
-
 // Round-to-nearest-even fp32 -> bf16 bit pattern (NaN kept quiet).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
@@ -84,11 +80,6 @@ __device__ __forceinline__ u32x4 ld_lds_16(const void *p) {
 }
 
 __device__ __forceinline__ void st_lds_16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
-
-// Value held by lane (lane ^ 32): the other half of the wave.
-__device__ __forceinline__ float swap_halves(float x) {
-  return __shfl_xor(x, 32, 64);
-}
 
 // max / sum of x over the lane pair (lane, lane ^ 32), in every lane, without LDS: one
 // v_permlane32_swap gives each lane both halves' values.
