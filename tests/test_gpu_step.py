@@ -575,6 +575,45 @@ def test_full_size_loop_32k_as_benchmarked():
     assert torch.equal(tok, tok_kept)
 
 
+def test_full_size_first_step_logits_and_decisions_against_oracle():
+    """First denoise step of the 32K loop at full size (8 sequences x 16 positions, vocabulary
+    131072): every logit against the oracle's lm-head on the step's final residual stream, every
+    row's confidence against the oracle on the step's own fp32 logits, and the commit decisions.
+    A random model's confidences are all far below the threshold, so each sequence commits its
+    most confident position (the fallback); the token is the row's first argmax over the same
+    fp32 logits on both sides, hence exact. Where a sequence's top two confidences are closer than
+    1e-4 (relative) the fp32 and fp64 sums may order them differently: the commit must then be
+    one of those positions."""
+    m = loop_model(5, device=DEV)
+    step = make_step(m, keep_logits=True)
+    masked = torch.ones((m.B, m.S), dtype=torch.uint8, device=DEV)
+    tokens = torch.full((m.B, m.S), -1, dtype=torch.int32, device=DEV)
+    m0, t0 = masked.cpu().numpy(), tokens.cpu().numpy()
+    conf, n = step(m.h_steps[0], masked, tokens, threshold=0.9, min_commit=True)
+    torch.cuda.synchronize()
+    logits = step.logits.cpu().numpy()
+    assert logits.shape == (m.B, m.S, m.vocab)
+    ref = ostep.lm_head(f64(step.h_work), f64(m.w_lm))
+    assert max_abs(logits, ref) <= 1e-4 + 1e-5 * np.abs(ref).max()
+    del ref
+    ot, om, oc, on = ounmask.confidence_unmask(logits, m0, t0, np.float32(0.9), min_commit=True)
+    gc = conf.cpu().numpy().astype(np.float64)
+    assert np.all(oc < 0.5)                                # far below the threshold
+    np.testing.assert_allclose(gc, oc, rtol=1e-5, atol=0)
+    gm, gt, gn = masked.cpu().numpy(), tokens.cpu().numpy(), n.cpu().numpy()
+    assert (gn == 1).all() and np.array_equal(gn, on)
+    first_argmax = logits.argmax(axis=2)
+    for b in range(m.B):
+        (i,) = np.flatnonzero(gm[b] == 0)                  # exactly one commit
+        assert gt[b, i] == first_argmax[b, i]
+        assert (gt[b, gm[b] == 1] == -1).all()             # the rest untouched
+        c = np.sort(oc[b])[::-1]
+        if c[0] - c[1] >= 1e-4 * c[0]:
+            assert np.array_equal(gm[b], om[b]) and np.array_equal(gt[b], ot[b])
+        else:
+            assert oc[b, i] >= c[0] * (1 - 1e-4)
+
+
 @pytest.mark.parametrize("S", [32, 128])
 def test_block_sizes_of_the_pages(S):
     """The block sizes the pages train and sample with besides 16 (32 in training, 128 at
