@@ -86,6 +86,36 @@ def test_attention_workspace_query_and_plan():
     assert st == _lib.TT_OK and n == 0
 
 
+def ws_bytes(slots, rows, batch):
+    up = lambda x: -(-x // 256) * 256
+    return up(slots * rows * 128 * 2) + up(slots * rows * 8) + up(batch * 2 * 4)
+
+
+def test_attention_short_partitions_use_128_row_groups():
+    # one sequence of 131072 tokens: at 256 query rows the automatic plan would cut each KV head's
+    # 2048 tiles into 128 partitions of 16 tiles (< 24), so the rows go into two groups of 128 and
+    # every (KV head, row group) gets 64 partitions of 32 tiles: 2 x 2 x 64 slots of 128 rows
+    a = attn_args(batch=1, page_size=131072, max_ctx_len=131072)
+    st, n = query("twotower_block_attn", a)
+    assert st == _lib.TT_OK and n == ws_bytes(2 * 2 * 64, 128, 1)
+    # an explicit partition count keeps one group of 256 rows
+    st, n = query("twotower_block_attn", attn_args(batch=1, page_size=131072, max_ctx_len=131072,
+                                                   num_splits=128))
+    assert st == _lib.TT_OK
+    up = lambda x: -(-x // 256) * 256
+    assert n == up(2 * 128 * 256 * 128 * 2) + up(2 * 128 * 256 * 8)
+    # 4096 tokens: 64 tiles per KV head, one tile per partition either way
+    st, n = query("twotower_block_attn", attn_args(batch=1, page_size=4096, max_ctx_len=4096))
+    assert st == _lib.TT_OK and n == ws_bytes(2 * 2 * 64, 128, 1)
+    # the 32K loop (32 tiles per partition) keeps 256 rows: the workspace pinned above
+    st, n = query("twotower_block_attn", attn_args())
+    assert st == _lib.TT_OK and n == ws_bytes(8 * 2 * 16, 256, 8)
+    # 128 rows or fewer (G * S <= 128) are one group already
+    st, n = query("twotower_block_attn", attn_args(batch=1, num_q_heads=16, page_size=131072,
+                                                   max_ctx_len=131072))
+    assert st == _lib.TT_OK and n == ws_bytes(2 * 128, 128, 1)
+
+
 def test_attention_workspace_too_small_reports_size():
     a = attn_args()
     st, need = query("twotower_block_attn", a)

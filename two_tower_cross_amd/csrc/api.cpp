@@ -21,6 +21,8 @@ constexpr int kMinChunk = 256;          // context tokens per partition, lower b
 constexpr int kMaxPartitionTiles = 4096;  // 64-token tile indices one attention work-group stages in LDS
 constexpr int kMinPartTiles = 1;          // the balanced plan's smallest partition (64 tokens)
 constexpr int kPlanMaxB = 256;            // sequences the balanced plan handles
+constexpr int kHalfGroupRows = 128;       // query rows per work-group when partitions are short
+constexpr int kHalfGroupBelowTiles = 24;  // ... i.e. below this many 64-token tiles at 256 rows
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -130,7 +132,7 @@ tt_status plan_attn(const tt_block_attn_args *a, bool check_pointers, AttnPlan *
   p.rows_per_group = std::min(rows_pad, 256);
   p.row_groups = (int)cdiv(rows_pad, p.rows_per_group);
   const int64_t t_max = cdiv(a->max_ctx_len, 64);
-  const int64_t groups = (int64_t)p.Hkv * p.row_groups;
+  int64_t groups = (int64_t)p.Hkv * p.row_groups;
   if (!out->use_bf16 || a->max_ctx_len == 0) {
     p.splits = 1;
     p.chunk = std::max(64, (int)cdiv(std::max(a->max_ctx_len, 1), 64) * 64);
@@ -139,8 +141,21 @@ tt_status plan_attn(const tt_block_attn_args *a, bool check_pointers, AttnPlan *
     // Balanced plan: the kernels size the partitions from the actual lengths; here the case of
     // every sequence at max_ctx_len (the same search as on the device) gives the speculative
     // split, and the bounds give the grid and the workspace.
-    const int64_t parts = std::max<int64_t>(1, kTargetWorkgroups / groups);
-    const int64_t c = balanced_tiles(p.B, t_max, parts);
+    int64_t parts = std::max<int64_t>(1, kTargetWorkgroups / groups);
+    int64_t c = balanced_tiles(p.B, t_max, parts);
+    if (p.row_groups == 1 && rows_pad > kHalfGroupRows && c < kHalfGroupBelowTiles) {
+      // Short partitions: the query rows go into groups of 128 (one active wave per SIMD), so
+      // each work-group walks twice the tiles for half the rows and the split-KV partials and
+      // their merge halve, which outweighs the slower half-height tiles below about 24 tiles
+      // per partition (131072-token context, batch 1: 54.5 against 57.7 us per call; 4K
+      // context: 21.7 against 23.6 us; the 32K loop at 32 tiles per partition is faster with
+      // 256 rows: 80.0 against 84.4 us).
+      p.rows_per_group = kHalfGroupRows;
+      p.row_groups = (int)cdiv(rows_pad, kHalfGroupRows);
+      groups = (int64_t)p.Hkv * p.row_groups;
+      parts = std::max<int64_t>(1, kTargetWorkgroups / groups);
+      c = balanced_tiles(p.B, t_max, parts);
+    }
     p.balanced = 1;
     p.parts = (int)parts;
     p.splits = (int)std::max<int64_t>(1, cdiv(t_max, c));
